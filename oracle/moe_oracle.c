@@ -1,0 +1,357 @@
+/*
+ * moe_oracle.c -- plain, slow CPU reference for MoE token dispatch and combine.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing in the product path may link, load or call
+ * this file: only the tests, the smoke check and the CPU-baseline leg of the
+ * benchmark use it. It shares no source, header, table or helper with the HIP
+ * library; the two only ever see the same seeded inputs.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fPIC -shared (no fast-math). Every fused
+ * multiply-add is written out as fmaf(); nothing else may be contracted.
+ *
+ * What it follows (the pages):
+ *  [P1] CANN SHMEM examples, "双平面 MoE Combine 示例" (combine_doubleplane
+ *       README): section 功能说明 defines the dispatch outputs expand_x,
+ *       assist_info_for_combine ([src_rank_id, src_token_id, src_topk_id] per
+ *       expert-output row), ep_recv_count (cumulative count per
+ *       (local_expert_id, src_rank_id) segment), and the check formula
+ *       x_out[token] = sum_k topk_output[token,k] * expert_scales[token,k];
+ *       section 方案设计 defines the large-segment predicate; section 实现逻辑
+ *       describes the push-style return and the weighted sum on the source.
+ *  [P3] CANN 9.1.0-beta.3 API reference, "aclnnMoeDistributeDispatchV4":
+ *       接口功能 / 计算公式 (optional quantisation, then expandXOut =
+ *       AllToAllV(X)), the quantMode list (2 = per-token dynamic
+ *       quantisation, dynamicScalesOut only in that mode), and 约束说明
+ *       (deterministic by default).
+ *
+ * Readings taken where the pages leave a step open (each one is also listed in
+ * the design notes):
+ *  - expert e lives on rank r = e / epr as local expert el = e % epr;
+ *  - src_token_id is the token index inside its source rank, tok in [0, bs);
+ *  - a rank's segments are ordered local-expert-major, source-rank-minor
+ *    (index el*W + s), which matches the (epWorldSize*localExpertNum,) shape
+ *    of epRecvCountsOut in [P3];
+ *  - "cumulative" means an inclusive prefix sum over that index;
+ *  - rows inside one segment are in ascending src_token order;
+ *  - the emulated per-rank windows are packed back to back, rank 0 first,
+ *    so expand_x holds exactly N*K rows;
+ *  - quantMode 2: scale = max|x| / 127 in fp32, q = rint(x / scale) with
+ *    ties to even, clamped to [-127, 127]; an all-zero token gets scale 0 and
+ *    q = 0; one scale per expand_x row;
+ *  - combine accumulates in fp32 with one fused multiply-add per k, k
+ *    ascending from 0.0f, and rounds once (to nearest even) to the output
+ *    type; int32 data combine in wrapping 32-bit integer arithmetic.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_INT32 = 0, OR_FP16 = 1, OR_BF16 = 2 };
+enum { OR_OK = 0, OR_BAD_ARG = -1, OR_BAD_ID = -2, OR_DUP_ID = -3, OR_BAD_ASSIST = -4 };
+
+/* ------------------------------------------------------------------------ */
+/* Scalar type conversions, written from the IEEE 754 binary16 and bfloat16  */
+/* definitions (sign, biased exponent, fraction).                            */
+/* ------------------------------------------------------------------------ */
+
+static uint32_t f32_bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
+static float bits_f32(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. */
+float oracle_f16_to_f32(uint16_t v)
+{
+    int sign = (v >> 15) & 1;
+    int expo = (v >> 10) & 0x1f;
+    int frac = v & 0x3ff;
+    float mag;
+    if (expo == 0)
+        mag = ldexpf((float)frac, -24);                 /* subnormal: frac * 2^-24 */
+    else if (expo == 31)
+        mag = frac ? NAN : INFINITY;
+    else
+        mag = ldexpf((float)(1024 + frac), expo - 25);  /* (1 + frac/1024) * 2^(expo-15) */
+    return sign ? -mag : mag;
+}
+
+/* Round a float to the nearest binary16 value, ties to even. The quantum
+ * (spacing of representable values) is 2^-24 below 2^-14 and 2^(E-10) for a
+ * value in [2^E, 2^(E+1)); the value divided by its quantum is rounded to an
+ * integer with rint (ties to even), which is exact because both are powers of
+ * two apart. Anything that rounds to 2^16 or above is infinite. */
+uint16_t oracle_f32_to_f16(float f)
+{
+    uint16_t sign = (f32_bits(f) >> 31) ? 0x8000 : 0;
+    float a = fabsf(f);
+    if (isnan(f))
+        return sign | 0x7e00;
+    if (a == 0.0f)
+        return sign;
+    if (a < ldexpf(1.0f, -14)) {                       /* subnormal range */
+        float n = rintf(a / ldexpf(1.0f, -24));        /* 0..1024 */
+        return sign | (uint16_t)n;                     /* 1024 encodes 2^-14 exactly */
+    }
+    int e2;
+    frexpf(a, &e2);                                    /* a = m * 2^e2, m in [0.5,1) */
+    int E = e2 - 1;                                    /* a in [2^E, 2^(E+1)) */
+    float n = rintf(ldexpf(a, 10 - E));                /* in [1024, 2048] */
+    if (n == 2048.0f) { n = 1024.0f; E += 1; }
+    if (E + 15 >= 31)
+        return sign | 0x7c00;
+    return sign | (uint16_t)((E + 15) << 10) | (uint16_t)((int)n - 1024);
+}
+
+/* bfloat16 is the top half of a binary32. */
+float oracle_bf16_to_f32(uint16_t v) { return bits_f32((uint32_t)v << 16); }
+
+/* Keep the upper 16 bits of the binary32 encoding and round on the lower 16:
+ * above half rounds up, below half down, exactly half to the even neighbour.
+ * A carry out of the fraction moves into the exponent, which is the correct
+ * next value (and reaches infinity past the largest finite bfloat16). */
+uint16_t oracle_f32_to_bf16(float f)
+{
+    uint32_t u = f32_bits(f);
+    if (isnan(f))
+        return (uint16_t)((u >> 16) | 0x0040);
+    uint32_t hi = u >> 16, lo = u & 0xffff;
+    if (lo > 0x8000 || (lo == 0x8000 && (hi & 1)))
+        hi += 1;
+    return (uint16_t)hi;
+}
+
+static float load_f32(const void *base, size_t i, int dtype)
+{
+    const uint16_t *p = (const uint16_t *)base;
+    return dtype == OR_FP16 ? oracle_f16_to_f32(p[i]) : oracle_bf16_to_f32(p[i]);
+}
+
+static uint16_t store_16(float v, int dtype)
+{
+    return dtype == OR_FP16 ? oracle_f32_to_f16(v) : oracle_f32_to_bf16(v);
+}
+
+static size_t elem_size(int dtype) { return dtype == OR_INT32 ? 4 : 2; }
+
+/* ------------------------------------------------------------------------ */
+/* Dispatch                                                                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * x            [W*bs, h] dtype           tokens, source rank s owns rows s*bs..s*bs+bs-1
+ * ids          [W*bs, K] int32           global expert ids, distinct per token
+ * expand_x     [W*bs*K, h]               dtype, or int8 when quant == 2
+ * dyn_scales   [W*bs*K] fp32             written only when quant == 2
+ * assist       [W*bs*K, 3] int32         (src_rank, src_token, topk_id) per row
+ * ep_recv_count[W, epr*W] int32          inclusive per-rank segment counts
+ * expand_scales[W*bs*K] fp32|int32|NULL  expert_scales[t,k] moved to row(t,k)
+ *
+ * The steps are the plain counting sort by expert that the all-to-all of
+ * [P3] 计算公式 amounts to when every rank's window sits in one memory.
+ */
+int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales,
+                    int W, int bs, int epr, int h, int K, int dtype, int quant,
+                    void *expand_x, float *dyn_scales, int32_t *assist,
+                    int32_t *ep_recv_count, void *expand_scales)
+{
+    if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
+    if (quant != 0 && quant != 2) return OR_BAD_ARG;
+    if (quant == 2 && dtype == OR_INT32) return OR_BAD_ARG;
+    const long long E = (long long)W * epr, N = (long long)W * bs, S = (long long)epr * W;
+    if (K > E) return OR_BAD_ARG;
+
+    /* Step 1: count the (token, k) pairs of every segment (r, el*W + s). */
+    long long *cnt = calloc((size_t)(W * S), sizeof(long long));
+    if (!cnt) return OR_BAD_ARG;
+    for (long long t = 0; t < N; ++t) {
+        for (int k = 0; k < K; ++k) {
+            int32_t e = ids[t * K + k];
+            if (e < 0 || e >= E) { free(cnt); return OR_BAD_ID; }
+            for (int j = 0; j < k; ++j)
+                if (ids[t * K + j] == e) { free(cnt); return OR_DUP_ID; }
+            long long r = e / epr, el = e % epr, s = t / bs;
+            cnt[r * S + el * W + s] += 1;
+        }
+    }
+
+    /* Step 2: inclusive prefix per rank -> ep_recv_count; window base B_r. */
+    long long *base = malloc((size_t)W * sizeof(long long));
+    long long running = 0;
+    for (long long r = 0; r < W; ++r) {
+        base[r] = running;
+        long long c = 0;
+        for (long long i = 0; i < S; ++i) {
+            c += cnt[r * S + i];
+            ep_recv_count[r * S + i] = (int32_t)c;
+        }
+        running += c;
+    }
+
+    /* Steps 3-6: walk tokens in order; each pair takes the next free row of
+     * its segment, so rows inside a segment come out in ascending src_token. */
+    long long *fill = calloc((size_t)(W * S), sizeof(long long));
+    const size_t xs = elem_size(dtype);
+    for (long long t = 0; t < N; ++t) {
+        long long s = t / bs, tok = t % bs;
+        float scale = 0.0f;
+        if (quant == 2) {
+            float amax = 0.0f;
+            for (int j = 0; j < h; ++j) {
+                float v = fabsf(load_f32(x, (size_t)(t * h + j), dtype));
+                if (v > amax) amax = v;
+            }
+            scale = amax / 127.0f;
+        }
+        for (int k = 0; k < K; ++k) {
+            int32_t e = ids[t * K + k];
+            long long r = e / epr, el = e % epr, i = el * W + s;
+            long long start = i == 0 ? 0 : ep_recv_count[r * S + i - 1];
+            long long row = base[r] + start + fill[r * S + i];
+            fill[r * S + i] += 1;
+
+            assist[row * 3 + 0] = (int32_t)s;
+            assist[row * 3 + 1] = (int32_t)tok;
+            assist[row * 3 + 2] = k;
+
+            if (expand_scales)   /* fp32 and int32 scales are both 4-byte words */
+                memcpy((char *)expand_scales + row * 4, (const char *)expert_scales + (t * K + k) * 4, 4);
+
+            if (quant == 0) {
+                memcpy((char *)expand_x + (size_t)row * h * xs, (const char *)x + (size_t)t * h * xs,
+                       (size_t)h * xs);
+            } else {
+                int8_t *q = (int8_t *)expand_x + (size_t)row * h;
+                for (int j = 0; j < h; ++j) {
+                    float v = load_f32(x, (size_t)(t * h + j), dtype);
+                    float n = scale == 0.0f ? 0.0f : rintf(v / scale);
+                    if (n > 127.0f) n = 127.0f;
+                    if (n < -127.0f) n = -127.0f;
+                    q[j] = (int8_t)n;
+                }
+                dyn_scales[row] = scale;
+            }
+        }
+    }
+    free(fill);
+    free(base);
+    free(cnt);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Combine                                                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Push-style, as [P1] 实现逻辑 describes it: every expert-output row is
+ * returned to slot (src_token, topk_id) of its source rank's window; the
+ * source then forms, per token, the weighted sum of its K returned rows
+ * ([P1] 功能说明, check formula).
+ *
+ * expand_x [rows, h] dtype (fp16/bf16/int32), scales [W*bs, K] fp32 (int32 for
+ * int32 data), x_out [W*bs, h] dtype. The row's segment (hence its expert) is
+ * recovered from ep_recv_count and must equal ids[t,k]; every (t,k) slot
+ * must be filled exactly once.
+ */
+int oracle_combine(const void *expand_x, const int32_t *assist, const int32_t *ep_recv_count,
+                   const int32_t *ids, const void *scales, int W, int bs, int epr, int h, int K,
+                   int dtype, void *x_out)
+{
+    if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
+    const long long N = (long long)W * bs, S = (long long)epr * W;
+
+    long long rows = 0;
+    for (long long r = 0; r < W; ++r) rows += ep_recv_count[r * S + S - 1];
+    if (rows != N * K) return OR_BAD_ASSIST;
+
+    /* The source rank's window: slot[t*K + k] = index of the returned row. */
+    long long *slot = malloc((size_t)(N * K > 0 ? N * K : 1) * sizeof(long long));
+    for (long long i = 0; i < N * K; ++i) slot[i] = -1;
+
+    long long row = 0;
+    for (long long r = 0; r < W; ++r) {
+        long long prev = 0;
+        for (long long i = 0; i < S; ++i) {
+            long long end = ep_recv_count[r * S + i];
+            long long e = r * epr + i / W;          /* segment index = el*W + s */
+            for (long long c = prev; c < end; ++c, ++row) {
+                long long s = assist[row * 3 + 0], tok = assist[row * 3 + 1], k = assist[row * 3 + 2];
+                if (s != i % W || tok < 0 || tok >= bs || k < 0 || k >= K) { free(slot); return OR_BAD_ASSIST; }
+                long long t = s * bs + tok;
+                if (ids[t * K + k] != e || slot[t * K + k] != -1) { free(slot); return OR_BAD_ASSIST; }
+                slot[t * K + k] = row;
+            }
+            prev = end;
+        }
+    }
+
+    for (long long t = 0; t < N; ++t) {
+        for (int j = 0; j < h; ++j) {
+            if (dtype == OR_INT32) {
+                uint32_t acc = 0;
+                for (int k = 0; k < K; ++k) {
+                    const int32_t *y = (const int32_t *)expand_x + (size_t)slot[t * K + k] * h;
+                    int32_t sc = ((const int32_t *)scales)[t * K + k];
+                    acc += (uint32_t)y[j] * (uint32_t)sc;
+                }
+                ((int32_t *)x_out)[t * h + j] = (int32_t)acc;
+            } else {
+                float acc = 0.0f;
+                for (int k = 0; k < K; ++k) {
+                    float y = load_f32(expand_x, (size_t)slot[t * K + k] * h + j, dtype);
+                    float sc = ((const float *)scales)[t * K + k];
+                    acc = fmaf(y, sc, acc);
+                }
+                ((uint16_t *)x_out)[t * h + j] = store_16(acc, dtype);
+            }
+        }
+    }
+    free(slot);
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Large-segment predicate ([P1] 方案设计)                                   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * For every segment (el, s) of every rank r, flag[r*S + el*W + s] = 1 when
+ *   s != r, the segment is non-empty, its payload bytes are at least
+ *   threshold_bytes, and its payload bytes exceed the mean payload of rank r's
+ *   remote segments. The mean is compared by cross-multiplication, with
+ *   num = (rows r receives from other ranks) * h * elem_bytes and
+ *   den = max(W - 1, 1) * epr, all in 64-bit integers.
+ */
+int oracle_large_segments(const int32_t *ep_recv_count, int W, int epr, int h, int elem_bytes,
+                          long long threshold_bytes, uint8_t *flag)
+{
+    const long long S = (long long)epr * W;
+    for (long long r = 0; r < W; ++r) {
+        long long remote = 0;
+        for (long long i = 0; i < S; ++i) {
+            long long c = ep_recv_count[r * S + i] - (i ? ep_recv_count[r * S + i - 1] : 0);
+            if (i % W != r) remote += c;
+        }
+        long long num = remote * h * elem_bytes;
+        long long den = (long long)(W - 1 > 1 ? W - 1 : 1) * epr;
+        for (long long i = 0; i < S; ++i) {
+            long long c = ep_recv_count[r * S + i] - (i ? ep_recv_count[r * S + i - 1] : 0);
+            long long bytes = c * h * elem_bytes;
+            flag[r * S + i] = (i % W != r) && c > 0 && bytes >= threshold_bytes && bytes * den > num;
+        }
+    }
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Identity expert for int8 rows (harness, not part of the method)           */
+/* ------------------------------------------------------------------------ */
+
+/* y[i, j] = bf16(f32(q[i, j]) * scale[i]): what an identity expert hands to
+ * combine when dispatch quantised its input; one fp32 product, one rounding. */
+void oracle_identity_expert_dequant(const int8_t *q, const float *scale, long long rows, int h,
+                                    uint16_t *y)
+{
+    for (long long i = 0; i < rows; ++i)
+        for (int j = 0; j < h; ++j)
+            y[i * h + j] = oracle_f32_to_bf16((float)q[i * h + j] * scale[i]);
+}

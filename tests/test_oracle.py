@@ -1,0 +1,442 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+* hand-worked fixtures under tests/golden/ (each cites the page it follows);
+* brute-force definitions (segment counts by direct counting, every routing
+  of a tiny problem);
+* a library routine the result must reduce to (numpy's stable argsort gives
+  the expand_x row order; numpy / torch give IEEE binary16 / bfloat16 casts);
+* closed forms (identity expert: x_out = x * sum_k s for int32, x_out == x for
+  softmax weights), invariants (assist_info is a bijection, counts sum to N*K),
+  error bounds (quantisation and the fp32 accumulation), and exact rational
+  arithmetic for the large-segment predicate.
+"""
+import itertools
+import json
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _run(w, inp=None):
+    inp = inp or wl.make_inputs(w)
+    d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
+                        expert_scales=inp["scales"], bf16=(w.dtype == "bf16"))
+    return inp, d
+
+
+SMALL = [w for w in wl.WORKLOADS if w.h <= 16] + [
+    wl.custom(3, 5, 7, 3, 2, "int32", name="w3_ragged"),
+    wl.custom(4, 9, 24, 4, 3, "fp16", "gauss_topk", name="w4_fp16"),
+    wl.custom(2, 17, 40, 2, 4, "bf16", "zipf_topk", quant_mode=2, name="w2_bf16_q"),
+]
+ALL = SMALL + [w for w in wl.WORKLOADS if w.h > 16]
+
+
+# --------------------------------------------------------------------------
+# hand-worked fixtures
+# --------------------------------------------------------------------------
+
+def test_golden_dispatch_combine_int32():
+    g = _golden("dispatch_combine_int32_w2.json")
+    x = np.array(g["x"], np.int32)
+    ids = np.array(g["expert_ids"], np.int32)
+    sc = np.array(g["expert_scales"], np.int32)
+    d = oracle.dispatch(x, ids, g["ep_world"], g["experts_per_rank"])
+    assert d["expand_x"].tolist() == g["expand_x"]
+    assert d["assist_info"].tolist() == g["assist_info"]
+    assert d["ep_recv_count"].tolist() == g["ep_recv_count"]
+    y = np.array(g["expert_out"], np.int32)
+    out = oracle.combine(y, d["assist_info"], d["ep_recv_count"], ids, sc, g["ep_world"],
+                         g["experts_per_rank"])
+    assert out.tolist() == g["x_out_expert_out"]
+    out = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], ids, sc,
+                         g["ep_world"], g["experts_per_rank"])
+    assert out.tolist() == g["x_out_identity"]
+
+
+def test_golden_quant_ties_to_even():
+    g = _golden("quant_fp16_ties.json")
+    x = np.array(g["x"], np.float32).astype(np.float16)
+    ids = np.array(g["expert_ids"], np.int32)
+    d = oracle.dispatch(x, ids, g["ep_world"], g["experts_per_rank"], quant_mode=2)
+    assert d["expand_x"].tolist() == g["expand_x"]
+    assert d["dynamic_scales"].tolist() == g["dynamic_scales"]
+    assert d["assist_info"].tolist() == g["assist_info"]
+    assert d["ep_recv_count"].tolist() == g["ep_recv_count"]
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_golden_combine_final_rounding(dtype):
+    g = _golden("combine_rounding.json")
+    sub = g[dtype]
+    y32 = np.array(sub["expert_out"], np.float32)
+    y = y32.astype(np.float16) if dtype == "fp16" else wl.f32_to_bf16_bits(y32)
+    ids = np.array(g["expert_ids"], np.int32)
+    sc = np.array(g["expert_scales"], np.float32)
+    out = oracle.combine(y, np.array(g["assist_info"], np.int32), np.array(g["ep_recv_count"], np.int32),
+                         ids, sc, g["ep_world"], g["experts_per_rank"], bf16=(dtype == "bf16"))
+    want32 = np.array(sub["x_out"], np.float32)
+    want = want32.astype(np.float16) if dtype == "fp16" else wl.f32_to_bf16_bits(want32)
+    assert out.view(np.uint16).tolist() == want.view(np.uint16).tolist()
+
+
+# --------------------------------------------------------------------------
+# counts, layout, assist_info
+# --------------------------------------------------------------------------
+
+def _brute_counts(ids, W, bs, epr):
+    """cnt[r][el*W+s] = number of tokens of source rank s routed to expert r*epr+el."""
+    E = W * epr
+    cnt = np.zeros((W, epr * W), np.int64)
+    for s in range(W):
+        for e in range(E):
+            n = sum(1 for tok in range(bs) if e in set(ids[s * bs + tok].tolist()))
+            cnt[e // epr, (e % epr) * W + s] = n
+    return cnt
+
+
+@pytest.mark.parametrize("w", ALL, ids=lambda w: w.name)
+def test_counts_match_direct_count(w):
+    inp, d = _run(w)
+    erc = d["ep_recv_count"].astype(np.int64)
+    cnt = _brute_counts(inp["ids"], w.ep_world, w.bs, w.experts_per_rank)
+    assert (erc == np.cumsum(cnt, axis=1)).all()
+    assert erc[:, -1].sum() == w.num_tokens * w.topk
+    assert (np.diff(erc, axis=1) >= 0).all() and (erc[:, :1] >= 0).all()
+    assert cnt.max() <= w.bs
+
+
+@pytest.mark.parametrize("w", ALL, ids=lambda w: w.name)
+def test_row_order_is_stable_argsort_by_expert(w):
+    inp, d = _run(w)
+    a = d["assist_info"].astype(np.int64)
+    pair = (a[:, 0] * w.bs + a[:, 1]) * w.topk + a[:, 2]
+    assert (pair == np.argsort(inp["ids"].ravel(), kind="stable")).all()
+
+
+@pytest.mark.parametrize("w", ALL, ids=lambda w: w.name)
+def test_assist_info_is_a_bijection_onto_pairs(w):
+    inp, d = _run(w)
+    a = d["assist_info"]
+    W, bs, K, epr = w.ep_world, w.bs, w.topk, w.experts_per_rank
+    assert ((a[:, 0] >= 0) & (a[:, 0] < W) & (a[:, 1] >= 0) & (a[:, 1] < bs) & (a[:, 2] >= 0) & (a[:, 2] < K)).all()
+    pair = (a[:, 0].astype(np.int64) * bs + a[:, 1]) * K + a[:, 2]
+    assert len(set(pair.tolist())) == w.rows == len(pair)
+    # every row sits in the segment of its pair's expert and source; src_token ascends inside a segment
+    erc = d["ep_recv_count"]
+    row = 0
+    for r in range(W):
+        prev = 0
+        for i in range(epr * W):
+            e, s = r * epr + i // W, i % W
+            seg = a[row:row + erc[r, i] - prev]
+            assert (seg[:, 0] == s).all()
+            assert (inp["ids"][s * bs + seg[:, 1], seg[:, 2]] == e).all()
+            assert (np.diff(seg[:, 1]) > 0).all()
+            row += erc[r, i] - prev
+            prev = erc[r, i]
+    assert row == w.rows
+
+
+@pytest.mark.parametrize("w", [w for w in ALL if w.quant_mode == 0], ids=lambda w: w.name)
+def test_expand_x_rows_are_source_tokens_bitwise(w):
+    inp, d = _run(w)
+    a = d["assist_info"].astype(np.int64)
+    t = a[:, 0] * w.bs + a[:, 1]
+    assert d["expand_x"].view(np.uint8).tobytes() == inp["x"][t].view(np.uint8).tobytes()
+    assert (d["expand_scales"] == inp["scales"][t, a[:, 2]]).all()
+
+
+# --------------------------------------------------------------------------
+# quantisation
+# --------------------------------------------------------------------------
+
+def _token_f32(w, x):
+    if w.dtype == "bf16":
+        return (x.astype(np.uint32) << 16).view(np.float32)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("w", [w for w in ALL if w.quant_mode == 2], ids=lambda w: w.name)
+def test_quant_bounds_and_ties(w):
+    inp, d = _run(w)
+    a = d["assist_info"].astype(np.int64)
+    t = a[:, 0] * w.bs + a[:, 1]
+    xf = _token_f32(w, inp["x"])[t].astype(np.float64)
+    q = d["expand_x"].astype(np.float64)
+    sc = d["dynamic_scales"].astype(np.float64)
+    amax = np.abs(xf).max(axis=1)
+    # the scale is the fp32 quotient amax/127 (relative error at most 2^-24)
+    assert (np.abs(sc * 127 - amax) <= amax * 2.0 ** -23).all()
+    nz = amax > 0
+    assert (np.abs(q[nz]).max(axis=1) == 127).all()
+    assert (q[~nz] == 0).all() and (sc[~nz] == 0).all()
+    # q is a nearest integer of x/scale: |x/scale - q| <= 1/2 up to the fp32 quotient's rounding
+    ratio = xf[nz] / sc[nz, None]
+    assert (np.abs(ratio - q[nz]) <= 0.5 + 1e-5 * np.maximum(1.0, np.abs(ratio))).all()
+    assert (np.abs(q) <= 127).all()
+
+
+def test_quant_is_odd_and_ties_go_to_even():
+    # A token and its negation quantise to negated codes with the same scale; a
+    # value whose quotient is an exact half goes to the even neighbour.
+    w = wl.custom(2, 4, 64, 1, 1, "fp16", name="odd")
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((8, 64)).astype(np.float16)
+    # token 0: amax 127 (scale 1.0) and halves in between
+    x[0, :8] = np.array([127, 0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 3.5], np.float16)
+    x[4:] = -x[:4]
+    ids = np.zeros((8, 1), np.int32)
+    ids[4:] = 1
+    d = oracle.dispatch(x, ids, 2, 1, quant_mode=2)
+    a = d["assist_info"].astype(np.int64)
+    t = a[:, 0] * 4 + a[:, 1]
+    q = np.empty_like(d["expand_x"])
+    q[t] = d["expand_x"]
+    scl = np.empty_like(d["dynamic_scales"])
+    scl[t] = d["dynamic_scales"]
+    assert (q[4:] == -q[:4]).all() and (scl[4:] == scl[:4]).all()
+    assert q[0, :8].tolist() == [127, 0, 2, 2, 0, -2, -2, 4]
+    assert scl[0] == 1.0
+    del w
+
+
+# --------------------------------------------------------------------------
+# combine
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", [w for w in ALL if w.dtype == "int32"], ids=lambda w: w.name)
+def test_combine_int32_identity_closed_form(w):
+    inp, d = _run(w)
+    out = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"],
+                         w.ep_world, w.experts_per_rank)
+    want = inp["x"].astype(np.int64) * inp["scales"].astype(np.int64).sum(axis=1, keepdims=True)
+    assert (out.astype(np.int64) == want).all()
+
+
+@pytest.mark.parametrize("w", [w for w in ALL if w.dtype != "int32" and w.routing != "uniform_distinct"],
+                         ids=lambda w: w.name)
+def test_combine_identity_softmax_closed_form(w):
+    """Identity expert + softmax weights: sum_k x * s_k rounds back to x exactly."""
+    inp, d = _run(w)
+    bf = w.dtype == "bf16"
+    y = oracle.identity_expert(d["expand_x"], d["dynamic_scales"])
+    out = oracle.combine(y, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"],
+                         w.ep_world, w.experts_per_rank, bf16=bf)
+    if w.quant_mode == 0:
+        assert out.view(np.uint16).tobytes() == inp["x"].view(np.uint16).tobytes()
+    else:
+        # every row of token t carries the same dequantised vector, so x_out[t] is that vector
+        a = d["assist_info"].astype(np.int64)
+        t = a[:, 0] * w.bs + a[:, 1]
+        per_token = np.zeros_like(out.view(np.uint16))
+        per_token[t] = y
+        assert (out.view(np.uint16) == per_token).all()
+
+
+def _exact_sum(yf, sc):
+    return sum(Fraction(float(a)) * Fraction(float(b)) for a, b in zip(yf, sc))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_combine_random_rows_within_error_bound(dtype):
+    """Random expert outputs and weights: x_out is within half an output ulp
+    plus the fp32 accumulation bound of the exact weighted sum."""
+    w = wl.custom(2, 6, 33, 5, 4, dtype, "gauss_topk", name="rand")
+    inp, d = _run(w)
+    rng = np.random.default_rng(99)
+    g = (rng.standard_normal(d["expand_x"].shape) * 3).astype(np.float32)
+    y = g.astype(np.float16) if dtype == "fp16" else wl.f32_to_bf16_bits(g)
+    sc = rng.uniform(-1.0, 1.0, size=inp["scales"].shape).astype(np.float32)
+    out = oracle.combine(y, d["assist_info"], d["ep_recv_count"], inp["ids"], sc, w.ep_world,
+                         w.experts_per_rank, bf16=(dtype == "bf16"))
+    yf = _token_f32(wl.custom(1, 1, 1, 1, 1, dtype), y)
+    of = _token_f32(wl.custom(1, 1, 1, 1, 1, dtype), out)
+    # pull each pair's row through the library argsort (independent of the oracle's slot table)
+    order = np.argsort(inp["ids"].ravel(), kind="stable")
+    row_of = np.empty_like(order)
+    row_of[order] = np.arange(order.size)
+    K = w.topk
+    mant = 10 if dtype == "fp16" else 7
+    for t in range(w.num_tokens):
+        rows = row_of[t * K:(t + 1) * K]
+        for j in range(w.h):
+            terms = yf[rows, j]
+            ex = _exact_sum(terms, sc[t])
+            mag = float(sum(abs(Fraction(float(a)) * Fraction(float(b))) for a, b in zip(terms, sc[t])))
+            got = float(of[t, j])
+            ulp = 2.0 ** (np.floor(np.log2(max(abs(got), 2.0 ** -14))) - mant)
+            assert abs(got - float(ex)) <= ulp / 2 + K * 2.0 ** -24 * mag + 1e-30, (t, j)
+
+
+def test_combine_rejects_tampered_assist():
+    w = wl.WORKLOADS[0]
+    inp, d = _run(w)
+    a = d["assist_info"].copy()
+    a[0, 2] = (a[0, 2] + 1) % w.topk    # row 0 now claims a pair routed to another expert
+    with pytest.raises(oracle.OracleError):
+        oracle.combine(d["expand_x"], a, d["ep_recv_count"], inp["ids"], inp["scales"], w.ep_world,
+                       w.experts_per_rank)
+
+
+def test_dispatch_rejects_bad_ids():
+    x = np.zeros((4, 2), np.int32)
+    ids = np.array([[0, 0], [1, 2], [3, 1], [2, 0]], np.int32)   # duplicate in token 0
+    with pytest.raises(oracle.OracleError):
+        oracle.dispatch(x, ids, 2, 2)
+    ids[0] = [0, 4]                                                # out of range
+    with pytest.raises(oracle.OracleError):
+        oracle.dispatch(x, ids, 2, 2)
+
+
+def test_empty_batch():
+    x = np.zeros((0, 8), np.float16)
+    ids = np.zeros((0, 2), np.int32)
+    d = oracle.dispatch(x, ids, 4, 2)
+    assert d["expand_x"].shape == (0, 8) and (d["ep_recv_count"] == 0).all()
+    out = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], ids,
+                         np.zeros((0, 2), np.float32), 4, 2)
+    assert out.shape == (0, 8)
+
+
+# --------------------------------------------------------------------------
+# every routing of a tiny problem
+# --------------------------------------------------------------------------
+
+def test_all_1296_routings_end_to_end():
+    W, bs, epr, K, h = 2, 2, 2, 2, 4
+    E, N = W * epr, W * bs
+    rng = np.random.default_rng(5)
+    x = rng.integers(-50, 51, size=(N, h)).astype(np.int32)
+    sc = rng.integers(1, 5, size=(N, K)).astype(np.int32)
+    choices = list(itertools.permutations(range(E), K))   # ordered, distinct
+    pick = [c for c in choices if c[0] < c[1]]             # 6 per token -> 6^4 = 1296 routings
+    assert len(pick) ** N == 1296
+    for combo in itertools.product(pick, repeat=N):
+        ids = np.array(combo, np.int32)
+        d = oracle.dispatch(x, ids, W, epr)
+        cnt = _brute_counts(ids, W, bs, epr)
+        assert (d["ep_recv_count"] == np.cumsum(cnt, axis=1)).all()
+        order = np.argsort(ids.ravel(), kind="stable")
+        a = d["assist_info"].astype(np.int64)
+        assert ((a[:, 0] * bs + a[:, 1]) * K + a[:, 2] == order).all()
+        assert (d["expand_x"] == x[order // K]).all()
+        y = (np.arange(N * K * h, dtype=np.int32).reshape(N * K, h) * 7 - 11)
+        out = oracle.combine(y, d["assist_info"], d["ep_recv_count"], ids, sc, W, epr)
+        row_of = np.empty_like(order)
+        row_of[order] = np.arange(order.size)
+        want = sum(y[row_of[np.arange(N) * K + k]].astype(np.int64) * sc[:, k:k + 1] for k in range(K))
+        assert (out == want).all()
+
+
+# --------------------------------------------------------------------------
+# IEEE conversions used by the oracle
+# --------------------------------------------------------------------------
+
+def test_f16_decode_all_patterns():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    want = bits.view(np.float16).astype(np.float32)
+    got = np.array([oracle.f16_to_f32(int(b)) for b in bits], np.float32)
+    fin = np.isfinite(want)
+    assert (got[fin].view(np.uint32) == want[fin].view(np.uint32)).all()
+    assert np.isnan(got[np.isnan(want)]).all()
+
+
+def test_f16_encode_matches_numpy():
+    rng = np.random.default_rng(3)
+    vals = np.concatenate([
+        rng.standard_normal(20000).astype(np.float32) * 10.0 ** rng.integers(-9, 6, 20000),
+        np.arange(65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float32),
+        # exact midpoints between neighbouring halves (ties), incl. subnormal and overflow edges
+        ((np.arange(65535, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)
+          + np.arange(1, 65536, dtype=np.uint32).astype(np.uint16).view(np.float16).astype(np.float64)) / 2
+         ).astype(np.float32),
+        np.array([65504, 65519.99, 65520, 70000, 2.0 ** -25, 2.0 ** -24, 3 * 2.0 ** -26, 1e-30], np.float32),
+    ]).astype(np.float32)
+    vals = vals[np.isfinite(vals)]
+    vals = np.concatenate([vals, -vals])
+    want = vals.astype(np.float16).view(np.uint16)
+    got = np.array([oracle.f32_to_f16(float(v)) for v in vals], np.uint16)
+    assert (got == want).all()
+
+
+def test_bf16_roundtrip_matches_torch():
+    import torch
+
+    rng = np.random.default_rng(4)
+    u = rng.integers(0, 2 ** 32, size=40000, dtype=np.uint64).astype(np.uint32)
+    u = np.concatenate([u, (rng.integers(0, 2 ** 16, 2000).astype(np.uint32) << 16) | 0x8000])  # ties
+    f = u.view(np.float32)
+    f = f[np.isfinite(f)]
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([oracle.f32_to_bf16(float(v)) for v in f], np.uint16)
+    assert (got == want).all()
+    back = np.array([oracle.bf16_to_f32(int(b)) for b in want[:5000]], np.float32)
+    tb = torch.from_numpy(want[:5000].view(np.int16).copy()).view(torch.bfloat16).float().numpy()
+    fin = np.isfinite(tb)
+    assert (back[fin].view(np.uint32) == tb[fin].view(np.uint32)).all()
+
+
+# --------------------------------------------------------------------------
+# the large-segment predicate
+# --------------------------------------------------------------------------
+
+def _rule_exact(erc, W, epr, h, sz, T):
+    S = epr * W
+    out = np.zeros((W, S), np.uint8)
+    for r in range(W):
+        c = np.diff(np.concatenate([[0], erc[r].astype(np.int64)]))
+        remote = sum(int(c[i]) for i in range(S) if i % W != r)
+        mean = Fraction(remote * h * sz, max(W - 1, 1) * epr)
+        for i in range(S):
+            b = int(c[i]) * h * sz
+            out[r, i] = (i % W != r) and c[i] > 0 and b >= T and Fraction(b) > mean
+    return out
+
+
+def test_large_segment_predicate_matches_exact_rationals():
+    rng = np.random.default_rng(11)
+    n = 0
+    for W in (2, 3, 4, 5):
+        for epr in (1, 2, 3):
+            for h, sz in ((1, 1), (3, 2), (7, 4), (7168, 2)):
+                for _ in range(12):
+                    cnt = rng.integers(0, 9, size=(W, epr * W)) * rng.integers(0, 2, size=(W, epr * W))
+                    erc = np.cumsum(cnt, axis=1).astype(np.int32)
+                    for T in (0, 1, 5 * h * sz, 2 * 1024 * 1024):
+                        got = oracle.large_segments(erc, W, epr, h, sz, T)
+                        assert (got == _rule_exact(erc, W, epr, h, sz, T)).all()
+                        n += 1
+    assert n > 500
+
+
+def test_literal_2mib_rule_selects_nothing_on_the_page_workloads():
+    """A segment holds at most bs tokens: at most 32*7168*2 B = 448 KiB on the
+    8-rank h=7168 workloads, so the literal 2 MiB threshold never fires there."""
+    for w in wl.WORKLOADS:
+        inp, d = _run(w)
+        sz = 1 if w.quant_mode == 2 else (4 if w.dtype == "int32" else 2)
+        flags = oracle.large_segments(d["ep_recv_count"], w.ep_world, w.experts_per_rank, w.h, sz,
+                                      2 * 1024 * 1024)
+        assert flags.sum() == 0, w.name
+    # and a skewed shape with bs >= 147 at h=7168 fp16 does fire
+    w = wl.custom(4, 192, 7168, 4, 2, "fp16", "zipf_topk", name="big_zipf")
+    inp = wl.make_inputs(w)
+    d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank)
+    flags = oracle.large_segments(d["ep_recv_count"], w.ep_world, w.experts_per_rank, w.h, 2,
+                                  2 * 1024 * 1024)
+    assert flags.sum() > 0
+    assert (flags == _rule_exact(d["ep_recv_count"], w.ep_world, w.experts_per_rank, w.h, 2,
+                                 2 * 1024 * 1024)).all()

@@ -1,0 +1,138 @@
+"""Seeded synthetic inputs for MoE dispatch/combine.
+
+This module is the only thing the oracle side and the HIP side share. It
+draws tokens, routings and routing weights; it holds none of the dispatch or
+combine arithmetic.
+
+Workloads (shapes and value distributions of the pages' runs):
+  * ``w2_h16_int32``  -- 2 ranks, 8 tokens/rank, h=16, top-2, 2 experts/rank,
+    int32 tokens in [-100, 100], distinct uniform expert ids, int32 weights in
+    [1, 4] (the 2-card functional run of the combine_doubleplane README, 运行).
+  * ``w8_h16_int32``  -- 8 ranks, 8 tokens/rank, h=16, top-2, 8 experts/rank
+    (64 experts), int32 tokens in [-1000, 1000], as above (the 8-card,
+    64-expert functional run).
+  * ``w8_h7168_fp16_uniform`` -- 8 ranks, 32 tokens/rank, h=7168, top-8, 8
+    experts/rank; fp16 N(0,1) tokens; ids = top-8 of N(0,1) router logits;
+    fp32 weights = softmax over the chosen 8 logits (the README's perf shape,
+    如何选择使用, with fp16 data).
+  * ``w8_h7168_fp16_zipf`` -- as above with expert popularity Zipf(s=1.2):
+    logits = z + ln p_e, p_e proportional to (e+1)^-1.2, so expert 0 is the
+    most popular and rank 0 the hottest destination.
+  * ``w16_h7168_bf16_q8`` -- 16 ranks, 256 tokens/rank, h=7168, top-8, 16
+    experts/rank (256 experts); bf16 N(0,1) tokens; per-token dynamic int8
+    quantisation in dispatch; combine on bf16 expert outputs; softmax weights.
+
+Routing rule for the logit-driven workloads: each token's experts are its 8
+largest logits in descending order, ties to the lower id (stable argsort of
+-logits); weights are the softmax of those 8 logits in fp32 after subtracting
+their max.
+
+Tokens are seeded with ``numpy.random.default_rng(1234 + index)``. bf16 tokens
+are fp32 draws rounded to nearest-even by torch's CPU conversion and carried as
+uint16 bit patterns (numpy has no bfloat16).
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+
+@dataclasses.dataclass(frozen=True)
+class Workload:
+    name: str
+    index: int
+    ep_world: int
+    bs: int
+    h: int
+    topk: int
+    experts_per_rank: int
+    dtype: str              # "int32" | "fp16" | "bf16"
+    routing: str            # "uniform_distinct" | "gauss_topk" | "zipf_topk"
+    quant_mode: int = 0
+    x_lo: int = 0           # int32 token range (inclusive)
+    x_hi: int = 0
+    zipf_s: float = 1.2
+
+    @property
+    def num_experts(self) -> int:
+        return self.ep_world * self.experts_per_rank
+
+    @property
+    def num_tokens(self) -> int:
+        return self.ep_world * self.bs
+
+    @property
+    def rows(self) -> int:
+        return self.num_tokens * self.topk
+
+
+WORKLOADS = [
+    Workload("w2_h16_int32", 0, 2, 8, 16, 2, 2, "int32", "uniform_distinct", x_lo=-100, x_hi=100),
+    Workload("w8_h16_int32", 1, 8, 8, 16, 2, 8, "int32", "uniform_distinct", x_lo=-1000, x_hi=1000),
+    Workload("w8_h7168_fp16_uniform", 2, 8, 32, 7168, 8, 8, "fp16", "gauss_topk"),
+    Workload("w8_h7168_fp16_zipf", 3, 8, 32, 7168, 8, 8, "fp16", "zipf_topk"),
+    Workload("w16_h7168_bf16_q8", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2),
+]
+BY_NAME = {w.name: w for w in WORKLOADS}
+
+
+def custom(ep_world, bs, h, topk, experts_per_rank, dtype="int32", routing="uniform_distinct",
+           quant_mode=0, x_lo=-1000, x_hi=1000, name="custom", index=100):
+    """A workload of arbitrary shape, for edge-case tests."""
+    return Workload(name, index, ep_world, bs, h, topk, experts_per_rank, dtype, routing,
+                    quant_mode=quant_mode, x_lo=x_lo, x_hi=x_hi)
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """Round fp32 draws to bf16 (nearest-even) with torch's CPU cast."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16).copy()
+
+
+def _routing(w: Workload, rng: np.random.Generator):
+    N, E, K = w.num_tokens, w.num_experts, w.topk
+    if w.routing == "uniform_distinct":
+        ids = np.stack([rng.permutation(E)[:K] for _ in range(N)]).astype(np.int32) if N else \
+            np.zeros((0, K), np.int32)
+        return ids, None
+    logits = rng.standard_normal((N, E)).astype(np.float32)
+    if w.routing == "zipf_topk":
+        p = (np.arange(1, E + 1, dtype=np.float64) ** -w.zipf_s)
+        p /= p.sum()
+        logits = (logits + np.log(p).astype(np.float32)).astype(np.float32)
+    elif w.routing != "gauss_topk":
+        raise ValueError(w.routing)
+    order = np.argsort(-logits, axis=1, kind="stable")[:, :K]
+    ids = order.astype(np.int32)
+    chosen = np.take_along_axis(logits, order, axis=1).astype(np.float32)
+    z = np.exp(chosen - chosen.max(axis=1, keepdims=True), dtype=np.float32)
+    weights = (z / z.sum(axis=1, keepdims=True, dtype=np.float32)).astype(np.float32)
+    return ids, weights
+
+
+def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
+    """Seeded tokens, expert ids and routing weights for a workload.
+
+    Returns a dict with:
+      x        [N, h]  int32 | float16 | uint16 (bf16 bits)
+      ids      [N, K]  int32
+      scales   [N, K]  int32 for int32 tokens (uniform in [1, 4]), else fp32
+    """
+    rng = np.random.default_rng(1234 + w.index if seed is None else seed)
+    N, h = w.num_tokens, w.h
+    ids, weights = _routing(w, rng)
+    if w.dtype == "int32":
+        x = rng.integers(w.x_lo, w.x_hi + 1, size=(N, h), dtype=np.int64).astype(np.int32)
+        scales = rng.integers(1, 5, size=(N, w.topk), dtype=np.int64).astype(np.int32)
+        if weights is not None:
+            raise ValueError("int32 workloads use integer weights")
+    else:
+        g = rng.standard_normal((N, h)).astype(np.float32)
+        x = g.astype(np.float16) if w.dtype == "fp16" else f32_to_bf16_bits(g)
+        scales = weights if weights is not None else \
+            rng.uniform(0.0, 1.0, size=(N, w.topk)).astype(np.float32)
+    return dict(x=x, ids=ids, scales=scales)
