@@ -1,0 +1,215 @@
+#!/usr/bin/env python3
+"""Dispatch + combine throughput on one MI355X.
+
+One step = moe_dispatch (route, scan, scatter with per-token int8
+quantisation) + moe_combine (gather + fp32 weighted reduce) over one batch of
+synthetic tokens, inputs resident in HBM. The expert between them is the
+identity expert; its output (bf16(q * scale) for int8 rows) is produced once,
+before timing, as an input of combine.
+
+Timing: every step is preceded by an untimed 1 GiB read that evicts L2 and
+the Infinity Cache, then bracketed by HIP events on the stream the kernels
+run on (launch gaps included); an event between dispatch and combine times
+the combine kernel alone, the dominant kernel for the roofline. A warm figure
+(steps back to back, no eviction) is reported beside it.
+
+    python bench.py [--steps 50] [--warmup 5] [--workload w16_h7168_bf16_q8]
+
+Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads as wl  # noqa: E402
+
+METRIC = "dispatch+combine effective HBM GB/s (and % roofline), tokens/s at h=7168"
+HBM_PEAK_GBPS = 8000.0
+
+
+def algorithmic_bytes(w: wl.Workload):
+    """Bytes the method must move, each array once.
+
+    dispatch: read x once + ids; write expand_x, assist_info, ep_recv_count
+              (+ dynamic_scales when quantising)
+    combine:  read expand_x (expert output), scales, assist_info,
+              ep_recv_count, ids; write x_out
+    """
+    N, K, h, rows = w.num_tokens, w.topk, w.h, w.rows
+    sx = 4 if w.dtype == "int32" else 2
+    s_exp = 1 if w.quant_mode == 2 else sx
+    s_y = 2 if w.quant_mode == 2 else sx          # identity-expert output for int8 rows is bf16
+    erc = w.ep_world * w.num_experts * 4
+    disp = N * h * sx + N * K * 4 + rows * h * s_exp + rows * 12 + erc + (rows * 4 if w.quant_mode == 2 else 0)
+    comb = rows * h * s_y + N * K * 4 + rows * 12 + erc + N * K * 4 + N * h * s_y
+    return disp, comb
+
+
+def _device_inputs(w, torch):
+    inp = wl.make_inputs(w)
+    bf = w.dtype == "bf16"
+    x = torch.from_numpy(inp["x"].view(np.int16) if bf else inp["x"]).cuda()
+    if bf:
+        x = x.view(torch.bfloat16)
+    return inp, x, torch.from_numpy(inp["ids"]).cuda(), torch.from_numpy(inp["scales"]).cuda()
+
+
+def measure(w, steps, warmup, flush, torch, moe):
+    _, x, ids, sc = _device_inputs(w, torch)
+    tdt = {"int32": torch.int32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    W, epr = w.ep_world, w.experts_per_rank
+    buf = moe.DispatchBuffers(W, w.bs, epr, w.h, w.topk, tdt, w.quant_mode, "cuda")
+    moe.dispatch_into(buf, x, ids)
+    if w.quant_mode == 2:
+        y = (buf.expand_x.float() * buf.dynamic_scales[:, None]).to(torch.bfloat16)
+    else:
+        y = buf.expand_x                       # identity expert: combine reads dispatch's rows
+    x_out = torch.empty((w.num_tokens, w.h), dtype=y.dtype, device="cuda")
+
+    def step():
+        moe.dispatch_into(buf, x, ids)
+        moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr)
+
+    for _ in range(warmup):
+        flush.max()
+        step()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.max()                            # untimed eviction of L2 / Infinity Cache
+        ev[i][0].record()
+        moe.dispatch_into(buf, x, ids)
+        ev[i][1].record()
+        moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t_step = [a.elapsed_time(c) for a, b, c in ev]
+    t_disp = [a.elapsed_time(b) for a, b, c in ev]
+    t_comb = [b.elapsed_time(c) for a, b, c in ev]
+
+    # warm: back to back, no eviction
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    warm = e0.elapsed_time(e1) / steps
+    return dict(step=t_step, disp=t_disp, comb=t_comb, warm=warm)
+
+
+def cpu_baseline(w, reps=3):
+    """The oracle as it stands (single-threaded C), timed on the host."""
+    import oracle
+
+    inp = wl.make_inputs(w)
+    bf = w.dtype == "bf16"
+    d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode, bf16=bf)
+    y = oracle.identity_expert(d["expand_x"], d["dynamic_scales"])
+    out_bf = bf or w.quant_mode == 2
+    times = []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode, bf16=bf)
+        oracle.combine(y, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"], w.ep_world,
+                       w.experts_per_rank, bf16=out_bf)
+        times.append(time.perf_counter() - t0)
+    disp_b, comb_b = algorithmic_bytes(w)
+    t = statistics.median(times)
+    return {"value": round((disp_b + comb_b) / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "one full %s step (dispatch + combine, %d tokens), 1 warm-up + median of %d runs, "
+                      "single-threaded C oracle (gcc -O2), identity-expert dequantisation untimed; %.2f s/step"
+                      % (w.name, w.num_tokens, reps, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="w16_h7168_bf16_q8", choices=sorted(wl.BY_NAME))
+    ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf",
+                    help="comma-separated extra workloads reported under 'also' ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: the expert-parallel ranks are emulated as partitions of one GPU's "
+              "HBM, so --gpus %d is not offered (use --gpus 1)." % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import combine_ep_recv_amd as moe
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.library()
+    flush = torch.empty(1 << 27, dtype=torch.int64, device="cuda").fill_(1)   # 1 GiB
+
+    w = wl.BY_NAME[args.workload]
+    r = measure(w, args.steps, args.warmup, flush, torch, moe)
+    disp_b, comb_b = algorithmic_bytes(w)
+    ms = statistics.mean(r["step"])
+    gbps = (disp_b + comb_b) / (ms * 1e-3) / 1e9
+    comb_ms = statistics.mean(r["comb"])
+    comb_gbps = comb_b / (comb_ms * 1e-3) / 1e9
+    kernel = "combine_half_kernel<BF16,true>" if (w.dtype == "bf16" or w.quant_mode == 2) else \
+        ("combine_half_kernel<F16,true>" if w.dtype == "fp16" else "combine_i32_kernel<true>")
+
+    also = {}
+    for name in [n for n in args.also.split(",") if n]:
+        wa = wl.BY_NAME[name]
+        ra = measure(wa, args.steps, args.warmup, flush, torch, moe)
+        da, ca = algorithmic_bytes(wa)
+        msa = statistics.mean(ra["step"])
+        also[name] = {"ms_per_step": round(msa, 5), "GB/s": round((da + ca) / (msa * 1e-3) / 1e9, 1),
+                      "frac_of_hbm_peak": round((da + ca) / (msa * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "tokens_per_s": round(wa.num_tokens / (msa * 1e-3), 1),
+                      "median_ms": round(statistics.median(ra["step"]), 5),
+                      "dispatch_ms": round(statistics.mean(ra["disp"]), 5),
+                      "combine_ms": round(statistics.mean(ra["comb"]), 5),
+                      "warm_ms_per_step": round(ra["warm"], 5), "algorithmic_bytes": da + ca}
+
+    line = {
+        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype,
+        "data": "synthetic, seeded: %s" % ("bf16 N(0,1) tokens, top-8 of N(0,1) router logits, softmax weights"
+                                           if w.routing == "gauss_topk" else w.routing),
+        "config": {"workload": w.name, "ep_world": w.ep_world, "bs": w.bs, "h": w.h, "topk": w.topk,
+                   "experts_per_rank": w.experts_per_rank, "experts": w.num_experts, "tokens": w.num_tokens,
+                   "quant": "per-token dynamic int8" if w.quant_mode == 2 else "none",
+                   "combine_input": "bf16 identity-expert output" if w.quant_mode == 2 else w.dtype,
+                   "cache": "L2 + Infinity Cache evicted (1 GiB read) before every timed step",
+                   "algorithmic_bytes": disp_b + comb_b},
+        "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
+        "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(comb_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(comb_gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": kernel,
+                     "bytes_per_launch": comb_b, "avg_launch_ms": round(comb_ms, 5)},
+        "timing": {"median_ms": round(statistics.median(r["step"]), 5), "min_ms": round(min(r["step"]), 5),
+                   "dispatch_ms": round(statistics.mean(r["disp"]), 5), "combine_ms": round(comb_ms, 5),
+                   "warm_ms_per_step": round(r["warm"], 5),
+                   "warm_GB/s": round((disp_b + comb_b) / (r["warm"] * 1e-3) / 1e9, 1)},
+        "also": also,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

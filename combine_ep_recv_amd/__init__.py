@@ -1,0 +1,211 @@
+"""MoE token dispatch / combine on MI355X: thin Python binding over libmoe_ep.so.
+
+Every step of the path runs in the HIP kernels of ``csrc/moe_ep.hip``; this
+module only allocates outputs with torch (device memory + the current stream)
+and marshals pointers to the C ABI of ``include/moe_ep.h``. There is no CPU
+fallback: importing works without the library, but any call raises when
+``libmoe_ep.so`` has not been built (``python -m combine_ep_recv_amd._build``
+or ``__graft_entry__.build()``).
+
+    expand_x, dynamic_scales, assist_info, ep_recv_count = dispatch(
+        x, expert_ids, ep_world, experts_per_rank, quant_mode=0)
+    x_out = combine(expand_x, assist_info, ep_recv_count, expert_ids,
+                    expert_scales, ep_world, experts_per_rank)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.so")
+
+MOE_OK = 0
+MOE_INT32, MOE_FP16, MOE_BF16 = 0, 1, 2
+MOE_QUANT_NONE, MOE_QUANT_DYN_TOKEN = 0, 2
+MOE_SCHED_TOKEN, MOE_SCHED_SEGMENT = 0, 1
+
+EXPORTS = ("moe_dispatch_workspace_size", "moe_dispatch", "moe_combine_workspace_size", "moe_combine",
+           "moe_status_str")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn, status, msg):
+        super().__init__("%s failed: status %d (%s)" % (fn, status, msg))
+        self.status = status
+
+
+class MoeSchedule(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("large_segment_bytes", ctypes.c_int64), ("segment_is_large", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def library() -> ctypes.CDLL:
+    """Load libmoe_ep.so (raises if it was not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libmoe_ep.so is not built (%s); build it with __graft_entry__.build()" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.moe_dispatch_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(SZ)]
+    lib.moe_dispatch_workspace_size.restype = I
+    lib.moe_dispatch.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(MoeSchedule), P,
+                                 SZ, P]
+    lib.moe_dispatch.restype = I
+    lib.moe_combine_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(SZ)]
+    lib.moe_combine_workspace_size.restype = I
+    lib.moe_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, SZ, P]
+    lib.moe_combine.restype = I
+    lib.moe_status_str.argtypes = [I]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_str(status: int) -> str:
+    return library().moe_status_str(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != MOE_OK:
+        raise MoeError(fn, status, status_str(status))
+
+
+def dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.int32:
+        return MOE_INT32
+    if dt == torch.float16:
+        return MOE_FP16
+    if dt == torch.bfloat16:
+        return MOE_BF16
+    raise MoeError("dtype", 3, "unsupported token dtype %s" % dt)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(device) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def dispatch_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype, quant_mode=0) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_dispatch_workspace_size",
+           library().moe_dispatch_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype, quant_mode,
+                                                 ctypes.byref(n)))
+    return n.value
+
+
+def combine_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_combine_workspace_size",
+           library().moe_combine_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype, ctypes.byref(n)))
+    return n.value
+
+
+class DispatchBuffers:
+    """Preallocated outputs + workspace for repeated dispatch calls of one shape."""
+
+    def __init__(self, ep_world, bs, experts_per_rank, h, topk, dtype: torch.dtype, quant_mode=0,
+                 device="cuda", with_expand_scales=False):
+        N, rows = ep_world * bs, ep_world * bs * topk
+        self.shape = (ep_world, bs, experts_per_rank, h, topk)
+        self.dtype, self.quant_mode = dtype, quant_mode
+        out_dt = torch.int8 if quant_mode == MOE_QUANT_DYN_TOKEN else dtype
+        self.expand_x = torch.empty((rows, h), dtype=out_dt, device=device)
+        self.dynamic_scales = (torch.empty((rows,), dtype=torch.float32, device=device)
+                               if quant_mode == MOE_QUANT_DYN_TOKEN else None)
+        self.assist_info = torch.empty((rows, 3), dtype=torch.int32, device=device)
+        self.ep_recv_count = torch.empty((ep_world, experts_per_rank * ep_world), dtype=torch.int32,
+                                         device=device)
+        self.expand_scales = (torch.empty((rows,), dtype=torch.float32 if dtype != torch.int32 else torch.int32,
+                                          device=device) if with_expand_scales else None)
+        ws = dispatch_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype_code(dtype), quant_mode)
+        self.workspace = torch.empty((max(ws, 16),), dtype=torch.uint8, device=device)
+        del N
+
+
+def dispatch_into(buf: DispatchBuffers, x: torch.Tensor, expert_ids: torch.Tensor,
+                  expert_scales: Optional[torch.Tensor] = None, schedule: Optional[MoeSchedule] = None):
+    """moe_dispatch into preallocated buffers on the current stream."""
+    W, bs, epr, h, K = buf.shape
+    rc = library().moe_dispatch(
+        _ptr(x), _ptr(expert_ids), _ptr(expert_scales), W, bs, epr, h, K, dtype_code(buf.dtype), buf.quant_mode,
+        _ptr(buf.expand_x), _ptr(buf.dynamic_scales), _ptr(buf.assist_info), _ptr(buf.ep_recv_count),
+        _ptr(buf.expand_scales), ctypes.byref(schedule) if schedule is not None else None,
+        _ptr(buf.workspace), buf.workspace.numel(), _stream_ptr(x.device))
+    _check("moe_dispatch", rc)
+    return buf
+
+
+def _check_tensor(name, t, dtype, shape, device):
+    if t.dtype != dtype or tuple(t.shape) != tuple(shape) or not t.is_contiguous() or t.device != device:
+        raise MoeError(name, 2, "%s must be a contiguous %s tensor of shape %s on %s (got %s %s %s)"
+                       % (name, dtype, tuple(shape), device, t.dtype, tuple(t.shape), t.device))
+
+
+def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_per_rank: int,
+             quant_mode: int = MOE_QUANT_NONE, expert_scales: Optional[torch.Tensor] = None,
+             schedule: Optional[MoeSchedule] = None):
+    """Dispatch tokens into expert-grouped rows.
+
+    x: [ep_world*bs, h] int32/fp16/bf16 on a GPU; expert_ids: [ep_world*bs, topk]
+    int32. Returns (expand_x, dynamic_scales or None, assist_info, ep_recv_count)
+    and, when expert_scales is given, a fifth item expand_scales.
+    """
+    N, h = x.shape
+    K = expert_ids.shape[1]
+    if N % ep_world:
+        raise MoeError("moe_dispatch", 2, "token count %d is not a multiple of ep_world %d" % (N, ep_world))
+    _check_tensor("x", x, x.dtype, (N, h), x.device)
+    _check_tensor("expert_ids", expert_ids, torch.int32, (N, K), x.device)
+    if expert_scales is not None:
+        _check_tensor("expert_scales", expert_scales, expert_scales.dtype, (N, K), x.device)
+    buf = DispatchBuffers(ep_world, N // ep_world, experts_per_rank, h, K, x.dtype, quant_mode, x.device,
+                          with_expand_scales=expert_scales is not None)
+    if expert_scales is not None:
+        buf.expand_scales = torch.empty((N * K,), dtype=expert_scales.dtype, device=x.device)
+    dispatch_into(buf, x, expert_ids, expert_scales, schedule)
+    out = (buf.expand_x, buf.dynamic_scales, buf.assist_info, buf.ep_recv_count)
+    return out + (buf.expand_scales,) if expert_scales is not None else out
+
+
+def combine_into(x_out: torch.Tensor, expand_x: torch.Tensor, assist_info: torch.Tensor,
+                 ep_recv_count: torch.Tensor, expert_ids: torch.Tensor, expert_scales: torch.Tensor,
+                 ep_world: int, experts_per_rank: int):
+    """moe_combine into a preallocated x_out on the current stream."""
+    N, K = expert_ids.shape
+    h = expand_x.shape[1]
+    rc = library().moe_combine(
+        _ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_count), _ptr(expert_ids), _ptr(expert_scales),
+        ep_world, N // ep_world, experts_per_rank, h, K, dtype_code(expand_x.dtype), _ptr(x_out), None, 0,
+        _stream_ptr(expand_x.device))
+    _check("moe_combine", rc)
+    return x_out
+
+
+def combine(expand_x: torch.Tensor, assist_info: torch.Tensor, ep_recv_count: torch.Tensor,
+            expert_ids: torch.Tensor, expert_scales: torch.Tensor, ep_world: int, experts_per_rank: int):
+    """x_out[t] = sum_k expand_x[row(t,k)] * expert_scales[t,k] (fp32 accumulation)."""
+    N, K = expert_ids.shape
+    rows, h = expand_x.shape
+    dev = expand_x.device
+    if N % ep_world or rows != N * K:
+        raise MoeError("moe_combine", 2, "expand_x must have ep_world*bs*topk rows")
+    _check_tensor("expand_x", expand_x, expand_x.dtype, (rows, h), dev)
+    _check_tensor("assist_info", assist_info, torch.int32, (rows, 3), dev)
+    _check_tensor("ep_recv_count", ep_recv_count, torch.int32, (ep_world, experts_per_rank * ep_world), dev)
+    _check_tensor("expert_ids", expert_ids, torch.int32, (N, K), dev)
+    sdt = torch.int32 if expand_x.dtype == torch.int32 else torch.float32
+    _check_tensor("expert_scales", expert_scales, sdt, (N, K), dev)
+    x_out = torch.empty((N, h), dtype=expand_x.dtype, device=dev)
+    return combine_into(x_out, expand_x, assist_info, ep_recv_count, expert_ids, expert_scales, ep_world,
+                        experts_per_rank)

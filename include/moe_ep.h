@@ -1,0 +1,168 @@
+/*
+ * moe_ep.h -- MoE token dispatch and combine on one MI355X (gfx950).
+ *
+ * C ABI. Every tensor argument is a plain DEVICE pointer to row-major,
+ * densely packed memory that the caller allocated and owns; sizes are plain
+ * integers; the stream is a hipStream_t passed as void* (NULL = the default
+ * stream). The library never allocates, frees or synchronises: a call
+ * validates its arguments on the host, enqueues its kernels on `stream` and
+ * returns. MOE_OK means "validated and enqueued". On any error status no
+ * kernel has been launched and no output has been touched. The library keeps
+ * no mutable global state, so calls on different streams are independent;
+ * calls that share a workspace must be ordered by the caller.
+ *
+ * Notation: W = ep_world (logical expert-parallel ranks), bs = tokens per
+ * rank, N = W*bs, K = topk, epr = experts_per_rank, E = W*epr experts,
+ * S = epr*W segments per rank, ROWS = N*K. Token t = s*bs + tok belongs to
+ * source rank s. Expert e lives on rank r = e / epr as local expert
+ * el = e % epr. The logical ranks' receive windows are back-to-back
+ * partitions of one expand_x buffer, rank 0 first.
+ *
+ * Pages this interface follows:
+ *  - "aclnnMoeDistributeDispatchV4" (CANN 9.1.0-beta.3 API reference):
+ *    接口功能 and 计算公式 (optional quantisation, then the expert-parallel
+ *    all-to-all expandXOut = AllToAllV(X)); the two-phase call (a workspace
+ *    query that validates, then the execution); the aclnnStatus return code;
+ *    parameter ranges (epWorldSize in [2, 768], moeExpertNum in (0, 1024],
+ *    quantMode 0 or 2 on the A2/A3 parts); 约束说明: deterministic by default,
+ *    dispatch outputs are handed to combine unchanged and are opaque to the
+ *    caller, and scalar parameters must match between dispatch and combine.
+ *  - "双平面 MoE Combine 示例" (CANN SHMEM combine_doubleplane README):
+ *    功能说明 (expand_x grouped by expert; assist_info_for_combine rows
+ *    [src_rank_id, src_token_id, src_topk_id]; ep_recv_count, the cumulative
+ *    receive count per (local_expert_id, src_rank_id) segment; the combine
+ *    check formula) and 方案设计 (the large-segment predicate).
+ */
+#ifndef MOE_EP_H
+#define MOE_EP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes (the two-phase API of aclnnMoeDistributeDispatchV4 returns a
+ * status and validates in its first phase). */
+enum moe_status {
+    MOE_OK = 0,
+    MOE_ERR_NULLPTR = 1,   /* a required pointer is NULL, or a forbidden one is not */
+    MOE_ERR_SHAPE = 2,     /* a size is out of range or a product overflows */
+    MOE_ERR_DTYPE = 3,     /* unknown token dtype */
+    MOE_ERR_QUANT = 4,     /* unknown quant mode, or quantisation of int32 data */
+    MOE_ERR_WORKSPACE = 5, /* workspace smaller than the queried size */
+    MOE_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch */
+    MOE_ERR_SCHEDULE = 7,  /* unknown schedule mode, or the segment schedule (or the
+                              segment_is_large output) at W*S above 11264 */
+    MOE_ERR_ALIGN = 8      /* a pointer is not aligned to its element size (16 bytes for
+                              the workspace) */
+};
+
+/* Token element types. */
+enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
+
+/* Quantisation modes; the numbering follows quantMode of
+ * aclnnMoeDistributeDispatchV4 (0 = none, 2 = per-token dynamic). */
+enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_DYN_TOKEN = 2 };
+
+/* How dispatch assigns its payload copies to workgroups. Both modes produce
+ * bitwise identical outputs (the combine_doubleplane README requires the same
+ * x_out whichever return path a segment takes).
+ *  MOE_SCHED_TOKEN:   one workgroup per source token reads the row once and
+ *                     writes its K copies (default).
+ *  MOE_SCHED_SEGMENT: workgroups walk expand_x in destination order; a segment
+ *                     selected by the large-segment predicate gets whole
+ *                     workgroups of its own (split by rows), the other
+ *                     segments are packed together. */
+enum moe_sched_mode { MOE_SCHED_TOKEN = 0, MOE_SCHED_SEGMENT = 1 };
+
+/* Optional dispatch schedule (host struct; pass NULL for the defaults).
+ *  large_segment_bytes: threshold T of the predicate (README 方案设计): a
+ *      segment (el, s) of rank r is large iff s != r, it is non-empty, its
+ *      payload count*h*elem_bytes is >= T, and count*h*elem_bytes*den > num
+ *      with num = (rows r receives from other ranks)*h*elem_bytes and
+ *      den = max(W-1, 1)*epr (64-bit integers). elem_bytes is the size of an
+ *      expand_x element (1 when quantising). A negative value selects the
+ *      README's 2 MiB.
+ *  segment_is_large: optional DEVICE output, int32 [W, S] in ep_recv_count's
+ *      layout, set to 1 for the selected segments and 0 otherwise. */
+typedef struct moe_schedule {
+    int32_t mode;
+    int32_t reserved;
+    int64_t large_segment_bytes;
+    int32_t *segment_is_large;
+} moe_schedule;
+
+/* Phase one of dispatch: validates the scalars and writes the workspace size
+ * (bytes, host pointer) that moe_dispatch needs for them. */
+int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int h, int topk,
+                                int dtype, int quant_mode, size_t *bytes);
+
+/*
+ * Dispatch: the expert-parallel all-to-all of aclnnMoeDistributeDispatchV4
+ * (计算公式, expandXOut = AllToAllV(X)) with every logical rank's window in
+ * one HBM, preceded by optional per-token dynamic int8 quantisation.
+ *
+ *  x              [N, h] dtype           tokens; rows s*bs..s*bs+bs-1 are rank s's
+ *  expert_ids     [N, K] int32           global expert ids in [0, E), distinct per token
+ *  expert_scales  [N, K] 4-byte or NULL  only read when expand_scales is given
+ *  expand_x       [ROWS, h]              dtype, or int8 when quant_mode == 2. Row order:
+ *                                        rank r, then local expert, then source rank,
+ *                                        then ascending source token
+ *  dynamic_scales [ROWS] fp32            per-row token scale max|x|/127; required iff
+ *                                        quant_mode == 2, must be NULL otherwise
+ *  assist_info    [ROWS, 3] int32        (src_rank, src_token, topk_id) of each row
+ *  ep_recv_count  [W, S] int32           per rank, inclusive prefix of the row counts of
+ *                                        its segments ordered el*W + s
+ *  expand_scales  [ROWS] 4-byte or NULL  expert_scales[t, k] moved to row(t, k)
+ *  schedule       host pointer or NULL   see moe_schedule
+ *  workspace      device scratch of at least the queried size; its contents on
+ *                 entry do not matter
+ *
+ * Ranges: ep_world in [2, 768], experts_per_rank >= 1, E <= 1024,
+ * 1 <= topk <= E, bs >= 0 (bs == 0 writes zero counts and nothing else),
+ * h >= 1, N*K < 2^31, N < 2^24. Ids outside [0, E) or repeated within a token are a
+ * precondition violation: the kernels stay in bounds but the outputs are
+ * unspecified. Outputs are bitwise deterministic.
+ */
+int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales,
+                 int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype,
+                 int quant_mode, void *expand_x, float *dynamic_scales, int32_t *assist_info,
+                 int32_t *ep_recv_count, void *expand_scales, const moe_schedule *schedule,
+                 void *workspace, size_t workspace_bytes, void *stream);
+
+/* Phase one of combine: validates the scalars and writes the workspace size. */
+int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h, int topk,
+                               int dtype, size_t *bytes);
+
+/*
+ * Combine (README 功能说明, check formula):
+ *   x_out[t] = sum_k expand_x[row(t, k)] * expert_scales[t, k]
+ * where row(t, k) is the row dispatch gave to pair (t, k). It is recovered
+ * from ep_recv_count (segment bounds of expert ids[t, k] and source rank s)
+ * and assist_info (the row of that segment whose src_token is tok).
+ * fp16/bf16: accumulated in fp32, one fused multiply-add per k with k
+ * ascending from 0.0f, rounded once to nearest-even; int32: wrapping 32-bit
+ * integer arithmetic.
+ *
+ *  expand_x       [ROWS, h] dtype (fp16, bf16 or int32; the expert outputs)
+ *  assist_info    [ROWS, 3], ep_recv_count [W, S]: dispatch's, unchanged
+ *  expert_ids     [N, K] int32: the ids given to dispatch
+ *  expert_scales  [N, K] fp32 for fp16/bf16, int32 for int32 data
+ *  x_out          [N, h] dtype
+ * The scalars must equal those given to dispatch.
+ */
+int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t *ep_recv_count,
+                const int32_t *expert_ids, const void *expert_scales, int ep_world, int bs,
+                int experts_per_rank, int h, int topk, int dtype, void *x_out,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+/* A static, human-readable name for a status code. */
+const char *moe_status_str(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_EP_H */

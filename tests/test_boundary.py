@@ -1,0 +1,170 @@
+"""The C-ABI boundary, host side only (no kernel is ever launched here).
+
+* libmoe_ep.so loads and exports every function include/moe_ep.h declares;
+* the workspace queries validate their scalars and size the workspace;
+* every validation error of moe_dispatch / moe_combine is returned before any
+  launch. The pointers passed here are fake addresses: each call below is
+  rejected on the host by a check that runs before anything dereferences or
+  launches, which is exactly the property under test.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import combine_ep_recv_amd as moe
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_ep.h")
+
+OK, NULLPTR, SHAPE, DTYPE, QUANT, WORKSPACE, LAUNCH, SCHEDULE, ALIGN = range(9)
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", src, flags=re.M)))
+
+
+def test_library_exports_every_declared_function():
+    names = _declared_functions()
+    assert set(names) == set(moe.EXPORTS), names
+    lib = ctypes.CDLL(moe.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for s in range(9):
+        assert moe.status_str(s) and moe.status_str(s) != "unknown status"
+    assert moe.status_str(99) == "unknown status"
+
+
+def _ws(*args):
+    n = ctypes.c_size_t(0)
+    rc = moe.library().moe_dispatch_workspace_size(*args, ctypes.byref(n))
+    return rc, n.value
+
+
+@pytest.mark.parametrize("args,want", [
+    ((8, 32, 8, 7168, 8, 1, 0), OK),
+    ((16, 256, 16, 7168, 8, 2, 2), OK),
+    ((2, 0, 1, 1, 1, 0, 0), OK),              # bs = 0 is valid
+    ((768, 1, 1, 16, 1, 1, 0), OK),           # largest world
+    ((8, 1, 128, 16, 8, 1, 0), OK),           # 1024 experts
+    ((1, 8, 8, 16, 2, 0, 0), SHAPE),          # ep_world below 2
+    ((769, 1, 1, 16, 1, 0, 0), SHAPE),        # ep_world above 768
+    ((8, 1, 129, 16, 8, 0, 0), SHAPE),        # 1032 experts
+    ((2, 4, 2, 16, 5, 0, 0), SHAPE),          # topk > experts
+    ((2, 4, 2, 16, 0, 0, 0), SHAPE),          # topk 0
+    ((2, -1, 2, 16, 1, 0, 0), SHAPE),         # negative bs
+    ((2, 4, 2, 0, 1, 0, 0), SHAPE),           # h 0
+    ((2, 4, 0, 16, 1, 0, 0), SHAPE),          # no experts
+    ((512, 40000, 2, 16, 1, 0, 0), SHAPE),    # N beyond the launch limit
+    ((8, 2 ** 27, 8, 16, 8, 0, 0), SHAPE),    # N*K >= 2^31
+    ((2, 4, 2, 16, 1, 3, 0), DTYPE),
+    ((2, 4, 2, 16, 1, 1, 1), QUANT),          # quant mode 1 not offered
+    ((2, 4, 2, 16, 1, 0, 2), QUANT),          # int32 cannot be quantised
+])
+def test_dispatch_workspace_query(args, want):
+    rc, n = _ws(*args)
+    assert rc == want, moe.status_str(rc)
+    if rc == OK:
+        assert n > 0 and n % 256 == 0
+
+
+def test_workspace_grows_with_shape():
+    a = _ws(8, 32, 8, 7168, 8, 1, 0)[1]
+    b = _ws(16, 256, 16, 7168, 8, 2, 2)[1]
+    assert b > a
+
+
+def test_combine_workspace_query():
+    n = ctypes.c_size_t(7)
+    lib = moe.library()
+    assert lib.moe_combine_workspace_size(8, 32, 8, 7168, 8, 1, ctypes.byref(n)) == OK
+    assert n.value == 0
+    assert lib.moe_combine_workspace_size(1, 32, 8, 7168, 8, 1, ctypes.byref(n)) == SHAPE
+    assert lib.moe_combine_workspace_size(8, 32, 8, 7168, 8, 5, ctypes.byref(n)) == DTYPE
+    assert lib.moe_combine_workspace_size(8, 32, 8, 7168, 8, 1, None) == NULLPTR
+    assert lib.moe_dispatch_workspace_size(8, 32, 8, 7168, 8, 1, 0, None) == NULLPTR
+
+
+A = 1 << 20   # fake, 256-aligned "device" addresses; never dereferenced by these calls
+
+
+def _dispatch(**kw):
+    p = dict(x=A, ids=2 * A, esc=None, W=2, bs=4, epr=2, h=16, K=2, dtype=1, quant=0, ex=3 * A, dyn=None,
+             assist=4 * A, erc=5 * A, esc_out=None, sched=None, ws=6 * A, wsb=1 << 30)
+    p.update(kw)
+    P = lambda v: None if v is None else ctypes.c_void_p(v)
+    return moe.library().moe_dispatch(
+        P(p["x"]), P(p["ids"]), P(p["esc"]), p["W"], p["bs"], p["epr"], p["h"], p["K"], p["dtype"], p["quant"],
+        P(p["ex"]), P(p["dyn"]), P(p["assist"]), P(p["erc"]), P(p["esc_out"]),
+        ctypes.byref(p["sched"]) if p["sched"] is not None else None, P(p["ws"]), p["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(W=1), SHAPE),
+    (dict(K=5), SHAPE),
+    (dict(dtype=7), DTYPE),
+    (dict(quant=3), QUANT),
+    (dict(dtype=0, quant=2, dyn=7 * A), QUANT),
+    (dict(x=None), NULLPTR),
+    (dict(ids=None), NULLPTR),
+    (dict(ex=None), NULLPTR),
+    (dict(assist=None), NULLPTR),
+    (dict(erc=None), NULLPTR),
+    (dict(ws=None), NULLPTR),
+    (dict(quant=2), NULLPTR),                        # quantising needs dynamic_scales
+    (dict(dyn=7 * A), NULLPTR),                      # ... and forbids it otherwise
+    (dict(esc_out=7 * A), NULLPTR),                  # expand_scales needs expert_scales
+    (dict(wsb=16), WORKSPACE),
+    (dict(x=A + 1), ALIGN),                          # fp16 tokens at an odd address
+    (dict(ids=2 * A + 2), ALIGN),
+    (dict(erc=5 * A + 2), ALIGN),
+    (dict(ws=6 * A + 8), ALIGN),
+    (dict(sched=moe.MoeSchedule(mode=5)), SCHEDULE),
+    (dict(W=128, epr=8, K=2, sched=moe.MoeSchedule(mode=1)), SCHEDULE),   # W*S = 131072 > LDS budget
+])
+def test_dispatch_rejects_before_launch(kw, want):
+    rc = _dispatch(**kw)
+    assert rc == want, (kw, rc, moe.status_str(rc))
+
+
+def _combine(**kw):
+    p = dict(ex=A, assist=2 * A, erc=3 * A, ids=4 * A, sc=5 * A, W=2, bs=4, epr=2, h=16, K=2, dtype=1, out=6 * A)
+    p.update(kw)
+    P = lambda v: None if v is None else ctypes.c_void_p(v)
+    return moe.library().moe_combine(P(p["ex"]), P(p["assist"]), P(p["erc"]), P(p["ids"]), P(p["sc"]), p["W"],
+                                     p["bs"], p["epr"], p["h"], p["K"], p["dtype"], P(p["out"]), None, 0, None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(W=769), SHAPE),
+    (dict(h=0), SHAPE),
+    (dict(dtype=-1), DTYPE),
+    (dict(ex=None), NULLPTR),
+    (dict(assist=None), NULLPTR),
+    (dict(erc=None), NULLPTR),
+    (dict(ids=None), NULLPTR),
+    (dict(sc=None), NULLPTR),
+    (dict(out=None), NULLPTR),
+    (dict(ex=A + 1), ALIGN),
+    (dict(out=6 * A + 1), ALIGN),
+    (dict(dtype=0, ex=A + 2), ALIGN),
+    (dict(bs=0), OK),                                # empty batch: nothing to launch
+])
+def test_combine_rejects_before_launch(kw, want):
+    rc = _combine(**kw)
+    assert rc == want, (kw, rc, moe.status_str(rc))
+
+
+def test_product_path_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "combine_ep_recv_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".hpp", ".cpp")):
+                text = open(os.path.join(dirpath, f), encoding="utf-8").read()
+                assert "import oracle" not in text and "from oracle" not in text and "moe_oracle" not in text, f
