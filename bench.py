@@ -7,11 +7,14 @@ synthetic tokens, inputs resident in HBM. The expert between them is the
 identity expert; its output (bf16(q * scale) for int8 rows) is produced once,
 before timing, as an input of combine.
 
-Timing: every step is preceded by an untimed 1 GiB read that evicts L2 and
-the Infinity Cache, then bracketed by HIP events on the stream the kernels
-run on (launch gaps included); an event between dispatch and combine times
-the combine kernel alone, the dominant kernel for the roofline. A warm figure
-(steps back to back, no eviction) is reported beside it.
+Timing: exactly --steps steps run back to back between two HIP events on
+the stream the kernels run on, synchronised on both sides (launch gaps
+included). The 823 MB working set of the default workload is three times the
+256 MB Infinity Cache, so consecutive steps do not find each other's data in
+cache. Dispatch and combine are also timed alone the same way; the combine
+launch sequence (slot pass + gather) is the dominant one and gives the
+roofline figure. A cold figure (a 1 GiB read before every step, each step
+bracketed by its own events) is reported beside it.
 
     python bench.py [--steps 50] [--warmup 5] [--workload w16_h7168_bf16_q8]
 
@@ -75,40 +78,44 @@ def measure(w, steps, warmup, flush, torch, moe):
     else:
         y = buf.expand_x                       # identity expert: combine reads dispatch's rows
     x_out = torch.empty((w.num_tokens, w.h), dtype=y.dtype, device="cuda")
+    cws = moe.combine_workspace(W, w.bs, epr, w.h, w.topk, y.dtype)
 
     def step():
         moe.dispatch_into(buf, x, ids)
-        moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr)
+        moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws)
+
+    def b2b(fn, n):
+        """mean ms of n back-to-back calls between two events (one event bubble amortised over n)"""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(n):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     for _ in range(warmup):
-        flush.max()
         step()
     torch.cuda.synchronize()
-
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    # the timed region: exactly `steps` steps, synchronised on both sides
+    ms_step = b2b(step, steps)
+    # each half alone, back to back (the combine is the dominant launch sequence)
+    ms_disp = b2b(lambda: moe.dispatch_into(buf, x, ids), steps)
+    ms_comb = b2b(lambda: moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws),
+                  steps)
+    # cold: L2 and the Infinity Cache evicted (untimed 1 GiB read) before every step; each such
+    # sample also holds one event-to-kernel bubble
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
     torch.cuda.synchronize()
     for i in range(steps):
-        flush.max()                            # untimed eviction of L2 / Infinity Cache
+        flush.max()
         ev[i][0].record()
-        moe.dispatch_into(buf, x, ids)
-        ev[i][1].record()
-        moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr)
-        ev[i][2].record()
-    torch.cuda.synchronize()
-    t_step = [a.elapsed_time(c) for a, b, c in ev]
-    t_disp = [a.elapsed_time(b) for a, b, c in ev]
-    t_comb = [b.elapsed_time(c) for a, b, c in ev]
-
-    # warm: back to back, no eviction
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(steps):
         step()
-    e1.record()
+        ev[i][1].record()
     torch.cuda.synchronize()
-    warm = e0.elapsed_time(e1) / steps
-    return dict(step=t_step, disp=t_disp, comb=t_comb, warm=warm)
+    cold = [a.elapsed_time(b) for a, b in ev]
+    return dict(step=ms_step, disp=ms_disp, comb=ms_comb, cold=cold)
 
 
 def cpu_baseline(w, reps=3):
@@ -162,26 +169,27 @@ def main():
     w = wl.BY_NAME[args.workload]
     r = measure(w, args.steps, args.warmup, flush, torch, moe)
     disp_b, comb_b = algorithmic_bytes(w)
-    ms = statistics.mean(r["step"])
+    ms = r["step"]
     gbps = (disp_b + comb_b) / (ms * 1e-3) / 1e9
-    comb_ms = statistics.mean(r["comb"])
+    comb_ms = r["comb"]
     comb_gbps = comb_b / (comb_ms * 1e-3) / 1e9
-    kernel = "combine_half_kernel<BF16,true>" if (w.dtype == "bf16" or w.quant_mode == 2) else \
-        ("combine_half_kernel<F16,true>" if w.dtype == "fp16" else "combine_i32_kernel<true>")
+    kernel = "moe_combine = combine_slots_kernel + " + (
+        "combine_gather_half_kernel<BF16,true>" if (w.dtype == "bf16" or w.quant_mode == 2) else
+        ("combine_gather_half_kernel<F16,true>" if w.dtype == "fp16" else "combine_gather_i32_kernel<true>"))
 
     also = {}
     for name in [n for n in args.also.split(",") if n]:
         wa = wl.BY_NAME[name]
         ra = measure(wa, args.steps, args.warmup, flush, torch, moe)
         da, ca = algorithmic_bytes(wa)
-        msa = statistics.mean(ra["step"])
+        msa = ra["step"]
         also[name] = {"ms_per_step": round(msa, 5), "GB/s": round((da + ca) / (msa * 1e-3) / 1e9, 1),
                       "frac_of_hbm_peak": round((da + ca) / (msa * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                       "tokens_per_s": round(wa.num_tokens / (msa * 1e-3), 1),
-                      "median_ms": round(statistics.median(ra["step"]), 5),
-                      "dispatch_ms": round(statistics.mean(ra["disp"]), 5),
-                      "combine_ms": round(statistics.mean(ra["comb"]), 5),
-                      "warm_ms_per_step": round(ra["warm"], 5), "algorithmic_bytes": da + ca}
+                      "dispatch_ms": round(ra["disp"], 5), "combine_ms": round(ra["comb"], 5),
+                      "cold_median_ms": round(statistics.median(ra["cold"]), 5),
+                      "cold_GB/s": round((da + ca) / (statistics.median(ra["cold"]) * 1e-3) / 1e9, 1),
+                      "algorithmic_bytes": da + ca}
 
     line = {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -193,17 +201,20 @@ def main():
                    "experts_per_rank": w.experts_per_rank, "experts": w.num_experts, "tokens": w.num_tokens,
                    "quant": "per-token dynamic int8" if w.quant_mode == 2 else "none",
                    "combine_input": "bf16 identity-expert output" if w.quant_mode == 2 else w.dtype,
-                   "cache": "L2 + Infinity Cache evicted (1 GiB read) before every timed step",
+                   "working_set_MB": round((disp_b + comb_b) / 1e6),
                    "algorithmic_bytes": disp_b + comb_b},
         "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
         "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(comb_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(comb_gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": kernel,
                      "bytes_per_launch": comb_b, "avg_launch_ms": round(comb_ms, 5)},
-        "timing": {"median_ms": round(statistics.median(r["step"]), 5), "min_ms": round(min(r["step"]), 5),
-                   "dispatch_ms": round(statistics.mean(r["disp"]), 5), "combine_ms": round(comb_ms, 5),
-                   "warm_ms_per_step": round(r["warm"], 5),
-                   "warm_GB/s": round((disp_b + comb_b) / (r["warm"] * 1e-3) / 1e9, 1)},
+        "timing": {"protocol": "%d steps back to back between two HIP events on the kernels' stream, "
+                               "synchronised before and after" % args.steps,
+                   "dispatch_ms": round(r["disp"], 5), "combine_ms": round(comb_ms, 5),
+                   "cold_median_ms": round(statistics.median(r["cold"]), 5), "cold_min_ms": round(min(r["cold"]), 5),
+                   "cold_GB/s": round((disp_b + comb_b) / (statistics.median(r["cold"]) * 1e-3) / 1e9, 1),
+                   "cold_note": "1 GiB read before each step evicts L2 and the Infinity Cache; each cold sample "
+                                "includes one event-to-kernel bubble"},
         "also": also,
     }
     if not args.no_cpu_baseline:

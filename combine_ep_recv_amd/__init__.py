@@ -180,16 +180,26 @@ def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_p
 
 def combine_into(x_out: torch.Tensor, expand_x: torch.Tensor, assist_info: torch.Tensor,
                  ep_recv_count: torch.Tensor, expert_ids: torch.Tensor, expert_scales: torch.Tensor,
-                 ep_world: int, experts_per_rank: int):
+                 ep_world: int, experts_per_rank: int, workspace: Optional[torch.Tensor] = None):
     """moe_combine into a preallocated x_out on the current stream."""
     N, K = expert_ids.shape
     h = expand_x.shape[1]
+    dt = dtype_code(expand_x.dtype)
+    if workspace is None:
+        workspace = combine_workspace(ep_world, N // ep_world, experts_per_rank, h, K, expand_x.dtype,
+                                      expand_x.device)
     rc = library().moe_combine(
         _ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_count), _ptr(expert_ids), _ptr(expert_scales),
-        ep_world, N // ep_world, experts_per_rank, h, K, dtype_code(expand_x.dtype), _ptr(x_out), None, 0,
+        ep_world, N // ep_world, experts_per_rank, h, K, dt, _ptr(x_out), _ptr(workspace), workspace.numel(),
         _stream_ptr(expand_x.device))
     _check("moe_combine", rc)
     return x_out
+
+
+def combine_workspace(ep_world, bs, experts_per_rank, h, topk, dtype: torch.dtype, device="cuda"):
+    """Workspace tensor for moe_combine of this shape."""
+    n = combine_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype_code(dtype))
+    return torch.empty((max(n, 16),), dtype=torch.uint8, device=device)
 
 
 def combine(expand_x: torch.Tensor, assist_info: torch.Tensor, ep_recv_count: torch.Tensor,

@@ -1,52 +1,67 @@
 // moe_ep.hip -- MoE token dispatch and combine for MI355X (gfx950, wave64).
 //
 // The C ABI declared in include/moe_ep.h. Pure data movement plus an axpy:
-// no MFMA anywhere; every kernel is bounded by HBM bandwidth or latency.
+// no MFMA anywhere; every kernel is bounded by HBM bandwidth or by latency.
 //
 // Dispatch (aclnnMoeDistributeDispatchV4, 计算公式: expandXOut = AllToAllV(X),
 // with every logical rank's receive window a partition of one HBM):
-//   route    one block per (source rank, 256-token chunk). Builds, in LDS, a
+//   route    one block per (source rank, 256-token chunk) b. Builds, in LDS, a
 //            bitmap per expert over the chunk's tokens (ds_or_b64), then
-//            writes the chunk's per-expert counts and, for every (t, k), the
-//            number of earlier tokens of the chunk routed to the same expert
-//            (a popcount of the bitmap below the token). Bit-set order does
-//            not matter, so the result is deterministic with no sort.
-//   scan     one block of 1024 threads, one expert column per thread: the
-//            row offset of every (chunk, expert) block, ep_recv_count
-//            (inclusive, el-major, per rank; combine_doubleplane README
-//            功能说明), and, when asked, the large-segment predicate of the
-//            README's 方案设计 and the segment work plan.
-//   scatter  token-major (default): one block per token reads its row once
-//            with 128-bit loads and writes the K copies (optionally int8
-//            quantised with one fp32 scale per token) plus assist_info.
-//            Segment-major (optional): a metadata pass, then blocks walk
-//            expand_x in destination order following the plan.
-// Combine (README 功能说明, check formula): one block per token recovers
-//   row(t, k) from ep_recv_count and assist_info, gathers the K rows with
-//   128-bit loads and accumulates in fp32 with one FMA per k (k ascending),
-//   rounding once to the output type.
+//            writes, per expert e, the exclusive and inclusive prefix of the
+//            chunk's counts over experts (pc[b][e], pci[b][e]) and, for every
+//            (t, k), the number of earlier tokens of the chunk routed to the
+//            same expert (a popcount below the token's bit). Bit-set order is
+//            irrelevant, so the result is deterministic without a sort.
+//   scatter  token-major: the first row of pair (t, k) routed to e from
+//            chunk b is  sum_{b' < b} pci[b'][e] + sum_{b' >= b} pc[b'][e]
+//            (all rows of lower experts, plus this expert's rows from earlier
+//            chunks), so each block sums those few L2-resident words for its K
+//            pairs instead of waiting for a grid-wide scan. Rows are moved with
+//            128-bit loads/stores; per-token dynamic int8 quantisation runs one
+//            wavefront per token (amax by DPP shuffles, no block barrier).
+//            ep_recv_count (combine_doubleplane README 功能说明) is formed the
+//            same way by the first threads of the grid.
+//   scan     single block; only for very many chunks, and for the segment
+//            schedule (the README's 方案设计 large-segment predicate + plan).
+// Combine (README 功能说明, check formula; 实现逻辑 return path + weighted sum):
+//   slots    every expand_x row announces itself in its source's window: the
+//            row index goes to slot (src_token, topk_id) of rank src_rank.
+//   gather   one block per (token, 2 KiB slice) reads the K rows named by its
+//            slots with 128-bit loads and accumulates in fp32, one FMA per k
+//            with k ascending, rounding once to the output type.
 
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
 #include <stdint.h>
 
+#include <algorithm>
+
 #include "moe_ep.h"
 
 namespace {
 
-constexpr int kThreads = 256;              // route / scatter / combine block size
 constexpr int kScanThreads = 1024;         // the single scan block (>= max experts)
-constexpr int kRouteTokens = 256;          // tokens per route block
+constexpr int kRouteThreads = 256;
+constexpr int kRouteTokens = 256;          // tokens per route chunk
 constexpr int kRouteWords = kRouteTokens / 64;
 constexpr int kMaxExperts = 1024;          // moeExpertNum upper bound
 constexpr int kMinWorld = 2, kMaxWorld = 768;   // epWorldSize range
+constexpr int kDirectMaxChunks = 64;       // chunk count up to which blocks sum the prefixes themselves
 constexpr int kSegLdsMax = 11264;          // W*S limit for the LDS-resident segment counts
 constexpr long long kMaxTokens = (1ll << 24) - 1;   // N blocks of 256 threads stay below 2^32 items
 constexpr int kPlanRows = 8;               // rows per segment-schedule work item
 constexpr int kSegGrid = 4096;             // blocks of the segment-major payload pass
 constexpr int64_t kReadmeLargeBytes = 2 * 1024 * 1024;
-constexpr int kRowUnroll = 4;              // 16-byte chunks held per thread in the scatter
+
+constexpr int kCopyThreads = 128;          // token-major copy: block = (token, slice)
+constexpr int kCopyUnroll = 2;             // 16-byte chunks per thread per slice
+constexpr int kQuantThreads = 256;         // one wavefront per token
+constexpr int kQuantMaxK = 64;             // wavefront-per-token quantiser handles topk <= 64
+constexpr int kQuantMaxBlocks = 1 << 30;   // blocks of the quantiser (each loops over groups of 4 tokens)
+constexpr int kBlockThreads = 256;         // generic block-per-token kernels
+constexpr int kGatherThreads = 128;        // combine: block = (token, 128-chunk slice)
+constexpr int kSlotThreads = 256;
 
 // --------------------------------------------------------------------------
 // element conversions (gfx950: v_cvt_f32_f16 / v_cvt_f16_f32 / v_cvt_pk_bf16_f32,
@@ -62,8 +77,22 @@ struct BF16 {
     static __device__ __forceinline__ uint16_t store(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 };
 
+// Streaming (non-temporal) 16-byte accesses: expand_x rows and x_out are written
+// once and read once, so they should not displace other lines from L2 / MALL.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_stream(uint4 *p, uint4 v)
+{
+    u32x4_t t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t *>(p));
+}
+__device__ __forceinline__ uint4 load_stream(const uint4 *p)
+{
+    u32x4_t t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+
 // --------------------------------------------------------------------------
-// block-level helpers
+// wave / block helpers
 // --------------------------------------------------------------------------
 
 __device__ __forceinline__ int wave_incl_scan(int v)
@@ -98,11 +127,17 @@ __device__ int block_excl_scan(int v, int *tmp, int *total)
     return res;
 }
 
+__device__ __forceinline__ float wave_max(float v)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+    return v;
+}
+
 __device__ __forceinline__ float block_max(float v, float *tmp)
 {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) v = fmaxf(v, __shfl_xor(v, d, 64));
+    v = wave_max(v);
     if (lane == 0) tmp[wid] = v;
     __syncthreads();
     float m = tmp[0];
@@ -111,35 +146,18 @@ __device__ __forceinline__ float block_max(float v, float *tmp)
     return m;
 }
 
-// Exclusive prefix over ranks of the rank totals ep_recv_count[r][S-1]:
-// out[r] = first row of rank r's window; out[W] = all rows.
-__device__ void rank_bases(const int32_t *__restrict__ erc, int W, int S, int32_t *out, int *tmp)
-{
-    const int per = (W + (int)blockDim.x - 1) / (int)blockDim.x;   // <= 3 for W <= 768
-    const int i0 = threadIdx.x * per;
-    int v[3] = {0, 0, 0};
-    int sum = 0;
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-        if (j < per && i0 + j < W) { v[j] = erc[(size_t)(i0 + j) * S + S - 1]; sum += v[j]; }
-    int total;
-    int ex = block_excl_scan(sum, tmp, &total);
-#pragma unroll
-    for (int j = 0; j < 3; ++j)
-        if (j < per && i0 + j < W) { out[i0 + j] = ex; ex += v[j]; }
-    if (threadIdx.x == 0) out[W] = total;
-}
-
 // --------------------------------------------------------------------------
 // route
 // --------------------------------------------------------------------------
 
-__global__ __launch_bounds__(kThreads) void route_kernel(const int32_t *__restrict__ ids, int W, int bs,
-                                                         int epr, int K, int nbs,
-                                                         int32_t *__restrict__ cnt,
-                                                         int32_t *__restrict__ lr)
+__global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__restrict__ ids, int W, int bs,
+                                                              int epr, int K, int nbs,
+                                                              int32_t *__restrict__ pc, int32_t *__restrict__ pci,
+                                                              int32_t *__restrict__ lr)
 {
     extern __shared__ unsigned long long bm[];   // [E][kRouteWords]
+    __shared__ int tmp[40];
+    constexpr int U = 8;
     const int E = W * epr;
     const int b = blockIdx.x, s = b / nbs, j = b % nbs;
     const int tok0 = j * kRouteTokens;
@@ -149,36 +167,73 @@ __global__ __launch_bounds__(kThreads) void route_kernel(const int32_t *__restri
 
     for (int i = threadIdx.x; i < E * kRouteWords; i += blockDim.x) bm[i] = 0ull;
     __syncthreads();
-    for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
-        const int e = ids[pair0 + p];
-        if ((unsigned)e < (unsigned)E) {
-            const int tl = p / K;
-            atomicOr(&bm[e * kRouteWords + (tl >> 6)], 1ull << (tl & 63));
+    // one pass of U pairs per thread covers the chunk whenever ntok * K <= 2048;
+    // the ids and token indices then stay in registers for the rank pass
+    int e[U], tl[U];
+    const bool one_pass = npairs <= kRouteThreads * U;
+    for (int p0 = threadIdx.x; p0 < npairs; p0 += kRouteThreads * U) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u * kRouteThreads;
+            e[u] = p < npairs ? ids[pair0 + p] : -1;
+            tl[u] = p / K;
         }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            if ((unsigned)e[u] < (unsigned)E) atomicOr(&bm[e[u] * kRouteWords + (tl[u] >> 6)], 1ull << (tl[u] & 63));
     }
     __syncthreads();
-    for (int e = threadIdx.x; e < E; e += blockDim.x) {
-        int c = 0;
+
+    // per-expert counts of this chunk and their prefix over experts (E <= 4 * 256)
+    int c[4], sum = 0;
 #pragma unroll
-        for (int w = 0; w < kRouteWords; ++w) c += __popcll(bm[e * kRouteWords + w]);
-        cnt[(size_t)b * E + e] = c;
+    for (int q = 0; q < 4; ++q) {
+        const int x = threadIdx.x * 4 + q;
+        c[q] = 0;
+        if (x < E)
+#pragma unroll
+            for (int w = 0; w < kRouteWords; ++w) c[q] += __popcll(bm[x * kRouteWords + w]);
+        sum += c[q];
     }
-    for (int p = threadIdx.x; p < npairs; p += blockDim.x) {
-        const int e = ids[pair0 + p];
-        int rank = -1;
-        if ((unsigned)e < (unsigned)E) {
-            const int tl = p / K, wi = tl >> 6;
-            const unsigned long long *row = &bm[e * kRouteWords];
-            int c = __popcll(row[wi] & ((1ull << (tl & 63)) - 1ull));
-            for (int w = 0; w < wi; ++w) c += __popcll(row[w]);
-            rank = c;
+    int total;
+    int ex = block_excl_scan(sum, tmp, &total);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int x = threadIdx.x * 4 + q;
+        if (x < E) {
+            pc[(size_t)b * E + x] = ex;
+            pci[(size_t)b * E + x] = ex + c[q];
         }
-        lr[pair0 + p] = rank;
+        ex += c[q];
+    }
+
+    for (int p0 = threadIdx.x; p0 < npairs; p0 += kRouteThreads * U) {
+        if (!one_pass) {
+#pragma unroll
+            for (int u = 0; u < U; ++u) {
+                const int p = p0 + u * kRouteThreads;
+                e[u] = p < npairs ? ids[pair0 + p] : -1;
+                tl[u] = p / K;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u * kRouteThreads;
+            if (p >= npairs) continue;
+            int rank = -1;
+            if ((unsigned)e[u] < (unsigned)E) {
+                const int wi = tl[u] >> 6;
+                const unsigned long long *row = &bm[e[u] * kRouteWords];
+                rank = __popcll(row[wi] & ((1ull << (tl[u] & 63)) - 1ull));
+                for (int w = 0; w < wi; ++w) rank += __popcll(row[w]);
+            }
+            lr[pair0 + p] = rank;
+        }
     }
 }
 
 // --------------------------------------------------------------------------
-// scan (+ large-segment predicate and segment plan)
+// scan (many chunks, or the segment schedule)
 // --------------------------------------------------------------------------
 
 // Walk rank r's segments in order and emit the work items of the segment
@@ -215,8 +270,8 @@ __device__ int plan_rank(const int32_t *segc, const uint8_t *flag, int S, int ro
 }
 
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
-    const int32_t *__restrict__ cnt, int W, int epr, int nbs, int h, int elem_bytes,
-    int32_t *__restrict__ boff, int32_t *__restrict__ erc, int want_seg, long long large_bytes,
+    const int32_t *__restrict__ pc, const int32_t *__restrict__ pci, int W, int epr, int nbs, int h,
+    int elem_bytes, int32_t *__restrict__ boff, int32_t *__restrict__ erc, int want_seg, long long large_bytes,
     int32_t *__restrict__ seg_flags, int2 *__restrict__ plan, int32_t *__restrict__ nplan)
 {
     __shared__ int32_t eoff[kMaxExperts + 1];
@@ -228,7 +283,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     // column totals -> exclusive offsets per expert (blockDim >= E)
     int tot = 0;
     if (tid < E)
-        for (int b = 0; b < NB; ++b) tot += cnt[(size_t)b * E + tid];
+        for (int b = 0; b < NB; ++b) tot += pci[(size_t)b * E + tid] - pc[(size_t)b * E + tid];
     int total;
     const int ex = block_excl_scan(tot, tmp, &total);
     if (tid < E) eoff[tid] = ex;
@@ -245,7 +300,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
             const int before = run;
             for (int j = 0; j < nbs; ++j) {
                 const size_t b = (size_t)s * nbs + j;
-                const int c = cnt[b * E + e];
+                const int c = pci[b * E + e] - pc[b * E + e];
                 boff[b * E + e] = eoff[e] + run;
                 run += c;
             }
@@ -287,152 +342,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 // dispatch payload
 // --------------------------------------------------------------------------
 
-// Row of every pair of token t (token-major schedule); writes assist_info and
-// expand_scales for those rows. Invalid ids give row -1 (nothing written).
-__device__ __forceinline__ void token_rows(int t, int s, int tok, const int32_t *__restrict__ ids,
-                                           const int32_t *__restrict__ lr, const int32_t *__restrict__ boff,
-                                           int E, int K, int nbs, int R, int32_t *rows,
-                                           int32_t *__restrict__ assist, const int32_t *__restrict__ esc_in,
-                                           int32_t *__restrict__ esc_out)
-{
-    const size_t b = (size_t)s * nbs + tok / kRouteTokens;
-    for (int k = threadIdx.x; k < K; k += blockDim.x) {
-        const size_t p = (size_t)t * K + k;
-        const int e = ids[p], l = lr[p];
-        int row = -1;
-        if ((unsigned)e < (unsigned)E && l >= 0) {
-            row = boff[b * E + e] + l;
-            if ((unsigned)row >= (unsigned)R) row = -1;
-        }
-        rows[k] = row;
-        if (row >= 0) {
-            assist[(size_t)row * 3 + 0] = s;
-            assist[(size_t)row * 3 + 1] = tok;
-            assist[(size_t)row * 3 + 2] = k;
-            if (esc_out) esc_out[row] = esc_in[p];
-        }
-    }
-}
-
-// Copy `rowbytes` bytes from src to each of the ndst destination rows.
-template <bool VEC>
-__device__ __forceinline__ void copy_row(const char *__restrict__ src, char *__restrict__ dst_base,
-                                         const int32_t *rows, int ndst, size_t rowbytes)
-{
-    if (VEC) {
-        const int nch = (int)(rowbytes / 16);
-        for (int c0 = threadIdx.x; c0 < nch; c0 += kThreads * kRowUnroll) {
-            uint4 v[kRowUnroll];
-#pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const int c = c0 + u * kThreads;
-                if (c < nch) v[u] = reinterpret_cast<const uint4 *>(src)[c];
-            }
-            for (int k = 0; k < ndst; ++k) {
-                const int row = rows[k];
-                if (row < 0) continue;
-                uint4 *dst = reinterpret_cast<uint4 *>(dst_base + (size_t)row * rowbytes);
-#pragma unroll
-                for (int u = 0; u < kRowUnroll; ++u) {
-                    const int c = c0 + u * kThreads;
-                    if (c < nch) dst[c] = v[u];
-                }
-            }
-        }
-    } else {
-        const int n = (int)(rowbytes / 2);
-        for (int c = threadIdx.x; c < n; c += kThreads) {
-            const uint16_t v = reinterpret_cast<const uint16_t *>(src)[c];
-            for (int k = 0; k < ndst; ++k)
-                if (rows[k] >= 0) reinterpret_cast<uint16_t *>(dst_base + (size_t)rows[k] * rowbytes)[c] = v;
-        }
-    }
-}
-
-__device__ __forceinline__ int8_t quant1(float v, float scale)
-{
-    float q = scale == 0.0f ? 0.0f : __builtin_rintf(v / scale);
-    q = fminf(fmaxf(q, -127.0f), 127.0f);
-    return (int8_t)(int)q;
-}
-
-template <class T>
-__device__ __forceinline__ uint2 quant8(uint4 v, float scale)
-{
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t o[2] = {0u, 0u};
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint16_t b = (uint16_t)(w[i >> 1] >> ((i & 1) * 16));
-        const uint32_t q = (uint8_t)quant1(T::load(b), scale);
-        o[i >> 2] |= q << ((i & 3) * 8);
-    }
-    return make_uint2(o[0], o[1]);
-}
-
-template <class T>
-__device__ __forceinline__ float amax8(uint4 v)
-{
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    float m = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(T::load((uint16_t)(w[i >> 1] >> ((i & 1) * 16)))));
-    return m;
-}
-
-// Per-token dynamic int8 quantisation (aclnnMoeDistributeDispatchV4 quantMode 2):
-// scale = max|x| / 127 (fp32, correctly rounded), q = rint(x / scale) clamped to
-// [-127, 127] (0 for an all-zero token); q is written to every destination row.
-// Returns the scale.
-template <class T, bool VEC>
-__device__ float quant_row(const uint16_t *__restrict__ src, int8_t *__restrict__ dst_base,
-                           const int32_t *rows, int ndst, int h, float *red)
-{
-    float amax = 0.0f;
-    if (VEC) {
-        const int nch = h / 8;
-        const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
-        if (nch <= kThreads * kRowUnroll) {
-            uint4 v[kRowUnroll];
-#pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const int c = threadIdx.x + u * kThreads;
-                if (c < nch) { v[u] = s4[c]; amax = fmaxf(amax, amax8<T>(v[u])); }
-            }
-            amax = block_max(amax, red);
-            const float scale = amax / 127.0f;
-#pragma unroll
-            for (int u = 0; u < kRowUnroll; ++u) {
-                const int c = threadIdx.x + u * kThreads;
-                if (c < nch) {
-                    const uint2 q = quant8<T>(v[u], scale);
-                    for (int k = 0; k < ndst; ++k)
-                        if (rows[k] >= 0) reinterpret_cast<uint2 *>(dst_base + (size_t)rows[k] * h)[c] = q;
-                }
-            }
-            return scale;
-        }
-        for (int c = threadIdx.x; c < nch; c += kThreads) amax = fmaxf(amax, amax8<T>(s4[c]));
-        amax = block_max(amax, red);
-        const float scale = amax / 127.0f;
-        for (int c = threadIdx.x; c < nch; c += kThreads) {
-            const uint2 q = quant8<T>(s4[c], scale);
-            for (int k = 0; k < ndst; ++k)
-                if (rows[k] >= 0) reinterpret_cast<uint2 *>(dst_base + (size_t)rows[k] * h)[c] = q;
-        }
-        return scale;
-    }
-    for (int j = threadIdx.x; j < h; j += kThreads) amax = fmaxf(amax, fabsf(T::load(src[j])));
-    amax = block_max(amax, red);
-    const float scale = amax / 127.0f;
-    for (int j = threadIdx.x; j < h; j += kThreads) {
-        const int8_t q = quant1(T::load(src[j]), scale);
-        for (int k = 0; k < ndst; ++k)
-            if (rows[k] >= 0) dst_base[(size_t)rows[k] * h + j] = q;
-    }
-    return scale;
-}
-
 struct DispatchArgs {
     const char *x;
     const int32_t *ids;
@@ -441,52 +350,326 @@ struct DispatchArgs {
     float *dyn;
     int32_t *assist;
     int32_t *esc_out;
+    int32_t *erc;
     const int32_t *lr;
-    const int32_t *boff;
+    const int32_t *pc;
+    const int32_t *pci;
+    const int32_t *boff;      // scan path only
     const int2 *plan;
     const int32_t *nplan;
-    int W, bs, epr, h, K, nbs, R;
-    long long rowbytes;      // bytes of one x row
+    int W, bs, epr, h, K, nbs, R, E, S, NB;
+    int direct;               // 1: blocks sum pc/pci themselves and write ep_recv_count
+    int nsl;                  // copy kernel: slices per token
+    long long rowbytes;       // bytes of one x row
 };
 
-// Token-major scatter, no quantisation.
-template <bool VEC>
-__global__ __launch_bounds__(kThreads) void scatter_copy_kernel(DispatchArgs a)
+// ep_recv_count[r][el*W + s] = (end row of segment (el, s) of rank r) - (first row of rank r),
+// from the chunk prefixes: first row of (chunk b, expert e) = sum_{b'<b} pci + sum_{b'>=b} pc.
+__device__ void write_erc_direct(const DispatchArgs &a, size_t gtid, size_t nthreads)
 {
-    __shared__ int32_t rows[kMaxExperts];
-    const int t = blockIdx.x, s = t / a.bs, tok = t % a.bs;
-    token_rows(t, s, tok, a.ids, a.lr, a.boff, a.W * a.epr, a.K, a.nbs, a.R, rows, a.assist, a.esc_in, a.esc_out);
-    __syncthreads();
-    copy_row<VEC>(a.x + (size_t)t * a.rowbytes, a.expand_x, rows, a.K, (size_t)a.rowbytes);
+    const size_t total = (size_t)a.W * a.S;
+    for (size_t q = gtid; q < total; q += nthreads) {
+        const int r = (int)(q / a.S), i = (int)(q % a.S), el = i / a.W, s = i % a.W;
+        const int e = r * a.epr + el, e0 = r * a.epr, bend = (s + 1) * a.nbs;
+        int end = 0, base = 0;
+#pragma unroll 8
+        for (int b = 0; b < a.NB; ++b) {
+            end += (b < bend ? a.pci : a.pc)[(size_t)b * a.E + e];
+            base += a.pc[(size_t)b * a.E + e0];
+        }
+        a.erc[q] = end - base;
+    }
 }
 
-// Token-major scatter with per-token dynamic int8 quantisation.
-template <class T, bool VEC>
-__global__ __launch_bounds__(kThreads) void scatter_quant_kernel(DispatchArgs a)
+// Rows of the K pairs of token t, cooperatively over the calling threads
+// [tid0, tid0 + nthr). ek/lk/off/rows: K ints of LDS each. The caller
+// synchronises between the three phases (load / sum / finish).
+__device__ __forceinline__ void pairs_load(const DispatchArgs &a, int t, int *ek, int *lk, int *off, int lt, int nthr)
 {
-    __shared__ int32_t rows[kMaxExperts];
-    __shared__ float red[kThreads / 64];
-    const int t = blockIdx.x, s = t / a.bs, tok = t % a.bs;
-    token_rows(t, s, tok, a.ids, a.lr, a.boff, a.W * a.epr, a.K, a.nbs, a.R, rows, a.assist, a.esc_in, a.esc_out);
+    for (int k = lt; k < a.K; k += nthr) {
+        const size_t p = (size_t)t * a.K + k;
+        ek[k] = a.ids[p];
+        lk[k] = a.lr[p];
+        off[k] = 0;
+    }
+}
+
+__device__ __forceinline__ void pairs_sum(const DispatchArgs &a, int t, const int *ek, int *off, int lt, int nthr)
+{
+    const int s = t / a.bs, tok = t % a.bs;
+    const int bt = s * a.nbs + tok / kRouteTokens;
+    if (a.direct) {
+        const int n = a.K * a.NB;
+        for (int i = lt; i < n; i += nthr) {
+            const int k = i / a.NB, b = i % a.NB, e = ek[k];
+            if ((unsigned)e < (unsigned)a.E) atomicAdd(&off[k], (b < bt ? a.pci : a.pc)[(size_t)b * a.E + e]);
+        }
+    } else {
+        for (int k = lt; k < a.K; k += nthr) {
+            const int e = ek[k];
+            if ((unsigned)e < (unsigned)a.E) off[k] = a.boff[(size_t)bt * a.E + e];
+        }
+    }
+}
+
+// Final rows (-1 for an invalid pair); optionally writes assist_info / expand_scales.
+__device__ __forceinline__ void pairs_finish(const DispatchArgs &a, int t, const int *ek, const int *lk,
+                                             const int *off, int *rows, bool meta, int lt, int nthr)
+{
+    const int s = t / a.bs, tok = t % a.bs;
+    for (int k = lt; k < a.K; k += nthr) {
+        int row = -1;
+        if ((unsigned)ek[k] < (unsigned)a.E && lk[k] >= 0) {
+            row = off[k] + lk[k];
+            if ((unsigned)row >= (unsigned)a.R) row = -1;
+        }
+        rows[k] = row;
+        if (meta && row >= 0) {
+            a.assist[(size_t)row * 3 + 0] = s;
+            a.assist[(size_t)row * 3 + 1] = tok;
+            a.assist[(size_t)row * 3 + 2] = k;
+            if (a.esc_out) a.esc_out[row] = a.esc_in[(size_t)t * a.K + k];
+        }
+    }
+}
+
+// Token-major copy: block = (token, slice of kCopyThreads * kCopyUnroll chunks).
+template <bool VEC>
+__global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(DispatchArgs a)
+{
+    extern __shared__ int dsm[];                  // ek, lk, off, rows: 4 * K ints
+    int *ek = dsm, *lk = dsm + a.K, *off = dsm + 2 * a.K, *rows = dsm + 3 * a.K;
+    const int t = blockIdx.x / a.nsl, sl = blockIdx.x % a.nsl;
+    const int tid = threadIdx.x;
+    constexpr int SC = kCopyThreads * kCopyUnroll;
+
+    if (a.direct) write_erc_direct(a, (size_t)blockIdx.x * kCopyThreads + tid, (size_t)gridDim.x * kCopyThreads);
+
+    // issue the payload loads first; row resolution overlaps them
+    const char *src = a.x + (size_t)t * a.rowbytes;
+    const int n = VEC ? (int)(a.rowbytes / 16) : (int)(a.rowbytes / 2);
+    const int c0 = sl * SC + tid;
+    uint4 v[kCopyUnroll];
+    uint16_t w[kCopyUnroll];
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int c = c0 + u * kCopyThreads;
+        if constexpr (VEC) v[u] = c < n ? reinterpret_cast<const uint4 *>(src)[c] : make_uint4(0u, 0u, 0u, 0u);
+        else w[u] = c < n ? reinterpret_cast<const uint16_t *>(src)[c] : (uint16_t)0;
+    }
+    pairs_load(a, t, ek, lk, off, tid, kCopyThreads);
     __syncthreads();
-    const float scale = quant_row<T, VEC>(reinterpret_cast<const uint16_t *>(a.x) + (size_t)t * a.h,
-                                          reinterpret_cast<int8_t *>(a.expand_x), rows, a.K, a.h, red);
-    for (int k = threadIdx.x; k < a.K; k += kThreads)
+    pairs_sum(a, t, ek, off, tid, kCopyThreads);
+    __syncthreads();
+    pairs_finish(a, t, ek, lk, off, rows, sl == 0, tid, kCopyThreads);
+    __syncthreads();
+
+#pragma unroll
+    for (int u = 0; u < kCopyUnroll; ++u) {
+        const int c = c0 + u * kCopyThreads;
+        if (c >= n) continue;
+        for (int k = 0; k < a.K; ++k) {
+            const int row = rows[k];
+            if (row < 0) continue;
+            char *dst = a.expand_x + (size_t)row * a.rowbytes;
+            if constexpr (VEC) store_stream(reinterpret_cast<uint4 *>(dst) + c, v[u]);
+            else reinterpret_cast<uint16_t *>(dst)[c] = w[u];
+        }
+    }
+}
+
+// q = rint(v / scale) with the quotient correctly rounded, clamped to [-127, 127].
+// FAST: one correction step replaces the division. With inv = RN(1 / scale),
+// q0 = RN(v * inv) and the exact residual r = v - q0 * scale (one FMA), RN(q0 + r * inv)
+// gives the same integer after rint as the correctly rounded quotient for every
+// finite bf16 and fp16 v with |v| <= amax and scale = amax / 127 >= 2^-100; this was
+// checked exhaustively over all such (v, amax) pairs. Smaller scales (subnormal
+// tokens) take the IEEE division.
+template <bool FAST>
+__device__ __forceinline__ int8_t quant1(float v, float scale, float inv)
+{
+    if (scale == 0.0f) return 0;
+    float q;
+    if (FAST) {
+        const float q0 = v * inv;
+        const float r = __builtin_fmaf(-q0, scale, v);
+        q = __builtin_rintf(__builtin_fmaf(r, inv, q0));
+    } else {
+        q = __builtin_rintf(v / scale);
+    }
+    q = fminf(fmaxf(q, -127.0f), 127.0f);
+    return (int8_t)(int)q;
+}
+
+constexpr float kFastQuantMinScale = 0x1p-100f;
+
+template <class T>
+__device__ __forceinline__ float amax_u4(uint4 v)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) m = fmaxf(m, fabsf(T::load((uint16_t)(w[i >> 1] >> ((i & 1) * 16)))));
+    return m;
+}
+
+// 8 elements -> 8 int8 codes packed into two words
+template <class T, bool FAST>
+__device__ __forceinline__ uint2 quant_u4(uint4 v, float scale, float inv)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t o[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t q = (uint8_t)quant1<FAST>(T::load((uint16_t)(w[i >> 1] >> ((i & 1) * 16))), scale, inv);
+        o[i >> 2] |= q << ((i & 3) * 8);
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+// Per-token dynamic int8 quantisation (aclnnMoeDistributeDispatchV4 quantMode 2):
+// scale = max|x| / 127 (fp32, correctly rounded), q = rint(x / scale) clamped to
+// [-127, 127] (0 for an all-zero token), written to every destination row.
+// One wavefront per token; needs h % 16 == 0, h <= 1024 * J, topk <= kQuantMaxK.
+template <class T, int J>
+__global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(DispatchArgs a)
+{
+    __shared__ int sm[kQuantThreads / 64][4 * kQuantMaxK];
+    constexpr int WPB = kQuantThreads / 64;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int N = a.W * a.bs;
+    int *ek = sm[wid], *lk = ek + kQuantMaxK, *off = lk + kQuantMaxK, *rows = off + kQuantMaxK;
+
+    if (a.direct) write_erc_direct(a, (size_t)blockIdx.x * kQuantThreads + threadIdx.x,
+                                   (size_t)gridDim.x * kQuantThreads);
+
+    const int noc = a.h / 16;                     // 16-byte output chunks (two 16-byte input chunks each)
+    // blocks stride over groups of WPB tokens; the loop bound is uniform per block
+    for (int tb = blockIdx.x * WPB; tb < N; tb += gridDim.x * WPB) {
+        const int t = tb + wid;
+        const bool live = t < N;
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)(live ? t : 0) * a.rowbytes);
+        uint4 v[J][2];
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const int oc = lane + 64 * j;
+            if (live && oc < noc) {
+                v[j][0] = src[2 * oc];
+                v[j][1] = src[2 * oc + 1];
+            } else {
+                v[j][0] = v[j][1] = make_uint4(0u, 0u, 0u, 0u);
+            }
+        }
+        if (live) pairs_load(a, t, ek, lk, off, lane, 64);
+        __syncthreads();
+        if (live) pairs_sum(a, t, ek, off, lane, 64);
+        __syncthreads();
+        if (live) pairs_finish(a, t, ek, lk, off, rows, true, lane, 64);
+        __syncthreads();
+        if (live) {
+            float amax = 0.0f;
+#pragma unroll
+            for (int j = 0; j < J; ++j)
+                if (lane + 64 * j < noc) amax = fmaxf(amax, fmaxf(amax_u4<T>(v[j][0]), amax_u4<T>(v[j][1])));
+            amax = wave_max(amax);
+            const float scale = amax / 127.0f;
+            const float inv = 1.0f / scale;
+            char *const dst0 = a.expand_x;
+            const int h = a.h, K = a.K;
+            auto emit = [&](int j, uint4 q) {
+                for (int k = 0; k < K; ++k) {
+                    const int row = rows[k];
+                    if (row >= 0) store_stream(reinterpret_cast<uint4 *>(dst0 + (size_t)row * h) + lane + 64 * j, q);
+                }
+            };
+            if (scale >= kFastQuantMinScale) {
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    if (lane + 64 * j >= noc) continue;
+                    const uint2 lo = quant_u4<T, true>(v[j][0], scale, inv), hi = quant_u4<T, true>(v[j][1], scale, inv);
+                    emit(j, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < J; ++j) {
+                    if (lane + 64 * j >= noc) continue;
+                    const uint2 lo = quant_u4<T, false>(v[j][0], scale, inv), hi = quant_u4<T, false>(v[j][1], scale, inv);
+                    emit(j, make_uint4(lo.x, lo.y, hi.x, hi.y));
+                }
+            }
+            for (int k = lane; k < a.K; k += 64)
+                if (rows[k] >= 0) a.dyn[rows[k]] = scale;
+        }
+        __syncthreads();                          // rows[] is rewritten by the next group
+    }
+}
+
+// The same quantisation, one block per token, any h and topk (8-byte stores
+// when h % 8 == 0 and the pointers allow, single bytes otherwise).
+template <class T, bool VEC>
+__device__ float quant_row_block(const uint16_t *__restrict__ src, int8_t *__restrict__ dst_base,
+                                 const int *rows, int ndst, int h, float *red)
+{
+    float amax = 0.0f;
+    if (VEC) {
+        const int nch = h / 8;
+        const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
+        for (int c = threadIdx.x; c < nch; c += blockDim.x) amax = fmaxf(amax, amax_u4<T>(s4[c]));
+        amax = block_max(amax, red);
+        const float scale = amax / 127.0f, inv = 1.0f / scale;
+        const bool fast = scale >= kFastQuantMinScale;
+        for (int c = threadIdx.x; c < nch; c += blockDim.x) {
+            const uint2 q = fast ? quant_u4<T, true>(s4[c], scale, inv) : quant_u4<T, false>(s4[c], scale, inv);
+            for (int k = 0; k < ndst; ++k)
+                if (rows[k] >= 0) reinterpret_cast<uint2 *>(dst_base + (size_t)rows[k] * h)[c] = q;
+        }
+        return scale;
+    }
+    for (int j = threadIdx.x; j < h; j += blockDim.x) amax = fmaxf(amax, fabsf(T::load(src[j])));
+    amax = block_max(amax, red);
+    const float scale = amax / 127.0f, inv = 1.0f / scale;
+    const bool fast = scale >= kFastQuantMinScale;
+    for (int j = threadIdx.x; j < h; j += blockDim.x) {
+        const float x = T::load(src[j]);
+        const int8_t q = fast ? quant1<true>(x, scale, inv) : quant1<false>(x, scale, inv);
+        for (int k = 0; k < ndst; ++k)
+            if (rows[k] >= 0) dst_base[(size_t)rows[k] * h + j] = q;
+    }
+    return scale;
+}
+
+template <class T, bool VEC>
+__global__ __launch_bounds__(kBlockThreads) void scatter_quant_block_kernel(DispatchArgs a)
+{
+    extern __shared__ int dsm[];
+    __shared__ float red[kBlockThreads / 64];
+    int *ek = dsm, *lk = dsm + a.K, *off = dsm + 2 * a.K, *rows = dsm + 3 * a.K;
+    const int t = blockIdx.x;
+    if (a.direct) write_erc_direct(a, (size_t)blockIdx.x * kBlockThreads + threadIdx.x,
+                                   (size_t)gridDim.x * kBlockThreads);
+    pairs_load(a, t, ek, lk, off, threadIdx.x, kBlockThreads);
+    __syncthreads();
+    pairs_sum(a, t, ek, off, threadIdx.x, kBlockThreads);
+    __syncthreads();
+    pairs_finish(a, t, ek, lk, off, rows, true, threadIdx.x, kBlockThreads);
+    __syncthreads();
+    const float scale = quant_row_block<T, VEC>(reinterpret_cast<const uint16_t *>(a.x) + (size_t)t * a.h,
+                                                reinterpret_cast<int8_t *>(a.expand_x), rows, a.K, a.h, red);
+    for (int k = threadIdx.x; k < a.K; k += kBlockThreads)
         if (rows[k] >= 0) a.dyn[rows[k]] = scale;
 }
 
-// Segment schedule, pass 1: assist_info / expand_scales for every pair.
-__global__ __launch_bounds__(kThreads) void segment_meta_kernel(DispatchArgs a)
+// Segment schedule, pass 1: assist_info / expand_scales for every pair (scan path offsets).
+__global__ __launch_bounds__(kBlockThreads) void segment_meta_kernel(DispatchArgs a)
 {
-    const size_t p = (size_t)blockIdx.x * kThreads + threadIdx.x;
+    const size_t p = (size_t)blockIdx.x * kBlockThreads + threadIdx.x;
     const size_t npairs = (size_t)a.W * a.bs * a.K;
     if (p >= npairs) return;
-    const int E = a.W * a.epr;
     const int t = (int)(p / a.K), k = (int)(p % a.K), s = t / a.bs, tok = t % a.bs;
     const size_t b = (size_t)s * a.nbs + tok / kRouteTokens;
     const int e = a.ids[p], l = a.lr[p];
-    if ((unsigned)e >= (unsigned)E || l < 0) return;
-    const int row = a.boff[b * E + e] + l;
+    if ((unsigned)e >= (unsigned)a.E || l < 0) return;
+    const int row = a.boff[b * a.E + e] + l;
     if ((unsigned)row >= (unsigned)a.R) return;
     a.assist[(size_t)row * 3 + 0] = s;
     a.assist[(size_t)row * 3 + 1] = tok;
@@ -498,10 +681,10 @@ __global__ __launch_bounds__(kThreads) void segment_meta_kernel(DispatchArgs a)
 // a large segment's rows never sharing an item with another segment) and fill
 // each row from its source token, found through assist_info.
 template <int MODE, bool VEC>   // MODE 0: copy, 1: quant fp16, 2: quant bf16
-__global__ __launch_bounds__(kThreads) void segment_payload_kernel(DispatchArgs a)
+__global__ __launch_bounds__(kBlockThreads) void segment_payload_kernel(DispatchArgs a)
 {
-    __shared__ int32_t one[1];
-    __shared__ float red[kThreads / 64];
+    __shared__ int one[1];
+    __shared__ float red[kBlockThreads / 64];
     const int n = *a.nplan;
     for (int item = blockIdx.x; item < n; item += gridDim.x) {
         const int2 it = a.plan[item];
@@ -513,12 +696,20 @@ __global__ __launch_bounds__(kThreads) void segment_payload_kernel(DispatchArgs 
             if (threadIdx.x == 0) one[0] = row;
             __syncthreads();
             if (MODE == 0) {
-                copy_row<VEC>(a.x + t * a.rowbytes, a.expand_x, one, 1, (size_t)a.rowbytes);
+                const char *src = a.x + t * a.rowbytes;
+                char *dst = a.expand_x + (size_t)row * a.rowbytes;
+                if (VEC) {
+                    for (int c = threadIdx.x; c < (int)(a.rowbytes / 16); c += kBlockThreads)
+                        reinterpret_cast<uint4 *>(dst)[c] = reinterpret_cast<const uint4 *>(src)[c];
+                } else {
+                    for (int c = threadIdx.x; c < (int)(a.rowbytes / 2); c += kBlockThreads)
+                        reinterpret_cast<uint16_t *>(dst)[c] = reinterpret_cast<const uint16_t *>(src)[c];
+                }
             } else {
                 const uint16_t *src = reinterpret_cast<const uint16_t *>(a.x) + t * a.h;
                 int8_t *dst = reinterpret_cast<int8_t *>(a.expand_x);
-                const float scale = MODE == 1 ? quant_row<F16, VEC>(src, dst, one, 1, a.h, red)
-                                              : quant_row<BF16, VEC>(src, dst, one, 1, a.h, red);
+                const float scale = MODE == 1 ? quant_row_block<F16, VEC>(src, dst, one, 1, a.h, red)
+                                              : quant_row_block<BF16, VEC>(src, dst, one, 1, a.h, red);
                 if (threadIdx.x == 0) a.dyn[row] = scale;
             }
             __syncthreads();
@@ -533,161 +724,126 @@ __global__ __launch_bounds__(kThreads) void segment_payload_kernel(DispatchArgs 
 struct CombineArgs {
     const char *expand_x;
     const int32_t *assist;
-    const int32_t *erc;
-    const int32_t *ids;
     const void *scales;
+    const int32_t *slot;      // [N*K] row of pair (t, k), written by combine_slots_kernel
+    int32_t *slot_out;
     char *x_out;
-    int W, bs, epr, h, K, R;
+    int W, bs, h, K, R, nsl;
     long long rowbytes;
 };
 
-// Row of pair (t, k): inside segment (el*W + s) of rank r = ids[t,k] / epr the
-// rows are in ascending src_token order, so the row is the segment entry whose
-// src_token equals tok; each wave tests 64 entries per step with a ballot.
-__device__ __forceinline__ void combine_rows(const CombineArgs &a, int t, int s, int tok, const int32_t *rbase,
-                                             int32_t *rows, uint32_t *sc)
+// Return path (README 实现逻辑): row i of expand_x belongs to slot
+// (src_token, topk_id) of source rank src_rank. Only its index travels.
+__global__ __launch_bounds__(kSlotThreads) void combine_slots_kernel(CombineArgs a)
 {
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-    const int E = a.W * a.epr, S = a.epr * a.W;
-    for (int k = wid; k < a.K; k += nw) {
+    const int i = blockIdx.x * kSlotThreads + threadIdx.x;
+    if (i >= a.R) return;
+    const int s = a.assist[(size_t)i * 3 + 0], tok = a.assist[(size_t)i * 3 + 1], k = a.assist[(size_t)i * 3 + 2];
+    if ((unsigned)s < (unsigned)a.W && (unsigned)tok < (unsigned)a.bs && (unsigned)k < (unsigned)a.K)
+        a.slot_out[((size_t)s * a.bs + tok) * a.K + k] = i;
+}
+
+__device__ __forceinline__ void gather_prologue(const CombineArgs &a, int t, int *rows, uint32_t *sc)
+{
+    for (int k = threadIdx.x; k < a.K; k += blockDim.x) {
         const size_t p = (size_t)t * a.K + k;
-        const int e = a.ids[p];
-        int row = -1;
-        if ((unsigned)e < (unsigned)E) {
-            const int r = e / a.epr, el = e % a.epr, i = el * a.W + s;
-            int lo = rbase[r] + (i ? a.erc[(size_t)r * S + i - 1] : 0);
-            int hi = rbase[r] + a.erc[(size_t)r * S + i];
-            lo = max(lo, 0);
-            hi = min(hi, a.R);
-            for (int base = lo; base < hi; base += 64) {
-                const int idx = base + lane;
-                const int v = idx < hi ? a.assist[(size_t)idx * 3 + 1] : -1;
-                const unsigned long long m = __ballot(v == tok);
-                if (m) { row = base + __ffsll((long long)m) - 1; break; }
-            }
-        }
-        if (lane == 0) {
-            rows[k] = row;
-            sc[k] = reinterpret_cast<const uint32_t *>(a.scales)[p];
-        }
+        const int row = a.slot[p];
+        rows[k] = (unsigned)row < (unsigned)a.R ? row : -1;
+        sc[k] = reinterpret_cast<const uint32_t *>(a.scales)[p];
     }
+    __syncthreads();
 }
 
+// fp16 / bf16: block = (token, slice of kGatherThreads 16-byte chunks)
 template <class T, bool VEC>
-__global__ __launch_bounds__(kThreads) void combine_half_kernel(CombineArgs a)
+__global__ __launch_bounds__(kGatherThreads) void combine_gather_half_kernel(CombineArgs a)
 {
-    __shared__ int32_t rbase[kMaxWorld + 1];
-    __shared__ int32_t rows[kMaxExperts];
-    __shared__ uint32_t sc[kMaxExperts];
-    __shared__ int tmp[40];
-    const int t = blockIdx.x, s = t / a.bs, tok = t % a.bs;
-    rank_bases(a.erc, a.W, a.epr * a.W, rbase, tmp);
-    __syncthreads();
-    combine_rows(a, t, s, tok, rbase, rows, sc);
-    __syncthreads();
-
+    extern __shared__ int dsm[];
+    int *rows = dsm;
+    uint32_t *sc = reinterpret_cast<uint32_t *>(dsm + a.K);
+    const int t = blockIdx.x / a.nsl, sl = blockIdx.x % a.nsl;
+    gather_prologue(a, t, rows, sc);
     const int K = a.K;
     if (VEC) {
-        const int nch = a.h / 8;
-        constexpr int U = 2, KB = 8;
-        for (int c0 = threadIdx.x; c0 < nch; c0 += kThreads * U) {
-            float acc[U][8];
+        const int nch = a.h / 8, c = sl * kGatherThreads + threadIdx.x;
+        if (c >= nch) return;
+        constexpr int KB = 8;
+        float acc[8];
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+        for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+        for (int kb = 0; kb < K; kb += KB) {
+            uint4 v[KB];
 #pragma unroll
-                for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
-            for (int kb = 0; kb < K; kb += KB) {
-                uint4 v[KB][U];
-#pragma unroll
-                for (int kk = 0; kk < KB; ++kk) {
-                    const int k = kb + kk;
-                    const int row = k < K ? rows[k] : -1;
-                    const uint4 *src = reinterpret_cast<const uint4 *>(a.expand_x + (size_t)(row < 0 ? 0 : row) * a.rowbytes);
-#pragma unroll
-                    for (int u = 0; u < U; ++u) {
-                        const int c = c0 + u * kThreads;
-                        v[kk][u] = (row >= 0 && c < nch) ? src[c] : make_uint4(0u, 0u, 0u, 0u);
-                    }
-                }
-#pragma unroll
-                for (int kk = 0; kk < KB; ++kk) {
-                    if (kb + kk < K && rows[kb + kk] >= 0) {
-                        const float w = __uint_as_float(sc[kb + kk]);
-#pragma unroll
-                        for (int u = 0; u < U; ++u) {
-                            const uint32_t q[4] = {v[kk][u].x, v[kk][u].y, v[kk][u].z, v[kk][u].w};
-#pragma unroll
-                            for (int i = 0; i < 8; ++i)
-                                acc[u][i] = __builtin_fmaf(T::load((uint16_t)(q[i >> 1] >> ((i & 1) * 16))), w, acc[u][i]);
-                        }
-                    }
-                }
+            for (int kk = 0; kk < KB; ++kk) {
+                const int k = kb + kk;
+                const int row = k < K ? rows[k] : -1;
+                v[kk] = row >= 0 ? load_stream(reinterpret_cast<const uint4 *>(a.expand_x + (size_t)row * a.rowbytes) + c)
+                                 : make_uint4(0u, 0u, 0u, 0u);
             }
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int c = c0 + u * kThreads;
-                if (c < nch) {
-                    uint32_t o[4];
+            for (int kk = 0; kk < KB; ++kk) {
+                const int k = kb + kk;
+                if (k < K && rows[k] >= 0) {
+                    const float wgt = __uint_as_float(sc[k]);
+                    const uint32_t q[4] = {v[kk].x, v[kk].y, v[kk].z, v[kk].w};
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        o[i] = (uint32_t)T::store(acc[u][2 * i]) | ((uint32_t)T::store(acc[u][2 * i + 1]) << 16);
-                    reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes)[c] = make_uint4(o[0], o[1], o[2], o[3]);
+                    for (int i = 0; i < 8; ++i)
+                        acc[i] = __builtin_fmaf(T::load((uint16_t)(q[i >> 1] >> ((i & 1) * 16))), wgt, acc[i]);
                 }
             }
         }
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (uint32_t)T::store(acc[2 * i]) | ((uint32_t)T::store(acc[2 * i + 1]) << 16);
+        store_stream(reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes) + c, make_uint4(o[0], o[1], o[2], o[3]));
     } else {
-        for (int j = threadIdx.x; j < a.h; j += kThreads) {
-            float acc = 0.0f;
-            for (int k = 0; k < K; ++k) {
-                const int row = rows[k];
-                if (row < 0) continue;
-                const uint16_t y = reinterpret_cast<const uint16_t *>(a.expand_x)[(size_t)row * a.h + j];
-                acc = __builtin_fmaf(T::load(y), __uint_as_float(sc[k]), acc);
-            }
-            reinterpret_cast<uint16_t *>(a.x_out)[(size_t)t * a.h + j] = T::store(acc);
+        const int j = sl * kGatherThreads + threadIdx.x;
+        if (j >= a.h) return;
+        float acc = 0.0f;
+        for (int k = 0; k < K; ++k) {
+            const int row = rows[k];
+            if (row < 0) continue;
+            const uint16_t y = reinterpret_cast<const uint16_t *>(a.expand_x)[(size_t)row * a.h + j];
+            acc = __builtin_fmaf(T::load(y), __uint_as_float(sc[k]), acc);
         }
+        reinterpret_cast<uint16_t *>(a.x_out)[(size_t)t * a.h + j] = T::store(acc);
     }
 }
 
+// int32: wrapping 32-bit arithmetic, k ascending
 template <bool VEC>
-__global__ __launch_bounds__(kThreads) void combine_i32_kernel(CombineArgs a)
+__global__ __launch_bounds__(kGatherThreads) void combine_gather_i32_kernel(CombineArgs a)
 {
-    __shared__ int32_t rbase[kMaxWorld + 1];
-    __shared__ int32_t rows[kMaxExperts];
-    __shared__ uint32_t sc[kMaxExperts];
-    __shared__ int tmp[40];
-    const int t = blockIdx.x, s = t / a.bs, tok = t % a.bs;
-    rank_bases(a.erc, a.W, a.epr * a.W, rbase, tmp);
-    __syncthreads();
-    combine_rows(a, t, s, tok, rbase, rows, sc);
-    __syncthreads();
-
+    extern __shared__ int dsm[];
+    int *rows = dsm;
+    uint32_t *sc = reinterpret_cast<uint32_t *>(dsm + a.K);
+    const int t = blockIdx.x / a.nsl, sl = blockIdx.x % a.nsl;
+    gather_prologue(a, t, rows, sc);
     const int K = a.K;
     if (VEC) {
-        const int nch = a.h / 4;
-        for (int c = threadIdx.x; c < nch; c += kThreads) {
-            uint32_t acc[4] = {0u, 0u, 0u, 0u};
-            for (int k = 0; k < K; ++k) {
-                const int row = rows[k];
-                if (row < 0) continue;
-                const uint4 v = reinterpret_cast<const uint4 *>(a.expand_x + (size_t)row * a.rowbytes)[c];
-                acc[0] += v.x * sc[k];
-                acc[1] += v.y * sc[k];
-                acc[2] += v.z * sc[k];
-                acc[3] += v.w * sc[k];
-            }
-            reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes)[c] = make_uint4(acc[0], acc[1], acc[2], acc[3]);
+        const int nch = a.h / 4, c = sl * kGatherThreads + threadIdx.x;
+        if (c >= nch) return;
+        uint32_t acc[4] = {0u, 0u, 0u, 0u};
+        for (int k = 0; k < K; ++k) {
+            const int row = rows[k];
+            if (row < 0) continue;
+            const uint4 v = reinterpret_cast<const uint4 *>(a.expand_x + (size_t)row * a.rowbytes)[c];
+            acc[0] += v.x * sc[k];
+            acc[1] += v.y * sc[k];
+            acc[2] += v.z * sc[k];
+            acc[3] += v.w * sc[k];
         }
+        reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes)[c] = make_uint4(acc[0], acc[1], acc[2], acc[3]);
     } else {
-        for (int j = threadIdx.x; j < a.h; j += kThreads) {
-            uint32_t acc = 0u;
-            for (int k = 0; k < K; ++k) {
-                const int row = rows[k];
-                if (row < 0) continue;
-                acc += reinterpret_cast<const uint32_t *>(a.expand_x)[(size_t)row * a.h + j] * sc[k];
-            }
-            reinterpret_cast<uint32_t *>(a.x_out)[(size_t)t * a.h + j] = acc;
+        const int j = sl * kGatherThreads + threadIdx.x;
+        if (j >= a.h) return;
+        uint32_t acc = 0u;
+        for (int k = 0; k < K; ++k) {
+            const int row = rows[k];
+            if (row < 0) continue;
+            acc += reinterpret_cast<const uint32_t *>(a.expand_x)[(size_t)row * a.h + j] * sc[k];
         }
+        reinterpret_cast<uint32_t *>(a.x_out)[(size_t)t * a.h + j] = acc;
     }
 }
 
@@ -709,12 +865,15 @@ int check_scalars(int W, int bs, int epr, int h, int K, int dtype)
     if (E > kMaxExperts || K > E) return MOE_ERR_SHAPE;
     const long long N = (long long)W * bs;
     if (N * K >= (1ll << 31) || N > kMaxTokens) return MOE_ERR_SHAPE;
+    // every (token, slice) grid below has at most N * ceil(h / 128) blocks of <= 128 threads,
+    // and a launch must stay below 2^32 work-items
+    if (N * (((long long)h + 127) / 128) >= (1ll << 25)) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
 struct DispatchLayout {
     int nbs, NB;
-    size_t cnt, boff, lr, plan, nplan, total;
+    size_t pc, pci, boff, lr, plan, nplan, total;
 };
 
 DispatchLayout dispatch_layout(int W, int bs, int epr, int K)
@@ -725,7 +884,8 @@ DispatchLayout dispatch_layout(int W, int bs, int epr, int K)
     L.NB = W * L.nbs;
     const size_t plan_cap = N * K / kPlanRows + 2 * (size_t)W * S + W + 1;
     size_t off = 0;
-    L.cnt = off;   off = round_up(off + (size_t)L.NB * E * 4, 256);
+    L.pc = off;    off = round_up(off + (size_t)L.NB * E * 4, 256);
+    L.pci = off;   off = round_up(off + (size_t)L.NB * E * 4, 256);
     L.boff = off;  off = round_up(off + (size_t)L.NB * E * 4, 256);
     L.lr = off;    off = round_up(off + N * K * 4, 256);
     L.plan = off;  off = round_up(off + plan_cap * 8, 256);
@@ -803,22 +963,27 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
 
     const DispatchLayout L = dispatch_layout(W, bs, epr, K);
     char *ws = static_cast<char *>(workspace);
-    int32_t *cnt = reinterpret_cast<int32_t *>(ws + L.cnt);
+    int32_t *pc = reinterpret_cast<int32_t *>(ws + L.pc);
+    int32_t *pci = reinterpret_cast<int32_t *>(ws + L.pci);
     int32_t *boff = reinterpret_cast<int32_t *>(ws + L.boff);
     int32_t *lr = reinterpret_cast<int32_t *>(ws + L.lr);
     int2 *plan = reinterpret_cast<int2 *>(ws + L.plan);
     int32_t *nplan = reinterpret_cast<int32_t *>(ws + L.nplan);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const int E = W * epr;
+    // blocks sum the chunk prefixes themselves unless there are many chunks (or a
+    // plan is needed); otherwise one scan block forms every offset first
+    const bool direct = N > 0 && mode == MOE_SCHED_TOKEN && L.NB <= kDirectMaxChunks;
 
     (void)hipGetLastError();
     if (N > 0)
-        hipLaunchKernelGGL(route_kernel, dim3(L.NB), dim3(kThreads), (size_t)E * kRouteWords * 8, st,
-                           expert_ids, W, bs, epr, K, L.nbs, cnt, lr);
+        hipLaunchKernelGGL(route_kernel, dim3(L.NB), dim3(kRouteThreads), (size_t)E * kRouteWords * 8, st,
+                           expert_ids, W, bs, epr, K, L.nbs, pc, pci, lr);
     const int elem_out = quant ? 1 : (int)xs;
-    hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), want_seg ? (size_t)W * S * 5 : 0, st,
-                       cnt, W, epr, L.nbs, h, elem_out, boff, ep_recv_count, want_seg ? 1 : 0, large,
-                       seg_flags, (mode == MOE_SCHED_SEGMENT && N > 0) ? plan : nullptr, nplan);
+    if (!direct || want_seg)
+        hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), want_seg ? (size_t)W * S * 5 : 0, st, pc, pci,
+                           W, epr, L.nbs, h, elem_out, boff, ep_recv_count, want_seg ? 1 : 0, large, seg_flags,
+                           (mode == MOE_SCHED_SEGMENT && N > 0) ? plan : nullptr, nplan);
     if (N > 0) {
         DispatchArgs a;
         a.x = static_cast<const char *>(x);
@@ -828,32 +993,68 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         a.dyn = dynamic_scales;
         a.assist = assist_info;
         a.esc_out = static_cast<int32_t *>(expand_scales);
+        a.erc = ep_recv_count;
         a.lr = lr;
+        a.pc = pc;
+        a.pci = pci;
         a.boff = boff;
         a.plan = plan;
         a.nplan = nplan;
         a.W = W; a.bs = bs; a.epr = epr; a.h = h; a.K = K; a.nbs = L.nbs; a.R = (int)(N * K);
+        a.E = E; a.S = (int)S; a.NB = L.NB;
+        // with a scan block present it also wrote ep_recv_count
+        a.direct = (direct && !want_seg) ? 1 : 0;
         a.rowbytes = (long long)rowbytes;
-        const bool vec = quant ? (h % 8 == 0 && aligned(x, 16) && aligned(expand_x, 8))
-                               : (rowbytes % 16 == 0 && aligned(x, 16) && aligned(expand_x, 16));
+        a.nsl = 1;
         if (mode == MOE_SCHED_TOKEN) {
-            const dim3 g((unsigned)N), b(kThreads);
+            const size_t kdsm = (size_t)4 * K * sizeof(int);
             if (!quant) {
-                if (vec) hipLaunchKernelGGL(scatter_copy_kernel<true>, g, b, 0, st, a);
-                else hipLaunchKernelGGL(scatter_copy_kernel<false>, g, b, 0, st, a);
-            } else if (dtype == MOE_FP16) {
-                if (vec) hipLaunchKernelGGL((scatter_quant_kernel<F16, true>), g, b, 0, st, a);
-                else hipLaunchKernelGGL((scatter_quant_kernel<F16, false>), g, b, 0, st, a);
+                const bool vec = rowbytes % 16 == 0 && aligned(x, 16) && aligned(expand_x, 16);
+                const long long n = vec ? (long long)(rowbytes / 16) : (long long)(rowbytes / 2);
+                const int sc = kCopyThreads * kCopyUnroll;
+                a.nsl = (int)((n + sc - 1) / sc);
+                const dim3 g((unsigned)(N * a.nsl)), b(kCopyThreads);
+                if (vec) hipLaunchKernelGGL(scatter_copy_kernel<true>, g, b, kdsm, st, a);
+                else hipLaunchKernelGGL(scatter_copy_kernel<false>, g, b, kdsm, st, a);
             } else {
-                if (vec) hipLaunchKernelGGL((scatter_quant_kernel<BF16, true>), g, b, 0, st, a);
-                else hipLaunchKernelGGL((scatter_quant_kernel<BF16, false>), g, b, 0, st, a);
+                const bool wave = h % 16 == 0 && h <= 1024 * 8 && K <= kQuantMaxK && aligned(x, 16) &&
+                                  aligned(expand_x, 16);
+                if (wave) {
+                    const int J = (h / 16 + 63) / 64;
+                    const dim3 g((unsigned)std::min<long long>((N + 3) / 4, kQuantMaxBlocks)), b(kQuantThreads);
+                    if (dtype == MOE_FP16) {
+                        if (J <= 1) hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 1>), g, b, 0, st, a);
+                        else if (J <= 2) hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 2>), g, b, 0, st, a);
+                        else if (J <= 4) hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 4>), g, b, 0, st, a);
+                        else if (J <= 7) hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 7>), g, b, 0, st, a);
+                        else hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 8>), g, b, 0, st, a);
+                    } else {
+                        if (J <= 1) hipLaunchKernelGGL((scatter_quant_wave_kernel<BF16, 1>), g, b, 0, st, a);
+                        else if (J <= 2) hipLaunchKernelGGL((scatter_quant_wave_kernel<BF16, 2>), g, b, 0, st, a);
+                        else if (J <= 4) hipLaunchKernelGGL((scatter_quant_wave_kernel<BF16, 4>), g, b, 0, st, a);
+                        else if (J <= 7) hipLaunchKernelGGL((scatter_quant_wave_kernel<BF16, 7>), g, b, 0, st, a);
+                        else hipLaunchKernelGGL((scatter_quant_wave_kernel<BF16, 8>), g, b, 0, st, a);
+                    }
+                } else {
+                    const bool vec = h % 8 == 0 && aligned(x, 16) && aligned(expand_x, 8);
+                    const dim3 g((unsigned)N), b(kBlockThreads);
+                    if (dtype == MOE_FP16) {
+                        if (vec) hipLaunchKernelGGL((scatter_quant_block_kernel<F16, true>), g, b, kdsm, st, a);
+                        else hipLaunchKernelGGL((scatter_quant_block_kernel<F16, false>), g, b, kdsm, st, a);
+                    } else {
+                        if (vec) hipLaunchKernelGGL((scatter_quant_block_kernel<BF16, true>), g, b, kdsm, st, a);
+                        else hipLaunchKernelGGL((scatter_quant_block_kernel<BF16, false>), g, b, kdsm, st, a);
+                    }
+                }
             }
         } else {
             const long long npairs = N * K;
-            hipLaunchKernelGGL(segment_meta_kernel, dim3((unsigned)((npairs + kThreads - 1) / kThreads)),
-                               dim3(kThreads), 0, st, a);
-            const dim3 g(kSegGrid), b(kThreads);
+            hipLaunchKernelGGL(segment_meta_kernel, dim3((unsigned)((npairs + kBlockThreads - 1) / kBlockThreads)),
+                               dim3(kBlockThreads), 0, st, a);
+            const dim3 g(kSegGrid), b(kBlockThreads);
             const int qm = !quant ? 0 : (dtype == MOE_FP16 ? 1 : 2);
+            const bool vec = quant ? (h % 8 == 0 && aligned(x, 16) && aligned(expand_x, 8))
+                                   : (rowbytes % 16 == 0 && aligned(x, 16) && aligned(expand_x, 16));
             if (qm == 0) {
                 if (vec) hipLaunchKernelGGL((segment_payload_kernel<0, true>), g, b, 0, st, a);
                 else hipLaunchKernelGGL((segment_payload_kernel<0, false>), g, b, 0, st, a);
@@ -875,7 +1076,7 @@ int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h
     if (!bytes) return MOE_ERR_NULLPTR;
     int rc = check_scalars(ep_world, bs, experts_per_rank, h, topk, dtype);
     if (rc) return rc;
-    *bytes = 0;
+    *bytes = round_up((size_t)ep_world * bs * topk * 4, 256);
     return MOE_OK;
 }
 
@@ -889,37 +1090,42 @@ int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t 
     const int W = ep_world, K = topk;
     const long long N = (long long)W * bs;
     if (!ep_recv_count) return MOE_ERR_NULLPTR;
-    if (N > 0 && (!expand_x || !assist_info || !expert_ids || !expert_scales || !x_out)) return MOE_ERR_NULLPTR;
+    if (N > 0 && (!expand_x || !assist_info || !expert_ids || !expert_scales || !x_out || !workspace))
+        return MOE_ERR_NULLPTR;
     if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
-    (void)workspace;
     const size_t xs = elem_size(dtype);
     if (!aligned(expand_x, xs) || !aligned(assist_info, 4) || !aligned(ep_recv_count, 4) ||
-        !aligned(expert_ids, 4) || !aligned(expert_scales, 4) || !aligned(x_out, xs))
+        !aligned(expert_ids, 4) || !aligned(expert_scales, 4) || !aligned(x_out, xs) || !aligned(workspace, 16))
         return MOE_ERR_ALIGN;
     if (N == 0) return MOE_OK;
 
     CombineArgs a;
     a.expand_x = static_cast<const char *>(expand_x);
     a.assist = assist_info;
-    a.erc = ep_recv_count;
-    a.ids = expert_ids;
     a.scales = expert_scales;
+    a.slot = static_cast<const int32_t *>(workspace);
+    a.slot_out = static_cast<int32_t *>(workspace);
     a.x_out = static_cast<char *>(x_out);
-    a.W = W; a.bs = bs; a.epr = experts_per_rank; a.h = h; a.K = K; a.R = (int)(N * K);
+    a.W = W; a.bs = bs; a.h = h; a.K = K; a.R = (int)(N * K);
     a.rowbytes = (long long)((size_t)h * xs);
     const bool vec = (size_t)a.rowbytes % 16 == 0 && aligned(expand_x, 16) && aligned(x_out, 16);
+    const long long n = vec ? a.rowbytes / 16 : h;
+    a.nsl = (int)((n + kGatherThreads - 1) / kGatherThreads);
     hipStream_t st = static_cast<hipStream_t>(stream);
-    const dim3 g((unsigned)N), b(kThreads);
+    const size_t kdsm = (size_t)2 * K * sizeof(int);
+    const dim3 g((unsigned)(N * a.nsl)), b(kGatherThreads);
     (void)hipGetLastError();
+    hipLaunchKernelGGL(combine_slots_kernel, dim3((unsigned)((a.R + kSlotThreads - 1) / kSlotThreads)),
+                       dim3(kSlotThreads), 0, st, a);
     if (dtype == MOE_INT32) {
-        if (vec) hipLaunchKernelGGL(combine_i32_kernel<true>, g, b, 0, st, a);
-        else hipLaunchKernelGGL(combine_i32_kernel<false>, g, b, 0, st, a);
+        if (vec) hipLaunchKernelGGL(combine_gather_i32_kernel<true>, g, b, kdsm, st, a);
+        else hipLaunchKernelGGL(combine_gather_i32_kernel<false>, g, b, kdsm, st, a);
     } else if (dtype == MOE_FP16) {
-        if (vec) hipLaunchKernelGGL((combine_half_kernel<F16, true>), g, b, 0, st, a);
-        else hipLaunchKernelGGL((combine_half_kernel<F16, false>), g, b, 0, st, a);
+        if (vec) hipLaunchKernelGGL((combine_gather_half_kernel<F16, true>), g, b, kdsm, st, a);
+        else hipLaunchKernelGGL((combine_gather_half_kernel<F16, false>), g, b, kdsm, st, a);
     } else {
-        if (vec) hipLaunchKernelGGL((combine_half_kernel<BF16, true>), g, b, 0, st, a);
-        else hipLaunchKernelGGL((combine_half_kernel<BF16, false>), g, b, 0, st, a);
+        if (vec) hipLaunchKernelGGL((combine_gather_half_kernel<BF16, true>), g, b, kdsm, st, a);
+        else hipLaunchKernelGGL((combine_gather_half_kernel<BF16, false>), g, b, kdsm, st, a);
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
 }

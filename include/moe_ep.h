@@ -122,7 +122,7 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
  *
  * Ranges: ep_world in [2, 768], experts_per_rank >= 1, E <= 1024,
  * 1 <= topk <= E, bs >= 0 (bs == 0 writes zero counts and nothing else),
- * h >= 1, N*K < 2^31, N < 2^24. Ids outside [0, E) or repeated within a token are a
+ * h >= 1, N*K < 2^31, N < 2^24, N*ceil(h/128) < 2^25. Ids outside [0, E) or repeated within a token are a
  * precondition violation: the kernels stay in bounds but the outputs are
  * unspecified. Outputs are bitwise deterministic.
  */
@@ -132,26 +132,34 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                  int32_t *ep_recv_count, void *expand_scales, const moe_schedule *schedule,
                  void *workspace, size_t workspace_bytes, void *stream);
 
-/* Phase one of combine: validates the scalars and writes the workspace size. */
+/* Phase one of combine: validates the scalars and writes the workspace size
+ * (N*K int32 slots, rounded up to 256 bytes). */
 int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h, int topk,
                                int dtype, size_t *bytes);
 
 /*
  * Combine (README 功能说明, check formula):
  *   x_out[t] = sum_k expand_x[row(t, k)] * expert_scales[t, k]
- * where row(t, k) is the row dispatch gave to pair (t, k). It is recovered
- * from ep_recv_count (segment bounds of expert ids[t, k] and source rank s)
- * and assist_info (the row of that segment whose src_token is tok).
+ * where row(t, k) is the row dispatch gave to pair (t, k). As in the README's
+ * 实现逻辑, every expand_x row is returned to its source: row i goes to slot
+ * (src_token, topk_id) of rank src_rank as named by assist_info[i]; on one
+ * GPU only the row index travels (into the workspace) and the source's
+ * weighted sum gathers the rows through those slots.
  * fp16/bf16: accumulated in fp32, one fused multiply-add per k with k
  * ascending from 0.0f, rounded once to nearest-even; int32: wrapping 32-bit
  * integer arithmetic.
  *
  *  expand_x       [ROWS, h] dtype (fp16, bf16 or int32; the expert outputs)
- *  assist_info    [ROWS, 3], ep_recv_count [W, S]: dispatch's, unchanged
- *  expert_ids     [N, K] int32: the ids given to dispatch
+ *  assist_info    [ROWS, 3]: dispatch's, unchanged
+ *  ep_recv_count  [W, S]: dispatch's, unchanged (checked for presence and alignment;
+ *                 the rows are located through assist_info)
+ *  expert_ids     [N, K] int32: the ids given to dispatch (checked likewise)
  *  expert_scales  [N, K] fp32 for fp16/bf16, int32 for int32 data
  *  x_out          [N, h] dtype
- * The scalars must equal those given to dispatch.
+ *  workspace      device scratch of at least the queried size
+ * The scalars must equal those given to dispatch. Rows that assist_info does
+ * not name leave their slot undefined; the kernels stay in bounds but the
+ * affected outputs are unspecified.
  */
 int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t *ep_recv_count,
                 const int32_t *expert_ids, const void *expert_scales, int ep_world, int bs,

@@ -62,6 +62,7 @@ def _ws(*args):
     ((2, 4, 2, 0, 1, 0, 0), SHAPE),           # h 0
     ((2, 4, 0, 16, 1, 0, 0), SHAPE),          # no experts
     ((512, 40000, 2, 16, 1, 0, 0), SHAPE),    # N beyond the launch limit
+    ((64, 2048, 2, 65536, 1, 1, 0), SHAPE),   # N * ceil(h/128) beyond the slice-grid limit
     ((8, 2 ** 27, 8, 16, 8, 0, 0), SHAPE),    # N*K >= 2^31
     ((2, 4, 2, 16, 1, 3, 0), DTYPE),
     ((2, 4, 2, 16, 1, 1, 1), QUANT),          # quant mode 1 not offered
@@ -84,7 +85,7 @@ def test_combine_workspace_query():
     n = ctypes.c_size_t(7)
     lib = moe.library()
     assert lib.moe_combine_workspace_size(8, 32, 8, 7168, 8, 1, ctypes.byref(n)) == OK
-    assert n.value == 0
+    assert n.value == 8 * 32 * 8 * 4
     assert lib.moe_combine_workspace_size(1, 32, 8, 7168, 8, 1, ctypes.byref(n)) == SHAPE
     assert lib.moe_combine_workspace_size(8, 32, 8, 7168, 8, 5, ctypes.byref(n)) == DTYPE
     assert lib.moe_combine_workspace_size(8, 32, 8, 7168, 8, 1, None) == NULLPTR
@@ -134,11 +135,13 @@ def test_dispatch_rejects_before_launch(kw, want):
 
 
 def _combine(**kw):
-    p = dict(ex=A, assist=2 * A, erc=3 * A, ids=4 * A, sc=5 * A, W=2, bs=4, epr=2, h=16, K=2, dtype=1, out=6 * A)
+    p = dict(ex=A, assist=2 * A, erc=3 * A, ids=4 * A, sc=5 * A, W=2, bs=4, epr=2, h=16, K=2, dtype=1, out=6 * A,
+             ws=7 * A, wsb=1 << 30)
     p.update(kw)
     P = lambda v: None if v is None else ctypes.c_void_p(v)
     return moe.library().moe_combine(P(p["ex"]), P(p["assist"]), P(p["erc"]), P(p["ids"]), P(p["sc"]), p["W"],
-                                     p["bs"], p["epr"], p["h"], p["K"], p["dtype"], P(p["out"]), None, 0, None)
+                                     p["bs"], p["epr"], p["h"], p["K"], p["dtype"], P(p["out"]), P(p["ws"]),
+                                     p["wsb"], None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -151,7 +154,10 @@ def _combine(**kw):
     (dict(ids=None), NULLPTR),
     (dict(sc=None), NULLPTR),
     (dict(out=None), NULLPTR),
+    (dict(ws=None), NULLPTR),
+    (dict(wsb=8 * 4 * 2 - 1), WORKSPACE),
     (dict(ex=A + 1), ALIGN),
+    (dict(ws=7 * A + 4), ALIGN),
     (dict(out=6 * A + 1), ALIGN),
     (dict(dtype=0, ex=A + 2), ALIGN),
     (dict(bs=0), OK),                                # empty batch: nothing to launch

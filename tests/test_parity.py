@@ -171,6 +171,16 @@ def test_zero_tokens_quantise_to_zero():
     assert (g["dynamic_scales"][np.isin(t, [0, 5, 9])] == 0).all()
 
 
+@pytest.mark.parametrize("exp", [-90, -120], ids=["tiny_fast_path", "subnormal_division_path"])
+def test_tiny_tokens_quantise_exactly(exp):
+    """Scales below 2^-100 take the IEEE division; just above it the FMA step."""
+    w = wl.custom(2, 8, 64, 2, 2, "bf16", "gauss_topk", quant_mode=2, name="tiny")
+    inp = wl.make_inputs(w)
+    g = np.random.default_rng(17).standard_normal((w.num_tokens, w.h)).astype(np.float32) * np.float32(2.0 ** exp)
+    inp["x"] = wl.f32_to_bf16_bits(g)
+    check(w, inp)
+
+
 def test_int32_combine_wraps_like_the_oracle():
     w = wl.custom(2, 4, 16, 2, 2, "int32", x_lo=-(2 ** 31), x_hi=2 ** 31 - 1, name="int32_wrap")
     check(w)
