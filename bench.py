@@ -151,6 +151,8 @@ def main():
     ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (HBM counter calibration)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -163,6 +165,17 @@ def main():
     import combine_ep_recv_amd as moe
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.calibrate_copy:
+        n = 256 << 20
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(7)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "device-to-device copy", "bytes_read": n, "bytes_written": n,
+                          "launches": 5}), flush=True)
+        return
     moe.library()
     flush = torch.empty(1 << 27, dtype=torch.int64, device="cuda").fill_(1)   # 1 GiB
 

@@ -6,10 +6,12 @@
  * fp32 quotient. The kernel replaces the division by one correction step:
  *     inv = RN(1 / scale), q0 = RN(x * inv), r = fma(-q0, scale, x),
  *     q = RN(fma(r, inv, q0))
- * and claims rint(q) == rint(RN(x / scale)) whenever scale >= 2^-100. This
- * program checks that claim for every finite 16-bit x (bf16 or fp16) and every
- * positive finite 16-bit amax with |x| <= amax, i.e. for every pair a token row
- * can produce. Prints the counts; exits 1 on any integer mismatch.
+ * and claims rint(q) == rint(RN(x / scale)) whenever scale >= 2^-100; it also
+ * relies on |rint(q)| <= 127 (no clamp) and forms rint(q) as RN(q + 1.5 * 2^23),
+ * whose low byte is the two's-complement code. This program checks those claims
+ * for every finite 16-bit x (bf16 or fp16) and every positive finite 16-bit amax
+ * with |x| <= amax, i.e. for every pair a token row can produce. Prints the
+ * counts; exits 1 on any mismatch.
  */
 #include <math.h>
 #include <stdint.h>
@@ -28,8 +30,8 @@ static float from_fp16(uint16_t h)
 int main(int argc, char **argv)
 {
     const int bf = argc > 1 && argv[1][0] == 'b';
-    long long pairs = 0, int_bad = 0, quot_bad = 0, slow_scales = 0;
-#pragma omp parallel for reduction(+ : pairs, int_bad, quot_bad, slow_scales) schedule(dynamic, 64)
+    long long pairs = 0, int_bad = 0, quot_bad = 0, slow_scales = 0, range_bad = 0, byte_bad = 0;
+#pragma omp parallel for reduction(+ : pairs, int_bad, quot_bad, slow_scales, range_bad, byte_bad) schedule(dynamic, 64)
     for (int a = 1; a < 0x8000; ++a) {
         const float amax = bf ? from_bf16((uint16_t)a) : from_fp16((uint16_t)a);
         if (!isfinite(amax) || amax <= 0.0f) continue;
@@ -47,9 +49,15 @@ int main(int argc, char **argv)
             pairs++;
             quot_bad += q != d;
             int_bad += rintf(q) != rintf(d);
+            range_bad += fabsf(rintf(d)) > 127.0f;
+            const float u = q + 0x1.8p23f;
+            uint32_t ub;
+            memcpy(&ub, &u, 4);
+            byte_bad += (int8_t)(ub & 0xff) != (int8_t)(int)rintf(d);
         }
     }
-    printf("%s pairs=%lld integer_mismatches=%lld quotient_mismatches=%lld scales_below_2^-100=%lld\n",
-           bf ? "bf16" : "fp16", pairs, int_bad, quot_bad, slow_scales);
-    return int_bad != 0;
+    printf("%s pairs=%lld integer_mismatches=%lld quotient_mismatches=%lld out_of_range=%lld byte_mismatches=%lld "
+           "scales_below_2^-100=%lld\n", bf ? "bf16" : "fp16", pairs, int_bad, quot_bad, range_bad, byte_bad,
+           slow_scales);
+    return int_bad != 0 || range_bad != 0 || byte_bad != 0;
 }
