@@ -118,6 +118,22 @@ def measure(w, steps, warmup, flush, torch, moe):
     return dict(step=ms_step, disp=ms_disp, comb=ms_comb, cold=cold)
 
 
+def counted_traffic(w):
+    """HBM bytes per moe_combine launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (profiles/), or None when the kernel source has changed since they were taken."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.json" % w.name)
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
+        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
+            return None
+    return rec["per_launch_bytes"]["moe_combine"]
+
+
 def cpu_baseline(w, reps=3):
     """The oracle as it stands (single-threaded C), timed on the host."""
     import oracle
@@ -219,7 +235,7 @@ def main():
         "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
         "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
         "roofline": {"bound": "hbm", "achieved": round(comb_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(comb_gbps / HBM_PEAK_GBPS, 4), "traffic": None, "kernel": kernel,
+                     "frac": round(comb_gbps / HBM_PEAK_GBPS, 4), "traffic": counted_traffic(w), "kernel": kernel,
                      "bytes_per_launch": comb_b, "avg_launch_ms": round(comb_ms, 5)},
         "timing": {"protocol": "%d steps back to back between two HIP events on the kernels' stream, "
                                "synchronised before and after" % args.steps,
