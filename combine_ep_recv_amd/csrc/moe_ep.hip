@@ -58,7 +58,6 @@ constexpr int kCopyThreads = 128;          // token-major copy: block = (token, 
 constexpr int kCopyUnroll = 2;             // 16-byte chunks per thread per slice
 constexpr int kQuantThreads = 256;         // one wavefront per token
 constexpr int kQuantMaxK = 64;             // wavefront-per-token quantiser handles topk <= 64
-constexpr int kQuantMaxBlocks = 1 << 30;   // blocks of the quantiser (each loops over groups of 4 tokens)
 constexpr int kBlockThreads = 256;         // generic block-per-token kernels
 constexpr int kGatherThreads = 128;        // combine: block = (token, 128-chunk slice)
 constexpr int kSlotThreads = 256;
@@ -446,19 +445,55 @@ __device__ __forceinline__ void pairs_finish(const DispatchArgs &a, int t, const
     }
 }
 
+// Row of pair (t, lane) for lanes < K (-1 for other lanes and invalid pairs), from
+// registers only: the chunk prefixes are summed by the lane itself (direct path)
+// or read from the scan's table. Writes assist_info / expand_scales when asked.
+__device__ __forceinline__ int lane_pair_row(const DispatchArgs &a, int t, int lane, int e, int l, bool meta)
+{
+    const int s = t / a.bs, tok = t - s * a.bs;
+    int row = -1;
+    if (lane < a.K && (unsigned)e < (unsigned)a.E && l >= 0) {
+        const int bt = s * a.nbs + tok / kRouteTokens;
+        int off = 0;
+        if (a.direct) {
+#pragma unroll 8
+            for (int b = 0; b < a.NB; ++b) off += (b < bt ? a.pci : a.pc)[(size_t)b * a.E + e];
+        } else {
+            off = a.boff[(size_t)bt * a.E + e];
+        }
+        row = off + l;
+        if ((unsigned)row >= (unsigned)a.R) row = -1;
+    }
+    if (meta && row >= 0) {
+        a.assist[(size_t)row * 3 + 0] = s;
+        a.assist[(size_t)row * 3 + 1] = tok;
+        a.assist[(size_t)row * 3 + 2] = lane;
+        if (a.esc_out) a.esc_out[row] = a.esc_in[(size_t)t * a.K + lane];
+    }
+    return row;
+}
+
 // Token-major copy: block = (token, slice of kCopyThreads * kCopyUnroll chunks).
+// For topk <= 64 each wavefront resolves the K rows in its own lanes (pair k in
+// lane k, loaded before the payload) and reads them back with readlane: no LDS and
+// no barrier; larger topk goes through LDS.
 template <bool VEC>
 __global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(DispatchArgs a)
 {
-    extern __shared__ int dsm[];                  // ek, lk, off, rows: 4 * K ints
-    int *ek = dsm, *lk = dsm + a.K, *off = dsm + 2 * a.K, *rows = dsm + 3 * a.K;
+    extern __shared__ int dsm[];                  // ek, lk, off, rows: 4 * K ints (topk > 64 only)
     const int t = blockIdx.x / a.nsl, sl = blockIdx.x % a.nsl;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
     constexpr int SC = kCopyThreads * kCopyUnroll;
 
     if (a.direct) write_erc_direct(a, (size_t)blockIdx.x * kCopyThreads + tid, (size_t)gridDim.x * kCopyThreads);
 
-    // issue the payload loads first; row resolution overlaps them
+    const bool small_k = a.K <= 64;
+    int e = -1, l = -1;
+    if (small_k) {
+        const size_t pk = (size_t)t * a.K + (lane < a.K ? lane : 0);
+        e = a.ids[pk];
+        l = a.lr[pk];
+    }
     const char *src = a.x + (size_t)t * a.rowbytes;
     const int n = VEC ? (int)(a.rowbytes / 16) : (int)(a.rowbytes / 2);
     const int c0 = sl * SC + tid;
@@ -470,13 +505,30 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(DispatchArgs
         if constexpr (VEC) v[u] = c < n ? reinterpret_cast<const uint4 *>(src)[c] : make_uint4(0u, 0u, 0u, 0u);
         else w[u] = c < n ? reinterpret_cast<const uint16_t *>(src)[c] : (uint16_t)0;
     }
+
+    if (small_k) {
+        const int my_row = lane_pair_row(a, t, lane, e, l, sl == 0 && tid < 64);
+#pragma unroll
+        for (int u = 0; u < kCopyUnroll; ++u) {
+            const int c = c0 + u * kCopyThreads;
+            for (int k = 0; k < a.K; ++k) {
+                const int row = __builtin_amdgcn_readlane(my_row, k);
+                if (row < 0 || c >= n) continue;
+                char *dst = a.expand_x + (size_t)row * a.rowbytes;
+                if constexpr (VEC) store_stream(reinterpret_cast<uint4 *>(dst) + c, v[u]);
+                else reinterpret_cast<uint16_t *>(dst)[c] = w[u];
+            }
+        }
+        return;
+    }
+
+    int *ek = dsm, *lk = dsm + a.K, *off = dsm + 2 * a.K, *rows = dsm + 3 * a.K;
     pairs_load(a, t, ek, lk, off, tid, kCopyThreads);
     __syncthreads();
     pairs_sum(a, t, ek, off, tid, kCopyThreads);
     __syncthreads();
     pairs_finish(a, t, ek, lk, off, rows, sl == 0, tid, kCopyThreads);
     __syncthreads();
-
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
         const int c = c0 + u * kCopyThreads;
@@ -491,13 +543,6 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(DispatchArgs
     }
 }
 
-// q = rint(v / scale) with the quotient correctly rounded, clamped to [-127, 127].
-// FAST: one correction step replaces the division. With inv = RN(1 / scale),
-// q0 = RN(v * inv) and the exact residual r = v - q0 * scale (one FMA), RN(q0 + r * inv)
-// gives the same integer after rint as the correctly rounded quotient for every
-// finite bf16 and fp16 v with |v| <= amax and scale = amax / 127 >= 2^-100; this was
-// checked exhaustively over all such (v, amax) pairs. Smaller scales (subnormal
-// tokens) take the IEEE division.
 template <bool FAST>
 __device__ __forceinline__ int8_t quant1(float v, float scale, float inv)
 {
@@ -553,79 +598,58 @@ __device__ __forceinline__ uint2 quant_u4(uint4 v, float scale, float inv)
 }
 
 // Per-token dynamic int8 quantisation (aclnnMoeDistributeDispatchV4 quantMode 2):
-// scale = max|x| / 127 (fp32, correctly rounded), q = rint(x / scale) clamped to
-// [-127, 127] (0 for an all-zero token), written to every destination row.
-// One wavefront per token; needs h % 16 == 0, h <= 1024 * J, topk <= kQuantMaxK.
+// scale = max|x| / 127 (fp32, correctly rounded), q = rint(x / scale) (0 for an
+// all-zero token), written to every destination row. One wavefront per token:
+// lane k loads pair k's id and in-chunk rank before the row's 16-byte loads, so
+// both are in flight together; rows reach the store loop through readlane. No
+// LDS, no barrier. Needs h % 16 == 0, h <= 1024 * J, topk <= kQuantMaxK.
 template <class T, int J>
 __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(DispatchArgs a)
 {
-    __shared__ int sm[kQuantThreads / 64][4 * kQuantMaxK];
-    constexpr int WPB = kQuantThreads / 64;
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    const int N = a.W * a.bs;
-    int *ek = sm[wid], *lk = ek + kQuantMaxK, *off = lk + kQuantMaxK, *rows = off + kQuantMaxK;
-
+    const int lane = threadIdx.x & 63;
+    const int N = a.W * a.bs, K = a.K, noc = a.h / 16;
     if (a.direct) write_erc_direct(a, (size_t)blockIdx.x * kQuantThreads + threadIdx.x,
                                    (size_t)gridDim.x * kQuantThreads);
-
-    const int noc = a.h / 16;                     // 16-byte output chunks (two 16-byte input chunks each)
-    // blocks stride over groups of WPB tokens; the loop bound is uniform per block
-    for (int tb = blockIdx.x * WPB; tb < N; tb += gridDim.x * WPB) {
-        const int t = tb + wid;
-        const bool live = t < N;
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)(live ? t : 0) * a.rowbytes);
+    const int nwaves = gridDim.x * (kQuantThreads / 64);
+    for (int t = blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6); t < N; t += nwaves) {
+        const size_t pk = (size_t)t * K + (lane < K ? lane : 0);
+        const int e = a.ids[pk], l = a.lr[pk];
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
         uint4 v[J][2];
 #pragma unroll
         for (int j = 0; j < J; ++j) {
-            const int oc = lane + 64 * j;
-            if (live && oc < noc) {
-                v[j][0] = src[2 * oc];
-                v[j][1] = src[2 * oc + 1];
+            const int oc = min(lane + 64 * j, noc - 1);     // duplicate loads past the row end are ignored
+            v[j][0] = src[2 * oc];
+            v[j][1] = src[2 * oc + 1];
+        }
+        const int my_row = lane_pair_row(a, t, lane, e, l, true);
+
+        float amax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < J; ++j)
+            if (lane + 64 * j < noc) amax = fmaxf(amax, fmaxf(amax_u4<T>(v[j][0]), amax_u4<T>(v[j][1])));
+        amax = wave_max(amax);
+        const float scale = amax / 127.0f;
+        const float inv = 1.0f / scale;
+        const bool fast = scale >= kFastQuantMinScale;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            if (lane + 64 * j >= noc) continue;
+            uint2 lo, hi;
+            if (fast) {
+                lo = quant_u4<T, true>(v[j][0], scale, inv);
+                hi = quant_u4<T, true>(v[j][1], scale, inv);
             } else {
-                v[j][0] = v[j][1] = make_uint4(0u, 0u, 0u, 0u);
+                lo = quant_u4<T, false>(v[j][0], scale, inv);
+                hi = quant_u4<T, false>(v[j][1], scale, inv);
+            }
+            const uint4 q = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            for (int k = 0; k < K; ++k) {
+                const int row = __builtin_amdgcn_readlane(my_row, k);
+                if (row >= 0) store_stream(reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + lane + 64 * j, q);
             }
         }
-        if (live) pairs_load(a, t, ek, lk, off, lane, 64);
-        __syncthreads();
-        if (live) pairs_sum(a, t, ek, off, lane, 64);
-        __syncthreads();
-        if (live) pairs_finish(a, t, ek, lk, off, rows, true, lane, 64);
-        __syncthreads();
-        if (live) {
-            float amax = 0.0f;
-#pragma unroll
-            for (int j = 0; j < J; ++j)
-                if (lane + 64 * j < noc) amax = fmaxf(amax, fmaxf(amax_u4<T>(v[j][0]), amax_u4<T>(v[j][1])));
-            amax = wave_max(amax);
-            const float scale = amax / 127.0f;
-            const float inv = 1.0f / scale;
-            char *const dst0 = a.expand_x;
-            const int h = a.h, K = a.K;
-            auto emit = [&](int j, uint4 q) {
-                for (int k = 0; k < K; ++k) {
-                    const int row = rows[k];
-                    if (row >= 0) store_stream(reinterpret_cast<uint4 *>(dst0 + (size_t)row * h) + lane + 64 * j, q);
-                }
-            };
-            if (scale >= kFastQuantMinScale) {
-#pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    if (lane + 64 * j >= noc) continue;
-                    const uint2 lo = quant_u4<T, true>(v[j][0], scale, inv), hi = quant_u4<T, true>(v[j][1], scale, inv);
-                    emit(j, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                }
-            } else {
-#pragma unroll
-                for (int j = 0; j < J; ++j) {
-                    if (lane + 64 * j >= noc) continue;
-                    const uint2 lo = quant_u4<T, false>(v[j][0], scale, inv), hi = quant_u4<T, false>(v[j][1], scale, inv);
-                    emit(j, make_uint4(lo.x, lo.y, hi.x, hi.y));
-                }
-            }
-            for (int k = lane; k < a.K; k += 64)
-                if (rows[k] >= 0) a.dyn[rows[k]] = scale;
-        }
-        __syncthreads();                          // rows[] is rewritten by the next group
+        if (my_row >= 0) a.dyn[my_row] = scale;
     }
 }
 
@@ -1046,7 +1070,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                                   aligned(expand_x, 16);
                 if (wave) {
                     const int J = (h / 16 + 63) / 64;
-                    const dim3 g((unsigned)std::min<long long>((N + 3) / 4, kQuantMaxBlocks)), b(kQuantThreads);
+                    const dim3 g((unsigned)((N + 3) / 4)), b(kQuantThreads);
                     if (dtype == MOE_FP16) {
                         if (J <= 1) hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 1>), g, b, 0, st, a);
                         else if (J <= 2) hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 2>), g, b, 0, st, a);

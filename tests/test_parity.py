@@ -145,6 +145,8 @@ EDGE = [
     wl.custom(2, 5, 16, 4, 2, "int32", name="topk_equals_experts"),
     wl.custom(4, 1, 24, 1, 1, "fp16", "gauss_topk", name="topk1_bs1"),
     wl.custom(3, 70, 7176, 5, 3, "bf16", "zipf_topk", name="bf16_h7176_ragged_tiles"),
+    wl.custom(2, 3, 16, 70, 40, "int32", name="topk70_copy_lds_path"),
+    wl.custom(2, 2, 32, 66, 40, "bf16", "gauss_topk", quant_mode=2, name="topk66_quant_block_path"),
 ]
 
 
