@@ -226,6 +226,49 @@ def test_schedules_are_result_neutral_and_flag_the_right_segments(w, mode, T):
 
 
 # --------------------------------------------------------------------------
+# the wavefront-per-token quantiser across its row-length templates and the
+# two offset paths (chunk prefixes summed per pair up to 64 chunks, scan beyond)
+# --------------------------------------------------------------------------
+
+QUANT_WAVE = [
+    wl.custom(2, 5, 16, 3, 2, "bf16", "gauss_topk", quant_mode=2, name="h16_one_chunk_per_lane"),
+    wl.custom(3, 300, 1040, 4, 3, "fp16", "zipf_topk", quant_mode=2, name="h1040_two_chunks_per_rank"),
+    wl.custom(4, 257, 8192, 2, 4, "bf16", "gauss_topk", quant_mode=2, name="h8192_ragged_chunks"),
+    wl.custom(64, 3, 64, 2, 4, "fp16", "gauss_topk", quant_mode=2, name="64_chunks_direct_offsets"),
+    wl.custom(8, 16, 32, 8, 128, "bf16", "gauss_topk", quant_mode=2, name="e1024_quantised"),
+    wl.custom(65, 2, 64, 2, 4, "bf16", "gauss_topk", quant_mode=2, name="65_chunks_scanned_offsets"),
+]
+
+
+@pytest.mark.parametrize("w", QUANT_WAVE, ids=lambda w: w.name)
+def test_quantiser_shapes(w):
+    check(w)
+
+
+def test_workspace_contents_on_entry_do_not_matter():
+    """Dispatch into a workspace holding other bytes, or an earlier call's
+    counts for other ids, gives the same outputs."""
+    w = wl.custom(4, 300, 256, 4, 3, "bf16", "zipf_topk", quant_mode=2, name="stale_workspace")
+    print("parity case %s" % w.name, flush=True)
+    inp_a, inp_b = wl.make_inputs(w, seed=11), wl.make_inputs(w, seed=12)
+    o = run_oracle(w, inp_b)
+    buf = moe.DispatchBuffers(w.ep_world, w.bs, w.experts_per_rank, w.h, w.topk, torch.bfloat16, 2, DEV)
+    xa, ida = to_dev(inp_a["x"], True), to_dev(inp_a["ids"])
+    xb, idb = to_dev(inp_b["x"], True), to_dev(inp_b["ids"])
+    for fill in (None, 0x00, 0xFF, 0x80):
+        if fill is None:
+            moe.dispatch_into(buf, xa, ida)          # leaves this call's counts behind
+        else:
+            buf.workspace.fill_(fill)
+        moe.dispatch_into(buf, xb, idb)
+        torch.cuda.synchronize()
+        assert to_np(buf.expand_x).tobytes() == o["expand_x"].tobytes(), fill
+        assert to_np(buf.dynamic_scales).view(np.uint32).tobytes() == o["dynamic_scales"].view(np.uint32).tobytes()
+        assert (to_np(buf.assist_info) == o["assist_info"]).all(), fill
+        assert (to_np(buf.ep_recv_count) == o["ep_recv_count"]).all(), fill
+
+
+# --------------------------------------------------------------------------
 # determinism (aclnnMoeDistributeDispatchV4 约束说明: deterministic by default)
 # --------------------------------------------------------------------------
 
