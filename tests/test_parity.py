@@ -237,6 +237,7 @@ QUANT_WAVE = [
     wl.custom(64, 3, 64, 2, 4, "fp16", "gauss_topk", quant_mode=2, name="64_chunks_direct_offsets"),
     wl.custom(8, 16, 32, 8, 128, "bf16", "gauss_topk", quant_mode=2, name="e1024_quantised"),
     wl.custom(65, 2, 64, 2, 4, "bf16", "gauss_topk", quant_mode=2, name="65_chunks_scanned_offsets"),
+    wl.custom(4, 601, 7168, 8, 4, "fp16", "zipf_topk", quant_mode=2, name="138MB_mixed_store_kinds"),
 ]
 
 
