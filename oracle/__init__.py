@@ -44,9 +44,9 @@ def _load():
     if _lib is None:
         lib = ctypes.CDLL(build())
         P, I, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
-        lib.oracle_dispatch.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, P, P]
+        lib.oracle_dispatch.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, P, P, P, P, P]
         lib.oracle_dispatch.restype = I
-        lib.oracle_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P]
+        lib.oracle_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, P]
         lib.oracle_combine.restype = I
         lib.oracle_large_segments.argtypes = [P, I, I, I, I, LL, P]
         lib.oracle_large_segments.restype = I
@@ -82,9 +82,23 @@ def dtype_code(arr: np.ndarray, bf16: bool = False) -> int:
     raise OracleError("unsupported token dtype %s (bf16 must be passed as uint16 bits with bf16=True)" % arr.dtype)
 
 
-def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=None, bf16=False):
+def _mask(mask, N, K):
+    """(uint8 array or None, mask_kind): 1 for a per-token mask [N], 2 for a per-pair mask [N, K]."""
+    if mask is None:
+        return None, 0
+    m = np.ascontiguousarray(mask).astype(np.uint8)
+    if m.shape == (N,):
+        return m, 1
+    if m.shape == (N, K):
+        return m, 2
+    raise ValueError("mask must have shape (N,) or (N, K), got %s" % (m.shape,))
+
+
+def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=None, bf16=False, mask=None):
     """Counting-sort dispatch. Returns dict with expand_x, dynamic_scales,
-    assist_info, ep_recv_count and (when scales are given) expand_scales."""
+    assist_info, ep_recv_count, rows (the number of rows written: N*K, or the
+    active pairs under a mask) and (when scales are given) expand_scales.
+    mask: None, per-token [N] or per-pair [N, K] (nonzero = active)."""
     x = np.ascontiguousarray(x)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     N, h = x.shape
@@ -107,20 +121,23 @@ def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=Non
         expert_scales = np.ascontiguousarray(expert_scales)
         assert expert_scales.dtype.itemsize == 4 and expert_scales.shape == (N, K)
         esc = np.zeros((rows,), expert_scales.dtype)
+    m, mk = _mask(mask, N, K)
     rc = _load().oracle_dispatch(_ptr(x), _ptr(ids), _ptr(expert_scales), W, bs, epr, h, K, dt,
-                                 int(quant_mode), _ptr(expand_x), _ptr(dyn), _ptr(assist), _ptr(erc),
-                                 _ptr(esc))
+                                 int(quant_mode), _ptr(m), mk, _ptr(expand_x), _ptr(dyn), _ptr(assist),
+                                 _ptr(erc), _ptr(esc))
     if rc != 0:
         raise OracleError("oracle_dispatch returned %d" % rc)
-    out = dict(expand_x=expand_x, dynamic_scales=dyn, assist_info=assist, ep_recv_count=erc)
+    out = dict(expand_x=expand_x, dynamic_scales=dyn, assist_info=assist, ep_recv_count=erc,
+               rows=int(erc[:, -1].astype(np.int64).sum()) if erc.size else 0)
     if esc is not None:
         out["expand_scales"] = esc
     return out
 
 
 def combine(expand_x, assist_info, ep_recv_count, ids, expert_scales, ep_world, experts_per_rank,
-            bf16=False):
-    """Push-style combine: x_out[t] = sum_k expand_x[row(t,k)] * scales[t,k]."""
+            bf16=False, mask=None):
+    """Push-style combine: x_out[t] = sum over active k of expand_x[row(t,k)] * scales[t,k]
+    (0 for a token with no active pair); mask as for dispatch."""
     expand_x = np.ascontiguousarray(expand_x)
     assist_info = np.ascontiguousarray(assist_info, dtype=np.int32)
     ep_recv_count = np.ascontiguousarray(ep_recv_count, dtype=np.int32)
@@ -135,8 +152,9 @@ def combine(expand_x, assist_info, ep_recv_count, ids, expert_scales, ep_world, 
     if expert_scales.dtype != want:
         raise OracleError("scales must be %s for this dtype" % np.dtype(want))
     x_out = np.zeros((N, h), expand_x.dtype)
+    m, mk = _mask(mask, N, K)
     rc = _load().oracle_combine(_ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_count), _ptr(ids),
-                                _ptr(expert_scales), W, bs, epr, h, K, dt, _ptr(x_out))
+                                _ptr(expert_scales), W, bs, epr, h, K, dt, _ptr(m), mk, _ptr(x_out))
     if rc != 0:
         raise OracleError("oracle_combine returned %d" % rc)
     return x_out

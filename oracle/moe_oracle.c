@@ -137,6 +137,25 @@ static size_t elem_size(int dtype) { return dtype == OR_INT32 ? 4 : 2; }
 /* ------------------------------------------------------------------------ */
 
 /*
+ * Pair (t, k) takes part unless a token mask says otherwise ([P3] 参数说明,
+ * xActiveMaskOptional: a 1D mask (BS,) per rank, or a 2D mask (BS, K); a token
+ * whose K entries are all false is not exchanged). mask_kind 0: no mask;
+ * 1: mask[t], one byte per token of all W*bs tokens; 2: mask[t*K + k]; a
+ * nonzero byte is true. Reading taken: an inactive pair is not sent at all. It
+ * gets no row and is not counted, and its expert id is never read, so it is
+ * not checked either. Rows stay packed, so expand_x holds A rows, A = number
+ * of active pairs, and the buffers may be sized for N*K. The 1D rule that true
+ * entries come first is not needed by this definition, so any pattern is
+ * accepted.
+ */
+static int pair_active(const uint8_t *mask, int mask_kind, long long t, int k, int K)
+{
+    if (mask_kind == 1) return mask[t] != 0;
+    if (mask_kind == 2) return mask[t * K + k] != 0;
+    return 1;
+}
+
+/*
  * x            [W*bs, h] dtype           tokens, source rank s owns rows s*bs..s*bs+bs-1
  * ids          [W*bs, K] int32           global expert ids, distinct per token
  * expand_x     [W*bs*K, h]               dtype, or int8 when quant == 2
@@ -150,10 +169,12 @@ static size_t elem_size(int dtype) { return dtype == OR_INT32 ? 4 : 2; }
  */
 int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales,
                     int W, int bs, int epr, int h, int K, int dtype, int quant,
+                    const uint8_t *mask, int mask_kind,
                     void *expand_x, float *dyn_scales, int32_t *assist,
                     int32_t *ep_recv_count, void *expand_scales)
 {
     if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
+    if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0) != (mask != NULL)) return OR_BAD_ARG;
     if (quant != 0 && quant != 2) return OR_BAD_ARG;
     if (quant == 2 && dtype == OR_INT32) return OR_BAD_ARG;
     const long long E = (long long)W * epr, N = (long long)W * bs, S = (long long)epr * W;
@@ -164,10 +185,11 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
     if (!cnt) return OR_BAD_ARG;
     for (long long t = 0; t < N; ++t) {
         for (int k = 0; k < K; ++k) {
+            if (!pair_active(mask, mask_kind, t, k, K)) continue;
             int32_t e = ids[t * K + k];
             if (e < 0 || e >= E) { free(cnt); return OR_BAD_ID; }
             for (int j = 0; j < k; ++j)
-                if (ids[t * K + j] == e) { free(cnt); return OR_DUP_ID; }
+                if (pair_active(mask, mask_kind, t, j, K) && ids[t * K + j] == e) { free(cnt); return OR_DUP_ID; }
             long long r = e / epr, el = e % epr, s = t / bs;
             cnt[r * S + el * W + s] += 1;
         }
@@ -192,6 +214,9 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
     const size_t xs = elem_size(dtype);
     for (long long t = 0; t < N; ++t) {
         long long s = t / bs, tok = t % bs;
+        int any = 0;
+        for (int k = 0; k < K; ++k) any |= pair_active(mask, mask_kind, t, k, K);
+        if (!any) continue;
         float scale = 0.0f;
         if (quant == 2) {
             float amax = 0.0f;
@@ -202,6 +227,7 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
             scale = amax / 127.0f;
         }
         for (int k = 0; k < K; ++k) {
+            if (!pair_active(mask, mask_kind, t, k, K)) continue;
             int32_t e = ids[t * K + k];
             long long r = e / epr, el = e % epr, i = el * W + s;
             long long start = i == 0 ? 0 : ep_recv_count[r * S + i - 1];
@@ -249,19 +275,25 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
  *
  * expand_x [rows, h] dtype (fp16/bf16/int32), scales [W*bs, K] fp32 (int32 for
  * int32 data), x_out [W*bs, h] dtype. The row's segment (hence its expert) is
- * recovered from ep_recv_count and must equal ids[t,k]; every (t,k) slot
- * must be filled exactly once.
+ * recovered from ep_recv_count and must equal ids[t,k]; every active (t,k)
+ * slot must be filled exactly once and no inactive one (same mask as the
+ * dispatch). The sum runs over the active pairs in ascending k; a token with
+ * none gets 0 (reading: the pages say nothing about the output of a token
+ * that was not exchanged).
  */
 int oracle_combine(const void *expand_x, const int32_t *assist, const int32_t *ep_recv_count,
                    const int32_t *ids, const void *scales, int W, int bs, int epr, int h, int K,
-                   int dtype, void *x_out)
+                   int dtype, const uint8_t *mask, int mask_kind, void *x_out)
 {
     if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
+    if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0) != (mask != NULL)) return OR_BAD_ARG;
     const long long N = (long long)W * bs, S = (long long)epr * W;
 
-    long long rows = 0;
+    long long rows = 0, active = 0;
     for (long long r = 0; r < W; ++r) rows += ep_recv_count[r * S + S - 1];
-    if (rows != N * K) return OR_BAD_ASSIST;
+    for (long long t = 0; t < N; ++t)
+        for (int k = 0; k < K; ++k) active += pair_active(mask, mask_kind, t, k, K);
+    if (rows != active) return OR_BAD_ASSIST;
 
     /* The source rank's window: slot[t*K + k] = index of the returned row. */
     long long *slot = malloc((size_t)(N * K > 0 ? N * K : 1) * sizeof(long long));
@@ -277,7 +309,10 @@ int oracle_combine(const void *expand_x, const int32_t *assist, const int32_t *e
                 long long s = assist[row * 3 + 0], tok = assist[row * 3 + 1], k = assist[row * 3 + 2];
                 if (s != i % W || tok < 0 || tok >= bs || k < 0 || k >= K) { free(slot); return OR_BAD_ASSIST; }
                 long long t = s * bs + tok;
-                if (ids[t * K + k] != e || slot[t * K + k] != -1) { free(slot); return OR_BAD_ASSIST; }
+                if (!pair_active(mask, mask_kind, t, (int)k, K) || ids[t * K + k] != e || slot[t * K + k] != -1) {
+                    free(slot);
+                    return OR_BAD_ASSIST;
+                }
                 slot[t * K + k] = row;
             }
             prev = end;
@@ -289,6 +324,7 @@ int oracle_combine(const void *expand_x, const int32_t *assist, const int32_t *e
             if (dtype == OR_INT32) {
                 uint32_t acc = 0;
                 for (int k = 0; k < K; ++k) {
+                    if (slot[t * K + k] < 0) continue;
                     const int32_t *y = (const int32_t *)expand_x + (size_t)slot[t * K + k] * h;
                     int32_t sc = ((const int32_t *)scales)[t * K + k];
                     acc += (uint32_t)y[j] * (uint32_t)sc;
@@ -297,6 +333,7 @@ int oracle_combine(const void *expand_x, const int32_t *assist, const int32_t *e
             } else {
                 float acc = 0.0f;
                 for (int k = 0; k < K; ++k) {
+                    if (slot[t * K + k] < 0) continue;
                     float y = load_f32(expand_x, (size_t)slot[t * K + k] * h + j, dtype);
                     float sc = ((const float *)scales)[t * K + k];
                     acc = fmaf(y, sc, acc);

@@ -440,3 +440,129 @@ def test_literal_2mib_rule_selects_nothing_on_the_page_workloads():
     assert flags.sum() > 0
     assert (flags == _rule_exact(d["ep_recv_count"], w.ep_world, w.experts_per_rank, w.h, 2,
                                  2 * 1024 * 1024)).all()
+
+
+# --------------------------------------------------------------------------
+# token masks (aclnnMoeDistributeDispatchV4 参数说明, xActiveMaskOptional):
+# an inactive pair is not exchanged, so it has no row and no count
+# --------------------------------------------------------------------------
+
+def _mask_cases(rng, N, K, bs):
+    """(name, mask) pairs: per-token masks (each rank's active tokens first, as
+    the pages ask, and an arbitrary pattern) and per-pair masks (random, with
+    whole tokens switched off, and all off)."""
+    W = N // bs
+    prefix = np.zeros(N, bool)
+    for s in range(W):
+        prefix[s * bs: s * bs + rng.integers(0, bs + 1)] = True
+    pair = rng.random((N, K)) < 0.6
+    pair[rng.random(N) < 0.3] = False
+    return [("token_prefix", prefix), ("token_any", rng.random(N) < 0.5), ("pair", pair),
+            ("pair_all_off", np.zeros((N, K), bool)), ("token_all_on", np.ones(N, bool))]
+
+
+def _active(mask, N, K):
+    return np.repeat(mask[:, None], K, axis=1) if mask.ndim == 1 else mask
+
+
+def _brute_force_layout(ids, act, W, bs, epr):
+    """Rows by sorting the active pairs on (rank, local expert, source rank,
+    token): the definition of the row order, without the counting sort."""
+    N, K = ids.shape
+    keys = sorted((int(ids[t, k]) // epr, int(ids[t, k]) % epr, t // bs, t % bs, k)
+                  for t in range(N) for k in range(K) if act[t, k])
+    assist = np.array([[s, tok, k] for (_, _, s, tok, k) in keys], np.int32).reshape(-1, 3)
+    cnt = np.zeros((W, epr * W), np.int64)
+    for (r, el, s, _, _) in keys:
+        cnt[r, el * W + s] += 1
+    return assist, np.cumsum(cnt, axis=1).astype(np.int32)
+
+
+@pytest.mark.parametrize("w", [wl.custom(3, 7, 5, 3, 2, "int32", name="int32_small"),
+                               wl.custom(4, 9, 16, 4, 3, "bf16", "zipf_topk", quant_mode=2, name="bf16_q")],
+                         ids=lambda w: w.name)
+def test_masked_dispatch_matches_a_sort_of_the_active_pairs(w):
+    inp = wl.make_inputs(w)
+    N, K, bs = w.num_tokens, w.topk, w.bs
+    full = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
+                           bf16=w.dtype == "bf16")
+    full_row = {tuple(a): i for i, a in enumerate(full["assist_info"].tolist())}
+    for name, mask in _mask_cases(np.random.default_rng(7), N, K, bs):
+        act = _active(mask, N, K)
+        d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
+                            bf16=w.dtype == "bf16", mask=mask)
+        assist, erc = _brute_force_layout(inp["ids"], act, w.ep_world, bs, w.experts_per_rank)
+        A = len(assist)
+        assert d["rows"] == A == int(act.sum()), name
+        assert (d["assist_info"][:A] == assist).all(), name
+        assert (d["ep_recv_count"] == erc).all(), name
+        # each row holds its token's payload exactly as the unmasked dispatch does
+        for i, a in enumerate(assist.tolist()):
+            j = full_row[tuple(a)]
+            assert d["expand_x"][i].tobytes() == full["expand_x"][j].tobytes(), name
+            if w.quant_mode == 2:
+                assert d["dynamic_scales"][i] == full["dynamic_scales"][j], name
+
+
+def test_masked_int32_combine_closed_form():
+    """Identity expert, int32: x_out[t] = x[t] * sum over active k of s[t,k]
+    (wrapping), and 0 for a token with no active pair."""
+    w = wl.custom(4, 11, 6, 3, 2, "int32", name="int32_mask")
+    inp = wl.make_inputs(w)
+    N, K = w.num_tokens, w.topk
+    for name, mask in _mask_cases(np.random.default_rng(3), N, K, w.bs):
+        act = _active(mask, N, K)
+        d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, mask=mask)
+        out = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"],
+                             w.ep_world, w.experts_per_rank, mask=mask)
+        ssum = (inp["scales"].astype(np.int64) * act).sum(axis=1)
+        want = ((inp["x"].astype(np.int64) * ssum[:, None]) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+        assert (out == want).all(), name
+
+
+@pytest.mark.parametrize("dt", ["fp16", "bf16"])
+def test_masked_combine_equals_zero_weights(dt):
+    """fp16/bf16: skipping an inactive pair gives the same bits as keeping it
+    with weight 0 (fma(y, 0, acc) == acc for finite y, and acc never becomes
+    -0 from +0), so the masked combine must equal the unmasked one on weights
+    zeroed where the mask is off. Tokens with no active pair come out +0."""
+    w = wl.custom(3, 13, 24, 4, 3, dt, "gauss_topk", name="half_mask")
+    inp = wl.make_inputs(w)
+    N, K = w.num_tokens, w.topk
+    bf = dt == "bf16"
+    full = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, bf16=bf)
+    for name, mask in _mask_cases(np.random.default_rng(5), N, K, w.bs):
+        act = _active(mask, N, K)
+        d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, bf16=bf, mask=mask)
+        got = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"],
+                             w.ep_world, w.experts_per_rank, bf16=bf, mask=mask)
+        zeroed = (inp["scales"] * act).astype(np.float32)
+        want = oracle.combine(full["expand_x"], full["assist_info"], full["ep_recv_count"], inp["ids"], zeroed,
+                              w.ep_world, w.experts_per_rank, bf16=bf)
+        assert got.view(np.uint16).tobytes() == want.view(np.uint16).tobytes(), name
+        assert (got.view(np.uint16)[~act.any(axis=1)] == 0).all(), name
+
+
+def test_masks_that_keep_everything_change_nothing_and_mismatches_are_rejected():
+    w = wl.custom(2, 8, 16, 3, 3, "fp16", "gauss_topk", quant_mode=2, name="all_on")
+    inp = wl.make_inputs(w)
+    N, K = w.num_tokens, w.topk
+    ref = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, 2)
+    for mask in (np.ones(N, np.uint8), np.full((N, K), 3, np.uint8)):
+        d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, 2, mask=mask)
+        for key in ("expand_x", "dynamic_scales", "assist_info", "ep_recv_count"):
+            assert d[key].tobytes() == ref[key].tobytes(), key
+    # outputs of an unmasked dispatch do not describe a masked exchange
+    y = oracle.identity_expert(ref["expand_x"], ref["dynamic_scales"])
+    mask = np.ones((N, K), bool)
+    mask[0, 0] = False
+    with pytest.raises(oracle.OracleError):
+        oracle.combine(y, ref["assist_info"], ref["ep_recv_count"], inp["ids"], inp["scales"], w.ep_world,
+                       w.experts_per_rank, bf16=True, mask=mask)
+    # an inactive pair's id is never read: garbage there is accepted
+    ids = inp["ids"].copy()
+    ids[0, 0] = 10 ** 6
+    d = oracle.dispatch(inp["x"], ids, w.ep_world, w.experts_per_rank, 2, mask=mask)
+    assert d["rows"] == N * K - 1
+    with pytest.raises(oracle.OracleError):
+        oracle.dispatch(inp["x"], ids, w.ep_world, w.experts_per_rank, 2)
