@@ -26,6 +26,7 @@ MOE_OK = 0
 MOE_INT32, MOE_FP16, MOE_BF16 = 0, 1, 2
 MOE_QUANT_NONE, MOE_QUANT_DYN_TOKEN = 0, 2
 MOE_SCHED_TOKEN, MOE_SCHED_SEGMENT = 0, 1
+MOE_MASK_NONE, MOE_MASK_TOKEN, MOE_MASK_PAIR = 0, 1, 2
 
 EXPORTS = ("moe_dispatch_workspace_size", "moe_dispatch", "moe_combine_workspace_size", "moe_combine",
            "moe_status_str")
@@ -56,12 +57,12 @@ def library() -> ctypes.CDLL:
     P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.moe_dispatch_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(SZ)]
     lib.moe_dispatch_workspace_size.restype = I
-    lib.moe_dispatch.argtypes = [P, P, P, I, I, I, I, I, I, I, P, P, P, P, P, ctypes.POINTER(MoeSchedule), P,
-                                 SZ, P]
+    lib.moe_dispatch.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, P,
+                                 ctypes.POINTER(MoeSchedule), P, SZ, P]
     lib.moe_dispatch.restype = I
     lib.moe_combine_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(SZ)]
     lib.moe_combine_workspace_size.restype = I
-    lib.moe_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, P, SZ, P]
+    lib.moe_combine.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, SZ, P]
     lib.moe_combine.restype = I
     lib.moe_status_str.argtypes = [I]
     lib.moe_status_str.restype = ctypes.c_char_p
@@ -94,6 +95,19 @@ def _ptr(t: Optional[torch.Tensor]):
 
 def _stream_ptr(device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _mask_args(mask: Optional[torch.Tensor], N: int, K: int, device):
+    """(pointer, kind) for a token mask: None, bool/uint8 [N] (per token) or [N, K] (per pair)."""
+    if mask is None:
+        return None, MOE_MASK_NONE
+    if mask.dtype not in (torch.bool, torch.uint8) or not mask.is_contiguous() or mask.device != device:
+        raise MoeError("x_active_mask", 9, "mask must be a contiguous bool or uint8 tensor on %s" % device)
+    if tuple(mask.shape) == (N,):
+        return _ptr(mask), MOE_MASK_TOKEN
+    if tuple(mask.shape) == (N, K):
+        return _ptr(mask), MOE_MASK_PAIR
+    raise MoeError("x_active_mask", 9, "mask shape %s is neither (%d,) nor (%d, %d)" % (tuple(mask.shape), N, N, K))
 
 
 def dispatch_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype, quant_mode=0) -> int:
@@ -134,11 +148,14 @@ class DispatchBuffers:
 
 
 def dispatch_into(buf: DispatchBuffers, x: torch.Tensor, expert_ids: torch.Tensor,
-                  expert_scales: Optional[torch.Tensor] = None, schedule: Optional[MoeSchedule] = None):
+                  expert_scales: Optional[torch.Tensor] = None, schedule: Optional[MoeSchedule] = None,
+                  x_active_mask: Optional[torch.Tensor] = None):
     """moe_dispatch into preallocated buffers on the current stream."""
     W, bs, epr, h, K = buf.shape
+    mp, mk = _mask_args(x_active_mask, W * bs, K, x.device)
     rc = library().moe_dispatch(
-        _ptr(x), _ptr(expert_ids), _ptr(expert_scales), W, bs, epr, h, K, dtype_code(buf.dtype), buf.quant_mode,
+        _ptr(x), _ptr(expert_ids), _ptr(expert_scales), mp, mk, W, bs, epr, h, K, dtype_code(buf.dtype),
+        buf.quant_mode,
         _ptr(buf.expand_x), _ptr(buf.dynamic_scales), _ptr(buf.assist_info), _ptr(buf.ep_recv_count),
         _ptr(buf.expand_scales), ctypes.byref(schedule) if schedule is not None else None,
         _ptr(buf.workspace), buf.workspace.numel(), _stream_ptr(x.device))
@@ -154,12 +171,14 @@ def _check_tensor(name, t, dtype, shape, device):
 
 def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_per_rank: int,
              quant_mode: int = MOE_QUANT_NONE, expert_scales: Optional[torch.Tensor] = None,
-             schedule: Optional[MoeSchedule] = None):
+             schedule: Optional[MoeSchedule] = None, x_active_mask: Optional[torch.Tensor] = None):
     """Dispatch tokens into expert-grouped rows.
 
     x: [ep_world*bs, h] int32/fp16/bf16 on a GPU; expert_ids: [ep_world*bs, topk]
     int32. Returns (expand_x, dynamic_scales or None, assist_info, ep_recv_count)
-    and, when expert_scales is given, a fifth item expand_scales.
+    and, when expert_scales is given, a fifth item expand_scales. With a token
+    mask (bool/uint8 [N] or [N, topk]) only the first ep_recv_count[:, -1].sum()
+    rows of the row-indexed outputs are written.
     """
     N, h = x.shape
     K = expert_ids.shape[1]
@@ -173,23 +192,25 @@ def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_p
                           with_expand_scales=expert_scales is not None)
     if expert_scales is not None:
         buf.expand_scales = torch.empty((N * K,), dtype=expert_scales.dtype, device=x.device)
-    dispatch_into(buf, x, expert_ids, expert_scales, schedule)
+    dispatch_into(buf, x, expert_ids, expert_scales, schedule, x_active_mask)
     out = (buf.expand_x, buf.dynamic_scales, buf.assist_info, buf.ep_recv_count)
     return out + (buf.expand_scales,) if expert_scales is not None else out
 
 
 def combine_into(x_out: torch.Tensor, expand_x: torch.Tensor, assist_info: torch.Tensor,
                  ep_recv_count: torch.Tensor, expert_ids: torch.Tensor, expert_scales: torch.Tensor,
-                 ep_world: int, experts_per_rank: int, workspace: Optional[torch.Tensor] = None):
+                 ep_world: int, experts_per_rank: int, workspace: Optional[torch.Tensor] = None,
+                 x_active_mask: Optional[torch.Tensor] = None):
     """moe_combine into a preallocated x_out on the current stream."""
     N, K = expert_ids.shape
+    mp, mk = _mask_args(x_active_mask, N, K, expand_x.device)
     h = expand_x.shape[1]
     dt = dtype_code(expand_x.dtype)
     if workspace is None:
         workspace = combine_workspace(ep_world, N // ep_world, experts_per_rank, h, K, expand_x.dtype,
                                       expand_x.device)
     rc = library().moe_combine(
-        _ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_count), _ptr(expert_ids), _ptr(expert_scales),
+        _ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_count), _ptr(expert_ids), _ptr(expert_scales), mp, mk,
         ep_world, N // ep_world, experts_per_rank, h, K, dt, _ptr(x_out), _ptr(workspace), workspace.numel(),
         _stream_ptr(expand_x.device))
     _check("moe_combine", rc)
@@ -203,8 +224,10 @@ def combine_workspace(ep_world, bs, experts_per_rank, h, topk, dtype: torch.dtyp
 
 
 def combine(expand_x: torch.Tensor, assist_info: torch.Tensor, ep_recv_count: torch.Tensor,
-            expert_ids: torch.Tensor, expert_scales: torch.Tensor, ep_world: int, experts_per_rank: int):
-    """x_out[t] = sum_k expand_x[row(t,k)] * expert_scales[t,k] (fp32 accumulation)."""
+            expert_ids: torch.Tensor, expert_scales: torch.Tensor, ep_world: int, experts_per_rank: int,
+            x_active_mask: Optional[torch.Tensor] = None):
+    """x_out[t] = sum over active k of expand_x[row(t,k)] * expert_scales[t,k] (fp32 accumulation);
+    x_active_mask: the dispatch's."""
     N, K = expert_ids.shape
     rows, h = expand_x.shape
     dev = expand_x.device
@@ -218,4 +241,4 @@ def combine(expand_x: torch.Tensor, assist_info: torch.Tensor, ep_recv_count: to
     _check_tensor("expert_scales", expert_scales, sdt, (N, K), dev)
     x_out = torch.empty((N, h), dtype=expand_x.dtype, device=dev)
     return combine_into(x_out, expand_x, assist_info, ep_recv_count, expert_ids, expert_scales, ep_world,
-                        experts_per_rank)
+                        experts_per_rank, x_active_mask=x_active_mask)

@@ -188,6 +188,7 @@ __device__ __forceinline__ int bitmap_rank(const unsigned long long *row, int bi
 
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__restrict__ ids, int W, int bs,
                                                               int epr, int K, int nbs,
+                                                              const uint8_t *__restrict__ mask, int mask_kind,
                                                               int32_t *__restrict__ pc, int32_t *__restrict__ pci,
                                                               int32_t *__restrict__ lr)
 {
@@ -205,24 +206,29 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
     // one pass of U pairs per thread covers the chunk whenever ntok * K <= 2048;
     // the ids and token indices then stay in registers for the rank pass. The
     // first pass's ids are requested before the bitmaps are cleared.
+    // An inactive pair (token masks) is routed nowhere: its id reads as -1, so
+    // it sets no bit, is not counted and gets rank -1, and no kernel after this
+    // one writes a row for it.
+    const size_t tok_base = (size_t)s * bs + tok0;
+    auto load_pair = [&](int p, int &eu, int &tlu) {
+        tlu = div_small(p, K, rK);
+        eu = -1;
+        if (p < npairs) {
+            eu = ids[pair0 + p];
+            if (mask_kind == MOE_MASK_TOKEN && !mask[tok_base + tlu]) eu = -1;
+            if (mask_kind == MOE_MASK_PAIR && !mask[pair0 + p]) eu = -1;
+        }
+    };
     int e[U], tl[U];
     const bool one_pass = npairs <= kRouteThreads * U;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-        const int p = threadIdx.x + u * kRouteThreads;
-        e[u] = p < npairs ? ids[pair0 + p] : -1;
-        tl[u] = div_small(p, K, rK);
-    }
+    for (int u = 0; u < U; ++u) load_pair(threadIdx.x + u * kRouteThreads, e[u], tl[u]);
     for (int i = threadIdx.x; i < E * kRouteWords; i += blockDim.x) bm[i] = 0ull;
     __syncthreads();
     for (int p0 = threadIdx.x; p0 < npairs; p0 += kRouteThreads * U) {
         if (p0 != (int)threadIdx.x) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int p = p0 + u * kRouteThreads;
-                e[u] = p < npairs ? ids[pair0 + p] : -1;
-                tl[u] = div_small(p, K, rK);
-            }
+            for (int u = 0; u < U; ++u) load_pair(p0 + u * kRouteThreads, e[u], tl[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u)
@@ -258,11 +264,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
     for (int p0 = threadIdx.x; p0 < npairs; p0 += kRouteThreads * U) {
         if (!one_pass) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int p = p0 + u * kRouteThreads;
-                e[u] = p < npairs ? ids[pair0 + p] : -1;
-                tl[u] = div_small(p, K, rK);
-            }
+            for (int u = 0; u < U; ++u) load_pair(p0 + u * kRouteThreads, e[u], tl[u]);
         }
 #pragma unroll
         for (int u = 0; u < U; ++u) {
@@ -818,16 +820,33 @@ struct CombineArgs {
     const int32_t *slot;      // [N*K] row of pair (t, k), written by combine_slots_kernel
     int32_t *slot_out;
     char *x_out;
-    int W, bs, h, K, R, nsl;
+    const int32_t *erc;       // ep_recv_count [W, S]: with a mask, the row total comes from it
+    const uint8_t *mask;
+    int mask_kind;
+    int W, bs, h, K, R, S, nsl;
     long long rowbytes;
 };
 
 // Return path (README 实现逻辑): row i of expand_x belongs to slot
 // (src_token, topk_id) of source rank src_rank. Only its index travels.
+// Under a token mask only the first A rows exist (A = sum over ranks of the
+// last inclusive count) and an inactive pair's slot is set to -1, so the
+// gather skips it; a thread handles row i and pair i.
 __global__ __launch_bounds__(kSlotThreads) void combine_slots_kernel(CombineArgs a)
 {
+    __shared__ int tmp[40];
     const int i = blockIdx.x * kSlotThreads + threadIdx.x;
-    if (i >= a.R) return;
+    int rows = a.R;
+    if (a.mask_kind != MOE_MASK_NONE) {
+        int part = 0;
+        for (int r = threadIdx.x; r < a.W; r += kSlotThreads) part += a.erc[(size_t)r * a.S + a.S - 1];
+        block_excl_scan(part, tmp, &rows);
+        if (i < a.R) {
+            const bool on = a.mask_kind == MOE_MASK_TOKEN ? a.mask[i / a.K] != 0 : a.mask[i] != 0;
+            if (!on) a.slot_out[i] = -1;
+        }
+    }
+    if (i >= rows || i >= a.R) return;
     const int s = a.assist[(size_t)i * 3 + 0], tok = a.assist[(size_t)i * 3 + 1], k = a.assist[(size_t)i * 3 + 2];
     if ((unsigned)s < (unsigned)a.W && (unsigned)tok < (unsigned)a.bs && (unsigned)k < (unsigned)a.K)
         a.slot_out[((size_t)s * a.bs + tok) * a.K + k] = i;
@@ -1000,6 +1019,7 @@ const char *moe_status_str(int status)
     case MOE_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case MOE_ERR_SCHEDULE: return "unknown schedule mode, or segment schedule too large for this shape";
     case MOE_ERR_ALIGN: return "a pointer is not aligned to its element size";
+    case MOE_ERR_MASK: return "unknown mask kind, or the mask pointer does not match it";
     default: return "unknown status";
     }
 }
@@ -1016,7 +1036,8 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
     return MOE_OK;
 }
 
-int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales, int ep_world, int bs,
+int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales,
+                 const uint8_t *x_active_mask, int mask_kind, int ep_world, int bs,
                  int experts_per_rank, int h, int topk, int dtype, int quant_mode, void *expand_x,
                  float *dynamic_scales, int32_t *assist_info, int32_t *ep_recv_count, void *expand_scales,
                  const moe_schedule *schedule, void *workspace, size_t workspace_bytes, void *stream)
@@ -1032,6 +1053,9 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     if (quant != (dynamic_scales != nullptr) && N > 0) return MOE_ERR_NULLPTR;
     if (!quant && dynamic_scales) return MOE_ERR_NULLPTR;
     if (expand_scales && !expert_scales) return MOE_ERR_NULLPTR;
+    if (mask_kind < MOE_MASK_NONE || mask_kind > MOE_MASK_PAIR) return MOE_ERR_MASK;
+    if ((mask_kind != MOE_MASK_NONE) != (x_active_mask != nullptr) && N > 0) return MOE_ERR_MASK;
+    if (mask_kind == MOE_MASK_NONE && x_active_mask) return MOE_ERR_MASK;
     if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
 
     const int mode = schedule ? schedule->mode : MOE_SCHED_TOKEN;
@@ -1069,7 +1093,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     const int elem_out = quant ? 1 : (int)xs;
     if (N > 0)
         hipLaunchKernelGGL(route_kernel, dim3(L.NB), dim3(kRouteThreads), (size_t)E * kRouteWords * 8, st,
-                           expert_ids, W, bs, epr, K, L.nbs, pc, pci, lr);
+                           expert_ids, W, bs, epr, K, L.nbs, x_active_mask, mask_kind, pc, pci, lr);
     if (!direct || want_seg)
         hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), want_seg ? (size_t)W * S * 5 : 0, st, pc, pci,
                            W, epr, L.nbs, h, elem_out, boff, ep_recv_count, want_seg ? 1 : 0, large, seg_flags,
@@ -1171,8 +1195,9 @@ int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h
 }
 
 int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t *ep_recv_count,
-                const int32_t *expert_ids, const void *expert_scales, int ep_world, int bs, int experts_per_rank,
-                int h, int topk, int dtype, void *x_out, void *workspace, size_t workspace_bytes, void *stream)
+                const int32_t *expert_ids, const void *expert_scales, const uint8_t *x_active_mask,
+                int mask_kind, int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype,
+                void *x_out, void *workspace, size_t workspace_bytes, void *stream)
 {
     size_t need = 0;
     int rc = moe_combine_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype, &need);
@@ -1182,6 +1207,9 @@ int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t 
     if (!ep_recv_count) return MOE_ERR_NULLPTR;
     if (N > 0 && (!expand_x || !assist_info || !expert_ids || !expert_scales || !x_out || !workspace))
         return MOE_ERR_NULLPTR;
+    if (mask_kind < MOE_MASK_NONE || mask_kind > MOE_MASK_PAIR) return MOE_ERR_MASK;
+    if ((mask_kind != MOE_MASK_NONE) != (x_active_mask != nullptr) && N > 0) return MOE_ERR_MASK;
+    if (mask_kind == MOE_MASK_NONE && x_active_mask) return MOE_ERR_MASK;
     if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
     const size_t xs = elem_size(dtype);
     if (!aligned(expand_x, xs) || !aligned(assist_info, 4) || !aligned(ep_recv_count, 4) ||
@@ -1196,7 +1224,10 @@ int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t 
     a.slot = static_cast<const int32_t *>(workspace);
     a.slot_out = static_cast<int32_t *>(workspace);
     a.x_out = static_cast<char *>(x_out);
-    a.W = W; a.bs = bs; a.h = h; a.K = K; a.R = (int)(N * K);
+    a.erc = ep_recv_count;
+    a.mask = x_active_mask;
+    a.mask_kind = mask_kind;
+    a.W = W; a.bs = bs; a.h = h; a.K = K; a.R = (int)(N * K); a.S = experts_per_rank * W;
     a.rowbytes = (long long)((size_t)h * xs);
     const bool vec = (size_t)a.rowbytes % 16 == 0 && aligned(expand_x, 16) && aligned(x_out, 16);
     const long long n = vec ? a.rowbytes / 16 : h;

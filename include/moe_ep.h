@@ -55,8 +55,9 @@ enum moe_status {
     MOE_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch */
     MOE_ERR_SCHEDULE = 7,  /* unknown schedule mode, or the segment schedule (or the
                               segment_is_large output) at W*S above 11264 */
-    MOE_ERR_ALIGN = 8      /* a pointer is not aligned to its element size (16 bytes for
+    MOE_ERR_ALIGN = 8,     /* a pointer is not aligned to its element size (16 bytes for
                               the workspace) */
+    MOE_ERR_MASK = 9       /* unknown mask kind, or a mask pointer that does not match it */
 };
 
 /* Token element types. */
@@ -65,6 +66,21 @@ enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
 /* Quantisation modes; the numbering follows quantMode of
  * aclnnMoeDistributeDispatchV4 (0 = none, 2 = per-token dynamic). */
 enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_DYN_TOKEN = 2 };
+
+/* Token masks: xActiveMaskOptional of aclnnMoeDistributeDispatchV4 (参数说明):
+ * a 1D mask (BS,) per rank or a 2D mask (BS, K); a token whose K entries are
+ * all false is not exchanged. Here the mask covers all W*bs tokens, one byte
+ * per entry, nonzero = active (a torch.bool tensor qualifies):
+ *  MOE_MASK_NONE:  every pair takes part; the mask pointer must be NULL.
+ *  MOE_MASK_TOKEN: uint8 [N]; an inactive token sends none of its K pairs.
+ *                  The pages ask each rank's active tokens to come first;
+ *                  any pattern is accepted here.
+ *  MOE_MASK_PAIR:  uint8 [N, K]; pair (t, k) is sent iff its byte is nonzero.
+ * An inactive pair gets no row and no count, and its expert id is never read.
+ * The A active pairs fill expand_x rows 0..A-1 in the usual order, with
+ * A = sum over ranks r of ep_recv_count[r][S-1]; later rows of the N*K-row
+ * buffers are left untouched. Dispatch and combine take the same mask. */
+enum moe_mask { MOE_MASK_NONE = 0, MOE_MASK_TOKEN = 1, MOE_MASK_PAIR = 2 };
 
 /* How dispatch assigns its payload copies to workgroups. Both modes produce
  * bitwise identical outputs (the combine_doubleplane README requires the same
@@ -106,7 +122,10 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
  *
  *  x              [N, h] dtype           tokens; rows s*bs..s*bs+bs-1 are rank s's
  *  expert_ids     [N, K] int32           global expert ids in [0, E), distinct per token
+ *                                        (only active pairs' ids are read)
  *  expert_scales  [N, K] 4-byte or NULL  only read when expand_scales is given
+ *  x_active_mask  uint8 [N] or [N, K]    see moe_mask; NULL with MOE_MASK_NONE
+ *  mask_kind      moe_mask
  *  expand_x       [ROWS, h]              dtype, or int8 when quant_mode == 2. Row order:
  *                                        rank r, then local expert, then source rank,
  *                                        then ascending source token
@@ -127,6 +146,7 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
  * unspecified. Outputs are bitwise deterministic.
  */
 int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales,
+                 const uint8_t *x_active_mask, int mask_kind,
                  int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype,
                  int quant_mode, void *expand_x, float *dynamic_scales, int32_t *assist_info,
                  int32_t *ep_recv_count, void *expand_scales, const moe_schedule *schedule,
@@ -155,6 +175,9 @@ int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h
  *                 the rows are located through assist_info)
  *  expert_ids     [N, K] int32: the ids given to dispatch (checked likewise)
  *  expert_scales  [N, K] fp32 for fp16/bf16, int32 for int32 data
+ *  x_active_mask, mask_kind: the dispatch's. The sum then runs over the
+ *                 active pairs only (k ascending); a token with none gets 0.
+ *                 With a mask, ep_recv_count is read to find the row total.
  *  x_out          [N, h] dtype
  *  workspace      device scratch of at least the queried size
  * The scalars must equal those given to dispatch. Rows that assist_info does
@@ -162,7 +185,8 @@ int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h
  * affected outputs are unspecified.
  */
 int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t *ep_recv_count,
-                const int32_t *expert_ids, const void *expert_scales, int ep_world, int bs,
+                const int32_t *expert_ids, const void *expert_scales,
+                const uint8_t *x_active_mask, int mask_kind, int ep_world, int bs,
                 int experts_per_rank, int h, int topk, int dtype, void *x_out,
                 void *workspace, size_t workspace_bytes, void *stream);
 

@@ -18,7 +18,7 @@ import combine_ep_recv_amd as moe
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "moe_ep.h")
 
-OK, NULLPTR, SHAPE, DTYPE, QUANT, WORKSPACE, LAUNCH, SCHEDULE, ALIGN = range(9)
+OK, NULLPTR, SHAPE, DTYPE, QUANT, WORKSPACE, LAUNCH, SCHEDULE, ALIGN, MASK = range(10)
 
 
 def _declared_functions():
@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_status_strings():
-    for s in range(9):
+    for s in range(10):
         assert moe.status_str(s) and moe.status_str(s) != "unknown status"
     assert moe.status_str(99) == "unknown status"
 
@@ -96,12 +96,13 @@ A = 1 << 20   # fake, 256-aligned "device" addresses; never dereferenced by thes
 
 
 def _dispatch(**kw):
-    p = dict(x=A, ids=2 * A, esc=None, W=2, bs=4, epr=2, h=16, K=2, dtype=1, quant=0, ex=3 * A, dyn=None,
-             assist=4 * A, erc=5 * A, esc_out=None, sched=None, ws=6 * A, wsb=1 << 30)
+    p = dict(x=A, ids=2 * A, esc=None, mask=None, mk=0, W=2, bs=4, epr=2, h=16, K=2, dtype=1, quant=0, ex=3 * A,
+             dyn=None, assist=4 * A, erc=5 * A, esc_out=None, sched=None, ws=6 * A, wsb=1 << 30)
     p.update(kw)
     P = lambda v: None if v is None else ctypes.c_void_p(v)
     return moe.library().moe_dispatch(
-        P(p["x"]), P(p["ids"]), P(p["esc"]), p["W"], p["bs"], p["epr"], p["h"], p["K"], p["dtype"], p["quant"],
+        P(p["x"]), P(p["ids"]), P(p["esc"]), P(p["mask"]), p["mk"], p["W"], p["bs"], p["epr"], p["h"], p["K"],
+        p["dtype"], p["quant"],
         P(p["ex"]), P(p["dyn"]), P(p["assist"]), P(p["erc"]), P(p["esc_out"]),
         ctypes.byref(p["sched"]) if p["sched"] is not None else None, P(p["ws"]), p["wsb"], None)
 
@@ -128,6 +129,9 @@ def _dispatch(**kw):
     (dict(ws=6 * A + 8), ALIGN),
     (dict(sched=moe.MoeSchedule(mode=5)), SCHEDULE),
     (dict(W=128, epr=8, K=2, sched=moe.MoeSchedule(mode=1)), SCHEDULE),   # W*S = 131072 > LDS budget
+    (dict(mk=3, mask=8 * A), MASK),                                     # unknown mask kind
+    (dict(mk=1), MASK),                                                 # a kind without a mask
+    (dict(mask=8 * A), MASK),                                           # a mask without a kind
 ])
 def test_dispatch_rejects_before_launch(kw, want):
     rc = _dispatch(**kw)
@@ -135,11 +139,12 @@ def test_dispatch_rejects_before_launch(kw, want):
 
 
 def _combine(**kw):
-    p = dict(ex=A, assist=2 * A, erc=3 * A, ids=4 * A, sc=5 * A, W=2, bs=4, epr=2, h=16, K=2, dtype=1, out=6 * A,
-             ws=7 * A, wsb=1 << 30)
+    p = dict(ex=A, assist=2 * A, erc=3 * A, ids=4 * A, sc=5 * A, mask=None, mk=0, W=2, bs=4, epr=2, h=16, K=2,
+             dtype=1, out=6 * A, ws=7 * A, wsb=1 << 30)
     p.update(kw)
     P = lambda v: None if v is None else ctypes.c_void_p(v)
-    return moe.library().moe_combine(P(p["ex"]), P(p["assist"]), P(p["erc"]), P(p["ids"]), P(p["sc"]), p["W"],
+    return moe.library().moe_combine(P(p["ex"]), P(p["assist"]), P(p["erc"]), P(p["ids"]), P(p["sc"]),
+                                     P(p["mask"]), p["mk"], p["W"],
                                      p["bs"], p["epr"], p["h"], p["K"], p["dtype"], P(p["out"]), P(p["ws"]),
                                      p["wsb"], None)
 
@@ -161,6 +166,9 @@ def _combine(**kw):
     (dict(out=6 * A + 1), ALIGN),
     (dict(dtype=0, ex=A + 2), ALIGN),
     (dict(bs=0), OK),                                # empty batch: nothing to launch
+    (dict(mk=-1), MASK),
+    (dict(mk=2), MASK),                              # a kind without a mask
+    (dict(mask=8 * A), MASK),                        # a mask without a kind
 ])
 def test_combine_rejects_before_launch(kw, want):
     rc = _combine(**kw)

@@ -270,6 +270,108 @@ def test_workspace_contents_on_entry_do_not_matter():
 
 
 # --------------------------------------------------------------------------
+# token masks (aclnnMoeDistributeDispatchV4 参数说明, xActiveMaskOptional):
+# inactive pairs get no row and no count; the A active pairs fill rows 0..A-1;
+# a token with no active pair combines to 0
+# --------------------------------------------------------------------------
+
+def _make_mask(kind, w, seed):
+    rng = np.random.default_rng(seed)
+    N, K, bs = w.num_tokens, w.topk, w.bs
+    if kind == "token_prefix":          # each rank's active tokens first, as the pages ask
+        m = np.zeros(N, bool)
+        for s in range(w.ep_world):
+            m[s * bs: s * bs + rng.integers(0, bs + 1)] = True
+        return m
+    if kind == "token_any":
+        return rng.random(N) < 0.6
+    if kind == "pair":
+        m = rng.random((N, K)) < 0.7
+        m[rng.random(N) < 0.2] = False  # some tokens switched off entirely
+        return m
+    if kind == "pair_all_off":
+        return np.zeros((N, K), bool)
+    raise ValueError(kind)
+
+
+def check_masked(w, kind, seed=1, schedule=None):
+    inp = wl.make_inputs(w)
+    mask = _make_mask(kind, w, seed)
+    print("parity case %s mask=%s seed=%d W=%d bs=%d h=%d K=%d %s q%d sched=%s" % (
+        w.name, kind, seed, w.ep_world, w.bs, w.h, w.topk, w.dtype, w.quant_mode,
+        None if schedule is None else schedule.mode), flush=True)
+    bf = w.dtype == "bf16"
+    x, ids, sc = to_dev(inp["x"], bf), to_dev(inp["ids"]), to_dev(inp["scales"])
+    m = torch.from_numpy(mask).to(DEV)
+    ex, dyn, assist, erc, esc = moe.dispatch(x, ids, w.ep_world, w.experts_per_rank, w.quant_mode,
+                                             expert_scales=sc, schedule=schedule, x_active_mask=m)
+    y = gpu_identity_expert(ex, dyn)
+    xo = moe.combine(y, assist, erc, ids, sc, w.ep_world, w.experts_per_rank, x_active_mask=m)
+    torch.cuda.synchronize()
+    d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
+                        expert_scales=inp["scales"], bf16=bf, mask=mask)
+    yo = oracle.identity_expert(d["expand_x"], d["dynamic_scales"])
+    xo_o = oracle.combine(yo, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"], w.ep_world,
+                          w.experts_per_rank, bf16=bf or w.quant_mode == 2, mask=mask)
+    A = d["rows"]
+    assert (to_np(erc) == d["ep_recv_count"]).all(), "ep_recv_count"
+    assert (to_np(assist)[:A] == d["assist_info"][:A]).all(), "assist_info"
+    assert to_np(ex)[:A].tobytes() == d["expand_x"][:A].tobytes(), "expand_x"
+    assert to_np(esc)[:A].view(np.uint32).tobytes() == d["expand_scales"][:A].view(np.uint32).tobytes()
+    if w.quant_mode == 2:
+        assert to_np(dyn)[:A].view(np.uint32).tobytes() == d["dynamic_scales"][:A].view(np.uint32).tobytes()
+    g = to_np(xo)
+    if w.dtype == "int32":
+        assert (g == xo_o).all(), "x_out"
+    else:
+        assert g.view(np.uint16).tobytes() == xo_o.view(np.uint16).tobytes(), "x_out bits"
+        # and the tolerance metric over the active pairs
+        act = np.repeat(mask[:, None], w.topk, axis=1) if mask.ndim == 1 else mask
+        yf = as_f32(yo, True if (bf or w.quant_mode == 2) else False)
+        den = np.zeros(g.shape, np.float64)
+        a3 = d["assist_info"][:A].astype(np.int64)
+        row_of = np.full(w.num_tokens * w.topk, -1, np.int64)
+        row_of[(a3[:, 0] * w.bs + a3[:, 1]) * w.topk + a3[:, 2]] = np.arange(A)
+        for k in range(w.topk):
+            t_on = np.nonzero(act[:, k])[0]
+            r = row_of[t_on * w.topk + k]
+            assert (r >= 0).all()
+            den[t_on] += np.abs(yf[r].astype(np.float64)) * np.abs(inp["scales"][t_on, k].astype(np.float64))[:, None]
+        bfo = bf or w.quant_mode == 2
+        diff = np.abs(as_f32(g, bfo).astype(np.float64) - as_f32(xo_o, bfo).astype(np.float64))
+        assert (diff / np.maximum(den, np.finfo(np.float32).tiny)).max() <= 1e-3
+    return A
+
+
+MASK_CASES = [
+    (wl.WORKLOADS[1], "token_prefix"),
+    (wl.WORKLOADS[1], "pair"),
+    (wl.WORKLOADS[2], "token_prefix"),
+    (wl.WORKLOADS[3], "token_any"),
+    (wl.WORKLOADS[4], "pair"),
+    (wl.custom(3, 70, 7176, 5, 3, "bf16", "zipf_topk", name="bf16_h7176_scalar_copy"), "pair"),
+    (wl.custom(4, 9, 13, 3, 3, "fp16", "gauss_topk", quant_mode=2, name="fp16_q_h13_block_quant"), "token_any"),
+    (wl.custom(2, 2, 32, 66, 40, "bf16", "gauss_topk", quant_mode=2, name="topk66_quant_block"), "pair"),
+    (wl.custom(65, 2, 64, 2, 4, "bf16", "gauss_topk", quant_mode=2, name="65_chunks_scan"), "pair"),
+    (wl.custom(2, 600, 64, 3, 4, "fp16", "zipf_topk", name="bs600"), "token_prefix"),
+    (wl.custom(2, 5, 16, 4, 2, "int32", name="topk_equals_experts"), "pair_all_off"),
+]
+
+
+@pytest.mark.parametrize("w,kind", MASK_CASES, ids=lambda v: v if isinstance(v, str) else v.name)
+def test_token_masks(w, kind):
+    A = check_masked(w, kind)
+    if kind == "pair_all_off":
+        assert A == 0
+
+
+@pytest.mark.parametrize("kind", ["token_prefix", "pair"])
+def test_token_masks_with_the_segment_schedule(kind):
+    w = wl.custom(4, 192, 7168, 4, 2, "fp16", "zipf_topk", name="zipf_bs192")
+    check_masked(w, kind, schedule=moe.MoeSchedule(mode=moe.MOE_SCHED_SEGMENT, large_segment_bytes=64 * 1024))
+
+
+# --------------------------------------------------------------------------
 # determinism (aclnnMoeDistributeDispatchV4 约束说明: deterministic by default)
 # --------------------------------------------------------------------------
 
