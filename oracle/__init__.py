@@ -52,6 +52,12 @@ def _load():
         lib.oracle_large_segments.restype = I
         lib.oracle_identity_expert_dequant.argtypes = [P, P, LL, I, P]
         lib.oracle_identity_expert_dequant.restype = None
+        lib.oracle_identity_expert_dequant_fp8.argtypes = [P, P, LL, I, P]
+        lib.oracle_identity_expert_dequant_fp8.restype = None
+        lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+        lib.oracle_e4m3_to_f32.restype = ctypes.c_float
+        lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+        lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
         lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
         lib.oracle_f16_to_f32.restype = ctypes.c_float
         lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
@@ -111,6 +117,9 @@ def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=Non
     if quant_mode == 2:
         expand_x = np.zeros((rows, h), np.int8)
         dyn = np.zeros((rows,), np.float32)
+    elif quant_mode == 3:                     # E4M3 codes, ceil(h/128) group scales per row
+        expand_x = np.zeros((rows, h), np.uint8)
+        dyn = np.zeros((rows, (h + 127) // 128), np.float32)
     else:
         expand_x = np.zeros((rows, h), x.dtype)
         dyn = None
@@ -188,12 +197,28 @@ def f32_to_bf16(v: float) -> int:
 
 def identity_expert(expand_x, dynamic_scales=None):
     """The harness's identity expert (not part of the method): returns expand_x
-    unchanged, or, for int8 rows with per-row scales, the dequantised rows
-    bf16(f32(q) * scale) as uint16 bits (one fp32 product, one rounding)."""
+    unchanged, or the dequantised rows bf16(f32(q) * scale) as uint16 bits (one
+    fp32 product, one rounding): int8 rows with one scale per row, or E4M3 rows
+    (uint8) with one scale per 128-element group."""
     if dynamic_scales is None:
         return expand_x
+    if np.asarray(dynamic_scales).ndim == 2:
+        q = np.ascontiguousarray(expand_x, dtype=np.uint8)
+        sc = np.ascontiguousarray(dynamic_scales, dtype=np.float32)
+        y = np.zeros(q.shape, np.uint16)
+        _load().oracle_identity_expert_dequant_fp8(_ptr(q), _ptr(sc), q.shape[0], q.shape[1], _ptr(y))
+        return y
     q = np.ascontiguousarray(expand_x, dtype=np.int8)
     sc = np.ascontiguousarray(dynamic_scales, dtype=np.float32)
     y = np.zeros(q.shape, np.uint16)
     _load().oracle_identity_expert_dequant(_ptr(q), _ptr(sc), q.shape[0], q.shape[1], _ptr(y))
     return y
+
+
+def e4m3_to_f32(code: int) -> float:
+    return _load().oracle_e4m3_to_f32(code)
+
+
+def f32_to_e4m3(v: float) -> int:
+    """Nearest E4M3 code (ties to even) of a float with |v| <= 448."""
+    return _load().oracle_f32_to_e4m3(v)

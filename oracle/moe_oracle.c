@@ -38,6 +38,14 @@
  *  - quantMode 2: scale = max|x| / 127 in fp32, q = rint(x / scale) with
  *    ties to even, clamped to [-127, 127]; an all-zero token gets scale 0 and
  *    q = 0; one scale per expand_x row;
+ *  - quantMode 3 (per-group dynamic; [P3] lists it with garbled output types
+ *    and a garbled group size): groups of 128 consecutive elements of a token
+ *    (the last one shorter when 128 does not divide h); per group
+ *    scale = max|x| / 448 in fp32 (448 = largest finite E4M3); code = the
+ *    OCP FP8 E4M3 ("fn") value nearest to the correctly rounded quotient
+ *    x / scale, ties to even, after clamping the quotient to [-448, 448]; the
+ *    code keeps the sign of x (so -0 gives 0x80); an all-zero group gets
+ *    scale 0 and codes 0x00; G = ceil(h / 128) scales per expand_x row;
  *  - combine accumulates in fp32 with one fused multiply-add per k, k
  *    ascending from 0.0f, and rounds once (to nearest even) to the output
  *    type; int32 data combine in wrapping 32-bit integer arithmetic.
@@ -119,6 +127,44 @@ uint16_t oracle_f32_to_bf16(float f)
     return (uint16_t)hi;
 }
 
+/* OCP 8-bit floating point E4M3, "fn" variant: 1 sign bit, 4 exponent bits
+ * (bias 7), 3 fraction bits, no infinities; exponent 15 with fraction 7 is
+ * NaN, so the largest finite value is 1.75 * 2^8 = 448. Normal values are
+ * (1 + f/8) * 2^(e-7), subnormals (e = 0) f * 2^-9. */
+float oracle_e4m3_to_f32(uint8_t v)
+{
+    int sign = v >> 7, expo = (v >> 3) & 15, frac = v & 7;
+    float mag;
+    if (expo == 15 && frac == 7)
+        mag = NAN;
+    else if (expo == 0)
+        mag = ldexpf((float)frac, -9);
+    else
+        mag = ldexpf((float)(8 + frac), expo - 10);
+    return sign ? -mag : mag;
+}
+
+/* Nearest E4M3 value, ties to even, for |f| <= 448 (callers clamp first).
+ * Same quantum argument as for binary16: the spacing is 2^-9 below 2^-6 and
+ * 2^(E-3) in [2^E, 2^(E+1)), so value / quantum is rounded with rint. */
+uint8_t oracle_f32_to_e4m3(float f)
+{
+    uint8_t sign = (f32_bits(f) >> 31) ? 0x80 : 0;
+    float a = fabsf(f);
+    if (a == 0.0f)
+        return sign;
+    if (a < ldexpf(1.0f, -6)) {
+        float n = rintf(a / ldexpf(1.0f, -9));         /* 0..8; 8 encodes 2^-6 */
+        return sign | (uint8_t)n;
+    }
+    int e2;
+    frexpf(a, &e2);
+    int E = e2 - 1;                                    /* a in [2^E, 2^(E+1)) */
+    float n = rintf(ldexpf(a, 3 - E));                 /* in [8, 16] */
+    if (n == 16.0f) { n = 8.0f; E += 1; }
+    return sign | (uint8_t)((E + 7) << 3) | (uint8_t)((int)n - 8);
+}
+
 static float load_f32(const void *base, size_t i, int dtype)
 {
     const uint16_t *p = (const uint16_t *)base;
@@ -158,8 +204,9 @@ static int pair_active(const uint8_t *mask, int mask_kind, long long t, int k, i
 /*
  * x            [W*bs, h] dtype           tokens, source rank s owns rows s*bs..s*bs+bs-1
  * ids          [W*bs, K] int32           global expert ids, distinct per token
- * expand_x     [W*bs*K, h]               dtype, or int8 when quant == 2
- * dyn_scales   [W*bs*K] fp32             written only when quant == 2
+ * expand_x     [W*bs*K, h]               dtype; int8 when quant == 2; E4M3 bytes when quant == 3
+ * dyn_scales   [W*bs*K] fp32             quant == 2: one scale per row;
+ *              [W*bs*K, G] fp32          quant == 3: G = ceil(h / 128) group scales per row
  * assist       [W*bs*K, 3] int32         (src_rank, src_token, topk_id) per row
  * ep_recv_count[W, epr*W] int32          inclusive per-rank segment counts
  * expand_scales[W*bs*K] fp32|int32|NULL  expert_scales[t,k] moved to row(t,k)
@@ -175,8 +222,9 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
 {
     if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
     if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0) != (mask != NULL)) return OR_BAD_ARG;
-    if (quant != 0 && quant != 2) return OR_BAD_ARG;
-    if (quant == 2 && dtype == OR_INT32) return OR_BAD_ARG;
+    if (quant != 0 && quant != 2 && quant != 3) return OR_BAD_ARG;
+    if (quant != 0 && dtype == OR_INT32) return OR_BAD_ARG;
+    const int G = (h + 127) / 128;                     /* quantMode 3 groups per row */
     const long long E = (long long)W * epr, N = (long long)W * bs, S = (long long)epr * W;
     if (K > E) return OR_BAD_ARG;
 
@@ -244,6 +292,26 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
             if (quant == 0) {
                 memcpy((char *)expand_x + (size_t)row * h * xs, (const char *)x + (size_t)t * h * xs,
                        (size_t)h * xs);
+            } else if (quant == 3) {
+                uint8_t *q = (uint8_t *)expand_x + (size_t)row * h;
+                for (int g = 0; g < G; ++g) {
+                    int j0 = g * 128, j1 = j0 + 128 < h ? j0 + 128 : h;
+                    float amax = 0.0f;
+                    for (int j = j0; j < j1; ++j) {
+                        float v = fabsf(load_f32(x, (size_t)(t * h + j), dtype));
+                        if (v > amax) amax = v;
+                    }
+                    float gs = amax / 448.0f;
+                    for (int j = j0; j < j1; ++j) {
+                        float v = load_f32(x, (size_t)(t * h + j), dtype);
+                        if (gs == 0.0f) { q[j] = 0; continue; }
+                        float n = v / gs;
+                        if (n > 448.0f) n = 448.0f;
+                        if (n < -448.0f) n = -448.0f;
+                        q[j] = oracle_f32_to_e4m3(n);
+                    }
+                    dyn_scales[row * G + g] = gs;
+                }
             } else {
                 int8_t *q = (int8_t *)expand_x + (size_t)row * h;
                 for (int j = 0; j < h; ++j) {
@@ -385,6 +453,16 @@ int oracle_large_segments(const int32_t *ep_recv_count, int W, int epr, int h, i
 
 /* y[i, j] = bf16(f32(q[i, j]) * scale[i]): what an identity expert hands to
  * combine when dispatch quantised its input; one fp32 product, one rounding. */
+/* The same for E4M3 rows with per-group scales: bf16(f32(e4m3) * scale[g]). */
+void oracle_identity_expert_dequant_fp8(const uint8_t *q, const float *scale, long long rows, int h,
+                                        uint16_t *y)
+{
+    const int G = (h + 127) / 128;
+    for (long long i = 0; i < rows; ++i)
+        for (int j = 0; j < h; ++j)
+            y[i * h + j] = oracle_f32_to_bf16(oracle_e4m3_to_f32(q[i * h + j]) * scale[i * G + j / 128]);
+}
+
 void oracle_identity_expert_dequant(const int8_t *q, const float *scale, long long rows, int h,
                                     uint16_t *y)
 {

@@ -566,3 +566,100 @@ def test_masks_that_keep_everything_change_nothing_and_mismatches_are_rejected()
     assert d["rows"] == N * K - 1
     with pytest.raises(oracle.OracleError):
         oracle.dispatch(inp["x"], ids, w.ep_world, w.experts_per_rank, 2)
+
+
+# --------------------------------------------------------------------------
+# quantMode 3 (per-group dynamic, reading: groups of 128, OCP E4M3 codes,
+# scale = max|x| / 448): the E4M3 conversions and the quantiser
+# --------------------------------------------------------------------------
+
+def _e4m3_table():
+    """Every finite E4M3 value, from the format's definition (bias 7, 3
+    fraction bits, subnormals f * 2^-9, exponent 15 / fraction 7 is NaN)."""
+    vals = {}
+    for c in range(256):
+        s, e, f = c >> 7, (c >> 3) & 15, c & 7
+        if e == 15 and f == 7:
+            continue
+        v = f * 2.0 ** -9 if e == 0 else (1 + f / 8) * 2.0 ** (e - 7)
+        vals[c] = -v if s else v
+    return vals
+
+
+def test_e4m3_decode_matches_the_definition_and_torch():
+    import torch
+    tab = _e4m3_table()
+    ref = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+    for c in range(256):
+        got = oracle.e4m3_to_f32(c)
+        if c in tab:
+            assert got == tab[c] == ref[c], c
+        else:
+            assert np.isnan(got) and np.isnan(ref[c]), c
+    assert max(tab.values()) == 448.0 and min(v for v in tab.values() if v > 0) == 2.0 ** -9
+
+
+def test_e4m3_encode_is_nearest_ties_to_even():
+    """Brute-force nearest search over every finite code (ties to the even
+    code, the sign kept), and torch's float8_e4m3fn cast, on every
+    representable value, every midpoint, one float32 ulp either side of each
+    midpoint, and random values in [-448, 448]."""
+    import torch
+    tab = _e4m3_table()
+    pos = sorted((v, c) for c, v in tab.items() if v >= 0 and not (v == 0 and c == 0x80))
+    vals = [v for v, _ in pos]
+    pts = set(vals)
+    for a, b in zip(vals, vals[1:]):
+        m = np.float32((a + b) / 2)
+        pts.update([float(m), float(np.nextafter(m, np.float32(0))), float(np.nextafter(m, np.float32(1e9)))])
+    rng = np.random.default_rng(11)
+    pts.update(rng.uniform(0, 448, 3000).astype(np.float32).tolist())
+    pts.update((2.0 ** rng.uniform(-12, 8.8, 3000)).astype(np.float32).clip(0, 448).tolist())
+    xs = np.array(sorted(pts), np.float32)
+    xs = np.concatenate([xs, -xs])
+    want_torch = torch.from_numpy(xs).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    pos_codes = [(v, c) for v, c in pos]
+    n = 0
+    for x, wt in zip(xs.tolist(), want_torch.tolist()):
+        a = abs(x)
+        best = min(pos_codes, key=lambda vc: (abs(vc[0] - a), vc[1] & 1))
+        code = best[1] | (0x80 if np.signbit(np.float32(x)) else 0)
+        got = oracle.f32_to_e4m3(x)
+        assert got == code == wt, (x, got, code, wt)
+        n += 1
+    assert n > 10000
+
+
+def test_group_quantiser_properties():
+    """Per group of 128: scale = amax / 448 in fp32; the largest element maps to
+    +-448; every code decodes to within half an E4M3 quantum of x / scale; an
+    all-zero group has scale 0 and codes 0; a ragged last group is its own
+    group; -0 keeps its sign bit in a group with a nonzero scale."""
+    h = 128 * 3 + 40
+    rng = np.random.default_rng(4)
+    x = (rng.standard_normal((6, h)) * 2.0 ** rng.integers(-20, 10, size=(6, 1))).astype(np.float16)
+    x[2, 128:256] = 0.0                      # an all-zero group
+    x[3, 5] = -0.0
+    ids = np.array([[0], [1], [2], [3], [0], [1]], np.int32)
+    d = oracle.dispatch(x, ids, 2, 2, quant_mode=3)
+    assert d["expand_x"].dtype == np.uint8 and d["dynamic_scales"].shape == (6, 4)
+    row_of = {tuple(a): i for i, a in enumerate(d["assist_info"].tolist())}
+    dec = np.array([oracle.e4m3_to_f32(c) for c in range(256)], np.float32)
+    xf = x.astype(np.float32)
+    for t in range(6):
+        i = row_of[(t // 3, t % 3, 0)]
+        q, sc = d["expand_x"][i], d["dynamic_scales"][i]
+        for g in range(4):
+            seg = slice(g * 128, min(h, g * 128 + 128))
+            amax = np.abs(xf[t, seg]).max()
+            assert sc[g] == np.float32(amax) / np.float32(448.0)
+            if amax == 0:
+                assert sc[g] == 0 and (q[seg] == 0).all()
+                continue
+            quot = xf[t, seg] / sc[g]
+            deq = dec[q[seg]]
+            assert np.abs(deq).max() == 448.0
+            quantum = np.where(np.abs(quot) < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(np.abs(quot), 1e-30))) - 3))
+            assert (np.abs(deq - np.clip(quot, -448, 448)) <= quantum / 2 + 1e-12).all(), (t, g)
+    i = row_of[(1, 0, 0)]
+    assert d["expand_x"][i, 5] == 0x80
