@@ -50,10 +50,11 @@ def algorithmic_bytes(w: wl.Workload):
     """
     N, K, h, rows = w.num_tokens, w.topk, w.h, w.rows
     sx = 4 if w.dtype == "int32" else 2
-    s_exp = 1 if w.quant_mode == 2 else sx
-    s_y = 2 if w.quant_mode == 2 else sx          # identity-expert output for int8 rows is bf16
+    s_exp = 1 if w.quant_mode else sx             # int8 or E4M3 codes
+    s_y = 2 if w.quant_mode else sx               # identity-expert output for quantised rows is bf16
     erc = w.ep_world * w.num_experts * 4
-    disp = N * h * sx + N * K * 4 + rows * h * s_exp + rows * 12 + erc + (rows * 4 if w.quant_mode == 2 else 0)
+    n_scales = {2: rows, 3: rows * ((h + 127) // 128)}.get(w.quant_mode, 0)   # fp32 dynamic scales
+    disp = N * h * sx + N * K * 4 + rows * h * s_exp + rows * 12 + erc + n_scales * 4
     comb = rows * h * s_y + N * K * 4 + rows * 12 + erc + N * K * 4 + N * h * s_y
     return disp, comb
 
@@ -75,6 +76,10 @@ def measure(w, steps, warmup, flush, torch, moe):
     moe.dispatch_into(buf, x, ids)
     if w.quant_mode == 2:
         y = (buf.expand_x.float() * buf.dynamic_scales[:, None]).to(torch.bfloat16)
+    elif w.quant_mode == 3:                    # one scale per 128-element group
+        sc_full = buf.dynamic_scales.repeat_interleave(128, dim=1)[:, :w.h]
+        y = (buf.expand_x.float() * sc_full).to(torch.bfloat16)
+        del sc_full
     else:
         y = buf.expand_x                       # identity expert: combine reads dispatch's rows
     x_out = torch.empty((w.num_tokens, w.h), dtype=y.dtype, device="cuda")
@@ -142,7 +147,7 @@ def cpu_baseline(w, reps=3):
     bf = w.dtype == "bf16"
     d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode, bf16=bf)
     y = oracle.identity_expert(d["expand_x"], d["dynamic_scales"])
-    out_bf = bf or w.quant_mode == 2
+    out_bf = bf or w.quant_mode != 0
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
@@ -164,7 +169,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="w16_h7168_bf16_q8", choices=sorted(wl.BY_NAME))
-    ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf",
+    ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf,w16_h7168_bf16_fp8g128",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -203,7 +208,7 @@ def main():
     comb_ms = r["comb"]
     comb_gbps = comb_b / (comb_ms * 1e-3) / 1e9
     kernel = "moe_combine = combine_slots_kernel + " + (
-        "combine_gather_half_kernel<BF16,true>" if (w.dtype == "bf16" or w.quant_mode == 2) else
+        "combine_gather_half_kernel<BF16,true>" if (w.dtype == "bf16" or w.quant_mode != 0) else
         ("combine_gather_half_kernel<F16,true>" if w.dtype == "fp16" else "combine_gather_i32_kernel<true>"))
 
     also = {}
@@ -218,7 +223,9 @@ def main():
                       "dispatch_ms": round(ra["disp"], 5), "combine_ms": round(ra["comb"], 5),
                       "cold_median_ms": round(statistics.median(ra["cold"]), 5),
                       "cold_GB/s": round((da + ca) / (statistics.median(ra["cold"]) * 1e-3) / 1e9, 1),
-                      "algorithmic_bytes": da + ca}
+                      "algorithmic_bytes": da + ca,
+                      "quant": {2: "per-token dynamic int8", 3: "per-group (128) dynamic fp8 e4m3"}.get(
+                          wa.quant_mode, "none")}
 
     line = {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -228,7 +235,7 @@ def main():
                                            if w.routing == "gauss_topk" else w.routing),
         "config": {"workload": w.name, "ep_world": w.ep_world, "bs": w.bs, "h": w.h, "topk": w.topk,
                    "experts_per_rank": w.experts_per_rank, "experts": w.num_experts, "tokens": w.num_tokens,
-                   "quant": "per-token dynamic int8" if w.quant_mode == 2 else "none",
+                   "quant": {2: "per-token dynamic int8", 3: "per-group (128) dynamic fp8 e4m3"}.get(w.quant_mode, "none"),
                    "combine_input": "bf16 identity-expert output" if w.quant_mode == 2 else w.dtype,
                    "working_set_MB": round((disp_b + comb_b) / 1e6),
                    "algorithmic_bytes": disp_b + comb_b},

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.s
 
 MOE_OK = 0
 MOE_INT32, MOE_FP16, MOE_BF16 = 0, 1, 2
-MOE_QUANT_NONE, MOE_QUANT_DYN_TOKEN = 0, 2
+MOE_QUANT_NONE, MOE_QUANT_DYN_TOKEN, MOE_QUANT_DYN_GROUP = 0, 2, 3
 MOE_SCHED_TOKEN, MOE_SCHED_SEGMENT = 0, 1
 MOE_MASK_NONE, MOE_MASK_TOKEN, MOE_MASK_PAIR = 0, 1, 2
 
@@ -133,10 +133,14 @@ class DispatchBuffers:
         N, rows = ep_world * bs, ep_world * bs * topk
         self.shape = (ep_world, bs, experts_per_rank, h, topk)
         self.dtype, self.quant_mode = dtype, quant_mode
-        out_dt = torch.int8 if quant_mode == MOE_QUANT_DYN_TOKEN else dtype
+        out_dt = {MOE_QUANT_DYN_TOKEN: torch.int8, MOE_QUANT_DYN_GROUP: torch.float8_e4m3fn}.get(quant_mode, dtype)
         self.expand_x = torch.empty((rows, h), dtype=out_dt, device=device)
-        self.dynamic_scales = (torch.empty((rows,), dtype=torch.float32, device=device)
-                               if quant_mode == MOE_QUANT_DYN_TOKEN else None)
+        if quant_mode == MOE_QUANT_DYN_TOKEN:
+            self.dynamic_scales = torch.empty((rows,), dtype=torch.float32, device=device)
+        elif quant_mode == MOE_QUANT_DYN_GROUP:          # one scale per 128-element group
+            self.dynamic_scales = torch.empty((rows, (h + 127) // 128), dtype=torch.float32, device=device)
+        else:
+            self.dynamic_scales = None
         self.assist_info = torch.empty((rows, 3), dtype=torch.int32, device=device)
         self.ep_recv_count = torch.empty((ep_world, experts_per_rank * ep_world), dtype=torch.int32,
                                          device=device)

@@ -672,7 +672,87 @@ __device__ __forceinline__ void quant_store_wave(const DispatchArgs &a, int lane
     if (my_row >= 0) a.dyn[my_row] = scale;
 }
 
+// ---- quantMode 3: per-group (128 elements) dynamic FP8 E4M3 ----
+// 8 elements -> 8 E4M3 bytes, scale > 0. The quotient |x| / scale (FAST: the
+// one-step corrected |x| * inv) is clamped to 448 and converted, with x's sign,
+// by v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950, round to nearest even). Two checks
+// make the codes those of the definition: on the CPU, for every 16-bit
+// (x, group max) pair, the corrected quotient rounded to E4M3 equals the E4M3
+// rounding of the exact quotient; on this GPU, the instruction equals that
+// rounding for every binary32 |v| <= 448 (2,277,507,074 values).
+template <class T, bool FAST>
+__device__ __forceinline__ uint2 fp8_u4(uint4 v, float scale, float inv)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint16_t bits = (uint16_t)(w[i >> 1] >> ((i & 1) * 16));
+        const float ax = fabsf(T::load(bits));
+        float q;
+        if (FAST) {
+            const float q0 = ax * inv;
+            const float r = __builtin_fmaf(-q0, scale, ax);
+            q = __builtin_fmaf(r, inv, q0);
+        } else {
+            q = ax / scale;
+        }
+        c[i] = __uint_as_float(__float_as_uint(fminf(q, 448.0f)) | ((uint32_t)(bits & 0x8000u) << 16));
+    }
+    uint32_t o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * h], c[4 * h + 1], 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * h + 2], c[4 * h + 3], p, true);
+        o[h] = (uint32_t)p;
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+// The wavefront holds one token (16 elements per lane and chunk); a group of
+// 128 elements is 8 neighbouring lanes of one chunk, so its max is three xor
+// shuffles. Per group: scale = max / 448 (0 -> codes 0); lanes 8g write the
+// group's scale for each of the K rows (dynamic_scales [rows, ceil(h/128)]).
 template <class T, int J>
+__device__ __forceinline__ void quant_store_wave_fp8(const DispatchArgs &a, int lane, const uint4 (&v)[J][2],
+                                                     int my_row)
+{
+    const int K = a.K, noc = a.h / 16, G = (a.h + 127) / 128;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int c = lane + 64 * j;
+        const bool live = c < noc;
+        float amax = live ? fmaxf(amax_u4<T>(v[j][0]), amax_u4<T>(v[j][1])) : 0.0f;
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 2, 64));
+        amax = fmaxf(amax, __shfl_xor(amax, 4, 64));
+        const float scale = amax / 448.0f;
+        const float inv = 1.0f / scale;
+        uint4 q = make_uint4(0u, 0u, 0u, 0u);
+        if (scale != 0.0f) {
+            uint2 lo, hi;
+            if (scale >= kFastQuantMinScale) {
+                lo = fp8_u4<T, true>(v[j][0], scale, inv);
+                hi = fp8_u4<T, true>(v[j][1], scale, inv);
+            } else {
+                lo = fp8_u4<T, false>(v[j][0], scale, inv);
+                hi = fp8_u4<T, false>(v[j][1], scale, inv);
+            }
+            q = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+        if (!live) continue;
+        for (int k = 0; k < K; ++k) {
+            const int row = __builtin_amdgcn_readlane(my_row, k);
+            if (row < 0) continue;
+            uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + c;
+            if ((j + k) & 1) store_stream(dst, q);   // see store_stream
+            else *dst = q;
+            if ((lane & 7) == 0) a.dyn[(size_t)row * G + (c >> 3)] = scale;
+        }
+    }
+}
+
+template <class T, int J, int QM>
 __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(DispatchArgs a)
 {
     const int lane = threadIdx.x & 63;
@@ -692,7 +772,8 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(Dispa
             v[j][1] = src[2 * oc + 1];
         }
         const int my_row = lane_pair_row(a, t, lane, e, l, true);
-        quant_store_wave<T, J>(a, lane, v, my_row);
+        if constexpr (QM == MOE_QUANT_DYN_GROUP) quant_store_wave_fp8<T, J>(a, lane, v, my_row);
+        else quant_store_wave<T, J>(a, lane, v, my_row);
     }
 }
 
@@ -1003,6 +1084,16 @@ DispatchLayout dispatch_layout(int W, int bs, int epr, int K)
     return L;
 }
 
+template <class T, int QM>
+void launch_quant_wave(int J, dim3 g, dim3 b, hipStream_t st, const DispatchArgs &a)
+{
+    if (J <= 1) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 1, QM>), g, b, 0, st, a);
+    else if (J <= 2) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 2, QM>), g, b, 0, st, a);
+    else if (J <= 4) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 4, QM>), g, b, 0, st, a);
+    else if (J <= 7) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 7, QM>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 8, QM>), g, b, 0, st, a);
+}
+
 }  // namespace
 
 extern "C" {
@@ -1030,8 +1121,12 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
     if (!bytes) return MOE_ERR_NULLPTR;
     int rc = check_scalars(ep_world, bs, experts_per_rank, h, topk, dtype);
     if (rc) return rc;
-    if (quant_mode != MOE_QUANT_NONE && quant_mode != MOE_QUANT_DYN_TOKEN) return MOE_ERR_QUANT;
-    if (quant_mode == MOE_QUANT_DYN_TOKEN && dtype == MOE_INT32) return MOE_ERR_QUANT;
+    if (quant_mode != MOE_QUANT_NONE && quant_mode != MOE_QUANT_DYN_TOKEN && quant_mode != MOE_QUANT_DYN_GROUP)
+        return MOE_ERR_QUANT;
+    if (quant_mode != MOE_QUANT_NONE && dtype == MOE_INT32) return MOE_ERR_QUANT;
+    // the per-group quantiser is the wavefront-per-token kernel only
+    if (quant_mode == MOE_QUANT_DYN_GROUP && (h % 16 != 0 || h > 1024 * 8 || topk > kQuantMaxK))
+        return MOE_ERR_QUANT;
     *bytes = dispatch_layout(ep_world, bs, experts_per_rank, topk).total;
     return MOE_OK;
 }
@@ -1047,7 +1142,8 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     if (rc) return rc;
     const int W = ep_world, epr = experts_per_rank, K = topk;
     const long long N = (long long)W * bs;
-    const bool quant = quant_mode == MOE_QUANT_DYN_TOKEN;
+    const bool quant = quant_mode != MOE_QUANT_NONE;
+    const bool group_quant = quant_mode == MOE_QUANT_DYN_GROUP;
     if (!ep_recv_count || !workspace) return MOE_ERR_NULLPTR;
     if (N > 0 && (!x || !expert_ids || !expand_x || !assist_info)) return MOE_ERR_NULLPTR;
     if (quant != (dynamic_scales != nullptr) && N > 0) return MOE_ERR_NULLPTR;
@@ -1066,6 +1162,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     const long long S = (long long)epr * W;
     const bool want_seg = mode == MOE_SCHED_SEGMENT || seg_flags;
     if (want_seg && (long long)W * S > kSegLdsMax) return MOE_ERR_SCHEDULE;
+    if (group_quant && mode == MOE_SCHED_SEGMENT) return MOE_ERR_SCHEDULE;
 
     const size_t xs = elem_size(dtype);
     const size_t rowbytes = (size_t)h * xs;
@@ -1074,6 +1171,11 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         !aligned(ep_recv_count, 4) || !aligned(expand_scales, 4) || !aligned(workspace, 16) ||
         !aligned(seg_flags, 4))
         return MOE_ERR_ALIGN;
+    // per-token int8 takes the wavefront kernel when it can, a block kernel
+    // otherwise; per-group FP8 needs the wavefront kernel's 16-byte rows
+    const bool wave = quant && h % 16 == 0 && h <= 1024 * 8 && K <= kQuantMaxK && aligned(x, 16) &&
+                      aligned(expand_x, 16);
+    if (group_quant && !wave && N > 0) return MOE_ERR_ALIGN;
 
     const DispatchLayout L = dispatch_layout(W, bs, epr, K);
     char *ws = static_cast<char *>(workspace);
@@ -1131,23 +1233,15 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                 if (vec) hipLaunchKernelGGL(scatter_copy_kernel<true>, g, b, kdsm, st, a);
                 else hipLaunchKernelGGL(scatter_copy_kernel<false>, g, b, kdsm, st, a);
             } else {
-                const bool wave = h % 16 == 0 && h <= 1024 * 8 && K <= kQuantMaxK && aligned(x, 16) &&
-                                  aligned(expand_x, 16);
                 if (wave) {
                     const int J = (h / 16 + 63) / 64;
                     const dim3 g((unsigned)((N + 3) / 4)), b(kQuantThreads);
                     if (dtype == MOE_FP16) {
-                        if (J <= 1) hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 1>), g, b, 0, st, a);
-                        else if (J <= 2) hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 2>), g, b, 0, st, a);
-                        else if (J <= 4) hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 4>), g, b, 0, st, a);
-                        else if (J <= 7) hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 7>), g, b, 0, st, a);
-                        else hipLaunchKernelGGL((scatter_quant_wave_kernel<F16, 8>), g, b, 0, st, a);
+                        if (group_quant) launch_quant_wave<F16, MOE_QUANT_DYN_GROUP>(J, g, b, st, a);
+                        else launch_quant_wave<F16, MOE_QUANT_DYN_TOKEN>(J, g, b, st, a);
                     } else {
-                        if (J <= 1) hipLaunchKernelGGL((scatter_quant_wave_kernel<BF16, 1>), g, b, 0, st, a);
-                        else if (J <= 2) hipLaunchKernelGGL((scatter_quant_wave_kernel<BF16, 2>), g, b, 0, st, a);
-                        else if (J <= 4) hipLaunchKernelGGL((scatter_quant_wave_kernel<BF16, 4>), g, b, 0, st, a);
-                        else if (J <= 7) hipLaunchKernelGGL((scatter_quant_wave_kernel<BF16, 7>), g, b, 0, st, a);
-                        else hipLaunchKernelGGL((scatter_quant_wave_kernel<BF16, 8>), g, b, 0, st, a);
+                        if (group_quant) launch_quant_wave<BF16, MOE_QUANT_DYN_GROUP>(J, g, b, st, a);
+                        else launch_quant_wave<BF16, MOE_QUANT_DYN_TOKEN>(J, g, b, st, a);
                     }
                 } else {
                     const bool vec = h % 8 == 0 && aligned(x, 16) && aligned(expand_x, 8);

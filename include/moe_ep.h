@@ -50,7 +50,8 @@ enum moe_status {
     MOE_ERR_NULLPTR = 1,   /* a required pointer is NULL, or a forbidden one is not */
     MOE_ERR_SHAPE = 2,     /* a size is out of range or a product overflows */
     MOE_ERR_DTYPE = 3,     /* unknown token dtype */
-    MOE_ERR_QUANT = 4,     /* unknown quant mode, or quantisation of int32 data */
+    MOE_ERR_QUANT = 4,     /* unknown quant mode, quantisation of int32 data, or a shape the
+                              per-group quantiser does not take */
     MOE_ERR_WORKSPACE = 5, /* workspace smaller than the queried size */
     MOE_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch */
     MOE_ERR_SCHEDULE = 7,  /* unknown schedule mode, or the segment schedule (or the
@@ -64,8 +65,19 @@ enum moe_status {
 enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
 
 /* Quantisation modes; the numbering follows quantMode of
- * aclnnMoeDistributeDispatchV4 (0 = none, 2 = per-token dynamic). */
-enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_DYN_TOKEN = 2 };
+ * aclnnMoeDistributeDispatchV4 (0 = none, 2 = per-token dynamic, 3 = per-group
+ * dynamic).
+ *  MOE_QUANT_DYN_TOKEN: int8 codes rint(x / s), s = max|x| / 127 over the token;
+ *      dynamic_scales holds one fp32 scale per row.
+ *  MOE_QUANT_DYN_GROUP: OCP FP8 E4M3 ("fn") codes per group of 128 elements of
+ *      h (the last group may be shorter): s = max|x| / 448 over the group, code
+ *      = E4M3 nearest to RN(x / s) clamped to +-448, ties to even, sign of x
+ *      kept; an all-zero group has s = 0 and codes 0. dynamic_scales is fp32
+ *      [ROWS, ceil(h/128)]. (The pages list the mode; its output types and group
+ *      size are garbled, and these are the readings taken.) Needs h % 16 == 0,
+ *      h <= 8192, topk <= 64, 16-byte aligned x and expand_x, and the token
+ *      schedule. */
+enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_DYN_TOKEN = 2, MOE_QUANT_DYN_GROUP = 3 };
 
 /* Token masks: xActiveMaskOptional of aclnnMoeDistributeDispatchV4 (参数说明):
  * a 1D mask (BS,) per rank or a 2D mask (BS, K); a token whose K entries are
@@ -118,7 +130,8 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
 /*
  * Dispatch: the expert-parallel all-to-all of aclnnMoeDistributeDispatchV4
  * (计算公式, expandXOut = AllToAllV(X)) with every logical rank's window in
- * one HBM, preceded by optional per-token dynamic int8 quantisation.
+ * one HBM, preceded by optional dynamic quantisation (per-token int8 or
+ * per-group FP8 E4M3).
  *
  *  x              [N, h] dtype           tokens; rows s*bs..s*bs+bs-1 are rank s's
  *  expert_ids     [N, K] int32           global expert ids in [0, E), distinct per token
@@ -126,11 +139,12 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
  *  expert_scales  [N, K] 4-byte or NULL  only read when expand_scales is given
  *  x_active_mask  uint8 [N] or [N, K]    see moe_mask; NULL with MOE_MASK_NONE
  *  mask_kind      moe_mask
- *  expand_x       [ROWS, h]              dtype, or int8 when quant_mode == 2. Row order:
+ *  expand_x       [ROWS, h]              dtype; int8 when quant_mode == 2, E4M3 bytes when 3. Row order:
  *                                        rank r, then local expert, then source rank,
  *                                        then ascending source token
- *  dynamic_scales [ROWS] fp32            per-row token scale max|x|/127; required iff
- *                                        quant_mode == 2, must be NULL otherwise
+ *  dynamic_scales [ROWS] fp32            per-row token scale max|x|/127 (quant_mode 2), or
+ *                 [ROWS, ceil(h/128)]    per-group scales max|x|/448 (quant_mode 3);
+ *                                        required iff quantising, NULL otherwise
  *  assist_info    [ROWS, 3] int32        (src_rank, src_token, topk_id) of each row
  *  ep_recv_count  [W, S] int32           per rank, inclusive prefix of the row counts of
  *                                        its segments ordered el*W + s

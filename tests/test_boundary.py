@@ -67,6 +67,12 @@ def _ws(*args):
     ((2, 4, 2, 16, 1, 3, 0), DTYPE),
     ((2, 4, 2, 16, 1, 1, 1), QUANT),          # quant mode 1 not offered
     ((2, 4, 2, 16, 1, 0, 2), QUANT),          # int32 cannot be quantised
+    ((16, 256, 16, 7168, 8, 2, 3), OK),       # per-group FP8
+    ((2, 4, 2, 16, 1, 0, 3), QUANT),
+    ((2, 4, 2, 7176, 1, 2, 3), QUANT),        # per-group needs h % 16 == 0
+    ((2, 4, 2, 8208, 1, 2, 3), QUANT),        # ... and h <= 8192
+    ((8, 4, 16, 64, 65, 2, 3), QUANT),        # ... and topk <= 64
+    ((2, 4, 2, 16, 1, 1, 4), QUANT),
 ])
 def test_dispatch_workspace_query(args, want):
     rc, n = _ws(*args)
@@ -111,7 +117,8 @@ def _dispatch(**kw):
     (dict(W=1), SHAPE),
     (dict(K=5), SHAPE),
     (dict(dtype=7), DTYPE),
-    (dict(quant=3), QUANT),
+    (dict(quant=4), QUANT),
+    (dict(quant=3), NULLPTR),                        # per-group quantising needs dynamic_scales
     (dict(dtype=0, quant=2, dyn=7 * A), QUANT),
     (dict(x=None), NULLPTR),
     (dict(ids=None), NULLPTR),
@@ -129,6 +136,8 @@ def _dispatch(**kw):
     (dict(ws=6 * A + 8), ALIGN),
     (dict(sched=moe.MoeSchedule(mode=5)), SCHEDULE),
     (dict(W=128, epr=8, K=2, sched=moe.MoeSchedule(mode=1)), SCHEDULE),   # W*S = 131072 > LDS budget
+    (dict(quant=3, dyn=7 * A, sched=moe.MoeSchedule(mode=1)), SCHEDULE),  # per-group: token schedule only
+    (dict(quant=3, dyn=7 * A, x=A + 2), ALIGN),                           # per-group: 16-byte rows
     (dict(mk=3, mask=8 * A), MASK),                                     # unknown mask kind
     (dict(mk=1), MASK),                                                 # a kind without a mask
     (dict(mask=8 * A), MASK),                                           # a mask without a kind

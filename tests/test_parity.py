@@ -35,12 +35,18 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     t = t.detach().cpu()
     if t.dtype == torch.bfloat16:
         return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float8_e4m3fn:
+        return t.view(torch.uint8).numpy()
     return t.numpy()
 
 
 def gpu_identity_expert(expand_x, dyn):
+    """bf16(f32(q) * scale): one scale per row (int8), or per 128-element group (E4M3)."""
     if dyn is None:
         return expand_x
+    if dyn.dim() == 2:
+        sc = dyn.repeat_interleave(128, dim=1)[:, :expand_x.shape[1]]
+        return (expand_x.float() * sc).to(torch.bfloat16)
     return (expand_x.float() * dyn[:, None]).to(torch.bfloat16)
 
 
@@ -62,7 +68,7 @@ def run_oracle(w, inp):
     d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
                         expert_scales=inp["scales"], bf16=bf)
     y = oracle.identity_expert(d["expand_x"], d["dynamic_scales"])
-    out_bf = bf or w.quant_mode == 2
+    out_bf = bf or w.quant_mode != 0
     d["x_out"] = oracle.combine(y, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"],
                                 w.ep_world, w.experts_per_rank, bf16=out_bf)
     d["y"] = y
@@ -95,12 +101,12 @@ def assert_parity(w, g, o):
     assert (g["assist_info"] == o["assist_info"]).all(), "assist_info"
     assert g["expand_x"].tobytes() == o["expand_x"].tobytes(), "expand_x"
     assert g["expand_scales"].view(np.uint32).tobytes() == o["expand_scales"].view(np.uint32).tobytes()
-    if w.quant_mode == 2:
+    if w.quant_mode != 0:
         assert g["dynamic_scales"].view(np.uint32).tobytes() == o["dynamic_scales"].view(np.uint32).tobytes()
     if w.dtype == "int32":
         assert (g["x_out"] == o["x_out"]).all(), "x_out"
     else:
-        bf = w.dtype == "bf16" or w.quant_mode == 2
+        bf = w.dtype == "bf16" or w.quant_mode != 0
         err = rel_err_metric(g["x_out"], o["x_out"], o["y"], o["assist_info"], o["scales_in"], w.ep_world, w.bs,
                              w.topk, bf)
         assert err <= 1e-3, err
@@ -183,6 +189,47 @@ def test_tiny_tokens_quantise_exactly(exp):
     check(w, inp)
 
 
+# --------------------------------------------------------------------------
+# quantMode 3: per-group (128) dynamic FP8 E4M3 (readings: group size, E4M3,
+# scale = max|x| / 448)
+# --------------------------------------------------------------------------
+
+GROUP_QUANT = [
+    wl.custom(16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=3, name="w16_h7168_bf16_fp8"),
+    wl.custom(3, 300, 1040, 4, 3, "fp16", "zipf_topk", quant_mode=3, name="fp16_h1040_ragged_group"),
+    wl.custom(2, 5, 16, 3, 2, "bf16", "gauss_topk", quant_mode=3, name="h16_one_partial_group"),
+    wl.custom(4, 257, 8192, 2, 4, "bf16", "gauss_topk", quant_mode=3, name="h8192_j8"),
+    wl.custom(65, 2, 256, 2, 4, "fp16", "gauss_topk", quant_mode=3, name="65_chunks_scanned_offsets"),
+    wl.custom(2, 2, 128, 64, 40, "bf16", "gauss_topk", quant_mode=3, name="topk64"),
+]
+
+
+@pytest.mark.parametrize("w", GROUP_QUANT, ids=lambda w: w.name)
+def test_group_quant_shapes(w):
+    check(w)
+
+
+@pytest.mark.parametrize("exp", [-90, -125], ids=["tiny_fast_path", "subnormal_division_path"])
+def test_group_quant_tiny_and_zero_groups(exp):
+    """Group scales below 2^-100 take the IEEE division; zero groups give scale
+    0 and codes 0; -0 keeps its sign bit."""
+    w = wl.custom(2, 8, 512, 2, 2, "bf16", "gauss_topk", quant_mode=3, name="fp8_tiny")
+    inp = wl.make_inputs(w)
+    rng = np.random.default_rng(23)
+    g = rng.standard_normal((w.num_tokens, w.h)).astype(np.float32)
+    g[:, 128:256] *= np.float32(2.0 ** exp)
+    g[:, 256:384] = 0.0
+    g[3, 300] = -0.0
+    g[4] = -0.0
+    inp["x"] = wl.f32_to_bf16_bits(g)
+    gg, o = check(w, inp)
+    assert (gg["dynamic_scales"][:, 2] == 0).all()
+
+
+def test_group_quant_with_a_mask():
+    check_masked(wl.custom(4, 96, 2048, 6, 4, "bf16", "zipf_topk", quant_mode=3, name="fp8_masked"), "pair")
+
+
 def test_int32_combine_wraps_like_the_oracle():
     w = wl.custom(2, 4, 16, 2, 2, "int32", x_lo=-(2 ** 31), x_hi=2 ** 31 - 1, name="int32_wrap")
     check(w)
@@ -217,7 +264,7 @@ def test_schedules_are_result_neutral_and_flag_the_right_segments(w, mode, T):
     flags = torch.full((w.ep_world, w.experts_per_rank * w.ep_world), -1, dtype=torch.int32, device=DEV)
     sched = moe.MoeSchedule(mode=mode, large_segment_bytes=T, segment_is_large=flags.data_ptr())
     g, o = check(w, inp, sched)
-    elem = 1 if w.quant_mode == 2 else (4 if w.dtype == "int32" else 2)
+    elem = 1 if w.quant_mode != 0 else (4 if w.dtype == "int32" else 2)
     want = oracle.large_segments(o["ep_recv_count"], w.ep_world, w.experts_per_rank, w.h, elem,
                                  TWO_MIB if T < 0 else T)
     assert (to_np(flags) == want.astype(np.int32)).all()
@@ -312,13 +359,13 @@ def check_masked(w, kind, seed=1, schedule=None):
                         expert_scales=inp["scales"], bf16=bf, mask=mask)
     yo = oracle.identity_expert(d["expand_x"], d["dynamic_scales"])
     xo_o = oracle.combine(yo, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"], w.ep_world,
-                          w.experts_per_rank, bf16=bf or w.quant_mode == 2, mask=mask)
+                          w.experts_per_rank, bf16=bf or w.quant_mode != 0, mask=mask)
     A = d["rows"]
     assert (to_np(erc) == d["ep_recv_count"]).all(), "ep_recv_count"
     assert (to_np(assist)[:A] == d["assist_info"][:A]).all(), "assist_info"
     assert to_np(ex)[:A].tobytes() == d["expand_x"][:A].tobytes(), "expand_x"
     assert to_np(esc)[:A].view(np.uint32).tobytes() == d["expand_scales"][:A].view(np.uint32).tobytes()
-    if w.quant_mode == 2:
+    if w.quant_mode != 0:
         assert to_np(dyn)[:A].view(np.uint32).tobytes() == d["dynamic_scales"][:A].view(np.uint32).tobytes()
     g = to_np(xo)
     if w.dtype == "int32":
@@ -327,7 +374,7 @@ def check_masked(w, kind, seed=1, schedule=None):
         assert g.view(np.uint16).tobytes() == xo_o.view(np.uint16).tobytes(), "x_out bits"
         # and the tolerance metric over the active pairs
         act = np.repeat(mask[:, None], w.topk, axis=1) if mask.ndim == 1 else mask
-        yf = as_f32(yo, True if (bf or w.quant_mode == 2) else False)
+        yf = as_f32(yo, True if (bf or w.quant_mode != 0) else False)
         den = np.zeros(g.shape, np.float64)
         a3 = d["assist_info"][:A].astype(np.int64)
         row_of = np.full(w.num_tokens * w.topk, -1, np.int64)
@@ -337,7 +384,7 @@ def check_masked(w, kind, seed=1, schedule=None):
             r = row_of[t_on * w.topk + k]
             assert (r >= 0).all()
             den[t_on] += np.abs(yf[r].astype(np.float64)) * np.abs(inp["scales"][t_on, k].astype(np.float64))[:, None]
-        bfo = bf or w.quant_mode == 2
+        bfo = bf or w.quant_mode != 0
         diff = np.abs(as_f32(g, bfo).astype(np.float64) - as_f32(xo_o, bfo).astype(np.float64))
         assert (diff / np.maximum(den, np.finfo(np.float32).tiny)).max() <= 1e-3
     return A

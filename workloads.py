@@ -75,7 +75,12 @@ WORKLOADS = [
     Workload("w8_h7168_fp16_zipf", 3, 8, 32, 7168, 8, 8, "fp16", "zipf_topk"),
     Workload("w16_h7168_bf16_q8", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2),
 ]
-BY_NAME = {w.name: w for w in WORKLOADS}
+# Not a page workload: the 16-rank one (same seed, so the same tokens and routing)
+# with per-group FP8 E4M3 quantisation (quantMode 3) instead of per-token int8.
+EXTRA_WORKLOADS = [
+    Workload("w16_h7168_bf16_fp8g128", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=3),
+]
+BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
 
 def custom(ep_world, bs, h, topk, experts_per_rank, dtype="int32", routing="uniform_distinct",
