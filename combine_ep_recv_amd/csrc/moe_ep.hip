@@ -186,9 +186,12 @@ __device__ __forceinline__ int bitmap_rank(const unsigned long long *row, int bi
     return r;
 }
 
+// MK: the token-mask kind, a template parameter so that the unmasked kernel
+// carries no mask code (it cost 0.6 us of latency at 16 chunks).
+template <int MK>
 __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__restrict__ ids, int W, int bs,
                                                               int epr, int K, int nbs,
-                                                              const uint8_t *__restrict__ mask, int mask_kind,
+                                                              const uint8_t *__restrict__ mask,
                                                               int32_t *__restrict__ pc, int32_t *__restrict__ pci,
                                                               int32_t *__restrict__ lr)
 {
@@ -215,8 +218,8 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
         eu = -1;
         if (p < npairs) {
             eu = ids[pair0 + p];
-            if (mask_kind == MOE_MASK_TOKEN && !mask[tok_base + tlu]) eu = -1;
-            if (mask_kind == MOE_MASK_PAIR && !mask[pair0 + p]) eu = -1;
+            if constexpr (MK == MOE_MASK_TOKEN) if (!mask[tok_base + tlu]) eu = -1;
+            if constexpr (MK == MOE_MASK_PAIR) if (!mask[pair0 + p]) eu = -1;
         }
     };
     int e[U], tl[U];
@@ -1193,9 +1196,19 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
 
     (void)hipGetLastError();
     const int elem_out = quant ? 1 : (int)xs;
-    if (N > 0)
-        hipLaunchKernelGGL(route_kernel, dim3(L.NB), dim3(kRouteThreads), (size_t)E * kRouteWords * 8, st,
-                           expert_ids, W, bs, epr, K, L.nbs, x_active_mask, mask_kind, pc, pci, lr);
+    if (N > 0) {
+        const dim3 g(L.NB), b(kRouteThreads);
+        const size_t lds = (size_t)E * kRouteWords * 8;
+        if (mask_kind == MOE_MASK_TOKEN)
+            hipLaunchKernelGGL(route_kernel<MOE_MASK_TOKEN>, g, b, lds, st, expert_ids, W, bs, epr, K, L.nbs,
+                               x_active_mask, pc, pci, lr);
+        else if (mask_kind == MOE_MASK_PAIR)
+            hipLaunchKernelGGL(route_kernel<MOE_MASK_PAIR>, g, b, lds, st, expert_ids, W, bs, epr, K, L.nbs,
+                               x_active_mask, pc, pci, lr);
+        else
+            hipLaunchKernelGGL(route_kernel<MOE_MASK_NONE>, g, b, lds, st, expert_ids, W, bs, epr, K, L.nbs,
+                               x_active_mask, pc, pci, lr);
+    }
     if (!direct || want_seg)
         hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), want_seg ? (size_t)W * S * 5 : 0, st, pc, pci,
                            W, epr, L.nbs, h, elem_out, boff, ep_recv_count, want_seg ? 1 : 0, large, seg_flags,
