@@ -194,6 +194,15 @@ static size_t elem_size(int dtype) { return dtype == OR_INT32 ? 4 : 2; }
  * entries come first is not needed by this definition, so any pattern is
  * accepted.
  */
+/*
+ * Special experts ([P3] 参数说明, zeroExpertNum / copyExpertNum): ids in
+ * [E, E + zero) are zero experts, ids in [E + zero, E + zero + copy) copy
+ * experts. The pages give only the id ranges; reading taken: a special pair is
+ * not exchanged (no row, no count); in the combine a zero expert contributes
+ * nothing and a copy expert contributes the token itself, ori_x[t] * weight,
+ * at its place in the k order. (constExpertNum is not supported, as in the
+ * page's current version.)
+ */
 static int pair_active(const uint8_t *mask, int mask_kind, long long t, int k, int K)
 {
     if (mask_kind == 1) return mask[t] != 0;
@@ -216,12 +225,13 @@ static int pair_active(const uint8_t *mask, int mask_kind, long long t, int k, i
  */
 int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales,
                     int W, int bs, int epr, int h, int K, int dtype, int quant,
-                    const uint8_t *mask, int mask_kind,
+                    const uint8_t *mask, int mask_kind, int zero_num, int copy_num,
                     void *expand_x, float *dyn_scales, int32_t *assist,
                     int32_t *ep_recv_count, void *expand_scales)
 {
     if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
     if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0) != (mask != NULL)) return OR_BAD_ARG;
+    if (zero_num < 0 || copy_num < 0) return OR_BAD_ARG;
     if (quant != 0 && quant != 2 && quant != 3) return OR_BAD_ARG;
     if (quant != 0 && dtype == OR_INT32) return OR_BAD_ARG;
     const int G = (h + 127) / 128;                     /* quantMode 3 groups per row */
@@ -235,9 +245,10 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
         for (int k = 0; k < K; ++k) {
             if (!pair_active(mask, mask_kind, t, k, K)) continue;
             int32_t e = ids[t * K + k];
-            if (e < 0 || e >= E) { free(cnt); return OR_BAD_ID; }
+            if (e < 0 || (long long)e >= E + zero_num + copy_num) { free(cnt); return OR_BAD_ID; }
             for (int j = 0; j < k; ++j)
                 if (pair_active(mask, mask_kind, t, j, K) && ids[t * K + j] == e) { free(cnt); return OR_DUP_ID; }
+            if (e >= E) continue;                      /* special expert: not exchanged */
             long long r = e / epr, el = e % epr, s = t / bs;
             cnt[r * S + el * W + s] += 1;
         }
@@ -263,7 +274,7 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
     for (long long t = 0; t < N; ++t) {
         long long s = t / bs, tok = t % bs;
         int any = 0;
-        for (int k = 0; k < K; ++k) any |= pair_active(mask, mask_kind, t, k, K);
+        for (int k = 0; k < K; ++k) any |= pair_active(mask, mask_kind, t, k, K) && ids[t * K + k] < E;
         if (!any) continue;
         float scale = 0.0f;
         if (quant == 2) {
@@ -277,6 +288,7 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
         for (int k = 0; k < K; ++k) {
             if (!pair_active(mask, mask_kind, t, k, K)) continue;
             int32_t e = ids[t * K + k];
+            if (e >= E) continue;
             long long r = e / epr, el = e % epr, i = el * W + s;
             long long start = i == 0 ? 0 : ep_recv_count[r * S + i - 1];
             long long row = base[r] + start + fill[r * S + i];
@@ -335,6 +347,13 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
 /* Combine                                                                   */
 /* ------------------------------------------------------------------------ */
 
+static int is_copy(const int32_t *ids, const uint8_t *mask, int mask_kind, long long t, int k, int K,
+                   long long E, int zero_num, int copy_num)
+{
+    long long e = ids[t * K + k];
+    return pair_active(mask, mask_kind, t, k, K) && e >= E + zero_num && e < E + zero_num + copy_num;
+}
+
 /*
  * Push-style, as [P1] 实现逻辑 describes it: every expert-output row is
  * returned to slot (src_token, topk_id) of its source rank's window; the
@@ -351,16 +370,18 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
  */
 int oracle_combine(const void *expand_x, const int32_t *assist, const int32_t *ep_recv_count,
                    const int32_t *ids, const void *scales, int W, int bs, int epr, int h, int K,
-                   int dtype, const uint8_t *mask, int mask_kind, void *x_out)
+                   int dtype, const uint8_t *mask, int mask_kind, int zero_num, int copy_num,
+                   const void *ori_x, void *x_out)
 {
     if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
     if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0) != (mask != NULL)) return OR_BAD_ARG;
-    const long long N = (long long)W * bs, S = (long long)epr * W;
+    if (zero_num < 0 || copy_num < 0 || (copy_num > 0 && !ori_x)) return OR_BAD_ARG;
+    const long long N = (long long)W * bs, S = (long long)epr * W, E = (long long)W * epr;
 
     long long rows = 0, active = 0;
     for (long long r = 0; r < W; ++r) rows += ep_recv_count[r * S + S - 1];
     for (long long t = 0; t < N; ++t)
-        for (int k = 0; k < K; ++k) active += pair_active(mask, mask_kind, t, k, K);
+        for (int k = 0; k < K; ++k) active += pair_active(mask, mask_kind, t, k, K) && ids[t * K + k] < E;
     if (rows != active) return OR_BAD_ASSIST;
 
     /* The source rank's window: slot[t*K + k] = index of the returned row. */
@@ -392,19 +413,23 @@ int oracle_combine(const void *expand_x, const int32_t *assist, const int32_t *e
             if (dtype == OR_INT32) {
                 uint32_t acc = 0;
                 for (int k = 0; k < K; ++k) {
-                    if (slot[t * K + k] < 0) continue;
-                    const int32_t *y = (const int32_t *)expand_x + (size_t)slot[t * K + k] * h;
                     int32_t sc = ((const int32_t *)scales)[t * K + k];
-                    acc += (uint32_t)y[j] * (uint32_t)sc;
+                    if (slot[t * K + k] >= 0) {
+                        const int32_t *y = (const int32_t *)expand_x + (size_t)slot[t * K + k] * h;
+                        acc += (uint32_t)y[j] * (uint32_t)sc;
+                    } else if (is_copy(ids, mask, mask_kind, t, k, K, E, zero_num, copy_num)) {
+                        acc += (uint32_t)((const int32_t *)ori_x)[t * h + j] * (uint32_t)sc;
+                    }
                 }
                 ((int32_t *)x_out)[t * h + j] = (int32_t)acc;
             } else {
                 float acc = 0.0f;
                 for (int k = 0; k < K; ++k) {
-                    if (slot[t * K + k] < 0) continue;
-                    float y = load_f32(expand_x, (size_t)slot[t * K + k] * h + j, dtype);
                     float sc = ((const float *)scales)[t * K + k];
-                    acc = fmaf(y, sc, acc);
+                    if (slot[t * K + k] >= 0)
+                        acc = fmaf(load_f32(expand_x, (size_t)slot[t * K + k] * h + j, dtype), sc, acc);
+                    else if (is_copy(ids, mask, mask_kind, t, k, K, E, zero_num, copy_num))
+                        acc = fmaf(load_f32(ori_x, (size_t)(t * h + j), dtype), sc, acc);
                 }
                 ((uint16_t *)x_out)[t * h + j] = store_16(acc, dtype);
             }

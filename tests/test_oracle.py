@@ -663,3 +663,78 @@ def test_group_quantiser_properties():
             assert (np.abs(deq - np.clip(quot, -448, 448)) <= quantum / 2 + 1e-12).all(), (t, g)
     i = row_of[(1, 0, 0)]
     assert d["expand_x"][i, 5] == 0x80
+
+
+# --------------------------------------------------------------------------
+# special experts (aclnnMoeDistributeDispatchV4 参数说明, zeroExpertNum /
+# copyExpertNum: id ranges after the E real experts). Reading: not exchanged;
+# a zero expert adds nothing, a copy expert adds the token itself
+# --------------------------------------------------------------------------
+
+def test_special_experts_match_a_dispatch_without_those_pairs():
+    """Pairs routed to a zero or copy expert behave exactly like pairs switched
+    off by a per-pair mask (a different code path in the oracle)."""
+    for w in (wl.custom(3, 7, 5, 3, 2, "int32", zero_experts=2, copy_experts=2, name="int32_special"),
+              wl.custom(4, 9, 16, 4, 3, "bf16", "zipf_topk", quant_mode=2, zero_experts=3, copy_experts=1,
+                        name="bf16_special")):
+        inp = wl.make_inputs(w)
+        E = w.num_experts
+        special = inp["ids"] >= E
+        assert special.any() and (~special).any()
+        d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
+                            bf16=w.dtype == "bf16", zero_experts=w.zero_experts, copy_experts=w.copy_experts)
+        ids_masked = np.where(special, 0, inp["ids"]).astype(np.int32)
+        m = oracle.dispatch(inp["x"], ids_masked, w.ep_world, w.experts_per_rank, w.quant_mode,
+                            bf16=w.dtype == "bf16", mask=~special)
+        for key in ("expand_x", "assist_info", "ep_recv_count"):
+            assert d[key].tobytes() == m[key].tobytes(), (w.name, key)
+        # ids beyond the special ranges are still an error
+        bad = inp["ids"].copy()
+        bad[0, 0] = E + w.zero_experts + w.copy_experts
+        with pytest.raises(oracle.OracleError):
+            oracle.dispatch(inp["x"], bad, w.ep_world, w.experts_per_rank, w.quant_mode, bf16=w.dtype == "bf16",
+                            zero_experts=w.zero_experts, copy_experts=w.copy_experts)
+
+
+def test_special_experts_int32_combine_closed_form():
+    """Identity expert, int32: x_out[t] = x[t] * (sum of the weights of its real
+    and copy experts), wrapping; zero experts add nothing."""
+    w = wl.custom(4, 11, 6, 4, 2, "int32", zero_experts=3, copy_experts=3, name="int32_special_combine")
+    inp = wl.make_inputs(w)
+    E, Z, C = w.num_experts, w.zero_experts, w.copy_experts
+    ids = inp["ids"]
+    d = oracle.dispatch(inp["x"], ids, w.ep_world, w.experts_per_rank, zero_experts=Z, copy_experts=C)
+    out = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], ids, inp["scales"], w.ep_world,
+                         w.experts_per_rank, zero_experts=Z, copy_experts=C, ori_x=inp["x"])
+    counted = (ids < E) | ((ids >= E + Z) & (ids < E + Z + C))
+    assert ((ids >= E) & (ids < E + Z)).any() and ((ids >= E + Z) & (ids < E + Z + C)).any()
+    ssum = (inp["scales"].astype(np.int64) * counted).sum(axis=1)
+    want = ((inp["x"].astype(np.int64) * ssum[:, None]) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+    assert (out == want).all()
+
+
+def test_copy_expert_adds_the_token_in_k_order():
+    """fp16/bf16: a copy expert's term is fma(x[t], w, acc) at its own k; the
+    same sum is obtained when that pair is instead sent to a real expert whose
+    output is the token itself (identity expert)."""
+    for dt in ("fp16", "bf16"):
+        w = wl.custom(3, 13, 24, 4, 3, dt, "gauss_topk", copy_experts=4, name="copy_" + dt)
+        inp = wl.make_inputs(w)
+        E, bf = w.num_experts, dt == "bf16"
+        ids = inp["ids"]
+        assert (ids >= E).any()
+        d = oracle.dispatch(inp["x"], ids, w.ep_world, w.experts_per_rank, bf16=bf, copy_experts=4)
+        got = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], ids, inp["scales"], w.ep_world,
+                             w.experts_per_rank, bf16=bf, copy_experts=4, ori_x=inp["x"])
+        # route every copy pair to a real expert the token does not use: the identity expert then returns
+        # x[t] for it, so the sum must be bitwise the same
+        real = ids.copy()
+        for t in range(w.num_tokens):
+            free = [e for e in range(E) if e not in set(ids[t].tolist())]
+            for k in range(w.topk):
+                if real[t, k] >= E:
+                    real[t, k] = free.pop()
+        r = oracle.dispatch(inp["x"], real, w.ep_world, w.experts_per_rank, bf16=bf)
+        want = oracle.combine(r["expand_x"], r["assist_info"], r["ep_recv_count"], real, inp["scales"], w.ep_world,
+                              w.experts_per_rank, bf16=bf)
+        assert got.view(np.uint16).tobytes() == want.view(np.uint16).tobytes(), dt

@@ -54,6 +54,8 @@ class Workload:
     x_lo: int = 0           # int32 token range (inclusive)
     x_hi: int = 0
     zipf_s: float = 1.2
+    zero_experts: int = 0   # special experts after the E real ones: ids E .. E+zero-1
+    copy_experts: int = 0   # then E+zero .. E+zero+copy-1
 
     @property
     def num_experts(self) -> int:
@@ -84,10 +86,12 @@ BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
 
 def custom(ep_world, bs, h, topk, experts_per_rank, dtype="int32", routing="uniform_distinct",
-           quant_mode=0, x_lo=-1000, x_hi=1000, name="custom", index=100):
-    """A workload of arbitrary shape, for edge-case tests."""
+           quant_mode=0, x_lo=-1000, x_hi=1000, name="custom", index=100, zero_experts=0, copy_experts=0):
+    """A workload of arbitrary shape, for edge-case tests. zero_experts / copy_experts add
+    special expert ids after the E real ones, drawn by the routing like any other."""
     return Workload(name, index, ep_world, bs, h, topk, experts_per_rank, dtype, routing,
-                    quant_mode=quant_mode, x_lo=x_lo, x_hi=x_hi)
+                    quant_mode=quant_mode, x_lo=x_lo, x_hi=x_hi, zero_experts=zero_experts,
+                    copy_experts=copy_experts)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -99,7 +103,8 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
 
 def _routing(w: Workload, rng: np.random.Generator):
-    N, E, K = w.num_tokens, w.num_experts, w.topk
+    N, K = w.num_tokens, w.topk
+    E = w.num_experts + w.zero_experts + w.copy_experts     # every id the router can pick
     if w.routing == "uniform_distinct":
         ids = np.stack([rng.permutation(E)[:K] for _ in range(N)]).astype(np.int32) if N else \
             np.zeros((0, K), np.int32)
