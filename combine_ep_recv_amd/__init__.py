@@ -38,6 +38,20 @@ class MoeError(RuntimeError):
         self.status = status
 
 
+class MoeSpecialExperts(ctypes.Structure):
+    _fields_ = [("zero_expert_num", ctypes.c_int32), ("copy_expert_num", ctypes.c_int32),
+                ("const_expert_num", ctypes.c_int32), ("reserved", ctypes.c_int32), ("ori_x", ctypes.c_void_p)]
+
+
+def _special(zero_experts: int, copy_experts: int, ori_x: Optional[torch.Tensor] = None):
+    """byref(moe_special_experts) or None when there are no special experts."""
+    if not zero_experts and not copy_experts:
+        return None
+    sp = MoeSpecialExperts(zero_expert_num=int(zero_experts), copy_expert_num=int(copy_experts),
+                           ori_x=None if ori_x is None else ori_x.data_ptr())
+    return ctypes.byref(sp)
+
+
 class MoeSchedule(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("large_segment_bytes", ctypes.c_int64), ("segment_is_large", ctypes.c_void_p)]
@@ -57,12 +71,13 @@ def library() -> ctypes.CDLL:
     P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.moe_dispatch_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(SZ)]
     lib.moe_dispatch_workspace_size.restype = I
-    lib.moe_dispatch.argtypes = [P, P, P, P, I, I, I, I, I, I, I, I, P, P, P, P, P,
-                                 ctypes.POINTER(MoeSchedule), P, SZ, P]
+    lib.moe_dispatch.argtypes = [P, P, P, P, I, ctypes.POINTER(MoeSpecialExperts), I, I, I, I, I, I, I, P, P, P,
+                                 P, P, ctypes.POINTER(MoeSchedule), P, SZ, P]
     lib.moe_dispatch.restype = I
     lib.moe_combine_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(SZ)]
     lib.moe_combine_workspace_size.restype = I
-    lib.moe_combine.argtypes = [P, P, P, P, P, P, I, I, I, I, I, I, I, P, P, SZ, P]
+    lib.moe_combine.argtypes = [P, P, P, P, P, P, I, ctypes.POINTER(MoeSpecialExperts), I, I, I, I, I, I, P, P,
+                                SZ, P]
     lib.moe_combine.restype = I
     lib.moe_status_str.argtypes = [I]
     lib.moe_status_str.restype = ctypes.c_char_p
@@ -153,12 +168,13 @@ class DispatchBuffers:
 
 def dispatch_into(buf: DispatchBuffers, x: torch.Tensor, expert_ids: torch.Tensor,
                   expert_scales: Optional[torch.Tensor] = None, schedule: Optional[MoeSchedule] = None,
-                  x_active_mask: Optional[torch.Tensor] = None):
+                  x_active_mask: Optional[torch.Tensor] = None, zero_experts: int = 0, copy_experts: int = 0):
     """moe_dispatch into preallocated buffers on the current stream."""
     W, bs, epr, h, K = buf.shape
     mp, mk = _mask_args(x_active_mask, W * bs, K, x.device)
     rc = library().moe_dispatch(
-        _ptr(x), _ptr(expert_ids), _ptr(expert_scales), mp, mk, W, bs, epr, h, K, dtype_code(buf.dtype),
+        _ptr(x), _ptr(expert_ids), _ptr(expert_scales), mp, mk, _special(zero_experts, copy_experts), W, bs, epr,
+        h, K, dtype_code(buf.dtype),
         buf.quant_mode,
         _ptr(buf.expand_x), _ptr(buf.dynamic_scales), _ptr(buf.assist_info), _ptr(buf.ep_recv_count),
         _ptr(buf.expand_scales), ctypes.byref(schedule) if schedule is not None else None,
@@ -175,14 +191,16 @@ def _check_tensor(name, t, dtype, shape, device):
 
 def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_per_rank: int,
              quant_mode: int = MOE_QUANT_NONE, expert_scales: Optional[torch.Tensor] = None,
-             schedule: Optional[MoeSchedule] = None, x_active_mask: Optional[torch.Tensor] = None):
+             schedule: Optional[MoeSchedule] = None, x_active_mask: Optional[torch.Tensor] = None,
+             zero_experts: int = 0, copy_experts: int = 0):
     """Dispatch tokens into expert-grouped rows.
 
     x: [ep_world*bs, h] int32/fp16/bf16 on a GPU; expert_ids: [ep_world*bs, topk]
     int32. Returns (expand_x, dynamic_scales or None, assist_info, ep_recv_count)
     and, when expert_scales is given, a fifth item expand_scales. With a token
     mask (bool/uint8 [N] or [N, topk]) only the first ep_recv_count[:, -1].sum()
-    rows of the row-indexed outputs are written.
+    rows of the row-indexed outputs are written; the same holds with special
+    experts (ids E.. for zero_experts, then copy_experts), whose pairs get no row.
     """
     N, h = x.shape
     K = expert_ids.shape[1]
@@ -196,7 +214,7 @@ def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_p
                           with_expand_scales=expert_scales is not None)
     if expert_scales is not None:
         buf.expand_scales = torch.empty((N * K,), dtype=expert_scales.dtype, device=x.device)
-    dispatch_into(buf, x, expert_ids, expert_scales, schedule, x_active_mask)
+    dispatch_into(buf, x, expert_ids, expert_scales, schedule, x_active_mask, zero_experts, copy_experts)
     out = (buf.expand_x, buf.dynamic_scales, buf.assist_info, buf.ep_recv_count)
     return out + (buf.expand_scales,) if expert_scales is not None else out
 
@@ -204,10 +222,16 @@ def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_p
 def combine_into(x_out: torch.Tensor, expand_x: torch.Tensor, assist_info: torch.Tensor,
                  ep_recv_count: torch.Tensor, expert_ids: torch.Tensor, expert_scales: torch.Tensor,
                  ep_world: int, experts_per_rank: int, workspace: Optional[torch.Tensor] = None,
-                 x_active_mask: Optional[torch.Tensor] = None):
-    """moe_combine into a preallocated x_out on the current stream."""
+                 x_active_mask: Optional[torch.Tensor] = None, zero_experts: int = 0, copy_experts: int = 0,
+                 ori_x: Optional[torch.Tensor] = None):
+    """moe_combine into a preallocated x_out on the current stream. Copy experts need ori_x,
+    the tokens given to dispatch, in expand_x's dtype."""
     N, K = expert_ids.shape
     mp, mk = _mask_args(x_active_mask, N, K, expand_x.device)
+    if copy_experts:
+        if ori_x is None:
+            raise MoeError("moe_combine", 1, "copy experts need ori_x, the tokens given to dispatch")
+        _check_tensor("ori_x", ori_x, expand_x.dtype, (N, expand_x.shape[1]), expand_x.device)
     h = expand_x.shape[1]
     dt = dtype_code(expand_x.dtype)
     if workspace is None:
@@ -215,7 +239,7 @@ def combine_into(x_out: torch.Tensor, expand_x: torch.Tensor, assist_info: torch
                                       expand_x.device)
     rc = library().moe_combine(
         _ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_count), _ptr(expert_ids), _ptr(expert_scales), mp, mk,
-        ep_world, N // ep_world, experts_per_rank, h, K, dt, _ptr(x_out), _ptr(workspace), workspace.numel(),
+        _special(zero_experts, copy_experts, ori_x), ep_world, N // ep_world, experts_per_rank, h, K, dt, _ptr(x_out), _ptr(workspace), workspace.numel(),
         _stream_ptr(expand_x.device))
     _check("moe_combine", rc)
     return x_out
@@ -229,7 +253,8 @@ def combine_workspace(ep_world, bs, experts_per_rank, h, topk, dtype: torch.dtyp
 
 def combine(expand_x: torch.Tensor, assist_info: torch.Tensor, ep_recv_count: torch.Tensor,
             expert_ids: torch.Tensor, expert_scales: torch.Tensor, ep_world: int, experts_per_rank: int,
-            x_active_mask: Optional[torch.Tensor] = None):
+            x_active_mask: Optional[torch.Tensor] = None, zero_experts: int = 0, copy_experts: int = 0,
+            ori_x: Optional[torch.Tensor] = None):
     """x_out[t] = sum over active k of expand_x[row(t,k)] * expert_scales[t,k] (fp32 accumulation);
     x_active_mask: the dispatch's."""
     N, K = expert_ids.shape
@@ -245,4 +270,5 @@ def combine(expand_x: torch.Tensor, assist_info: torch.Tensor, ep_recv_count: to
     _check_tensor("expert_scales", expert_scales, sdt, (N, K), dev)
     x_out = torch.empty((N, h), dtype=expand_x.dtype, device=dev)
     return combine_into(x_out, expand_x, assist_info, ep_recv_count, expert_ids, expert_scales, ep_world,
-                        experts_per_rank, x_active_mask=x_active_mask)
+                        experts_per_rank, x_active_mask=x_active_mask, zero_experts=zero_experts,
+                        copy_experts=copy_experts, ori_x=ori_x)

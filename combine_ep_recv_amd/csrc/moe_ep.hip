@@ -61,6 +61,7 @@ constexpr int kQuantMaxK = 64;             // wavefront-per-token quantiser hand
 constexpr int kBlockThreads = 256;         // generic block-per-token kernels
 constexpr int kGatherThreads = 128;        // combine: block = (token, 128-chunk slice)
 constexpr int kSlotThreads = 256;
+constexpr int kCopySlot = -2;             // slot of a copy-expert pair: the token itself
 
 // --------------------------------------------------------------------------
 // element conversions (gfx950: v_cvt_f32_f16 / v_cvt_f16_f32 / v_cvt_pk_bf16_f32,
@@ -906,28 +907,37 @@ struct CombineArgs {
     char *x_out;
     const int32_t *erc;       // ep_recv_count [W, S]: with a mask, the row total comes from it
     const uint8_t *mask;
+    const int32_t *ids;       // expert_ids [N, K]: special experts are recognised by id
+    const char *ori_x;        // [N, h]: the tokens, for copy experts
     int mask_kind;
+    int pair_pass;            // a mask or special experts: mark pairs that have no row
+    int E, zero_end, copy_end; // special ids: [E, zero_end) zero, [zero_end, copy_end) copy
     int W, bs, h, K, R, S, nsl;
     long long rowbytes;
 };
 
 // Return path (README 实现逻辑): row i of expand_x belongs to slot
 // (src_token, topk_id) of source rank src_rank. Only its index travels.
-// Under a token mask only the first A rows exist (A = sum over ranks of the
-// last inclusive count) and an inactive pair's slot is set to -1, so the
-// gather skips it; a thread handles row i and pair i.
+// Under a token mask or with special experts only the first A rows exist (A =
+// sum over ranks of the last inclusive count). A pair without a row gets slot
+// -1 (inactive, or a zero expert: the gather skips it) or -2 (a copy expert:
+// the gather reads the token itself). A thread handles row i and pair i.
 __global__ __launch_bounds__(kSlotThreads) void combine_slots_kernel(CombineArgs a)
 {
     __shared__ int tmp[40];
     const int i = blockIdx.x * kSlotThreads + threadIdx.x;
     int rows = a.R;
-    if (a.mask_kind != MOE_MASK_NONE) {
+    if (a.pair_pass) {
         int part = 0;
         for (int r = threadIdx.x; r < a.W; r += kSlotThreads) part += a.erc[(size_t)r * a.S + a.S - 1];
         block_excl_scan(part, tmp, &rows);
         if (i < a.R) {
-            const bool on = a.mask_kind == MOE_MASK_TOKEN ? a.mask[i / a.K] != 0 : a.mask[i] != 0;
-            if (!on) a.slot_out[i] = -1;
+            bool on = true;
+            if (a.mask_kind == MOE_MASK_TOKEN) on = a.mask[i / a.K] != 0;
+            if (a.mask_kind == MOE_MASK_PAIR) on = a.mask[i] != 0;
+            const int e = a.ids[i];
+            if (!on || (e >= a.E && e < a.zero_end)) a.slot_out[i] = -1;
+            else if (e >= a.zero_end && e < a.copy_end) a.slot_out[i] = -2;
         }
     }
     if (i >= rows || i >= a.R) return;
@@ -941,10 +951,18 @@ __device__ __forceinline__ void gather_prologue(const CombineArgs &a, int t, int
     for (int k = threadIdx.x; k < a.K; k += blockDim.x) {
         const size_t p = (size_t)t * a.K + k;
         const int row = a.slot[p];
-        rows[k] = (unsigned)row < (unsigned)a.R ? row : -1;
+        // -2 (copy expert) is honoured only when this call has copy experts, so a
+        // stale or foreign slot never sends the gather to a missing ori_x
+        rows[k] = (unsigned)row < (unsigned)a.R ? row : (row == kCopySlot && a.ori_x ? kCopySlot : -1);
         sc[k] = reinterpret_cast<const uint32_t *>(a.scales)[p];
     }
     __syncthreads();
+}
+
+// The row a slot names: an expand_x row, or (copy expert) token t of ori_x.
+__device__ __forceinline__ const char *slot_row(const CombineArgs &a, int t, int row)
+{
+    return row >= 0 ? a.expand_x + (size_t)row * a.rowbytes : a.ori_x + (size_t)t * a.rowbytes;
 }
 
 // fp16 / bf16: block = (token, slice of kGatherThreads 16-byte chunks)
@@ -970,13 +988,13 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_half_kernel(Com
             for (int kk = 0; kk < KB; ++kk) {
                 const int k = kb + kk;
                 const int row = k < K ? rows[k] : -1;
-                v[kk] = row >= 0 ? load_stream(reinterpret_cast<const uint4 *>(a.expand_x + (size_t)row * a.rowbytes) + c)
-                                 : make_uint4(0u, 0u, 0u, 0u);
+                v[kk] = row != -1 ? load_stream(reinterpret_cast<const uint4 *>(slot_row(a, t, row)) + c)
+                                  : make_uint4(0u, 0u, 0u, 0u);
             }
 #pragma unroll
             for (int kk = 0; kk < KB; ++kk) {
                 const int k = kb + kk;
-                if (k < K && rows[k] >= 0) {
+                if (k < K && rows[k] != -1) {
                     const float wgt = __uint_as_float(sc[k]);
                     const uint32_t q[4] = {v[kk].x, v[kk].y, v[kk].z, v[kk].w};
 #pragma unroll
@@ -995,8 +1013,8 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_half_kernel(Com
         float acc = 0.0f;
         for (int k = 0; k < K; ++k) {
             const int row = rows[k];
-            if (row < 0) continue;
-            const uint16_t y = reinterpret_cast<const uint16_t *>(a.expand_x)[(size_t)row * a.h + j];
+            if (row == -1) continue;
+            const uint16_t y = reinterpret_cast<const uint16_t *>(slot_row(a, t, row))[j];
             acc = __builtin_fmaf(T::load(y), __uint_as_float(sc[k]), acc);
         }
         reinterpret_cast<uint16_t *>(a.x_out)[(size_t)t * a.h + j] = T::store(acc);
@@ -1019,8 +1037,8 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_i32_kernel(Comb
         uint32_t acc[4] = {0u, 0u, 0u, 0u};
         for (int k = 0; k < K; ++k) {
             const int row = rows[k];
-            if (row < 0) continue;
-            const uint4 v = reinterpret_cast<const uint4 *>(a.expand_x + (size_t)row * a.rowbytes)[c];
+            if (row == -1) continue;
+            const uint4 v = reinterpret_cast<const uint4 *>(slot_row(a, t, row))[c];
             acc[0] += v.x * sc[k];
             acc[1] += v.y * sc[k];
             acc[2] += v.z * sc[k];
@@ -1033,8 +1051,8 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_i32_kernel(Comb
         uint32_t acc = 0u;
         for (int k = 0; k < K; ++k) {
             const int row = rows[k];
-            if (row < 0) continue;
-            acc += reinterpret_cast<const uint32_t *>(a.expand_x)[(size_t)row * a.h + j] * sc[k];
+            if (row == -1) continue;
+            acc += reinterpret_cast<const uint32_t *>(slot_row(a, t, row))[j] * sc[k];
         }
         reinterpret_cast<uint32_t *>(a.x_out)[(size_t)t * a.h + j] = acc;
     }
@@ -1061,6 +1079,15 @@ int check_scalars(int W, int bs, int epr, int h, int K, int dtype)
     // every (token, slice) grid below has at most N * ceil(h / 128) blocks of <= 128 threads,
     // and a launch must stay below 2^32 work-items
     if (N * (((long long)h + 127) / 128) >= (1ll << 25)) return MOE_ERR_SHAPE;
+    return MOE_OK;
+}
+
+// Special experts: counts >= 0, no const experts, ids below 2^31.
+int check_special(const moe_special_experts *sp, long long E)
+{
+    if (!sp) return MOE_OK;
+    if (sp->zero_expert_num < 0 || sp->copy_expert_num < 0 || sp->const_expert_num != 0) return MOE_ERR_SHAPE;
+    if (E + sp->zero_expert_num + sp->copy_expert_num >= (1ll << 31)) return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -1135,7 +1162,8 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
 }
 
 int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales,
-                 const uint8_t *x_active_mask, int mask_kind, int ep_world, int bs,
+                 const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special, int ep_world,
+                 int bs,
                  int experts_per_rank, int h, int topk, int dtype, int quant_mode, void *expand_x,
                  float *dynamic_scales, int32_t *assist_info, int32_t *ep_recv_count, void *expand_scales,
                  const moe_schedule *schedule, void *workspace, size_t workspace_bytes, void *stream)
@@ -1155,6 +1183,9 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     if (mask_kind < MOE_MASK_NONE || mask_kind > MOE_MASK_PAIR) return MOE_ERR_MASK;
     if ((mask_kind != MOE_MASK_NONE) != (x_active_mask != nullptr) && N > 0) return MOE_ERR_MASK;
     if (mask_kind == MOE_MASK_NONE && x_active_mask) return MOE_ERR_MASK;
+    // special experts: their ids are legal and, like any id past the E real
+    // experts, routed nowhere by the kernels
+    if ((rc = check_special(special, (long long)W * epr))) return rc;
     if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
 
     const int mode = schedule ? schedule->mode : MOE_SCHED_TOKEN;
@@ -1303,8 +1334,8 @@ int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h
 
 int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t *ep_recv_count,
                 const int32_t *expert_ids, const void *expert_scales, const uint8_t *x_active_mask,
-                int mask_kind, int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype,
-                void *x_out, void *workspace, size_t workspace_bytes, void *stream)
+                int mask_kind, const moe_special_experts *special, int ep_world, int bs, int experts_per_rank,
+                int h, int topk, int dtype, void *x_out, void *workspace, size_t workspace_bytes, void *stream)
 {
     size_t need = 0;
     int rc = moe_combine_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype, &need);
@@ -1317,10 +1348,15 @@ int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t 
     if (mask_kind < MOE_MASK_NONE || mask_kind > MOE_MASK_PAIR) return MOE_ERR_MASK;
     if ((mask_kind != MOE_MASK_NONE) != (x_active_mask != nullptr) && N > 0) return MOE_ERR_MASK;
     if (mask_kind == MOE_MASK_NONE && x_active_mask) return MOE_ERR_MASK;
+    if ((rc = check_special(special, (long long)W * experts_per_rank))) return rc;
+    const int zero_n = special ? special->zero_expert_num : 0, copy_n = special ? special->copy_expert_num : 0;
+    const void *ori_x = copy_n > 0 ? special->ori_x : nullptr;
+    if (copy_n > 0 && N > 0 && !ori_x) return MOE_ERR_NULLPTR;
     if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
     const size_t xs = elem_size(dtype);
     if (!aligned(expand_x, xs) || !aligned(assist_info, 4) || !aligned(ep_recv_count, 4) ||
-        !aligned(expert_ids, 4) || !aligned(expert_scales, 4) || !aligned(x_out, xs) || !aligned(workspace, 16))
+        !aligned(expert_ids, 4) || !aligned(expert_scales, 4) || !aligned(x_out, xs) || !aligned(workspace, 16) ||
+        !aligned(ori_x, xs))
         return MOE_ERR_ALIGN;
     if (N == 0) return MOE_OK;
 
@@ -1334,9 +1370,16 @@ int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t 
     a.erc = ep_recv_count;
     a.mask = x_active_mask;
     a.mask_kind = mask_kind;
+    a.ids = expert_ids;
+    a.ori_x = static_cast<const char *>(ori_x);
+    a.E = W * experts_per_rank;
+    a.zero_end = a.E + zero_n;
+    a.copy_end = a.zero_end + copy_n;
+    a.pair_pass = (mask_kind != MOE_MASK_NONE || zero_n + copy_n > 0) ? 1 : 0;
     a.W = W; a.bs = bs; a.h = h; a.K = K; a.R = (int)(N * K); a.S = experts_per_rank * W;
     a.rowbytes = (long long)((size_t)h * xs);
-    const bool vec = (size_t)a.rowbytes % 16 == 0 && aligned(expand_x, 16) && aligned(x_out, 16);
+    const bool vec = (size_t)a.rowbytes % 16 == 0 && aligned(expand_x, 16) && aligned(x_out, 16) &&
+                     aligned(ori_x, 16);
     const long long n = vec ? a.rowbytes / 16 : h;
     a.nsl = (int)((n + kGatherThreads - 1) / kGatherThreads);
     hipStream_t st = static_cast<hipStream_t>(stream);

@@ -94,6 +94,24 @@ enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_DYN_TOKEN = 2, MOE_QUANT_DYN_GROU
  * buffers are left untouched. Dispatch and combine take the same mask. */
 enum moe_mask { MOE_MASK_NONE = 0, MOE_MASK_TOKEN = 1, MOE_MASK_PAIR = 2 };
 
+/* Special experts: zeroExpertNum / copyExpertNum / constExpertNum of
+ * aclnnMoeDistributeDispatchV4 (参数说明), id ranges after the E real experts:
+ * zero experts [E, E + zero), copy experts [E + zero, E + zero + copy). The
+ * pages give only the ranges; here a pair routed to a special expert is not
+ * exchanged (no row, no count, like an inactive pair), and in the combine a
+ * zero expert adds nothing while a copy expert adds ori_x[t] * weight at its
+ * place in the k order. Const experts are not supported (const_expert_num
+ * must be 0, as the page's current version asks). Pass NULL for none.
+ *  ori_x: DEVICE [N, h], the tokens given to dispatch, in the combine's dtype;
+ *         read by moe_combine when copy_expert_num > 0, ignored by dispatch. */
+typedef struct moe_special_experts {
+    int32_t zero_expert_num;
+    int32_t copy_expert_num;
+    int32_t const_expert_num;
+    int32_t reserved;
+    const void *ori_x;
+} moe_special_experts;
+
 /* How dispatch assigns its payload copies to workgroups. Both modes produce
  * bitwise identical outputs (the combine_doubleplane README requires the same
  * x_out whichever return path a segment takes).
@@ -139,6 +157,8 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
  *  expert_scales  [N, K] 4-byte or NULL  only read when expand_scales is given
  *  x_active_mask  uint8 [N] or [N, K]    see moe_mask; NULL with MOE_MASK_NONE
  *  mask_kind      moe_mask
+ *  special        host pointer or NULL   see moe_special_experts; ids in the special
+ *                                        ranges are legal and produce no row
  *  expand_x       [ROWS, h]              dtype; int8 when quant_mode == 2, E4M3 bytes when 3. Row order:
  *                                        rank r, then local expert, then source rank,
  *                                        then ascending source token
@@ -155,12 +175,13 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
  *
  * Ranges: ep_world in [2, 768], experts_per_rank >= 1, E <= 1024,
  * 1 <= topk <= E, bs >= 0 (bs == 0 writes zero counts and nothing else),
- * h >= 1, N*K < 2^31, N < 2^24, N*ceil(h/128) < 2^25. Ids outside [0, E) or repeated within a token are a
+ * h >= 1, N*K < 2^31, N < 2^24, N*ceil(h/128) < 2^25, E + zero + copy experts < 2^31.
+ * Active ids outside [0, E + zero + copy) or repeated within a token are a
  * precondition violation: the kernels stay in bounds but the outputs are
  * unspecified. Outputs are bitwise deterministic.
  */
 int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales,
-                 const uint8_t *x_active_mask, int mask_kind,
+                 const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
                  int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype,
                  int quant_mode, void *expand_x, float *dynamic_scales, int32_t *assist_info,
                  int32_t *ep_recv_count, void *expand_scales, const moe_schedule *schedule,
@@ -191,7 +212,9 @@ int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h
  *  expert_scales  [N, K] fp32 for fp16/bf16, int32 for int32 data
  *  x_active_mask, mask_kind: the dispatch's. The sum then runs over the
  *                 active pairs only (k ascending); a token with none gets 0.
- *                 With a mask, ep_recv_count is read to find the row total.
+ *  special        the dispatch's (NULL for none); needs ori_x when copy experts
+ *                 exist. With a mask or special experts, ep_recv_count is read
+ *                 to find the row total.
  *  x_out          [N, h] dtype
  *  workspace      device scratch of at least the queried size
  * The scalars must equal those given to dispatch. Rows that assist_info does
@@ -200,7 +223,8 @@ int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h
  */
 int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t *ep_recv_count,
                 const int32_t *expert_ids, const void *expert_scales,
-                const uint8_t *x_active_mask, int mask_kind, int ep_world, int bs,
+                const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
+                int ep_world, int bs,
                 int experts_per_rank, int h, int topk, int dtype, void *x_out,
                 void *workspace, size_t workspace_bytes, void *stream);
 

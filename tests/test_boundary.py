@@ -102,12 +102,13 @@ A = 1 << 20   # fake, 256-aligned "device" addresses; never dereferenced by thes
 
 
 def _dispatch(**kw):
-    p = dict(x=A, ids=2 * A, esc=None, mask=None, mk=0, W=2, bs=4, epr=2, h=16, K=2, dtype=1, quant=0, ex=3 * A,
-             dyn=None, assist=4 * A, erc=5 * A, esc_out=None, sched=None, ws=6 * A, wsb=1 << 30)
+    p = dict(x=A, ids=2 * A, esc=None, mask=None, mk=0, sp=None, W=2, bs=4, epr=2, h=16, K=2, dtype=1, quant=0,
+             ex=3 * A, dyn=None, assist=4 * A, erc=5 * A, esc_out=None, sched=None, ws=6 * A, wsb=1 << 30)
     p.update(kw)
     P = lambda v: None if v is None else ctypes.c_void_p(v)
     return moe.library().moe_dispatch(
-        P(p["x"]), P(p["ids"]), P(p["esc"]), P(p["mask"]), p["mk"], p["W"], p["bs"], p["epr"], p["h"], p["K"],
+        P(p["x"]), P(p["ids"]), P(p["esc"]), P(p["mask"]), p["mk"],
+        ctypes.byref(p["sp"]) if p["sp"] is not None else None, p["W"], p["bs"], p["epr"], p["h"], p["K"],
         p["dtype"], p["quant"],
         P(p["ex"]), P(p["dyn"]), P(p["assist"]), P(p["erc"]), P(p["esc_out"]),
         ctypes.byref(p["sched"]) if p["sched"] is not None else None, P(p["ws"]), p["wsb"], None)
@@ -138,6 +139,9 @@ def _dispatch(**kw):
     (dict(W=128, epr=8, K=2, sched=moe.MoeSchedule(mode=1)), SCHEDULE),   # W*S = 131072 > LDS budget
     (dict(quant=3, dyn=7 * A, sched=moe.MoeSchedule(mode=1)), SCHEDULE),  # per-group: token schedule only
     (dict(quant=3, dyn=7 * A, x=A + 2), ALIGN),                           # per-group: 16-byte rows
+    (dict(sp=moe.MoeSpecialExperts(zero_expert_num=-1)), SHAPE),
+    (dict(sp=moe.MoeSpecialExperts(const_expert_num=1)), SHAPE),        # const experts are not supported
+    (dict(sp=moe.MoeSpecialExperts(zero_expert_num=2 ** 31 - 4)), SHAPE),   # E + zero = 2^31
     (dict(mk=3, mask=8 * A), MASK),                                     # unknown mask kind
     (dict(mk=1), MASK),                                                 # a kind without a mask
     (dict(mask=8 * A), MASK),                                           # a mask without a kind
@@ -148,12 +152,13 @@ def test_dispatch_rejects_before_launch(kw, want):
 
 
 def _combine(**kw):
-    p = dict(ex=A, assist=2 * A, erc=3 * A, ids=4 * A, sc=5 * A, mask=None, mk=0, W=2, bs=4, epr=2, h=16, K=2,
-             dtype=1, out=6 * A, ws=7 * A, wsb=1 << 30)
+    p = dict(ex=A, assist=2 * A, erc=3 * A, ids=4 * A, sc=5 * A, mask=None, mk=0, sp=None, W=2, bs=4, epr=2, h=16,
+             K=2, dtype=1, out=6 * A, ws=7 * A, wsb=1 << 30)
     p.update(kw)
     P = lambda v: None if v is None else ctypes.c_void_p(v)
     return moe.library().moe_combine(P(p["ex"]), P(p["assist"]), P(p["erc"]), P(p["ids"]), P(p["sc"]),
-                                     P(p["mask"]), p["mk"], p["W"],
+                                     P(p["mask"]), p["mk"], ctypes.byref(p["sp"]) if p["sp"] is not None else None,
+                                     p["W"],
                                      p["bs"], p["epr"], p["h"], p["K"], p["dtype"], P(p["out"]), P(p["ws"]),
                                      p["wsb"], None)
 
@@ -175,6 +180,9 @@ def _combine(**kw):
     (dict(out=6 * A + 1), ALIGN),
     (dict(dtype=0, ex=A + 2), ALIGN),
     (dict(bs=0), OK),                                # empty batch: nothing to launch
+    (dict(sp=moe.MoeSpecialExperts(copy_expert_num=2)), NULLPTR),      # copy experts need ori_x
+    (dict(sp=moe.MoeSpecialExperts(copy_expert_num=2, ori_x=8 * A + 1)), ALIGN),
+    (dict(sp=moe.MoeSpecialExperts(const_expert_num=3)), SHAPE),
     (dict(mk=-1), MASK),
     (dict(mk=2), MASK),                              # a kind without a mask
     (dict(mask=8 * A), MASK),                        # a mask without a kind
