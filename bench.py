@@ -123,19 +123,45 @@ def measure(w, steps, warmup, flush, torch, moe):
     return dict(step=ms_step, disp=ms_disp, comb=ms_comb, cold=cold)
 
 
-def counted_traffic(w):
-    """HBM bytes per moe_combine launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
-    runs (profiles/), or None when the kernel source has changed since they were taken."""
+def code_hash(path):
+    """sha256 of a C/C++/HIP source with its comments removed and whitespace collapsed:
+    it changes whenever the code can change, and not for an edited comment."""
     import hashlib
 
+    text, out, i = open(path, encoding="utf-8").read(), [], 0
+    n = len(text)
+    while i < n:
+        c = text[i]
+        if c in "\"'":                                  # string or character literal, kept verbatim
+            j = i + 1
+            while j < n and text[j] != c:
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            i = text.find("\n", i)
+            i = n if i < 0 else i
+        elif text.startswith("/*", i):
+            i = text.find("*/", i + 2)
+            i = n if i < 0 else i + 2
+            out.append(" ")
+        else:
+            out.append(c)
+            i += 1
+    code = " ".join("".join(out).split())
+    return hashlib.sha256(code.encode("utf-8")).hexdigest()
+
+
+def counted_traffic(w):
+    """HBM bytes per moe_combine launch from the committed rocprofv3 FETCH_SIZE / WRITE_SIZE
+    runs (profiles/), or None when the kernel code has changed since they were taken."""
     path = os.path.join(ROOT, "profiles", "hbm_traffic_%s.json" % w.name)
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
-    with open(os.path.join(ROOT, rec["source"]), "rb") as f:
-        if hashlib.sha256(f.read()).hexdigest() != rec["source_sha256"]:
-            return None
+    if code_hash(os.path.join(ROOT, rec["source"])) != rec["source_code_sha256"]:
+        return None
     return rec["per_launch_bytes"]["moe_combine"]
 
 

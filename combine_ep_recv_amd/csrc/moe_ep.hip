@@ -12,20 +12,25 @@
 //            (t, k), the number of earlier tokens of the chunk routed to the
 //            same expert (a popcount below the token's bit). Bit-set order is
 //            irrelevant, so the result is deterministic without a sort.
+//            Inactive pairs (token masks, xActiveMaskOptional) and pairs of
+//            special experts (ids past the E real ones) are routed nowhere.
 //   scatter  token-major: the first row of pair (t, k) routed to e from
 //            chunk b is  sum_{b' < b} pci[b'][e] + sum_{b' >= b} pc[b'][e]
 //            (all rows of lower experts, plus this expert's rows from earlier
 //            chunks), so each block sums those few L2-resident words for its K
 //            pairs instead of waiting for a grid-wide scan. Rows are moved with
-//            128-bit loads/stores; per-token dynamic int8 quantisation runs one
-//            wavefront per token (amax by DPP shuffles, no block barrier).
+//            128-bit loads/stores; dynamic quantisation (quantMode 2: per-token
+//            int8; quantMode 3: per-128-group FP8 E4M3) runs one wavefront per
+//            token (max by DPP shuffles, no block barrier).
 //            ep_recv_count (combine_doubleplane README 功能说明) is formed the
 //            same way by the first threads of the grid.
 //   scan     single block; only for very many chunks, and for the segment
 //            schedule (the README's 方案设计 large-segment predicate + plan).
 // Combine (README 功能说明, check formula; 实现逻辑 return path + weighted sum):
 //   slots    every expand_x row announces itself in its source's window: the
-//            row index goes to slot (src_token, topk_id) of rank src_rank.
+//            row index goes to slot (src_token, topk_id) of rank src_rank;
+//            pairs without a row get -1 (inactive, zero expert) or -2 (copy
+//            expert: the token itself).
 //   gather   one block per (token, 2 KiB slice) reads the K rows named by its
 //            slots with 128-bit loads and accumulates in fp32, one FMA per k
 //            with k ascending, rounding once to the output type.
