@@ -472,3 +472,54 @@ def test_repeat_runs_are_bitwise_identical():
     for k in a:
         if a[k] is not None:
             assert a[k].tobytes() == b[k].tobytes(), k
+
+
+# --------------------------------------------------------------------------
+# HIP graphs: every launch goes on the caller's stream, with no allocation and
+# no memset, so a step can be captured and replayed; each replay must equal
+# the eager result (checked after eager work between replays)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("w", [wl.WORKLOADS[2], wl.custom(4, 64, 1024, 8, 4, "bf16", "gauss_topk", quant_mode=2,
+                                                             name="bf16_q8_graph")], ids=lambda w: w.name)
+def test_graph_replay_matches_eager(w):
+    print("parity case %s graph replay" % w.name, flush=True)
+    inp = wl.make_inputs(w)
+    bf = w.dtype == "bf16"
+    x, ids, sc = to_dev(inp["x"], bf), to_dev(inp["ids"]), to_dev(inp["scales"])
+    tdt = torch.bfloat16 if bf else torch.float16
+    buf = moe.DispatchBuffers(w.ep_world, w.bs, w.experts_per_rank, w.h, w.topk, tdt, w.quant_mode, DEV)
+    moe.dispatch_into(buf, x, ids)
+    y = gpu_identity_expert(buf.expand_x, buf.dynamic_scales)
+    out = torch.empty((w.num_tokens, w.h), dtype=y.dtype, device=DEV)
+    cws = moe.combine_workspace(w.ep_world, w.bs, w.experts_per_rank, w.h, w.topk, y.dtype, DEV)
+
+    def step():
+        moe.dispatch_into(buf, x, ids)
+        moe.combine_into(out, y, buf.assist_info, buf.ep_recv_count, ids, sc, w.ep_world, w.experts_per_rank, cws)
+
+    def snapshot():
+        torch.cuda.synchronize()
+        return [t.clone() for t in (buf.expand_x, buf.assist_info, buf.ep_recv_count, out)] + \
+               ([buf.dynamic_scales.clone()] if buf.dynamic_scales is not None else [])
+
+    step()
+    want = snapshot()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()                                   # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    for rep in range(3):
+        for t in (buf.expand_x, buf.assist_info, buf.ep_recv_count, out):
+            t.zero_()                            # eager work between replays
+        step() if rep == 1 else None             # and an eager step
+        g.replay()
+        got = snapshot()
+        for a, b in zip(got, want):
+            assert torch.equal(a.view(torch.uint8) if a.dtype == torch.float8_e4m3fn else a,
+                               b.view(torch.uint8) if b.dtype == torch.float8_e4m3fn else b), rep
