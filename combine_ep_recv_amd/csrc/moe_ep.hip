@@ -637,12 +637,6 @@ __device__ __forceinline__ uint2 quant_u4(uint4 v, float scale, float inv)
     return make_uint2(o[0], o[1]);
 }
 
-// Per-token dynamic int8 quantisation (aclnnMoeDistributeDispatchV4 quantMode 2):
-// scale = max|x| / 127 (fp32, correctly rounded), q = rint(x / scale) (0 for an
-// all-zero token), written to every destination row. One wavefront per token:
-// lane k loads pair k's id and in-chunk rank before the row's 16-byte loads, so
-// both are in flight together; rows reach the store loop through readlane. No
-// LDS, no barrier. Needs h % 16 == 0, h <= 1024 * J, topk <= kQuantMaxK.
 // Quantise one token held by the wavefront (v: its row, 16 elements per lane
 // and chunk) and store it to the K rows named by lanes 0..K-1 of my_row, plus
 // the row scales.
@@ -685,10 +679,11 @@ __device__ __forceinline__ void quant_store_wave(const DispatchArgs &a, int lane
 // 8 elements -> 8 E4M3 bytes, scale > 0. The quotient |x| / scale (FAST: the
 // one-step corrected |x| * inv) is clamped to 448 and converted, with x's sign,
 // by v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950, round to nearest even). Two checks
-// make the codes those of the definition: on the CPU, for every 16-bit
-// (x, group max) pair, the corrected quotient rounded to E4M3 equals the E4M3
-// rounding of the exact quotient; on this GPU, the instruction equals that
-// rounding for every binary32 |v| <= 448 (2,277,507,074 values).
+// make the codes those of the definition: for every 16-bit (x, group max) pair,
+// the corrected quotient rounded to E4M3 equals the E4M3 rounding of the exact
+// quotient (checked exhaustively on the CPU); and on gfx950 the instruction
+// equals that rounding for every binary32 |v| <= 448 (all 2,277,507,074 such
+// values compared).
 template <class T, bool FAST>
 __device__ __forceinline__ uint2 fp8_u4(uint4 v, float scale, float inv)
 {
@@ -761,6 +756,13 @@ __device__ __forceinline__ void quant_store_wave_fp8(const DispatchArgs &a, int 
     }
 }
 
+// The quantising scatter (aclnnMoeDistributeDispatchV4 quantMode 2 and 3), one
+// wavefront per token. QM 2: scale = max|x| / 127 over the token (fp32,
+// correctly rounded), q = rint(x / scale) (0 for an all-zero token); QM 3: the
+// per-group FP8 codes above. Codes go to every destination row. Lane k loads
+// pair k's id and in-chunk rank before the row's 16-byte loads, so both are in
+// flight together; rows reach the store loop through readlane. No LDS, no
+// barrier. Needs h % 16 == 0, h <= 1024 * J, topk <= kQuantMaxK.
 template <class T, int J, int QM>
 __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(DispatchArgs a)
 {
