@@ -161,6 +161,14 @@ EDGE = [
     wl.custom(3, 70, 7176, 5, 3, "bf16", "zipf_topk", name="bf16_h7176_ragged_tiles"),
     wl.custom(2, 3, 16, 70, 40, "int32", name="topk70_copy_lds_path"),
     wl.custom(2, 2, 32, 66, 40, "bf16", "gauss_topk", quant_mode=2, name="topk66_quant_block_path"),
+    # the copy with one wavefront per token (from 1024 tokens): rows of 1, 14 and 16 pieces per lane, a row
+    # length between template sizes, and the fallbacks beyond 16 pieces or 64 copies
+    wl.custom(8, 128, 7168, 8, 8, "bf16", "gauss_topk", name="copy_wave_h7168_j14"),
+    wl.custom(4, 300, 8192, 4, 4, "fp16", "zipf_topk", name="copy_wave_h8192_j16"),
+    wl.custom(16, 128, 32, 4, 8, "int32", name="copy_wave_int32_j1"),
+    wl.custom(2, 700, 1040, 3, 4, "bf16", "gauss_topk", name="copy_wave_h1040_j3_ragged_chunks"),
+    wl.custom(2, 512, 8200, 2, 2, "fp16", "gauss_topk", name="copy_slices_h8200_past_16_pieces"),
+    wl.custom(4, 256, 16, 65, 20, "int32", name="copy_slices_topk65"),
 ]
 
 
@@ -252,6 +260,7 @@ SPECIAL = [
               name="bf16_fp8"),
     wl.custom(3, 70, 7176, 5, 3, "bf16", "zipf_topk", zero_experts=3, copy_experts=3, name="bf16_h7176_scalar"),
     wl.custom(8, 16, 64, 4, 2, "fp16", "gauss_topk", copy_experts=40, name="fp16_mostly_copy"),
+    wl.custom(8, 128, 1024, 8, 4, "bf16", "zipf_topk", zero_experts=8, copy_experts=8, name="bf16_copy_wave"),
     wl.custom(2, 6, 32, 2, 1, "fp16", "gauss_topk", zero_experts=30, name="fp16_mostly_zero"),
 ]
 
