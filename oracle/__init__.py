@@ -44,7 +44,7 @@ def _load():
     if _lib is None:
         lib = ctypes.CDLL(build())
         P, I, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
-        lib.oracle_dispatch.argtypes = [P, P, P, I, I, I, I, I, I, I, P, I, I, I, P, P, P, P, P]
+        lib.oracle_dispatch.argtypes = [P, P, P, I, I, I, I, I, I, I, P, LL, P, I, I, I, P, P, P, P, P]
         lib.oracle_dispatch.restype = I
         lib.oracle_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, I, I, P, P]
         lib.oracle_combine.restype = I
@@ -101,13 +101,14 @@ def _mask(mask, N, K):
 
 
 def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=None, bf16=False, mask=None,
-             zero_experts=0, copy_experts=0):
+             zero_experts=0, copy_experts=0, quant_scales=None):
     """Counting-sort dispatch. Returns dict with expand_x, dynamic_scales,
     assist_info, ep_recv_count, rows (the number of rows written: N*K, or the
     active pairs under a mask) and (when scales are given) expand_scales.
     mask: None, per-token [N] or per-pair [N, K] (nonzero = active).
     zero_experts / copy_experts: special expert ids E.. (zero) and E+zero.. (copy);
-    their pairs are not exchanged."""
+    their pairs are not exchanged.
+    quant_scales: quantMode 1's fp32 coefficients, 1, h or E*h values (q = sat8(rint(x * c)))."""
     x = np.ascontiguousarray(x)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     N, h = x.shape
@@ -117,7 +118,12 @@ def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=Non
     bs = N // W
     dt = dtype_code(x, bf16)
     rows = N * K
-    if quant_mode == 2:
+    qs = None
+    if quant_mode == 1:
+        qs = np.ascontiguousarray(quant_scales, dtype=np.float32).reshape(-1)
+        expand_x = np.zeros((rows, h), np.int8)
+        dyn = None
+    elif quant_mode == 2:
         expand_x = np.zeros((rows, h), np.int8)
         dyn = np.zeros((rows,), np.float32)
     elif quant_mode == 3:                     # E4M3 codes, ceil(h/128) group scales per row
@@ -135,7 +141,7 @@ def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=Non
         esc = np.zeros((rows,), expert_scales.dtype)
     m, mk = _mask(mask, N, K)
     rc = _load().oracle_dispatch(_ptr(x), _ptr(ids), _ptr(expert_scales), W, bs, epr, h, K, dt,
-                                 int(quant_mode), _ptr(m), mk, int(zero_experts), int(copy_experts),
+                                 int(quant_mode), _ptr(qs), 0 if qs is None else qs.size, _ptr(m), mk, int(zero_experts), int(copy_experts),
                                  _ptr(expand_x), _ptr(dyn), _ptr(assist),
                                  _ptr(erc), _ptr(esc))
     if rc != 0:

@@ -35,6 +35,14 @@
  *  - rows inside one segment are in ascending src_token order;
  *  - the emulated per-rank windows are packed back to back, rank 0 first,
  *    so expand_x holds exactly N*K rows;
+ *  - quantMode 1 (static; [P3] 参数说明 gives the coefficient input three
+ *    shapes: one value (1,), a smoothing vector shared by all experts (H,),
+ *    or per-expert coefficients fused with smoothing (E, H); the formula
+ *    itself is garbled): the coefficient multiplies the token,
+ *    q = rint(x * c) with the product rounded to fp32 first, ties to even,
+ *    saturated to int8's range [-128, 127]; c is qscale[0], qscale[j] or
+ *    qscale[e*h + j] for a row of expert e; a NaN product gives -128 (the
+ *    C fmax/fmin rule: the number wins over NaN); no dynamic scales;
  *  - quantMode 2: scale = max|x| / 127 in fp32, q = rint(x / scale) with
  *    ties to even, clamped to [-127, 127]; an all-zero token gets scale 0 and
  *    q = 0; one scale per expand_x row;
@@ -213,7 +221,8 @@ static int pair_active(const uint8_t *mask, int mask_kind, long long t, int k, i
 /*
  * x            [W*bs, h] dtype           tokens, source rank s owns rows s*bs..s*bs+bs-1
  * ids          [W*bs, K] int32           global expert ids, distinct per token
- * expand_x     [W*bs*K, h]               dtype; int8 when quant == 2; E4M3 bytes when quant == 3
+ * qscale       fp32 [qscale_n]           quant == 1 only: qscale_n is 1, h or E*h
+ * expand_x     [W*bs*K, h]               dtype; int8 when quant is 1 or 2; E4M3 bytes when 3
  * dyn_scales   [W*bs*K] fp32             quant == 2: one scale per row;
  *              [W*bs*K, G] fp32          quant == 3: G = ceil(h / 128) group scales per row
  * assist       [W*bs*K, 3] int32         (src_rank, src_token, topk_id) per row
@@ -225,18 +234,19 @@ static int pair_active(const uint8_t *mask, int mask_kind, long long t, int k, i
  */
 int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales,
                     int W, int bs, int epr, int h, int K, int dtype, int quant,
-                    const uint8_t *mask, int mask_kind, int zero_num, int copy_num,
+                    const float *qscale, long long qscale_n, const uint8_t *mask, int mask_kind, int zero_num, int copy_num,
                     void *expand_x, float *dyn_scales, int32_t *assist,
                     int32_t *ep_recv_count, void *expand_scales)
 {
     if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
     if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0) != (mask != NULL)) return OR_BAD_ARG;
     if (zero_num < 0 || copy_num < 0) return OR_BAD_ARG;
-    if (quant != 0 && quant != 2 && quant != 3) return OR_BAD_ARG;
+    if (quant < 0 || quant > 3) return OR_BAD_ARG;
     if (quant != 0 && dtype == OR_INT32) return OR_BAD_ARG;
     const int G = (h + 127) / 128;                     /* quantMode 3 groups per row */
     const long long E = (long long)W * epr, N = (long long)W * bs, S = (long long)epr * W;
     if (K > E) return OR_BAD_ARG;
+    if (quant == 1 && (!qscale || (qscale_n != 1 && qscale_n != h && qscale_n != E * h))) return OR_BAD_ARG;
 
     /* Step 1: count the (token, k) pairs of every segment (r, el*W + s). */
     long long *cnt = calloc((size_t)(W * S), sizeof(long long));
@@ -304,6 +314,16 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
             if (quant == 0) {
                 memcpy((char *)expand_x + (size_t)row * h * xs, (const char *)x + (size_t)t * h * xs,
                        (size_t)h * xs);
+            } else if (quant == 1) {
+                int8_t *q = (int8_t *)expand_x + (size_t)row * h;
+                for (int j = 0; j < h; ++j) {
+                    float c = qscale_n == 1 ? qscale[0] : qscale_n == h ? qscale[j] : qscale[(long long)e * h + j];
+                    float v = load_f32(x, (size_t)(t * h + j), dtype);
+                    float n = rintf(v * c);
+                    n = fmaxf(n, -128.0f);
+                    n = fminf(n, 127.0f);
+                    q[j] = (int8_t)n;
+                }
             } else if (quant == 3) {
                 uint8_t *q = (uint8_t *)expand_x + (size_t)row * h;
                 for (int g = 0; g < G; ++g) {

@@ -738,3 +738,87 @@ def test_copy_expert_adds_the_token_in_k_order():
         want = oracle.combine(r["expand_x"], r["assist_info"], r["ep_recv_count"], real, inp["scales"], w.ep_world,
                               w.experts_per_rank, bf16=bf)
         assert got.view(np.uint16).tobytes() == want.view(np.uint16).tobytes(), dt
+
+
+# --------------------------------------------------------------------------
+# static quantisation (aclnnMoeDistributeDispatchV4 参数说明, quantMode 1: the
+# coefficient input is one value, a per-column smoothing vector or per-expert
+# fused coefficients). Reading: q = sat_int8(rint(fp32(x * c)))
+# --------------------------------------------------------------------------
+
+def _codes_by_pair(d, bs):
+    """expand_x rows keyed by (token, k), from assist_info."""
+    a = d["assist_info"].astype(np.int64)
+    return {(int(s) * bs + int(tok), int(k)): d["expand_x"][i] for i, (s, tok, k) in enumerate(a)}
+
+
+def test_static_unit_coefficient_is_a_saturating_round():
+    """c = 1 on fp16 tokens: integers pass through, saturating at -128 and 127;
+    halves go to the even neighbour; NaN gives -128 and infinities saturate."""
+    x = np.zeros((4, 16), np.float16)
+    x[0] = np.arange(-8, 8) * 20                       # -160 .. 140: both ends saturate
+    x[1, :8] = [0.5, 1.5, 2.5, -0.5, -1.5, -2.5, 126.5, -127.5]
+    x[1, 8:12] = [np.nan, np.inf, -np.inf, -0.0]
+    x[2] = -x[0]
+    ids = np.array([[0], [1], [2], [3]], np.int32)
+    d = oracle.dispatch(x, ids, 2, 2, quant_mode=1, quant_scales=np.ones(1, np.float32))
+    assert d["dynamic_scales"] is None and d["expand_x"].dtype == np.int8
+    q = _codes_by_pair(d, 2)
+    assert q[(0, 0)].tolist() == [-128, -128, -120, -100, -80, -60, -40, -20, 0, 20, 40, 60, 80, 100, 120, 127]
+    assert q[(1, 0)][:12].tolist() == [0, 2, 2, 0, -2, -2, 126, -128, -128, 127, -128, 0]
+    assert q[(2, 0)].tolist() == [127, 127, 120, 100, 80, 60, 40, 20, 0, -20, -40, -60, -80, -100, -120, -128]
+    assert (q[(3, 0)] == 0).all()
+
+
+def test_static_coefficient_tables_name_their_expert_and_column():
+    """With x = 1 the code is the coefficient itself, so a table whose entries
+    encode (expert, column) shows which entry each code came from: the per-expert
+    table must be indexed by the row's own expert, the per-column one by the
+    column; all three shapes agree when they hold the same value."""
+    W, epr, h, K, bs = 3, 2, 24, 3, 5
+    E = W * epr
+    rng = np.random.default_rng(11)
+    ids = np.stack([rng.permutation(E)[:K] for _ in range(W * bs)]).astype(np.int32)
+    for bf in (False, True):
+        x = np.ones((W * bs, h), np.float32)
+        x = wl.f32_to_bf16_bits(x) if bf else x.astype(np.float16)
+        ce = np.array([[(5 * e + j) % 120 - 60 for j in range(h)] for e in range(E)], np.float32)
+        d = oracle.dispatch(x, ids, W, epr, quant_mode=1, quant_scales=ce, bf16=bf)
+        for (t, k), code in _codes_by_pair(d, bs).items():
+            assert code.tolist() == ce[ids[t, k]].astype(int).tolist(), (t, k)
+        cc = np.arange(h, dtype=np.float32) * 7 - 80
+        d = oracle.dispatch(x, ids, W, epr, quant_mode=1, quant_scales=cc, bf16=bf)
+        assert all(code.tolist() == np.clip(cc, -128, 127).astype(int).tolist()
+                   for code in _codes_by_pair(d, bs).values())
+        outs = [oracle.dispatch(x, ids, W, epr, quant_mode=1, quant_scales=np.full(n, 0.75, np.float32),
+                                bf16=bf)["expand_x"] for n in (1, h, E * h)]
+        assert (outs[0] == outs[1]).all() and (outs[0] == outs[2]).all() and (outs[0] == 1).all()
+
+
+def test_static_codes_are_nearest_integers_of_the_product():
+    """On the static workload's own inputs (per-expert coefficients, N(0,1) bf16
+    tokens at a reduced batch): each code is within 1/2 of x * c[e] computed in
+    float64 (plus the fp32 product's rounding), or saturated beyond the range."""
+    w = wl.custom(4, 16, 256, 8, 4, "bf16", "gauss_topk", quant_mode=1, name="static_small", index=4)
+    inp = wl.make_inputs(w)
+    c = inp["quant_scales"].reshape(w.num_experts, w.h).astype(np.float64)
+    d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, 1, quant_scales=inp["quant_scales"],
+                        bf16=True)
+    xf = (inp["x"].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    nsat = 0
+    for (t, k), code in _codes_by_pair(d, w.bs).items():
+        p = xf[t] * c[inp["ids"][t, k]]
+        q = code.astype(np.float64)
+        inside = (p > -128.5) & (p < 127.5)
+        assert (np.abs(p[inside] - q[inside]) <= 0.5 + 1e-5 * np.abs(p[inside])).all()
+        assert (q[p >= 127.5] == 127).all() and (q[p <= -128.5] == -128).all()
+        nsat += int((~inside).sum())
+    assert nsat > 0          # the coefficient range makes a few codes saturate
+
+
+def test_static_quant_rejects_bad_coefficient_counts():
+    x = np.ones((4, 8), np.float16)
+    ids = np.array([[0], [1], [2], [3]], np.int32)
+    for n in (0, 2, 7, 9, 4 * 8 + 1):
+        with pytest.raises(oracle.OracleError):
+            oracle.dispatch(x, ids, 2, 2, quant_mode=1, quant_scales=np.ones(n, np.float32))

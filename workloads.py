@@ -22,6 +22,13 @@ Workloads (shapes and value distributions of the pages' runs):
     experts/rank (256 experts); bf16 N(0,1) tokens; per-token dynamic int8
     quantisation in dispatch; combine on bf16 expert outputs; softmax weights.
 
+Static quantisation (quantMode 1) draws its coefficients from a generator of
+their own (seed 4321 + index), so a workload keeps its tokens and routing when
+only the quantiser changes: c = (127 / 4) * 2^u with u uniform in [-1, 1], one
+value, one per column (h) or one per expert and column (E*h). For N(0,1)
+tokens 127 / 4 maps |x| = 4 to the edge of the int8 range, so a few codes of a
+7168-wide row saturate.
+
 Routing rule for the logit-driven workloads: each token's experts are its 8
 largest logits in descending order, ties to the lower id (stable argsort of
 -logits); weights are the softmax of those 8 logits in fp32 after subtracting
@@ -56,6 +63,7 @@ class Workload:
     zipf_s: float = 1.2
     zero_experts: int = 0   # special experts after the E real ones: ids E .. E+zero-1
     copy_experts: int = 0   # then E+zero .. E+zero+copy-1
+    static_scales: str = "expert"   # quantMode 1 coefficients: "scalar" | "column" | "expert"
 
     @property
     def num_experts(self) -> int:
@@ -81,17 +89,27 @@ WORKLOADS = [
 # with per-group FP8 E4M3 quantisation (quantMode 3) instead of per-token int8.
 EXTRA_WORKLOADS = [
     Workload("w16_h7168_bf16_fp8g128", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=3),
+    # and with static int8 quantisation (quantMode 1), one coefficient per expert and column
+    Workload("w16_h7168_bf16_static_q8", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=1),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
 
 def custom(ep_world, bs, h, topk, experts_per_rank, dtype="int32", routing="uniform_distinct",
-           quant_mode=0, x_lo=-1000, x_hi=1000, name="custom", index=100, zero_experts=0, copy_experts=0):
+           quant_mode=0, x_lo=-1000, x_hi=1000, name="custom", index=100, zero_experts=0, copy_experts=0,
+           static_scales="expert"):
     """A workload of arbitrary shape, for edge-case tests. zero_experts / copy_experts add
     special expert ids after the E real ones, drawn by the routing like any other."""
     return Workload(name, index, ep_world, bs, h, topk, experts_per_rank, dtype, routing,
                     quant_mode=quant_mode, x_lo=x_lo, x_hi=x_hi, zero_experts=zero_experts,
-                    copy_experts=copy_experts)
+                    copy_experts=copy_experts, static_scales=static_scales)
+
+
+def static_scales(w: Workload) -> np.ndarray:
+    """quantMode 1 coefficients (fp32): 1, h or E*h values, from their own generator."""
+    n = {"scalar": 1, "column": w.h, "expert": w.num_experts * w.h}[w.static_scales]
+    u = np.random.default_rng(4321 + w.index).uniform(-1.0, 1.0, size=n)
+    return (31.75 * np.exp2(u)).astype(np.float32)
 
 
 def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
@@ -131,6 +149,7 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
       x        [N, h]  int32 | float16 | uint16 (bf16 bits)
       ids      [N, K]  int32
       scales   [N, K]  int32 for int32 tokens (uniform in [1, 4]), else fp32
+      quant_scales     fp32 quantMode 1 coefficients (only for quantMode 1)
     """
     rng = np.random.default_rng(1234 + w.index if seed is None else seed)
     N, h = w.num_tokens, w.h
@@ -145,4 +164,7 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
         x = g.astype(np.float16) if w.dtype == "fp16" else f32_to_bf16_bits(g)
         scales = weights if weights is not None else \
             rng.uniform(0.0, 1.0, size=(N, w.topk)).astype(np.float32)
-    return dict(x=x, ids=ids, scales=scales)
+    out = dict(x=x, ids=ids, scales=scales)
+    if w.quant_mode == 1:
+        out["quant_scales"] = static_scales(w)
+    return out
