@@ -108,7 +108,8 @@ def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=Non
     mask: None, per-token [N] or per-pair [N, K] (nonzero = active).
     zero_experts / copy_experts: special expert ids E.. (zero) and E+zero.. (copy);
     their pairs are not exchanged.
-    quant_scales: quantMode 1's fp32 coefficients, 1, h or E*h values (q = sat8(rint(x * c)))."""
+    quant_scales: quantMode 1's fp32 coefficients, 1, h or E*h values (q = sat8(rint(x * c)), the
+    exact product rounded once)."""
     x = np.ascontiguousarray(x)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     N, h = x.shape

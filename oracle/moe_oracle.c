@@ -38,10 +38,11 @@
  *  - quantMode 1 (static; [P3] 参数说明 gives the coefficient input three
  *    shapes: one value (1,), a smoothing vector shared by all experts (H,),
  *    or per-expert coefficients fused with smoothing (E, H); the formula
- *    itself is garbled): the coefficient multiplies the token,
- *    q = rint(x * c) with the product rounded to fp32 first, ties to even,
- *    saturated to int8's range [-128, 127]; c is qscale[0], qscale[j] or
- *    qscale[e*h + j] for a row of expert e; a NaN product gives -128 (the
+ *    itself is garbled): the coefficient multiplies the token and the exact
+ *    product is rounded to the nearest integer, ties to even, then saturated
+ *    to int8's range [-128, 127] (computed in double, where the product of a
+ *    16-bit float and a binary32 value is exact); c is qscale[0], qscale[j]
+ *    or qscale[e*h + j] for a row of expert e; a NaN product gives -128 (the
  *    C fmax/fmin rule: the number wins over NaN); no dynamic scales;
  *  - quantMode 2: scale = max|x| / 127 in fp32, q = rint(x / scale) with
  *    ties to even, clamped to [-127, 127]; an all-zero token gets scale 0 and
@@ -318,10 +319,10 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
                 int8_t *q = (int8_t *)expand_x + (size_t)row * h;
                 for (int j = 0; j < h; ++j) {
                     float c = qscale_n == 1 ? qscale[0] : qscale_n == h ? qscale[j] : qscale[(long long)e * h + j];
-                    float v = load_f32(x, (size_t)(t * h + j), dtype);
-                    float n = rintf(v * c);
-                    n = fmaxf(n, -128.0f);
-                    n = fminf(n, 127.0f);
+                    double p = (double)load_f32(x, (size_t)(t * h + j), dtype) * (double)c;   /* exact */
+                    double n = rint(p);
+                    n = fmax(n, -128.0);
+                    n = fmin(n, 127.0);
                     q[j] = (int8_t)n;
                 }
             } else if (quant == 3) {

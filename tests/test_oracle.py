@@ -743,7 +743,8 @@ def test_copy_expert_adds_the_token_in_k_order():
 # --------------------------------------------------------------------------
 # static quantisation (aclnnMoeDistributeDispatchV4 参数说明, quantMode 1: the
 # coefficient input is one value, a per-column smoothing vector or per-expert
-# fused coefficients). Reading: q = sat_int8(rint(fp32(x * c)))
+# fused coefficients). Reading: q = sat_int8(rint(x * c)), the exact product
+# rounded once to the nearest integer (ties to even)
 # --------------------------------------------------------------------------
 
 def _codes_by_pair(d, bs):
@@ -797,8 +798,8 @@ def test_static_coefficient_tables_name_their_expert_and_column():
 
 def test_static_codes_are_nearest_integers_of_the_product():
     """On the static workload's own inputs (per-expert coefficients, N(0,1) bf16
-    tokens at a reduced batch): each code is within 1/2 of x * c[e] computed in
-    float64 (plus the fp32 product's rounding), or saturated beyond the range."""
+    tokens at a reduced batch): each code is within 1/2 of x * c[e] (exact in
+    float64), or saturated beyond the range."""
     w = wl.custom(4, 16, 256, 8, 4, "bf16", "gauss_topk", quant_mode=1, name="static_small", index=4)
     inp = wl.make_inputs(w)
     c = inp["quant_scales"].reshape(w.num_experts, w.h).astype(np.float64)
@@ -810,7 +811,7 @@ def test_static_codes_are_nearest_integers_of_the_product():
         p = xf[t] * c[inp["ids"][t, k]]
         q = code.astype(np.float64)
         inside = (p > -128.5) & (p < 127.5)
-        assert (np.abs(p[inside] - q[inside]) <= 0.5 + 1e-5 * np.abs(p[inside])).all()
+        assert (np.abs(p[inside] - q[inside]) <= 0.5).all()
         assert (q[p >= 127.5] == 127).all() and (q[p <= -128.5] == -128).all()
         nsat += int((~inside).sum())
     assert nsat > 0          # the coefficient range makes a few codes saturate
@@ -822,3 +823,25 @@ def test_static_quant_rejects_bad_coefficient_counts():
     for n in (0, 2, 7, 9, 4 * 8 + 1):
         with pytest.raises(oracle.OracleError):
             oracle.dispatch(x, ids, 2, 2, quant_mode=1, quant_scales=np.ones(n, np.float32))
+
+
+def test_static_codes_round_the_exact_product_once():
+    """Products whose binary32 rounding lands on a half-integer while the exact
+    value does not: the code follows the exact product (a plain rint of x * c),
+    not a rounding of the rounded product. The products are exact in float64
+    (8-bit by 24-bit significands), and numpy's rint is the reference."""
+    xs = (1.0 + np.arange(128) / 128.0).astype(np.float32)          # every bf16 in [1, 2)
+    k = np.arange(120, dtype=np.float64)
+    cs = ((2 * k[:, None] + 1) / (2 * xs[None, :].astype(np.float64))).astype(np.float32)   # x * c near k + 1/2
+    p64 = xs[None, :].astype(np.float64) * cs.astype(np.float64)
+    p32 = (xs[None, :] * cs).astype(np.float64)
+    ki, xi = np.nonzero(np.rint(p64) != np.rint(p32))
+    assert ki.size >= 16                                              # such products exist
+    sel = list(zip(ki[:64], xi[:64]))
+    n = len(sel)
+    x = wl.f32_to_bf16_bits(np.array([[xs[j]] * 16 for _, j in sel], np.float32))
+    ids = np.arange(n, dtype=np.int32)[:, None]                       # W = n, token r -> expert r
+    ce = np.repeat(np.array([cs[i, j] for i, j in sel], np.float32)[:, None], 16, axis=1)
+    d = oracle.dispatch(x, ids, n, 1, quant_mode=1, quant_scales=ce, bf16=True)
+    for r, (i, j) in enumerate(sel):                                  # row r belongs to expert r
+        assert (d["expand_x"][r] == np.rint(p64[i, j])).all(), (cs[i, j], xs[j])
