@@ -44,7 +44,8 @@ def algorithmic_bytes(w: wl.Workload):
     """Bytes the method must move, each array once.
 
     dispatch: read x once + ids; write expand_x, assist_info, ep_recv_count
-              (+ dynamic_scales when quantising)
+              (+ dynamic_scales when quantising dynamically; + the static
+              coefficients read once for quantMode 1)
     combine:  read expand_x (expert output), scales, assist_info,
               ep_recv_count, ids; write x_out
     """
@@ -54,6 +55,8 @@ def algorithmic_bytes(w: wl.Workload):
     s_y = 2 if w.quant_mode else sx               # identity-expert output for quantised rows is bf16
     erc = w.ep_world * w.num_experts * 4
     n_scales = {2: rows, 3: rows * ((h + 127) // 128)}.get(w.quant_mode, 0)   # fp32 dynamic scales
+    if w.quant_mode == 1:                         # fp32 static coefficients, read
+        n_scales = {"scalar": 1, "column": h, "expert": w.num_experts * h}[w.static_scales]
     disp = N * h * sx + N * K * 4 + rows * h * s_exp + rows * 12 + erc + n_scales * 4
     comb = rows * h * s_y + N * K * 4 + rows * 12 + erc + N * K * 4 + N * h * s_y
     return disp, comb
@@ -68,13 +71,27 @@ def _device_inputs(w, torch):
     return inp, x, torch.from_numpy(inp["ids"]).cuda(), torch.from_numpy(inp["scales"]).cuda()
 
 
+QUANT_LABELS = {1: "static int8, one coefficient per %s", 2: "per-token dynamic int8",
+                3: "per-group (128) dynamic fp8 e4m3"}
+
+
+def quant_label(w):
+    lab = QUANT_LABELS.get(w.quant_mode, "none")
+    if w.quant_mode == 1:
+        lab %= {"scalar": "dispatch", "column": "column", "expert": "expert and column"}[w.static_scales]
+    return lab
+
+
 def measure(w, steps, warmup, flush, torch, moe):
-    _, x, ids, sc = _device_inputs(w, torch)
+    inp, x, ids, sc = _device_inputs(w, torch)
     tdt = {"int32": torch.int32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     W, epr = w.ep_world, w.experts_per_rank
+    qs = torch.from_numpy(inp["quant_scales"]).cuda() if w.quant_mode == 1 else None
     buf = moe.DispatchBuffers(W, w.bs, epr, w.h, w.topk, tdt, w.quant_mode, "cuda")
-    moe.dispatch_into(buf, x, ids)
-    if w.quant_mode == 2:
+    moe.dispatch_into(buf, x, ids, quant_scales=qs)
+    if w.quant_mode == 1:                      # static codes: the expert sees bf16(q)
+        y = buf.expand_x.to(torch.bfloat16)
+    elif w.quant_mode == 2:
         y = (buf.expand_x.float() * buf.dynamic_scales[:, None]).to(torch.bfloat16)
     elif w.quant_mode == 3:                    # one scale per 128-element group
         sc_full = buf.dynamic_scales.repeat_interleave(128, dim=1)[:, :w.h]
@@ -86,7 +103,7 @@ def measure(w, steps, warmup, flush, torch, moe):
     cws = moe.combine_workspace(W, w.bs, epr, w.h, w.topk, y.dtype)
 
     def step():
-        moe.dispatch_into(buf, x, ids)
+        moe.dispatch_into(buf, x, ids, quant_scales=qs)
         moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws)
 
     def b2b(fn, n):
@@ -106,7 +123,7 @@ def measure(w, steps, warmup, flush, torch, moe):
     # the timed region: exactly `steps` steps, synchronised on both sides
     ms_step = b2b(step, steps)
     # each half alone, back to back (the combine is the dominant launch sequence)
-    ms_disp = b2b(lambda: moe.dispatch_into(buf, x, ids), steps)
+    ms_disp = b2b(lambda: moe.dispatch_into(buf, x, ids, quant_scales=qs), steps)
     ms_comb = b2b(lambda: moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws),
                   steps)
     # cold: L2 and the Infinity Cache evicted (untimed 1 GiB read) before every step; each such
@@ -186,13 +203,17 @@ def cpu_baseline(w, reps=3):
 
     inp = wl.make_inputs(w)
     bf = w.dtype == "bf16"
-    d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode, bf16=bf)
-    y = oracle.identity_expert(d["expand_x"], d["dynamic_scales"])
+    qs = inp.get("quant_scales")
+    d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode, bf16=bf,
+                        quant_scales=qs)
+    y = oracle.identity_expert(d["expand_x"], d["dynamic_scales"] if w.quant_mode != 1
+                               else np.ones(w.rows, np.float32))
     out_bf = bf or w.quant_mode != 0
     times = []
     for _ in range(reps):
         t0 = time.perf_counter()
-        d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode, bf16=bf)
+        d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode, bf16=bf,
+                            quant_scales=qs)
         oracle.combine(y, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"], w.ep_world,
                        w.experts_per_rank, bf16=out_bf)
         times.append(time.perf_counter() - t0)
@@ -210,7 +231,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="w16_h7168_bf16_q8", choices=sorted(wl.BY_NAME))
-    ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf,w16_h7168_bf16_fp8g128",
+    ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf,w16_h7168_bf16_fp8g128,"
+                                      "w16_h7168_bf16_static_q8",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -266,8 +288,7 @@ def main():
                       "cold_GB/s": round((da + ca) / (statistics.median(ra["cold"]) * 1e-3) / 1e9, 1),
                       "graph_ms_per_step": round(ra["graph"], 5),
                       "algorithmic_bytes": da + ca,
-                      "quant": {2: "per-token dynamic int8", 3: "per-group (128) dynamic fp8 e4m3"}.get(
-                          wa.quant_mode, "none")}
+                      "quant": quant_label(wa)}
 
     line = {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -277,7 +298,7 @@ def main():
                                            if w.routing == "gauss_topk" else w.routing),
         "config": {"workload": w.name, "ep_world": w.ep_world, "bs": w.bs, "h": w.h, "topk": w.topk,
                    "experts_per_rank": w.experts_per_rank, "experts": w.num_experts, "tokens": w.num_tokens,
-                   "quant": {2: "per-token dynamic int8", 3: "per-group (128) dynamic fp8 e4m3"}.get(w.quant_mode, "none"),
+                   "quant": quant_label(w),
                    "combine_input": "bf16 identity-expert output" if w.quant_mode != 0 else w.dtype,
                    "working_set_MB": round((disp_b + comb_b) / 1e6),
                    "algorithmic_bytes": disp_b + comb_b},

@@ -24,7 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmoe_ep.s
 
 MOE_OK = 0
 MOE_INT32, MOE_FP16, MOE_BF16 = 0, 1, 2
-MOE_QUANT_NONE, MOE_QUANT_DYN_TOKEN, MOE_QUANT_DYN_GROUP = 0, 2, 3
+MOE_QUANT_NONE, MOE_QUANT_STATIC, MOE_QUANT_DYN_TOKEN, MOE_QUANT_DYN_GROUP = 0, 1, 2, 3
 MOE_SCHED_TOKEN, MOE_SCHED_SEGMENT = 0, 1
 MOE_MASK_NONE, MOE_MASK_TOKEN, MOE_MASK_PAIR = 0, 1, 2
 
@@ -71,8 +71,8 @@ def library() -> ctypes.CDLL:
     P, I, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
     lib.moe_dispatch_workspace_size.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(SZ)]
     lib.moe_dispatch_workspace_size.restype = I
-    lib.moe_dispatch.argtypes = [P, P, P, P, I, ctypes.POINTER(MoeSpecialExperts), I, I, I, I, I, I, I, P, P, P,
-                                 P, P, ctypes.POINTER(MoeSchedule), P, SZ, P]
+    lib.moe_dispatch.argtypes = [P, P, P, P, I, ctypes.POINTER(MoeSpecialExperts), I, I, I, I, I, I, I, P,
+                                 ctypes.c_int64, P, P, P, P, P, ctypes.POINTER(MoeSchedule), P, SZ, P]
     lib.moe_dispatch.restype = I
     lib.moe_combine_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(SZ)]
     lib.moe_combine_workspace_size.restype = I
@@ -148,7 +148,8 @@ class DispatchBuffers:
         N, rows = ep_world * bs, ep_world * bs * topk
         self.shape = (ep_world, bs, experts_per_rank, h, topk)
         self.dtype, self.quant_mode = dtype, quant_mode
-        out_dt = {MOE_QUANT_DYN_TOKEN: torch.int8, MOE_QUANT_DYN_GROUP: torch.float8_e4m3fn}.get(quant_mode, dtype)
+        out_dt = {MOE_QUANT_STATIC: torch.int8, MOE_QUANT_DYN_TOKEN: torch.int8,
+                  MOE_QUANT_DYN_GROUP: torch.float8_e4m3fn}.get(quant_mode, dtype)
         self.expand_x = torch.empty((rows, h), dtype=out_dt, device=device)
         if quant_mode == MOE_QUANT_DYN_TOKEN:
             self.dynamic_scales = torch.empty((rows,), dtype=torch.float32, device=device)
@@ -166,16 +167,28 @@ class DispatchBuffers:
         del N
 
 
+def _quant_scales_args(qs: Optional[torch.Tensor], device):
+    """(pointer, count) for quantMode 1's fp32 coefficients: 1, h or E*h values."""
+    if qs is None:
+        return None, 0
+    if qs.dtype != torch.float32 or not qs.is_contiguous() or qs.device != device:
+        raise MoeError("quant_scales", 4, "quant_scales must be a contiguous float32 tensor on %s" % device)
+    return _ptr(qs), qs.numel()
+
+
 def dispatch_into(buf: DispatchBuffers, x: torch.Tensor, expert_ids: torch.Tensor,
                   expert_scales: Optional[torch.Tensor] = None, schedule: Optional[MoeSchedule] = None,
-                  x_active_mask: Optional[torch.Tensor] = None, zero_experts: int = 0, copy_experts: int = 0):
-    """moe_dispatch into preallocated buffers on the current stream."""
+                  x_active_mask: Optional[torch.Tensor] = None, zero_experts: int = 0, copy_experts: int = 0,
+                  quant_scales: Optional[torch.Tensor] = None):
+    """moe_dispatch into preallocated buffers on the current stream. quant_scales: the static
+    quantiser's coefficients (quantMode 1 only): 1, h or E*h fp32 values."""
     W, bs, epr, h, K = buf.shape
     mp, mk = _mask_args(x_active_mask, W * bs, K, x.device)
+    qp, qn = _quant_scales_args(quant_scales, x.device)
     rc = library().moe_dispatch(
         _ptr(x), _ptr(expert_ids), _ptr(expert_scales), mp, mk, _special(zero_experts, copy_experts), W, bs, epr,
         h, K, dtype_code(buf.dtype),
-        buf.quant_mode,
+        buf.quant_mode, qp, ctypes.c_int64(qn),
         _ptr(buf.expand_x), _ptr(buf.dynamic_scales), _ptr(buf.assist_info), _ptr(buf.ep_recv_count),
         _ptr(buf.expand_scales), ctypes.byref(schedule) if schedule is not None else None,
         _ptr(buf.workspace), buf.workspace.numel(), _stream_ptr(x.device))
@@ -192,7 +205,7 @@ def _check_tensor(name, t, dtype, shape, device):
 def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_per_rank: int,
              quant_mode: int = MOE_QUANT_NONE, expert_scales: Optional[torch.Tensor] = None,
              schedule: Optional[MoeSchedule] = None, x_active_mask: Optional[torch.Tensor] = None,
-             zero_experts: int = 0, copy_experts: int = 0):
+             zero_experts: int = 0, copy_experts: int = 0, quant_scales: Optional[torch.Tensor] = None):
     """Dispatch tokens into expert-grouped rows.
 
     x: [ep_world*bs, h] int32/fp16/bf16 on a GPU; expert_ids: [ep_world*bs, topk]
@@ -201,6 +214,8 @@ def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_p
     mask (bool/uint8 [N] or [N, topk]) only the first ep_recv_count[:, -1].sum()
     rows of the row-indexed outputs are written; the same holds with special
     experts (ids E.. for zero_experts, then copy_experts), whose pairs get no row.
+    quant_mode 1 (static int8) takes its coefficients in quant_scales (fp32, 1, h or
+    E*h values) and returns no dynamic scales.
     """
     N, h = x.shape
     K = expert_ids.shape[1]
@@ -214,7 +229,8 @@ def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_p
                           with_expand_scales=expert_scales is not None)
     if expert_scales is not None:
         buf.expand_scales = torch.empty((N * K,), dtype=expert_scales.dtype, device=x.device)
-    dispatch_into(buf, x, expert_ids, expert_scales, schedule, x_active_mask, zero_experts, copy_experts)
+    dispatch_into(buf, x, expert_ids, expert_scales, schedule, x_active_mask, zero_experts, copy_experts,
+                  quant_scales)
     out = (buf.expand_x, buf.dynamic_scales, buf.assist_info, buf.ep_recv_count)
     return out + (buf.expand_scales,) if expert_scales is not None else out
 

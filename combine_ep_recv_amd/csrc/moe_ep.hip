@@ -68,6 +68,9 @@ constexpr int kBlockThreads = 256;         // generic block-per-token kernels
 constexpr int kGatherThreads = 128;        // combine: block = (token, 128-chunk slice)
 constexpr int kSlotThreads = 256;
 constexpr int kCopySlot = -2;             // slot of a copy-expert pair: the token itself
+// shapes of the static quantisation coefficients: 1, h or E*h values
+constexpr int kStaticOne = 0, kStaticColumn = 1, kStaticExpert = 2;
+constexpr int kXcds = 8;                   // gfx950 XCDs; consecutive workgroups go to consecutive XCDs
 
 // --------------------------------------------------------------------------
 // element conversions (gfx950: v_cvt_f32_f16 / v_cvt_f16_f32 / v_cvt_pk_bf16_f32,
@@ -414,6 +417,8 @@ struct DispatchArgs {
     int direct;               // 1: blocks sum pc/pci themselves and write ep_recv_count
     int nsl;                  // copy kernel: slices per token
     long long rowbytes;       // bytes of one x row
+    const float *qs;          // static quantisation coefficients
+    int qkind;                // their shape: kStaticOne, kStaticColumn or kStaticExpert
 };
 
 // ep_recv_count[r][el*W + s] = (end row of segment (el, s) of rank r) - (first row of rank r),
@@ -676,6 +681,73 @@ __device__ __forceinline__ void quant_store_wave(const DispatchArgs &a, int lane
     if (my_row >= 0) a.dyn[my_row] = scale;
 }
 
+// Static quantisation of 8 elements with their 8 coefficients: q = rint(x * c)
+// of the exact product, ties to even, saturated to [-128, 127]. One fused
+// multiply-add with M = 1.5 * 2^23 rounds x * c + M once; for |x * c| < 2^22
+// that sum lies in [2^23, 2^24), where binary32 spacing is 1, so the result is
+// M + rint(x * c) (M is even, so ties go to even as well), and larger
+// magnitudes land outside [M - 128, M + 127]. Clamping to that range (a NaN
+// clamps to M - 128) saturates, and the low mantissa byte is then the code in
+// two's complement. Three byte permutes pack four codes.
+template <class T>
+__device__ __forceinline__ uint2 static_u4(uint4 v, float4 c0, float4 c1)
+{
+    constexpr float M = 0x1.8p23f;
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    const float c[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+    uint32_t r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x = T::load((uint16_t)(w[i >> 1] >> ((i & 1) * 16)));
+        r[i] = __float_as_uint(fminf(fmaxf(__builtin_fmaf(x, c[i], M), M - 128.0f), M + 127.0f));
+    }
+    // v_perm_b32 (a, b, sel): byte n of the result is byte sel.n of the 8-byte
+    // value a:b (b in bytes 0-3); 0x0c gives a zero byte
+    uint32_t o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const uint32_t lo = __builtin_amdgcn_perm(r[4 * h + 1], r[4 * h], 0x0c0c0400u);
+        const uint32_t hi = __builtin_amdgcn_perm(r[4 * h + 3], r[4 * h + 2], 0x0c0c0400u);
+        o[h] = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+// Static quantisation of one token held by the wavefront with one coefficient
+// or one per column (the same codes for every row, formed once), stored to the
+// K rows named by lanes 0..K-1 of my_row.
+template <class T, int J>
+__device__ __forceinline__ void quant_store_wave_static(const DispatchArgs &a, int lane, const uint4 (&v)[J][2],
+                                                        int my_row)
+{
+    const int K = a.K, noc = a.h / 16;
+    const float c = a.qs[0];
+    const float4 cc = make_float4(c, c, c, c);
+    const float4 *cb = reinterpret_cast<const float4 *>(a.qs);
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int oc = lane + 64 * j;
+        if (oc >= noc) continue;
+        float4 c0 = cc, c1 = cc, c2 = cc, c3 = cc;
+        if (a.qkind == kStaticColumn) {       // a single value has no element past qs[0]
+            c0 = cb[4 * oc];
+            c1 = cb[4 * oc + 1];
+            c2 = cb[4 * oc + 2];
+            c3 = cb[4 * oc + 3];
+        }
+        const uint2 lo = static_u4<T>(v[j][0], c0, c1);
+        const uint2 hi = static_u4<T>(v[j][1], c2, c3);
+        const uint4 q = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        for (int k = 0; k < K; ++k) {
+            const int row = __builtin_amdgcn_readlane(my_row, k);
+            if (row < 0) continue;
+            uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + oc;
+            if ((j + k) & 1) store_stream(dst, q);
+            else *dst = q;
+        }
+    }
+}
+
 // Token-major copy for many tokens: one wavefront per token holds the row in
 // registers (J 16-byte pieces per lane) and writes its K copies, like the
 // quantising scatter, with the same checkerboard of plain and non-temporal
@@ -793,13 +865,15 @@ __device__ __forceinline__ void quant_store_wave_fp8(const DispatchArgs &a, int 
     }
 }
 
-// The quantising scatter (aclnnMoeDistributeDispatchV4 quantMode 2 and 3), one
-// wavefront per token. QM 2: scale = max|x| / 127 over the token (fp32,
-// correctly rounded), q = rint(x / scale) (0 for an all-zero token); QM 3: the
-// per-group FP8 codes above. Codes go to every destination row. Lane k loads
-// pair k's id and in-chunk rank before the row's 16-byte loads, so both are in
-// flight together; rows reach the store loop through readlane. No LDS, no
-// barrier. Needs h % 16 == 0, h <= 1024 * J, topk <= kQuantMaxK.
+// The quantising scatter (aclnnMoeDistributeDispatchV4 quantMode 1, 2 and 3),
+// one wavefront per token. QM 1: the static codes above (one coefficient or one
+// per column; per-expert coefficients take the XCD kernel below); QM 2:
+// scale = max|x| / 127 over the token (fp32, correctly rounded),
+// q = rint(x / scale) (0 for an all-zero token); QM 3: the per-group FP8 codes
+// above. Codes go to every destination row. Lane k loads pair k's id and
+// in-chunk rank before the row's 16-byte loads, so both are in flight together;
+// rows reach the store loop through readlane. No LDS, no barrier. Needs
+// h % 16 == 0, h <= 1024 * J, topk <= kQuantMaxK.
 template <class T, int J, int QM>
 __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(DispatchArgs a)
 {
@@ -821,7 +895,56 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(Dispa
         }
         const int my_row = lane_pair_row(a, t, lane, e, l, true);
         if constexpr (QM == MOE_QUANT_DYN_GROUP) quant_store_wave_fp8<T, J>(a, lane, v, my_row);
+        else if constexpr (QM == MOE_QUANT_STATIC) quant_store_wave_static<T, J>(a, lane, v, my_row);
         else quant_store_wave<T, J>(a, lane, v, my_row);
+    }
+}
+
+// Static quantisation with one coefficient per expert and column, XCD-aware.
+// Workgroup b serves column slice b % kXcds (about h / kXcds columns) of the
+// tokens of tile b / kXcds, one wavefront per token and one 16-element piece
+// per lane, and writes that slice of all K rows. As workgroups are dealt
+// round-robin to the XCDs, each XCD reads only its slice of every expert's
+// coefficients (E*h*4 / kXcds bytes: 0.9 MB at 256 experts and h = 7168),
+// which stays in its L2; the whole table (7.3 MB) would not fit one XCD's 4 MB
+// L2. No token byte is read twice. assist_info and expand_scales are
+// written by the slice-0 wavefronts. Needs h <= 1024 * kXcds (64 pieces per slice).
+template <class T>
+__global__ __launch_bounds__(kQuantThreads) void scatter_static_xcd_kernel(DispatchArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int N = a.W * a.bs, K = a.K, noc = a.h / 16;
+    if (a.direct) write_erc_direct(a, (size_t)blockIdx.x * kQuantThreads + threadIdx.x,
+                                   (size_t)gridDim.x * kQuantThreads);
+    const int g = (int)(blockIdx.x % kXcds);
+    const int per = (noc + kXcds - 1) / kXcds, oc = g * per + lane;
+    const bool mine = lane < per && oc < noc;
+    const int wpb = kQuantThreads / 64, tiles = (N + wpb - 1) / wpb, tstep = (int)(gridDim.x / kXcds);
+    for (int tile = (int)(blockIdx.x / kXcds); tile < tiles; tile += tstep) {
+        const int t = tile * wpb + (threadIdx.x >> 6);
+        if (t >= N) continue;
+        const size_t pk = (size_t)t * K + (lane < K ? lane : 0);
+        const int e = a.ids[pk], l = a.lr[pk];
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
+        uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
+        if (mine) {
+            v0 = src[2 * oc];
+            v1 = src[2 * oc + 1];
+        }
+        const int my_row = lane_pair_row(a, t, lane, e, l, g == 0);
+        for (int k = 0; k < K; ++k) {
+            const int row = __builtin_amdgcn_readlane(my_row, k);
+            if (row < 0 || !mine) continue;
+            // a row exists only for an id in [0, E), so the coefficient row is in bounds
+            const int ek = __builtin_amdgcn_readlane(e, k);
+            const float4 *cb = reinterpret_cast<const float4 *>(a.qs + (size_t)ek * a.h) + 4 * oc;
+            const uint2 lo = static_u4<T>(v0, cb[0], cb[1]);
+            const uint2 hi = static_u4<T>(v1, cb[2], cb[3]);
+            uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + oc;
+            const uint4 q = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            if (k & 1) store_stream(dst, q);
+            else *dst = q;
+        }
     }
 }
 
@@ -1189,7 +1312,7 @@ const char *moe_status_str(int status)
     case MOE_ERR_NULLPTR: return "a required pointer is NULL, or a forbidden one is not";
     case MOE_ERR_SHAPE: return "a size is out of range or a size product overflows";
     case MOE_ERR_DTYPE: return "unknown token dtype";
-    case MOE_ERR_QUANT: return "unknown quant mode, or quantisation of int32 data";
+    case MOE_ERR_QUANT: return "unknown quant mode, quantisation of int32 data, or a shape or coefficient count the quantiser does not take";
     case MOE_ERR_WORKSPACE: return "workspace smaller than the queried size";
     case MOE_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case MOE_ERR_SCHEDULE: return "unknown schedule mode, or segment schedule too large for this shape";
@@ -1205,11 +1328,11 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
     if (!bytes) return MOE_ERR_NULLPTR;
     int rc = check_scalars(ep_world, bs, experts_per_rank, h, topk, dtype);
     if (rc) return rc;
-    if (quant_mode != MOE_QUANT_NONE && quant_mode != MOE_QUANT_DYN_TOKEN && quant_mode != MOE_QUANT_DYN_GROUP)
-        return MOE_ERR_QUANT;
+    if (quant_mode < MOE_QUANT_NONE || quant_mode > MOE_QUANT_DYN_GROUP) return MOE_ERR_QUANT;
     if (quant_mode != MOE_QUANT_NONE && dtype == MOE_INT32) return MOE_ERR_QUANT;
-    // the per-group quantiser is the wavefront-per-token kernel only
-    if (quant_mode == MOE_QUANT_DYN_GROUP && (h % 16 != 0 || h > 1024 * 8 || topk > kQuantMaxK))
+    // the static and per-group quantisers are the wavefront-per-token kernel only
+    if ((quant_mode == MOE_QUANT_STATIC || quant_mode == MOE_QUANT_DYN_GROUP) &&
+        (h % 16 != 0 || h > 1024 * 8 || topk > kQuantMaxK))
         return MOE_ERR_QUANT;
     *bytes = dispatch_layout(ep_world, bs, experts_per_rank, topk).total;
     return MOE_OK;
@@ -1218,8 +1341,8 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
 int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales,
                  const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special, int ep_world,
                  int bs,
-                 int experts_per_rank, int h, int topk, int dtype, int quant_mode, void *expand_x,
-                 float *dynamic_scales, int32_t *assist_info, int32_t *ep_recv_count, void *expand_scales,
+                 int experts_per_rank, int h, int topk, int dtype, int quant_mode, const float *quant_scales,
+                 int64_t quant_scales_numel, void *expand_x, float *dynamic_scales, int32_t *assist_info, int32_t *ep_recv_count, void *expand_scales,
                  const moe_schedule *schedule, void *workspace, size_t workspace_bytes, void *stream)
 {
     size_t need = 0;
@@ -1229,10 +1352,23 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     const long long N = (long long)W * bs;
     const bool quant = quant_mode != MOE_QUANT_NONE;
     const bool group_quant = quant_mode == MOE_QUANT_DYN_GROUP;
+    const bool static_quant = quant_mode == MOE_QUANT_STATIC;
+    const bool dyn_quant = quant && !static_quant;       // writes dynamic_scales
     if (!ep_recv_count || !workspace) return MOE_ERR_NULLPTR;
     if (N > 0 && (!x || !expert_ids || !expand_x || !assist_info)) return MOE_ERR_NULLPTR;
-    if (quant != (dynamic_scales != nullptr) && N > 0) return MOE_ERR_NULLPTR;
-    if (!quant && dynamic_scales) return MOE_ERR_NULLPTR;
+    if (dyn_quant != (dynamic_scales != nullptr) && N > 0) return MOE_ERR_NULLPTR;
+    if (!dyn_quant && dynamic_scales) return MOE_ERR_NULLPTR;
+    const long long E_ = (long long)W * epr;
+    int qkind = kStaticOne;
+    if (static_quant) {
+        if (!quant_scales && N > 0) return MOE_ERR_NULLPTR;
+        if (quant_scales_numel == 1) qkind = kStaticOne;
+        else if (quant_scales_numel == h) qkind = kStaticColumn;
+        else if (quant_scales_numel == E_ * h) qkind = kStaticExpert;
+        else return MOE_ERR_QUANT;
+    } else if (quant_scales || quant_scales_numel != 0) {
+        return MOE_ERR_NULLPTR;
+    }
     if (expand_scales && !expert_scales) return MOE_ERR_NULLPTR;
     if (mask_kind < MOE_MASK_NONE || mask_kind > MOE_MASK_PAIR) return MOE_ERR_MASK;
     if ((mask_kind != MOE_MASK_NONE) != (x_active_mask != nullptr) && N > 0) return MOE_ERR_MASK;
@@ -1250,20 +1386,20 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     const long long S = (long long)epr * W;
     const bool want_seg = mode == MOE_SCHED_SEGMENT || seg_flags;
     if (want_seg && (long long)W * S > kSegLdsMax) return MOE_ERR_SCHEDULE;
-    if (group_quant && mode == MOE_SCHED_SEGMENT) return MOE_ERR_SCHEDULE;
+    if ((group_quant || static_quant) && mode == MOE_SCHED_SEGMENT) return MOE_ERR_SCHEDULE;
 
     const size_t xs = elem_size(dtype);
     const size_t rowbytes = (size_t)h * xs;
     if (!aligned(x, xs) || !aligned(expert_ids, 4) || !aligned(expert_scales, 4) ||
         !aligned(expand_x, quant ? 1 : xs) || !aligned(dynamic_scales, 4) || !aligned(assist_info, 4) ||
         !aligned(ep_recv_count, 4) || !aligned(expand_scales, 4) || !aligned(workspace, 16) ||
-        !aligned(seg_flags, 4))
+        !aligned(seg_flags, 4) || !aligned(quant_scales, qkind == kStaticOne ? 4 : 16))
         return MOE_ERR_ALIGN;
     // per-token int8 takes the wavefront kernel when it can, a block kernel
     // otherwise; per-group FP8 needs the wavefront kernel's 16-byte rows
     const bool wave = quant && h % 16 == 0 && h <= 1024 * 8 && K <= kQuantMaxK && aligned(x, 16) &&
                       aligned(expand_x, 16);
-    if (group_quant && !wave && N > 0) return MOE_ERR_ALIGN;
+    if ((group_quant || static_quant) && !wave && N > 0) return MOE_ERR_ALIGN;
 
     const DispatchLayout L = dispatch_layout(W, bs, epr, K);
     char *ws = static_cast<char *>(workspace);
@@ -1320,6 +1456,8 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         a.direct = (direct && !want_seg) ? 1 : 0;
         a.rowbytes = (long long)rowbytes;
         a.nsl = 1;
+        a.qs = quant_scales;
+        a.qkind = qkind;
         if (mode == MOE_SCHED_TOKEN) {
             const size_t kdsm = (size_t)4 * K * sizeof(int);
             if (!quant) {
@@ -1344,11 +1482,18 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                 if (wave) {
                     const int J = (h / 16 + 63) / 64;
                     const dim3 g((unsigned)((N + 3) / 4)), b(kQuantThreads);
-                    if (dtype == MOE_FP16) {
+                    if (static_quant && qkind == kStaticExpert) {
+                        // kXcds workgroups (column slices) per tile of 4 tokens, at most 2^16 tiles at once
+                        const dim3 gx((unsigned)(std::min<long long>((N + 3) / 4, 1 << 16) * kXcds));
+                        if (dtype == MOE_FP16) hipLaunchKernelGGL(scatter_static_xcd_kernel<F16>, gx, b, 0, st, a);
+                        else hipLaunchKernelGGL(scatter_static_xcd_kernel<BF16>, gx, b, 0, st, a);
+                    } else if (dtype == MOE_FP16) {
                         if (group_quant) launch_quant_wave<F16, MOE_QUANT_DYN_GROUP>(J, g, b, st, a);
+                        else if (static_quant) launch_quant_wave<F16, MOE_QUANT_STATIC>(J, g, b, st, a);
                         else launch_quant_wave<F16, MOE_QUANT_DYN_TOKEN>(J, g, b, st, a);
                     } else {
                         if (group_quant) launch_quant_wave<BF16, MOE_QUANT_DYN_GROUP>(J, g, b, st, a);
+                        else if (static_quant) launch_quant_wave<BF16, MOE_QUANT_STATIC>(J, g, b, st, a);
                         else launch_quant_wave<BF16, MOE_QUANT_DYN_TOKEN>(J, g, b, st, a);
                     }
                 } else {

@@ -50,8 +50,9 @@ enum moe_status {
     MOE_ERR_NULLPTR = 1,   /* a required pointer is NULL, or a forbidden one is not */
     MOE_ERR_SHAPE = 2,     /* a size is out of range or a product overflows */
     MOE_ERR_DTYPE = 3,     /* unknown token dtype */
-    MOE_ERR_QUANT = 4,     /* unknown quant mode, quantisation of int32 data, or a shape the
-                              per-group quantiser does not take */
+    MOE_ERR_QUANT = 4,     /* unknown quant mode, quantisation of int32 data, a shape the
+                              static or per-group quantiser does not take, or a static
+                              coefficient count other than 1, h or E*h */
     MOE_ERR_WORKSPACE = 5, /* workspace smaller than the queried size */
     MOE_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch */
     MOE_ERR_SCHEDULE = 7,  /* unknown schedule mode, or the segment schedule (or the
@@ -65,8 +66,19 @@ enum moe_status {
 enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
 
 /* Quantisation modes; the numbering follows quantMode of
- * aclnnMoeDistributeDispatchV4 (0 = none, 2 = per-token dynamic, 3 = per-group
- * dynamic).
+ * aclnnMoeDistributeDispatchV4 (0 = none, 1 = static, 2 = per-token dynamic,
+ * 3 = per-group dynamic).
+ *  MOE_QUANT_STATIC: int8 codes rint(x * c) of the exact product, ties to
+ *      even, saturated to [-128, 127] (a NaN product gives -128). c
+ *      comes from quant_scales (fp32, caller-owned device memory): one value,
+ *      one per column (h values), or one per expert and column (E*h values,
+ *      row e for the rows of expert e) -- the three shapes the page's 参数说明
+ *      gives the static coefficient input (one coefficient, a smoothing vector
+ *      shared by the experts, per-expert coefficients fused with smoothing);
+ *      its formula is garbled, and multiplying is the reading taken. No
+ *      dynamic_scales. Needs h % 16 == 0, h <= 8192, topk <= 64, 16-byte
+ *      aligned x, expand_x and (for h or E*h values) quant_scales, and the
+ *      token schedule.
  *  MOE_QUANT_DYN_TOKEN: int8 codes rint(x / s), s = max|x| / 127 over the token;
  *      dynamic_scales holds one fp32 scale per row.
  *  MOE_QUANT_DYN_GROUP: OCP FP8 E4M3 ("fn") codes per group of 128 elements of
@@ -77,7 +89,7 @@ enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
  *      size are garbled, and these are the readings taken.) Needs h % 16 == 0,
  *      h <= 8192, topk <= 64, 16-byte aligned x and expand_x, and the token
  *      schedule. */
-enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_DYN_TOKEN = 2, MOE_QUANT_DYN_GROUP = 3 };
+enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_STATIC = 1, MOE_QUANT_DYN_TOKEN = 2, MOE_QUANT_DYN_GROUP = 3 };
 
 /* Token masks: xActiveMaskOptional of aclnnMoeDistributeDispatchV4 (参数说明):
  * a 1D mask (BS,) per rank or a 2D mask (BS, K); a token whose K entries are
@@ -148,8 +160,8 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
 /*
  * Dispatch: the expert-parallel all-to-all of aclnnMoeDistributeDispatchV4
  * (计算公式, expandXOut = AllToAllV(X)) with every logical rank's window in
- * one HBM, preceded by optional dynamic quantisation (per-token int8 or
- * per-group FP8 E4M3).
+ * one HBM, preceded by optional quantisation (static int8, per-token dynamic
+ * int8 or per-group dynamic FP8 E4M3).
  *
  *  x              [N, h] dtype           tokens; rows s*bs..s*bs+bs-1 are rank s's
  *  expert_ids     [N, K] int32           global expert ids in [0, E), distinct per token
@@ -159,12 +171,14 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
  *  mask_kind      moe_mask
  *  special        host pointer or NULL   see moe_special_experts; ids in the special
  *                                        ranges are legal and produce no row
- *  expand_x       [ROWS, h]              dtype; int8 when quant_mode == 2, E4M3 bytes when 3. Row order:
+ *  quant_scales   fp32 [quant_scales_numel]  quant_mode 1 only (NULL and 0 otherwise):
+ *                                        1, h or E*h coefficients, see MOE_QUANT_STATIC
+ *  expand_x       [ROWS, h]              dtype; int8 when quant_mode is 1 or 2, E4M3 bytes when 3. Row order:
  *                                        rank r, then local expert, then source rank,
  *                                        then ascending source token
  *  dynamic_scales [ROWS] fp32            per-row token scale max|x|/127 (quant_mode 2), or
  *                 [ROWS, ceil(h/128)]    per-group scales max|x|/448 (quant_mode 3);
- *                                        required iff quantising, NULL otherwise
+ *                                        required for quant_mode 2 and 3, NULL otherwise
  *  assist_info    [ROWS, 3] int32        (src_rank, src_token, topk_id) of each row
  *  ep_recv_count  [W, S] int32           per rank, inclusive prefix of the row counts of
  *                                        its segments ordered el*W + s
@@ -183,7 +197,8 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
 int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales,
                  const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
                  int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype,
-                 int quant_mode, void *expand_x, float *dynamic_scales, int32_t *assist_info,
+                 int quant_mode, const float *quant_scales, int64_t quant_scales_numel,
+                 void *expand_x, float *dynamic_scales, int32_t *assist_info,
                  int32_t *ep_recv_count, void *expand_scales, const moe_schedule *schedule,
                  void *workspace, size_t workspace_bytes, void *stream);
 

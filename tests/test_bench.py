@@ -21,6 +21,9 @@ def test_algorithmic_bytes_of_the_workloads():
     d3, c3 = bench.algorithmic_bytes(wl.BY_NAME["w16_h7168_bf16_fp8g128"])
     assert c3 == c
     assert d3 == 294273024 - 32768 * 4 + 32768 * 56 * 4
+    # static int8: no row scales written, the 256 x 7168 fp32 coefficients read once
+    d1, c1 = bench.algorithmic_bytes(wl.BY_NAME["w16_h7168_bf16_static_q8"])
+    assert c1 == c and d1 == 294273024 - 32768 * 4 + 256 * 7168 * 4
 
 
 def test_code_hash_ignores_comments_and_spacing_only(tmp_path):

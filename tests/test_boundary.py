@@ -65,7 +65,12 @@ def _ws(*args):
     ((64, 2048, 2, 65536, 1, 1, 0), SHAPE),   # N * ceil(h/128) beyond the slice-grid limit
     ((8, 2 ** 27, 8, 16, 8, 0, 0), SHAPE),    # N*K >= 2^31
     ((2, 4, 2, 16, 1, 3, 0), DTYPE),
-    ((2, 4, 2, 16, 1, 1, 1), QUANT),          # quant mode 1 not offered
+    ((2, 4, 2, 16, 1, 1, 1), OK),             # static int8
+    ((2, 4, 2, 16, 1, 0, 1), QUANT),          # int32 cannot be quantised
+    ((2, 4, 2, 24, 1, 2, 1), QUANT),          # static needs h % 16 == 0
+    ((2, 4, 2, 8208, 1, 1, 1), QUANT),        # ... and h <= 8192
+    ((8, 4, 16, 64, 65, 1, 1), QUANT),        # ... and topk <= 64
+    ((2, 4, 2, 16, 1, 1, -1), QUANT),
     ((2, 4, 2, 16, 1, 0, 2), QUANT),          # int32 cannot be quantised
     ((16, 256, 16, 7168, 8, 2, 3), OK),       # per-group FP8
     ((2, 4, 2, 16, 1, 0, 3), QUANT),
@@ -103,13 +108,14 @@ A = 1 << 20   # fake, 256-aligned "device" addresses; never dereferenced by thes
 
 def _dispatch(**kw):
     p = dict(x=A, ids=2 * A, esc=None, mask=None, mk=0, sp=None, W=2, bs=4, epr=2, h=16, K=2, dtype=1, quant=0,
-             ex=3 * A, dyn=None, assist=4 * A, erc=5 * A, esc_out=None, sched=None, ws=6 * A, wsb=1 << 30)
+             qs=None, qn=0, ex=3 * A, dyn=None, assist=4 * A, erc=5 * A, esc_out=None, sched=None, ws=6 * A,
+             wsb=1 << 30)
     p.update(kw)
     P = lambda v: None if v is None else ctypes.c_void_p(v)
     return moe.library().moe_dispatch(
         P(p["x"]), P(p["ids"]), P(p["esc"]), P(p["mask"]), p["mk"],
         ctypes.byref(p["sp"]) if p["sp"] is not None else None, p["W"], p["bs"], p["epr"], p["h"], p["K"],
-        p["dtype"], p["quant"],
+        p["dtype"], p["quant"], P(p["qs"]), ctypes.c_int64(p["qn"]),
         P(p["ex"]), P(p["dyn"]), P(p["assist"]), P(p["erc"]), P(p["esc_out"]),
         ctypes.byref(p["sched"]) if p["sched"] is not None else None, P(p["ws"]), p["wsb"], None)
 
@@ -139,6 +145,17 @@ def _dispatch(**kw):
     (dict(W=128, epr=8, K=2, sched=moe.MoeSchedule(mode=1)), SCHEDULE),   # W*S = 131072 > LDS budget
     (dict(quant=3, dyn=7 * A, sched=moe.MoeSchedule(mode=1)), SCHEDULE),  # per-group: token schedule only
     (dict(quant=3, dyn=7 * A, x=A + 2), ALIGN),                           # per-group: 16-byte rows
+    (dict(quant=1), NULLPTR),                                  # static needs its coefficients
+    (dict(quant=1, qs=8 * A, qn=3), QUANT),                    # 1, h (16) or E*h (64) of them
+    (dict(quant=1, qs=8 * A, qn=32), QUANT),
+    (dict(quant=1, qs=8 * A, qn=16, dyn=7 * A), NULLPTR),      # and writes no dynamic scales
+    (dict(qs=8 * A, qn=16), NULLPTR),                          # coefficients only for quant mode 1
+    (dict(qn=16), NULLPTR),
+    (dict(quant=2, dyn=7 * A, qs=8 * A, qn=1), NULLPTR),
+    (dict(quant=1, qs=8 * A + 4, qn=64), ALIGN),               # h or E*h values: 16-byte aligned
+    (dict(quant=1, qs=8 * A + 2, qn=1), ALIGN),                # one value: 4-byte aligned
+    (dict(quant=1, qs=8 * A, qn=1, sched=moe.MoeSchedule(mode=1)), SCHEDULE),   # token schedule only
+    (dict(quant=1, qs=8 * A, qn=1, x=A + 2), ALIGN),           # 16-byte rows
     (dict(sp=moe.MoeSpecialExperts(zero_expert_num=-1)), SHAPE),
     (dict(sp=moe.MoeSpecialExperts(const_expert_num=1)), SHAPE),        # const experts are not supported
     (dict(sp=moe.MoeSpecialExperts(zero_expert_num=2 ** 31 - 4)), SHAPE),   # E + zero = 2^31

@@ -50,13 +50,18 @@ def gpu_identity_expert(expand_x, dyn):
     return (expand_x.float() * dyn[:, None]).to(torch.bfloat16)
 
 
+def gpu_quant_scales(w, inp):
+    return to_dev(inp["quant_scales"]) if w.quant_mode == 1 else None
+
+
 def run_gpu(w, inp, schedule=None):
     bf = w.dtype == "bf16"
     x, ids, sc = to_dev(inp["x"], bf), to_dev(inp["ids"]), to_dev(inp["scales"])
     special = dict(zero_experts=w.zero_experts, copy_experts=w.copy_experts)
     ex, dyn, assist, erc, esc = moe.dispatch(x, ids, w.ep_world, w.experts_per_rank, w.quant_mode,
-                                             expert_scales=sc, schedule=schedule, **special)
-    y = gpu_identity_expert(ex, dyn)
+                                             expert_scales=sc, schedule=schedule,
+                                             quant_scales=gpu_quant_scales(w, inp), **special)
+    y = gpu_identity_expert(ex, dyn if w.quant_mode != 1 else torch.ones(ex.shape[0], device=DEV))
     # copy experts read the tokens in the combine's dtype (bf16 tokens for quantised runs)
     xo = moe.combine(y, assist, erc, ids, sc, w.ep_world, w.experts_per_rank,
                      ori_x=x if w.copy_experts else None, **special)
@@ -70,8 +75,9 @@ def run_oracle(w, inp):
     bf = w.dtype == "bf16"
     special = dict(zero_experts=w.zero_experts, copy_experts=w.copy_experts)
     d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
-                        expert_scales=inp["scales"], bf16=bf, **special)
-    y = oracle.identity_expert(d["expand_x"], d["dynamic_scales"])
+                        expert_scales=inp["scales"], bf16=bf, quant_scales=inp.get("quant_scales"), **special)
+    y = oracle.identity_expert(d["expand_x"], d["dynamic_scales"] if w.quant_mode != 1
+                               else np.ones(w.rows, np.float32))
     out_bf = bf or w.quant_mode != 0
     d["x_out"] = oracle.combine(y, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"],
                                 w.ep_world, w.experts_per_rank, bf16=out_bf,
@@ -107,7 +113,7 @@ def assert_parity(w, g, o):
     assert (g["assist_info"][:A] == o["assist_info"][:A]).all(), "assist_info"
     assert g["expand_x"][:A].tobytes() == o["expand_x"][:A].tobytes(), "expand_x"
     assert g["expand_scales"][:A].view(np.uint32).tobytes() == o["expand_scales"][:A].view(np.uint32).tobytes()
-    if w.quant_mode != 0:
+    if w.quant_mode in (2, 3):
         assert (g["dynamic_scales"][:A].view(np.uint32).tobytes()
                 == o["dynamic_scales"][:A].view(np.uint32).tobytes()), "dynamic_scales"
     if w.dtype == "int32":
@@ -244,6 +250,64 @@ def test_group_quant_tiny_and_zero_groups(exp):
 
 def test_group_quant_with_a_mask():
     check_masked(wl.custom(4, 96, 2048, 6, 4, "bf16", "zipf_topk", quant_mode=3, name="fp8_masked"), "pair")
+
+
+# --------------------------------------------------------------------------
+# quantMode 1: static int8, q = sat8(rint(x * c)) with one coefficient, one per
+# column or one per expert and column (the page's three coefficient shapes)
+# --------------------------------------------------------------------------
+
+STATIC_QUANT = [
+    wl.BY_NAME["w16_h7168_bf16_static_q8"],
+    wl.custom(16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=1, static_scales="scalar", index=4,
+              name="w16_h7168_bf16_static_one"),
+    wl.custom(8, 32, 7168, 8, 8, "fp16", "zipf_topk", quant_mode=1, static_scales="column", name="fp16_h7168_column"),
+    wl.custom(2, 5, 16, 3, 2, "bf16", "gauss_topk", quant_mode=1, name="h16_j1_expert"),
+    wl.custom(3, 300, 1040, 4, 3, "fp16", "zipf_topk", quant_mode=1, static_scales="column", name="h1040_j2_ragged"),
+    wl.custom(4, 100, 4096, 6, 4, "bf16", "gauss_topk", quant_mode=1, name="h4096_j4_expert"),
+    wl.custom(4, 257, 8192, 2, 4, "fp16", "gauss_topk", quant_mode=1, static_scales="scalar", name="h8192_j8_one"),
+    wl.custom(4, 257, 8192, 2, 4, "bf16", "gauss_topk", quant_mode=1, name="h8192_j8_expert"),
+    wl.custom(65, 2, 256, 2, 4, "fp16", "gauss_topk", quant_mode=1, name="65_chunks_scanned_offsets"),
+    wl.custom(2, 2, 128, 64, 40, "bf16", "gauss_topk", quant_mode=1, name="topk64_expert"),
+]
+
+
+@pytest.mark.parametrize("w", STATIC_QUANT, ids=lambda w: w.name)
+def test_static_quant_shapes(w):
+    check(w)
+
+
+@pytest.mark.parametrize("kind", ["scalar", "column", "expert"])
+def test_static_quant_saturation_nan_and_infinities(kind):
+    """Products beyond the int8 range saturate, NaN gives -128, ties go to even."""
+    w = wl.custom(2, 8, 64, 2, 2, "bf16", "gauss_topk", quant_mode=1, static_scales=kind, name="static_edges")
+    inp = wl.make_inputs(w)
+    g = np.random.default_rng(29).standard_normal((w.num_tokens, w.h)).astype(np.float32) * 8
+    g[0, :6] = [np.nan, np.inf, -np.inf, -0.0, 1e30, -1e30]
+    g[1] = np.arange(w.h) - 32.5                  # halves: ties with a unit coefficient
+    inp["x"] = wl.f32_to_bf16_bits(g)
+    inp["quant_scales"][: min(4, inp["quant_scales"].size)] = 1.0
+    gg, o = check(w, inp)
+    assert (gg["expand_x"][:w.rows] == 127).any() and (gg["expand_x"][:w.rows] == -128).any()
+
+
+def test_static_quant_subnormal_tokens_and_large_coefficients():
+    """bf16 subnormal tokens times 2^127: the product is rounded exactly (no flush to zero)."""
+    w = wl.custom(2, 8, 64, 2, 2, "bf16", "gauss_topk", quant_mode=1, static_scales="scalar", name="static_subnormal")
+    inp = wl.make_inputs(w)
+    g = np.random.default_rng(31).standard_normal((w.num_tokens, w.h)).astype(np.float32)
+    g *= np.float32(2.0 ** -128)                 # mostly bf16 subnormals
+    g[0, :4] = [2.0 ** -127, -(2.0 ** -127), 2.0 ** -130, 3 * 2.0 ** -128]
+    inp["x"] = wl.f32_to_bf16_bits(g)
+    inp["quant_scales"][:] = 2.0 ** 127
+    gg, o = check(w, inp)
+    assert (np.abs(gg["expand_x"][:w.rows].astype(int)) > 0).any()
+
+
+def test_static_quant_with_a_mask_and_special_experts():
+    check_masked(wl.custom(4, 96, 2048, 6, 4, "bf16", "zipf_topk", quant_mode=1, name="static_masked"), "pair")
+    check(wl.custom(4, 33, 7168, 8, 4, "bf16", "gauss_topk", quant_mode=1, zero_experts=6, copy_experts=6,
+                    name="static_special"))
 
 
 # --------------------------------------------------------------------------
@@ -399,14 +463,17 @@ def check_masked(w, kind, seed=1, schedule=None):
     m = torch.from_numpy(mask).to(DEV)
     special = dict(zero_experts=w.zero_experts, copy_experts=w.copy_experts)
     ex, dyn, assist, erc, esc = moe.dispatch(x, ids, w.ep_world, w.experts_per_rank, w.quant_mode,
-                                             expert_scales=sc, schedule=schedule, x_active_mask=m, **special)
-    y = gpu_identity_expert(ex, dyn)
+                                             expert_scales=sc, schedule=schedule, x_active_mask=m,
+                                             quant_scales=gpu_quant_scales(w, inp), **special)
+    y = gpu_identity_expert(ex, dyn if w.quant_mode != 1 else torch.ones(ex.shape[0], device=DEV))
     xo = moe.combine(y, assist, erc, ids, sc, w.ep_world, w.experts_per_rank, x_active_mask=m,
                      ori_x=x if w.copy_experts else None, **special)
     torch.cuda.synchronize()
     d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
-                        expert_scales=inp["scales"], bf16=bf, mask=mask, **special)
-    yo = oracle.identity_expert(d["expand_x"], d["dynamic_scales"])
+                        expert_scales=inp["scales"], bf16=bf, mask=mask, quant_scales=inp.get("quant_scales"),
+                        **special)
+    yo = oracle.identity_expert(d["expand_x"], d["dynamic_scales"] if w.quant_mode != 1
+                                else np.ones(w.rows, np.float32))
     xo_o = oracle.combine(yo, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"], w.ep_world,
                           w.experts_per_rank, bf16=bf or w.quant_mode != 0, mask=mask,
                           ori_x=inp["x"] if w.copy_experts else None, **special)
@@ -415,7 +482,7 @@ def check_masked(w, kind, seed=1, schedule=None):
     assert (to_np(assist)[:A] == d["assist_info"][:A]).all(), "assist_info"
     assert to_np(ex)[:A].tobytes() == d["expand_x"][:A].tobytes(), "expand_x"
     assert to_np(esc)[:A].view(np.uint32).tobytes() == d["expand_scales"][:A].view(np.uint32).tobytes()
-    if w.quant_mode != 0:
+    if w.quant_mode in (2, 3):
         assert to_np(dyn)[:A].view(np.uint32).tobytes() == d["dynamic_scales"][:A].view(np.uint32).tobytes()
     g = to_np(xo)
     if w.dtype == "int32":
