@@ -255,8 +255,8 @@ def combine_into(x_out: torch.Tensor, expand_x: torch.Tensor, assist_info: torch
                                       expand_x.device)
     rc = library().moe_combine(
         _ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_count), _ptr(expert_ids), _ptr(expert_scales), mp, mk,
-        _special(zero_experts, copy_experts, ori_x), ep_world, N // ep_world, experts_per_rank, h, K, dt, _ptr(x_out), _ptr(workspace), workspace.numel(),
-        _stream_ptr(expand_x.device))
+        _special(zero_experts, copy_experts, ori_x), ep_world, N // ep_world, experts_per_rank, h, K, dt,
+        _ptr(x_out), _ptr(workspace), workspace.numel(), _stream_ptr(expand_x.device))
     _check("moe_combine", rc)
     return x_out
 

@@ -1173,7 +1173,8 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_half_kernel(Com
         uint32_t o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (uint32_t)T::store(acc[2 * i]) | ((uint32_t)T::store(acc[2 * i + 1]) << 16);
-        store_stream(reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes) + c, make_uint4(o[0], o[1], o[2], o[3]));
+        store_stream(reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes) + c,
+                     make_uint4(o[0], o[1], o[2], o[3]));
     } else {
         const int j = sl * kGatherThreads + threadIdx.x;
         if (j >= a.h) return;
@@ -1312,7 +1313,8 @@ const char *moe_status_str(int status)
     case MOE_ERR_NULLPTR: return "a required pointer is NULL, or a forbidden one is not";
     case MOE_ERR_SHAPE: return "a size is out of range or a size product overflows";
     case MOE_ERR_DTYPE: return "unknown token dtype";
-    case MOE_ERR_QUANT: return "unknown quant mode, quantisation of int32 data, or a shape or coefficient count the quantiser does not take";
+    case MOE_ERR_QUANT:
+        return "unknown quant mode, quantisation of int32 data, or a shape or coefficient count the quantiser does not take";
     case MOE_ERR_WORKSPACE: return "workspace smaller than the queried size";
     case MOE_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case MOE_ERR_SCHEDULE: return "unknown schedule mode, or segment schedule too large for this shape";
@@ -1339,10 +1341,10 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
 }
 
 int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales,
-                 const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special, int ep_world,
-                 int bs,
-                 int experts_per_rank, int h, int topk, int dtype, int quant_mode, const float *quant_scales,
-                 int64_t quant_scales_numel, void *expand_x, float *dynamic_scales, int32_t *assist_info, int32_t *ep_recv_count, void *expand_scales,
+                 const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
+                 int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype, int quant_mode,
+                 const float *quant_scales, int64_t quant_scales_numel, void *expand_x, float *dynamic_scales,
+                 int32_t *assist_info, int32_t *ep_recv_count, void *expand_scales,
                  const moe_schedule *schedule, void *workspace, size_t workspace_bytes, void *stream)
 {
     size_t need = 0;

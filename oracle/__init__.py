@@ -142,7 +142,8 @@ def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=Non
         esc = np.zeros((rows,), expert_scales.dtype)
     m, mk = _mask(mask, N, K)
     rc = _load().oracle_dispatch(_ptr(x), _ptr(ids), _ptr(expert_scales), W, bs, epr, h, K, dt,
-                                 int(quant_mode), _ptr(qs), 0 if qs is None else qs.size, _ptr(m), mk, int(zero_experts), int(copy_experts),
+                                 int(quant_mode), _ptr(qs), 0 if qs is None else qs.size, _ptr(m), mk,
+                                 int(zero_experts), int(copy_experts),
                                  _ptr(expand_x), _ptr(dyn), _ptr(assist),
                                  _ptr(erc), _ptr(esc))
     if rc != 0:

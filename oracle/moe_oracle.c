@@ -235,7 +235,8 @@ static int pair_active(const uint8_t *mask, int mask_kind, long long t, int k, i
  */
 int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales,
                     int W, int bs, int epr, int h, int K, int dtype, int quant,
-                    const float *qscale, long long qscale_n, const uint8_t *mask, int mask_kind, int zero_num, int copy_num,
+                    const float *qscale, long long qscale_n, const uint8_t *mask, int mask_kind, int zero_num,
+                    int copy_num,
                     void *expand_x, float *dyn_scales, int32_t *assist,
                     int32_t *ep_recv_count, void *expand_scales)
 {
