@@ -537,6 +537,41 @@ def test_token_masks_with_the_segment_schedule(kind):
 
 
 # --------------------------------------------------------------------------
+# seeded random configurations: features combined in ways the lists above do
+# not (quant mode x mask kind x special experts x ragged shapes x chunk counts)
+# --------------------------------------------------------------------------
+
+def random_case(i):
+    rng = np.random.default_rng(900 + i)
+    W = int(rng.choice([2, 3, 4, 8, 16, 65]))
+    bs = int(rng.integers(1, max(2, 2048 // W)))
+    epr = int(rng.integers(1, max(2, min(9, 1024 // W))))
+    K = int(rng.integers(1, min(W * epr, 12) + 1))
+    dtype = str(rng.choice(["int32", "fp16", "bf16"]))
+    quant = 0 if dtype == "int32" else int(rng.choice([0, 1, 2, 3]))
+    h = 16 * int(rng.integers(1, 257)) if quant in (1, 3) else int(rng.integers(1, 3000))
+    routing = "uniform_distinct" if dtype == "int32" else str(rng.choice(["gauss_topk", "zipf_topk"]))
+    zero = int(rng.integers(0, 3))
+    copy = 0 if (quant and dtype != "bf16") else int(rng.integers(0, 3))     # copy tokens in the combine's dtype
+    kind = str(rng.choice(["none", "token_any", "pair"]))
+    sk = str(rng.choice(["scalar", "column", "expert"]))
+    w = wl.custom(W, bs, h, K, epr, dtype, routing, quant_mode=quant, zero_experts=zero, copy_experts=copy,
+                  static_scales=sk, index=300 + i, name="random%d" % i)
+    return w, kind
+
+
+RANDOM_CASES = [random_case(i) for i in range(28)]
+
+
+@pytest.mark.parametrize("w,kind", RANDOM_CASES, ids=lambda v: v if isinstance(v, str) else v.name)
+def test_random_configurations(w, kind):
+    if kind == "none":
+        check(w)
+    else:
+        check_masked(w, kind)
+
+
+# --------------------------------------------------------------------------
 # determinism (aclnnMoeDistributeDispatchV4 约束说明: deterministic by default)
 # --------------------------------------------------------------------------
 
