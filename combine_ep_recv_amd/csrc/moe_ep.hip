@@ -47,6 +47,7 @@
 namespace {
 
 constexpr int kScanThreads = 1024;         // the single scan block (>= max experts)
+constexpr int kScanBatch = 32;             // chunks whose counts the scan loads at once
 constexpr int kRouteThreads = 256;
 constexpr int kRouteTokens = 256;          // tokens per route chunk
 constexpr int kRouteWords = kRouteTokens / 64;
@@ -61,7 +62,9 @@ constexpr int64_t kReadmeLargeBytes = 2 * 1024 * 1024;
 
 constexpr int kCopyThreads = 128;          // token-major copy: block = (token, slice)
 constexpr int kCopyUnroll = 2;             // 16-byte chunks per thread per slice
-constexpr int kCopyWaveMinTokens = 1024;   // from here on the copy runs one wavefront per token
+constexpr int kCopyWaveMinTokens = 1024;   // from here on the copy runs one wavefront per token ...
+constexpr long long kCopyWaveMaxBytes = 640ll << 20;    // ... up to this much expand_x
+constexpr long long kMixedStoreMaxBytes = 384ll << 20;  // quantised expand_x up to which stores are mixed
 constexpr int kQuantThreads = 256;         // one wavefront per token
 constexpr int kQuantMaxK = 64;             // wavefront-per-token quantiser handles topk <= 64
 constexpr int kBlockThreads = 256;         // generic block-per-token kernels
@@ -93,7 +96,11 @@ struct BF16 {
 // 16 ranks x 256 tokens, h = 7168 (294 MB moved) that kernel takes 45 us,
 // against 51 us with plain stores only and 55 us with non-temporal ones only;
 // a pure 235 MB scattered-row write reaches ~6.3 TB/s plain and ~4.8 TB/s
-// non-temporal. The mix is no slower on small outputs either.
+// non-temporal. The mix is no slower on small outputs either. It holds while
+// the rows written fit in about the Infinity Cache (256 MB): at 16 ranks x
+// 512 tokens (470 MB of int8 rows) non-temporal stores alone take 111 us
+// against 126 us mixed, at 16 x 1024 tokens 199 us against 258 us, so larger
+// outputs store non-temporally only (nt_stores).
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_stream(uint4 *p, uint4 v)
 {
@@ -331,40 +338,84 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     int32_t *__restrict__ seg_flags, int2 *__restrict__ plan, int32_t *__restrict__ nplan)
 {
     __shared__ int32_t eoff[kMaxExperts + 1];
+    __shared__ int32_t part[kScanThreads];        // [q][e]: chunk-range partial counts, then their prefixes
     __shared__ int32_t tmp[40];
     extern __shared__ int32_t seg_lds[];          // when want_seg: int32 counts [W*S], then uint8 flags [W*S]
     const int E = W * epr, S = epr * W, NB = W * nbs;
     const int tid = threadIdx.x;
+    // T threads per expert (kScanThreads / E, rounded down to a power of two);
+    // thread (e, q) = tid % E, tid / E owns chunks [q * NB / T, (q + 1) * NB / T)
+    int T = 1;
+    while (2 * T * E <= kScanThreads) T *= 2;
+    const int e = tid % E, q = tid / E;
+    const bool act = q < T;
+    const int bq0 = act ? (int)((long long)q * NB / T) : 0, bq1 = act ? (int)((long long)(q + 1) * NB / T) : 0;
 
-    // column totals -> exclusive offsets per expert (blockDim >= E)
+    // partial column sums; kScanBatch chunks' counts are loaded together, and
+    // the first batch stays in registers for the offsets below
+    int mine = 0, c0[kScanBatch];
+    for (int b0 = bq0; b0 < bq1; b0 += kScanBatch) {
+        int c[kScanBatch];
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) {
+            const size_t b = (size_t)min(b0 + u, bq1 - 1);
+            c[u] = b0 + u < bq1 ? pci[b * E + e] - pc[b * E + e] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < kScanBatch; ++u) mine += c[u];
+        if (b0 == bq0) {
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) c0[u] = c[u];
+        }
+    }
+    if (act) part[q * E + e] = mine;
+    __syncthreads();
+    // column totals -> exclusive offsets per expert (the q = 0 threads, tid = e)
     int tot = 0;
-    if (tid < E)
-        for (int b = 0; b < NB; ++b) tot += pci[(size_t)b * E + tid] - pc[(size_t)b * E + tid];
+    if (tid < E) {
+        for (int k = 0; k < T; ++k) {
+            const int v = part[k * E + tid];
+            part[k * E + tid] = tot;                  // now: offset of range k inside column e
+            tot += v;
+        }
+    }
     int total;
     const int ex = block_excl_scan(tot, tmp, &total);
     if (tid < E) eoff[tid] = ex;
     if (tid == 0) eoff[E] = total;
     __syncthreads();
 
-    int32_t *segc = seg_lds;
-    uint8_t *flag = reinterpret_cast<uint8_t *>(seg_lds + (size_t)W * S);
-    if (tid < E) {
-        const int e = tid, r = e / epr, el = e % epr;
+    // chunk offsets, and ep_recv_count at the last chunk of every source rank
+    if (act) {
+        const int r = e / epr, el = e % epr;
         const int base_r = eoff[r * epr];
-        int run = 0;
-        for (int s = 0; s < W; ++s) {
-            const int before = run;
-            for (int j = 0; j < nbs; ++j) {
-                const size_t b = (size_t)s * nbs + j;
-                const int c = pci[b * E + e] - pc[b * E + e];
-                boff[b * E + e] = eoff[e] + run;
-                run += c;
+        int run = part[q * E + e];
+        for (int b0 = bq0; b0 < bq1; b0 += kScanBatch) {
+            int c[kScanBatch];
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) {
+                const size_t b = (size_t)min(b0 + u, bq1 - 1);
+                c[u] = b0 == bq0 ? c0[u] : pci[b * E + e] - pc[b * E + e];
             }
-            erc[(size_t)r * S + el * W + s] = eoff[e] + run - base_r;
-            if (want_seg) segc[r * S + el * W + s] = run - before;
+#pragma unroll
+            for (int u = 0; u < kScanBatch; ++u) {
+                const int b = b0 + u;
+                if (b >= bq1) break;
+                boff[(size_t)b * E + e] = eoff[e] + run;
+                run += c[u];
+                if ((b + 1) % nbs == 0)               // last chunk of source rank b / nbs
+                    erc[(size_t)r * S + el * W + b / nbs] = eoff[e] + run - base_r;
+            }
         }
+        if (nbs == 0 && q == 0)                       // empty batch: zero counts
+            for (int s = 0; s < W; ++s) erc[(size_t)r * S + el * W + s] = 0;
     }
     if (!want_seg) return;
+    __syncthreads();
+    // segment counts: differences of consecutive inclusive counts within a rank
+    int32_t *segc = seg_lds;
+    uint8_t *flag = reinterpret_cast<uint8_t *>(seg_lds + (size_t)W * S);
+    for (int i = tid; i < W * S; i += blockDim.x) segc[i] = erc[i] - (i % S > 0 ? erc[i - 1] : 0);
     __syncthreads();
 
     // large-segment predicate (combine_doubleplane README 方案设计), one rank per thread
@@ -386,10 +437,10 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     if (!plan) return;
     __syncthreads();
 
-    int mine = 0;
-    if (tid < W) mine = plan_rank(segc + tid * S, flag + tid * S, S, eoff[tid * epr], kPlanRows, nullptr);
+    int items = 0;
+    if (tid < W) items = plan_rank(segc + tid * S, flag + tid * S, S, eoff[tid * epr], kPlanRows, nullptr);
     int nitems;
-    const int first = block_excl_scan(mine, tmp, &nitems);
+    const int first = block_excl_scan(items, tmp, &nitems);
     if (tid < W) plan_rank(segc + tid * S, flag + tid * S, S, eoff[tid * epr], kPlanRows, plan + first);
     if (tid == 0) *nplan = nitems;
 }
@@ -419,6 +470,7 @@ struct DispatchArgs {
     long long rowbytes;       // bytes of one x row
     const float *qs;          // static quantisation coefficients
     int qkind;                // their shape: kStaticOne, kStaticColumn or kStaticExpert
+    int nt_stores;            // 1: every payload store non-temporal (large outputs), 0: the mixed pattern
 };
 
 // ep_recv_count[r][el*W + s] = (end row of segment (el, s) of rank r) - (first row of rank r),
@@ -674,7 +726,7 @@ __device__ __forceinline__ void quant_store_wave(const DispatchArgs &a, int lane
             const int row = __builtin_amdgcn_readlane(my_row, k);
             if (row < 0) continue;
             uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + lane + 64 * j;
-            if ((j + k) & 1) store_stream(dst, q);   // see store_stream
+            if (a.nt_stores || ((j + k) & 1)) store_stream(dst, q);   // see store_stream
             else *dst = q;
         }
     }
@@ -742,7 +794,7 @@ __device__ __forceinline__ void quant_store_wave_static(const DispatchArgs &a, i
             const int row = __builtin_amdgcn_readlane(my_row, k);
             if (row < 0) continue;
             uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + oc;
-            if ((j + k) & 1) store_stream(dst, q);
+            if (a.nt_stores || ((j + k) & 1)) store_stream(dst, q);
             else *dst = q;
         }
     }
@@ -777,7 +829,7 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_copy_wave_kernel(Dispat
                 const int row = __builtin_amdgcn_readlane(my_row, k);
                 if (row < 0) continue;
                 uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.rowbytes) + c;
-                if ((j + k) & 1) store_stream(dst, v[j]);
+                if (a.nt_stores || ((j + k) & 1)) store_stream(dst, v[j]);
                 else *dst = v[j];
             }
         }
@@ -858,7 +910,7 @@ __device__ __forceinline__ void quant_store_wave_fp8(const DispatchArgs &a, int 
             const int row = __builtin_amdgcn_readlane(my_row, k);
             if (row < 0) continue;
             uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + c;
-            if ((j + k) & 1) store_stream(dst, q);   // see store_stream
+            if (a.nt_stores || ((j + k) & 1)) store_stream(dst, q);   // see store_stream
             else *dst = q;
             if ((lane & 7) == 0) a.dyn[(size_t)row * G + (c >> 3)] = scale;
         }
@@ -942,7 +994,7 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_static_xcd_kernel(Dispa
             const uint2 hi = static_u4<T>(v1, cb[2], cb[3]);
             uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + oc;
             const uint4 q = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            if (k & 1) store_stream(dst, q);
+            if (a.nt_stores || (k & 1)) store_stream(dst, q);
             else *dst = q;
         }
     }
@@ -1460,6 +1512,9 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         a.nsl = 1;
         a.qs = quant_scales;
         a.qkind = qkind;
+        // the mixed store pattern pays while the quantised rows fit in about the
+        // Infinity Cache; beyond that, non-temporal stores only
+        a.nt_stores = quant && (long long)N * K * h > kMixedStoreMaxBytes ? 1 : 0;
         if (mode == MOE_SCHED_TOKEN) {
             const size_t kdsm = (size_t)4 * K * sizeof(int);
             if (!quant) {
@@ -1470,8 +1525,10 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                 // Many tokens: one wavefront per token with mixed stores (a 529 MB bf16
                 // copy at 16 ranks x 256 tokens: 84 us against 106 us for the slice
                 // blocks). Few tokens: slice blocks, which keep more CUs busy (256
-                // tokens at h = 7168: 11 us against 20 us).
-                if (vec && K <= kQuantMaxK && Jc <= 16 && N >= kCopyWaveMinTokens) {
+                // tokens at h = 7168: 11 us against 20 us). Past about 650 MB of rows
+                // the slice blocks win again (16 x 1024 tokens: 378 us against 444 us).
+                if (vec && K <= kQuantMaxK && Jc <= 16 && N >= kCopyWaveMinTokens &&
+                    (long long)N * K * (long long)rowbytes <= kCopyWaveMaxBytes) {
                     const dim3 g((unsigned)((N + 3) / 4)), b(kQuantThreads);
                     launch_copy_wave(Jc, g, b, st, a);
                 } else {

@@ -175,11 +175,31 @@ EDGE = [
     wl.custom(2, 700, 1040, 3, 4, "bf16", "gauss_topk", name="copy_wave_h1040_j3_ragged_chunks"),
     wl.custom(2, 512, 8200, 2, 2, "fp16", "gauss_topk", name="copy_slices_h8200_past_16_pieces"),
     wl.custom(4, 256, 16, 65, 20, "int32", name="copy_slices_topk65"),
+    # 66 route chunks (the scan kernel), loaded 16 at a time with a partial last batch; ragged chunks of 44
+    wl.custom(33, 300, 64, 4, 2, "bf16", "zipf_topk", name="scan_66_chunks"),
+    wl.custom(33, 300, 64, 4, 2, "bf16", "gauss_topk", quant_mode=2, name="scan_66_chunks_q8"),
 ]
 
 
 @pytest.mark.parametrize("w", EDGE, ids=lambda w: w.name)
 def test_edge_shapes(w):
+    check(w)
+
+
+# outputs past the store-policy thresholds: quantised rows above 384 MiB store non-temporally only,
+# and a copy above 640 MiB of rows goes back to the (token, slice) blocks
+LARGE_OUTPUTS = [
+    wl.custom(16, 448, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2, index=4, name="int8_411MB_nt_stores"),
+    wl.custom(16, 448, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=3, index=4, name="fp8_411MB_nt_stores"),
+    wl.custom(16, 448, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=1, index=4, name="static_411MB_nt_stores"),
+    wl.custom(16, 448, 7168, 8, 16, "fp16", "zipf_topk", quant_mode=1, static_scales="column", index=4,
+              name="static_column_411MB_nt_stores"),
+    wl.custom(16, 384, 7168, 8, 16, "bf16", "gauss_topk", index=4, name="copy_705MB_slices"),
+]
+
+
+@pytest.mark.parametrize("w", LARGE_OUTPUTS, ids=lambda w: w.name)
+def test_large_outputs(w):
     check(w)
 
 
@@ -354,6 +374,11 @@ def test_empty_batch_writes_zero_counts():
     torch.cuda.synchronize()
     assert ex.shape == (0, h) and assist.shape == (0, 3) and dyn is None
     assert (to_np(erc) == 0).all() and erc.shape == (W, epr * W)
+    buf = moe.DispatchBuffers(W, 0, epr, h, K, torch.float16)
+    buf.ep_recv_count.fill_(7)                   # the counts are written, not left as they were
+    moe.dispatch_into(buf, x, ids)
+    torch.cuda.synchronize()
+    assert (to_np(buf.ep_recv_count) == 0).all()
     xo = moe.combine(ex, assist, erc, ids, torch.empty((0, K), dtype=torch.float32, device=DEV), W, epr)
     assert xo.shape == (0, h)
 
