@@ -23,6 +23,7 @@ Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import json
 import os
 import statistics
@@ -231,6 +232,8 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="w16_h7168_bf16_q8", choices=sorted(wl.BY_NAME))
+    ap.add_argument("--bs", type=int, default=None,
+                    help="tokens per rank for the main workload (same seed and recipe; default: the workload's)")
     ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf,w16_h7168_bf16_fp8g128,"
                                       "w16_h7168_bf16_static_q8",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
@@ -264,6 +267,8 @@ def main():
     flush = torch.empty(1 << 27, dtype=torch.int64, device="cuda").fill_(1)   # 1 GiB
 
     w = wl.BY_NAME[args.workload]
+    if args.bs is not None and args.bs != w.bs:
+        w = dataclasses.replace(w, bs=args.bs, name="%s_bs%d" % (w.name, args.bs))
     r = measure(w, args.steps, args.warmup, flush, torch, moe)
     disp_b, comb_b = algorithmic_bytes(w)
     ms = r["step"]
