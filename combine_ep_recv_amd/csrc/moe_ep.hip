@@ -400,7 +400,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 #pragma unroll
             for (int u = 0; u < kScanBatch; ++u) {
                 const int b = b0 + u;
-                if (b >= bq1) break;
+                if (b >= bq1) continue;
                 boff[(size_t)b * E + e] = eoff[e] + run;
                 run += c[u];
                 if ((b + 1) % nbs == 0)               // last chunk of source rank b / nbs
