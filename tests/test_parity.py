@@ -596,6 +596,37 @@ def test_random_configurations(w, kind):
         check_masked(w, kind)
 
 
+def random_large_case(i):
+    """Batches of 300 to 600 MB of rows, around the store-policy and copy-kernel thresholds (FP8 has its own
+    large case: its oracle is the slowest)."""
+    rng = np.random.default_rng(700 + i)
+    W = int(rng.choice([8, 16, 32]))
+    h = 16 * int(rng.integers(256, 513))                     # 4096 .. 8192
+    K = int(rng.choice([4, 6, 8]))
+    quant = int(rng.choice([0, 1, 2]))
+    dtype = "bf16" if quant else str(rng.choice(["fp16", "bf16"]))
+    target = float(rng.uniform(3e8, 6e8))                     # bytes of expand_x rows
+    bs = max(1, int(target / (W * K * h * (1 if quant else 2))))
+    epr = int(rng.choice([4, 8, 16]))
+    kind = str(rng.choice(["none", "pair"]))
+    w = wl.custom(W, bs, h, K, epr, dtype, str(rng.choice(["gauss_topk", "zipf_topk"])), quant_mode=quant,
+                  zero_experts=int(rng.integers(0, 2)), copy_experts=int(rng.integers(0, 2)) if dtype == "bf16" else 0,
+                  static_scales=str(rng.choice(["scalar", "column", "expert"])), index=500 + i,
+                  name="random_large%d" % i)
+    return w, kind
+
+
+RANDOM_LARGE_CASES = [random_large_case(i) for i in range(4)]
+
+
+@pytest.mark.parametrize("w,kind", RANDOM_LARGE_CASES, ids=lambda v: v if isinstance(v, str) else v.name)
+def test_random_large_configurations(w, kind):
+    if kind == "none":
+        check(w)
+    else:
+        check_masked(w, kind)
+
+
 # --------------------------------------------------------------------------
 # determinism (aclnnMoeDistributeDispatchV4 约束说明: deterministic by default)
 # --------------------------------------------------------------------------
