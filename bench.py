@@ -198,7 +198,7 @@ def counted_traffic(w):
     return rec["per_launch_bytes"]["moe_combine"]
 
 
-def cpu_baseline(w, reps=3):
+def cpu_baseline(w, reps=9):
     """The oracle as it stands (single-threaded C), timed on the host."""
     import oracle
 
