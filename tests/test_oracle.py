@@ -845,3 +845,27 @@ def test_static_codes_round_the_exact_product_once():
     d = oracle.dispatch(x, ids, n, 1, quant_mode=1, quant_scales=ce, bf16=True)
     for r, (i, j) in enumerate(sel):                                  # row r belongs to expert r
         assert (d["expand_x"][r] == np.rint(p64[i, j])).all(), (cs[i, j], xs[j])
+
+
+def test_identity_expert_dequantisation_matches_torch():
+    """The harness's identity expert, bf16(f32(q) * scale) with one scale per row (int8) or per 128-element
+    group (E4M3), against torch's int8 / float8_e4m3fn decoding, fp32 multiply and round-to-nearest-even
+    bfloat16 cast."""
+    import torch
+
+    rng = np.random.default_rng(41)
+    rows, h = 37, 300
+    q = rng.integers(-128, 128, size=(rows, h)).astype(np.int8)
+    sc = (rng.uniform(0.0, 1.0, rows) * 2.0 ** rng.integers(-30, 30, rows)).astype(np.float32)
+    sc[3] = 0.0
+    got = oracle.identity_expert(q, sc)
+    want = (torch.from_numpy(q).float() * torch.from_numpy(sc)[:, None]).bfloat16().view(torch.int16).numpy()
+    assert got.view(np.int16).tobytes() == want.tobytes()
+    codes = rng.integers(0, 256, size=(rows, h)).astype(np.uint8)
+    codes[(codes & 0x7f) == 0x7f] = 0                  # the two NaN codes are not produced by the quantiser
+    gs = (rng.uniform(0.0, 1.0, (rows, (h + 127) // 128)) * 2.0 ** rng.integers(-20, 20, (rows, 1))).astype(np.float32)
+    got = oracle.identity_expert(codes, gs)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).float()
+    full = torch.from_numpy(gs).repeat_interleave(128, dim=1)[:, :h]
+    want = (dec * full).bfloat16().view(torch.int16).numpy()
+    assert got.view(np.int16).tobytes() == want.tobytes()
