@@ -74,6 +74,7 @@ constexpr int kCopySlot = -2;             // slot of a copy-expert pair: the tok
 // shapes of the static quantisation coefficients: 1, h or E*h values
 constexpr int kStaticOne = 0, kStaticColumn = 1, kStaticExpert = 2;
 constexpr int kXcds = 8;                   // gfx950 XCDs; consecutive workgroups go to consecutive XCDs
+constexpr long long kStaticGroupBytes = 2ll << 20;   // token slices per XCD in one source group (L2 is 4 MB)
 
 // --------------------------------------------------------------------------
 // element conversions (gfx950: v_cvt_f32_f16 / v_cvt_f16_f32 / v_cvt_pk_bf16_f32,
@@ -163,6 +164,13 @@ __device__ int block_excl_scan(int v, int *tmp, int *total)
     *total = tmp[32];
     __syncthreads();
     return res;
+}
+
+__device__ __forceinline__ int wave_sum_i(int v)
+{
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, 64);
+    return v;
 }
 
 __device__ __forceinline__ float wave_max(float v)
@@ -919,7 +927,7 @@ __device__ __forceinline__ void quant_store_wave_fp8(const DispatchArgs &a, int 
 
 // The quantising scatter (aclnnMoeDistributeDispatchV4 quantMode 1, 2 and 3),
 // one wavefront per token. QM 1: the static codes above (one coefficient or one
-// per column; per-expert coefficients take the XCD kernel below); QM 2:
+// per column; per-expert coefficients take the source-group kernel below); QM 2:
 // scale = max|x| / 127 over the token (fp32, correctly rounded),
 // q = rint(x / scale) (0 for an all-zero token); QM 3: the per-group FP8 codes
 // above. Codes go to every destination row. Lane k loads pair k's id and
@@ -952,51 +960,72 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(Dispa
     }
 }
 
-// Static quantisation with one coefficient per expert and column, XCD-aware.
-// Workgroup b serves column slice b % kXcds (about h / kXcds columns) of the
-// tokens of tile b / kXcds, one wavefront per token and one 16-element piece
-// per lane, and writes that slice of all K rows. As workgroups are dealt
-// round-robin to the XCDs, each XCD reads only its slice of every expert's
-// coefficients (E*h*4 / kXcds bytes: 0.9 MB at 256 experts and h = 7168),
-// which stays in its L2; the whole table (7.3 MB) would not fit one XCD's 4 MB
-// L2. No token byte is read twice. assist_info and expand_scales are
-// written by the slice-0 wavefronts. Needs h <= 1024 * kXcds (64 pieces per slice).
-template <class T>
-__global__ __launch_bounds__(kQuantThreads) void scatter_static_xcd_kernel(DispatchArgs a)
+// Rows, assist_info, expand_scales (and, on the direct path, ep_recv_count)
+// without the payload: one wavefront per token. It runs before a payload pass
+// that walks expand_x in row order.
+__global__ __launch_bounds__(kQuantThreads) void dispatch_meta_kernel(DispatchArgs a)
 {
     const int lane = threadIdx.x & 63;
-    const int N = a.W * a.bs, K = a.K, noc = a.h / 16;
+    const int N = a.W * a.bs, K = a.K;
     if (a.direct) write_erc_direct(a, (size_t)blockIdx.x * kQuantThreads + threadIdx.x,
                                    (size_t)gridDim.x * kQuantThreads);
+    const int t = blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6);
+    if (t >= N) return;
+    const size_t pk = (size_t)t * K + (lane < K ? lane : 0);
+    lane_pair_row(a, t, lane, a.ids[pk], a.lr[pk], true);
+}
+
+// Static quantisation with one coefficient per expert and column, expert-major
+// in source-rank groups. Inside expert e's rows (rank r, local expert el) the
+// order is source rank, then token, so the rows of e from source ranks
+// [s0, s1) are one contiguous range whose bounds ep_recv_count gives.
+// Workgroup b serves column slice g = b % kXcds of the rows of expert
+// e = (b / kXcds) % E from source group grp (part of them when a group's rows
+// are many); workgroups run group by group. Per XCD the group's token slices
+// (kStaticGroupBytes: about 1170 tokens at h = 7168) and the coefficient slice
+// then fit in L2: each lane keeps its piece of expert e's coefficients in
+// registers and re-reads token pieces from L2. At 16 ranks x 256 bf16 tokens
+// the dispatch takes 66-68 us; token-major waves that read each row's
+// coefficients took 118 us, a hidden-dimension split without groups 85-95 us,
+// and expert-major without groups (tokens re-read from the Infinity Cache)
+// 92 us. Needs assist_info and ep_recv_count written (dispatch_meta_kernel)
+// and h <= 1024 * kXcds.
+template <class T>
+__global__ __launch_bounds__(kQuantThreads) void scatter_static_group_kernel(DispatchArgs a, int spg, int parts)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, noc = a.h / 16;
     const int g = (int)(blockIdx.x % kXcds);
+    const int q = (int)(blockIdx.x / kXcds), e = q % a.E, q2 = q / a.E, part = q2 % parts, grp = q2 / parts;
     const int per = (noc + kXcds - 1) / kXcds, oc = g * per + lane;
     const bool mine = lane < per && oc < noc;
-    const int wpb = kQuantThreads / 64, tiles = (N + wpb - 1) / wpb, tstep = (int)(gridDim.x / kXcds);
-    for (int tile = (int)(blockIdx.x / kXcds); tile < tiles; tile += tstep) {
-        const int t = tile * wpb + (threadIdx.x >> 6);
-        if (t >= N) continue;
-        const size_t pk = (size_t)t * K + (lane < K ? lane : 0);
-        const int e = a.ids[pk], l = a.lr[pk];
-        const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
-        uint4 v0 = make_uint4(0u, 0u, 0u, 0u), v1 = v0;
-        if (mine) {
-            v0 = src[2 * oc];
-            v1 = src[2 * oc + 1];
-        }
-        const int my_row = lane_pair_row(a, t, lane, e, l, g == 0);
-        for (int k = 0; k < K; ++k) {
-            const int row = __builtin_amdgcn_readlane(my_row, k);
-            if (row < 0 || !mine) continue;
-            // a row exists only for an id in [0, E), so the coefficient row is in bounds
-            const int ek = __builtin_amdgcn_readlane(e, k);
-            const float4 *cb = reinterpret_cast<const float4 *>(a.qs + (size_t)ek * a.h) + 4 * oc;
-            const uint2 lo = static_u4<T>(v0, cb[0], cb[1]);
-            const uint2 hi = static_u4<T>(v1, cb[2], cb[3]);
-            uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + oc;
-            const uint4 q = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            if (a.nt_stores || (k & 1)) store_stream(dst, q);
-            else *dst = q;
-        }
+    const int s0 = grp * spg, s1 = min(s0 + spg, a.W);
+    if (s0 >= s1) return;
+    const int r = e / a.epr, el = e - r * a.epr;
+    int b = 0;                                     // first row of rank r
+    for (int x = lane; x < r; x += 64) b += a.erc[(size_t)x * a.S + a.S - 1];
+    b = wave_sum_i(b);
+    const int i0 = el * a.W + s0, i1 = el * a.W + s1 - 1;
+    const int row0 = b + (i0 > 0 ? a.erc[(size_t)r * a.S + i0 - 1] : 0);
+    const int row1 = min(b + a.erc[(size_t)r * a.S + i1], a.R);
+    if (row0 >= row1) return;
+    float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0, c2 = c0, c3 = c0;
+    if (mine) {
+        const float4 *cb = reinterpret_cast<const float4 *>(a.qs + (size_t)e * a.h) + 4 * oc;
+        c0 = cb[0];
+        c1 = cb[1];
+        c2 = cb[2];
+        c3 = cb[3];
+    }
+    const int wstep = parts * (kQuantThreads / 64);
+    for (int row = row0 + part * (kQuantThreads / 64) + wave; row < row1; row += wstep) {
+        const int s = a.assist[(size_t)row * 3 + 0], tok = a.assist[(size_t)row * 3 + 1];
+        if ((unsigned)s >= (unsigned)a.W || (unsigned)tok >= (unsigned)a.bs || !mine) continue;
+        const uint4 *src = reinterpret_cast<const uint4 *>(a.x + ((size_t)s * a.bs + tok) * a.rowbytes);
+        const uint2 lo = static_u4<T>(src[2 * oc], c0, c1);
+        const uint2 hi = static_u4<T>(src[2 * oc + 1], c2, c3);
+        uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + oc;
+        const uint4 qv = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        store_stream(dst, qv);        // non-temporal only: 70 us against 78 us with the mix at 16 x 256 tokens
     }
 }
 
@@ -1366,7 +1395,8 @@ const char *moe_status_str(int status)
     case MOE_ERR_SHAPE: return "a size is out of range or a size product overflows";
     case MOE_ERR_DTYPE: return "unknown token dtype";
     case MOE_ERR_QUANT:
-        return "unknown quant mode, quantisation of int32 data, or a shape or coefficient count the quantiser does not take";
+        return "unknown quant mode, quantisation of int32 data, or a shape or coefficient count the quantiser "
+               "does not take";
     case MOE_ERR_WORKSPACE: return "workspace smaller than the queried size";
     case MOE_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case MOE_ERR_SCHEDULE: return "unknown schedule mode, or segment schedule too large for this shape";
@@ -1542,10 +1572,19 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                     const int J = (h / 16 + 63) / 64;
                     const dim3 g((unsigned)((N + 3) / 4)), b(kQuantThreads);
                     if (static_quant && qkind == kStaticExpert) {
-                        // kXcds workgroups (column slices) per tile of 4 tokens, at most 2^16 tiles at once
-                        const dim3 gx((unsigned)(std::min<long long>((N + 3) / 4, 1 << 16) * kXcds));
-                        if (dtype == MOE_FP16) hipLaunchKernelGGL(scatter_static_xcd_kernel<F16>, gx, b, 0, st, a);
-                        else hipLaunchKernelGGL(scatter_static_xcd_kernel<BF16>, gx, b, 0, st, a);
+                        hipLaunchKernelGGL(dispatch_meta_kernel, g, b, 0, st, a);
+                        // source ranks per group: the tokens whose column slices fill kStaticGroupBytes
+                        const long long slice = std::max<long long>(1, (long long)rowbytes / kXcds);
+                        const long long gtok = std::max<long long>(1, kStaticGroupBytes / slice);
+                        const int spg = (int)std::max<long long>(1, std::min<long long>(W, gtok / std::max(bs, 1)));
+                        const int ngrp = (W + spg - 1) / spg;
+                        const long long rows_per = std::max<long long>(1, N * K / ((long long)E * ngrp));
+                        const int parts = (int)std::min<long long>(64, std::max<long long>(1, rows_per / 32));
+                        const dim3 gx((unsigned)((long long)kXcds * E * parts * ngrp));
+                        if (dtype == MOE_FP16)
+                            hipLaunchKernelGGL(scatter_static_group_kernel<F16>, gx, b, 0, st, a, spg, parts);
+                        else
+                            hipLaunchKernelGGL(scatter_static_group_kernel<BF16>, gx, b, 0, st, a, spg, parts);
                     } else if (dtype == MOE_FP16) {
                         if (group_quant) launch_quant_wave<F16, MOE_QUANT_DYN_GROUP>(J, g, b, st, a);
                         else if (static_quant) launch_quant_wave<F16, MOE_QUANT_STATIC>(J, g, b, st, a);
