@@ -289,6 +289,11 @@ STATIC_QUANT = [
     wl.custom(4, 257, 8192, 2, 4, "bf16", "gauss_topk", quant_mode=1, name="h8192_j8_expert"),
     wl.custom(65, 2, 256, 2, 4, "fp16", "gauss_topk", quant_mode=1, name="65_chunks_scanned_offsets"),
     wl.custom(2, 2, 128, 64, 40, "bf16", "gauss_topk", quant_mode=1, name="topk64_expert"),
+    # per-expert coefficients run in groups of source ranks (about 1170 tokens at h = 7168): a ragged last group,
+    # several workgroups per (expert, group), and skewed expert loads
+    wl.custom(7, 300, 7168, 8, 4, "bf16", "gauss_topk", quant_mode=1, name="expert_ragged_groups"),
+    wl.custom(2, 2048, 7168, 2, 2, "fp16", "gauss_topk", quant_mode=1, name="expert_32_parts_per_group"),
+    wl.custom(8, 400, 4096, 8, 8, "bf16", "zipf_topk", quant_mode=1, name="expert_zipf_groups"),
 ]
 
 
