@@ -19,12 +19,15 @@
 //            (all rows of lower experts, plus this expert's rows from earlier
 //            chunks), so each block sums those few L2-resident words for its K
 //            pairs instead of waiting for a grid-wide scan. Rows are moved with
-//            128-bit loads/stores; dynamic quantisation (quantMode 2: per-token
-//            int8; quantMode 3: per-128-group FP8 E4M3) runs one wavefront per
-//            token (max by DPP shuffles, no block barrier).
+//            128-bit loads/stores; quantisation (quantMode 1: static int8 with
+//            one coefficient or one per column; quantMode 2: per-token int8;
+//            quantMode 3: per-128-group FP8 E4M3) runs one wavefront per token
+//            (max by DPP shuffles, no block barrier). Static int8 with one
+//            coefficient per expert and column instead writes the metadata
+//            first, then walks the rows expert-major in groups of source ranks.
 //            ep_recv_count (combine_doubleplane README 功能说明) is formed the
 //            same way by the first threads of the grid.
-//   scan     single block; only for very many chunks, and for the segment
+//   scan     single block; only for more than 64 chunks, and for the segment
 //            schedule (the README's 方案设计 large-segment predicate + plan).
 // Combine (README 功能说明, check formula; 实现逻辑 return path + weighted sum):
 //   slots    every expand_x row announces itself in its source's window: the
@@ -91,9 +94,10 @@ struct BF16 {
 };
 
 // Streaming (non-temporal) 16-byte accesses for data that is touched once. They
-// pay where reads dominate (the copy scatter, the combine's gather and its
-// x_out stores). The write-dominated quantising scatter splits its stores: a
-// checkerboard over (1 KiB chunk, copy) goes non-temporal, the rest plain. At
+// pay where reads dominate (the combine's gather and its x_out stores) and in
+// the (token, slice) copy. The write-dominated wavefront scatters (the
+// quantisers, the wavefront copy) split their stores: a checkerboard over
+// (1 KiB chunk, copy) goes non-temporal, the rest plain. At
 // 16 ranks x 256 tokens, h = 7168 (294 MB moved) that kernel takes 45 us,
 // against 51 us with plain stores only and 55 us with non-temporal ones only;
 // a pure 235 MB scattered-row write reaches ~6.3 TB/s plain and ~4.8 TB/s
