@@ -69,7 +69,8 @@ constexpr int kCopyWaveMinTokens = 1024;   // from here on the copy runs one wav
 constexpr long long kCopyWaveMaxBytes = 640ll << 20;    // ... up to this much expand_x
 constexpr long long kMixedStoreMaxBytes = 384ll << 20;  // quantised expand_x up to which stores are mixed
 constexpr int kQuantThreads = 256;         // one wavefront per token
-constexpr int kQuantMaxK = 64;             // wavefront-per-token quantiser handles topk <= 64
+constexpr int kQuantMaxK = 64;             // wavefront-per-token quantiser handles topk <= 64 ...
+constexpr int kQuantMaxH = 16384;          // ... and h <= 16384 (16 pieces of 16 elements per lane)
 constexpr int kBlockThreads = 256;         // generic block-per-token kernels
 constexpr int kGatherThreads = 128;        // combine: block = (token, 128-chunk slice)
 constexpr int kSlotThreads = 256;
@@ -993,15 +994,14 @@ __global__ __launch_bounds__(kQuantThreads) void dispatch_meta_kernel(DispatchAr
 // coefficients took 118 us, a hidden-dimension split without groups 85-95 us,
 // and expert-major without groups (tokens re-read from the Infinity Cache)
 // 92 us. Needs assist_info and ep_recv_count written (dispatch_meta_kernel)
-// and h <= 1024 * kXcds.
-template <class T>
+// and h <= 2048 * kXcds (PL = 1 up to 1024 * kXcds).
+template <class T, int PL>
 __global__ __launch_bounds__(kQuantThreads) void scatter_static_group_kernel(DispatchArgs a, int spg, int parts)
 {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, noc = a.h / 16;
     const int g = (int)(blockIdx.x % kXcds);
     const int q = (int)(blockIdx.x / kXcds), e = q % a.E, q2 = q / a.E, part = q2 % parts, grp = q2 / parts;
-    const int per = (noc + kXcds - 1) / kXcds, oc = g * per + lane;
-    const bool mine = lane < per && oc < noc;
+    const int per = (noc + kXcds - 1) / kXcds;
     const int s0 = grp * spg, s1 = min(s0 + spg, a.W);
     if (s0 >= s1) return;
     const int r = e / a.epr, el = e - r * a.epr;
@@ -1012,24 +1012,34 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_static_group_kernel(Dis
     const int row0 = b + (i0 > 0 ? a.erc[(size_t)r * a.S + i0 - 1] : 0);
     const int row1 = min(b + a.erc[(size_t)r * a.S + i1], a.R);
     if (row0 >= row1) return;
-    float4 c0 = make_float4(0.f, 0.f, 0.f, 0.f), c1 = c0, c2 = c0, c3 = c0;
-    if (mine) {
-        const float4 *cb = reinterpret_cast<const float4 *>(a.qs + (size_t)e * a.h) + 4 * oc;
-        c0 = cb[0];
-        c1 = cb[1];
-        c2 = cb[2];
-        c3 = cb[3];
+    // PL 16-element pieces per lane: piece p of the slice is lane + 64 * p
+    int oc[PL];
+    bool mine[PL];
+    float4 c[PL][4];
+#pragma unroll
+    for (int p = 0; p < PL; ++p) {
+        oc[p] = g * per + lane + 64 * p;
+        mine[p] = lane + 64 * p < per && oc[p] < noc;
+        const float4 *cb = reinterpret_cast<const float4 *>(a.qs + (size_t)e * a.h) + 4 * min(oc[p], noc - 1);
+        c[p][0] = cb[0];
+        c[p][1] = cb[1];
+        c[p][2] = cb[2];
+        c[p][3] = cb[3];
     }
     const int wstep = parts * (kQuantThreads / 64);
     for (int row = row0 + part * (kQuantThreads / 64) + wave; row < row1; row += wstep) {
         const int s = a.assist[(size_t)row * 3 + 0], tok = a.assist[(size_t)row * 3 + 1];
-        if ((unsigned)s >= (unsigned)a.W || (unsigned)tok >= (unsigned)a.bs || !mine) continue;
+        if ((unsigned)s >= (unsigned)a.W || (unsigned)tok >= (unsigned)a.bs) continue;
         const uint4 *src = reinterpret_cast<const uint4 *>(a.x + ((size_t)s * a.bs + tok) * a.rowbytes);
-        const uint2 lo = static_u4<T>(src[2 * oc], c0, c1);
-        const uint2 hi = static_u4<T>(src[2 * oc + 1], c2, c3);
-        uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + oc;
-        const uint4 qv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        store_stream(dst, qv);        // non-temporal only: 70 us against 78 us with the mix at 16 x 256 tokens
+#pragma unroll
+        for (int p = 0; p < PL; ++p) {
+            if (!mine[p]) continue;
+            const uint2 lo = static_u4<T>(src[2 * oc[p]], c[p][0], c[p][1]);
+            const uint2 hi = static_u4<T>(src[2 * oc[p] + 1], c[p][2], c[p][3]);
+            uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + oc[p];
+            // non-temporal only: 70 us against 78 us with the mixed stores at 16 x 256 tokens
+            store_stream(dst, make_uint4(lo.x, lo.y, hi.x, hi.y));
+        }
     }
 }
 
@@ -1384,7 +1394,9 @@ void launch_quant_wave(int J, dim3 g, dim3 b, hipStream_t st, const DispatchArgs
     else if (J <= 2) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 2, QM>), g, b, 0, st, a);
     else if (J <= 4) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 4, QM>), g, b, 0, st, a);
     else if (J <= 7) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 7, QM>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 8, QM>), g, b, 0, st, a);
+    else if (J <= 8) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 8, QM>), g, b, 0, st, a);
+    else if (J <= 12) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 12, QM>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 16, QM>), g, b, 0, st, a);
 }
 
 }  // namespace
@@ -1420,7 +1432,7 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
     if (quant_mode != MOE_QUANT_NONE && dtype == MOE_INT32) return MOE_ERR_QUANT;
     // the static and per-group quantisers are the wavefront-per-token kernel only
     if ((quant_mode == MOE_QUANT_STATIC || quant_mode == MOE_QUANT_DYN_GROUP) &&
-        (h % 16 != 0 || h > 1024 * 8 || topk > kQuantMaxK))
+        (h % 16 != 0 || h > kQuantMaxH || topk > kQuantMaxK))
         return MOE_ERR_QUANT;
     *bytes = dispatch_layout(ep_world, bs, experts_per_rank, topk).total;
     return MOE_OK;
@@ -1485,7 +1497,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         return MOE_ERR_ALIGN;
     // per-token int8 takes the wavefront kernel when it can, a block kernel
     // otherwise; per-group FP8 needs the wavefront kernel's 16-byte rows
-    const bool wave = quant && h % 16 == 0 && h <= 1024 * 8 && K <= kQuantMaxK && aligned(x, 16) &&
+    const bool wave = quant && h % 16 == 0 && h <= kQuantMaxH && K <= kQuantMaxK && aligned(x, 16) &&
                       aligned(expand_x, 16);
     if ((group_quant || static_quant) && !wave && N > 0) return MOE_ERR_ALIGN;
 
@@ -1585,10 +1597,14 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                         const long long rows_per = std::max<long long>(1, N * K / ((long long)E * ngrp));
                         const int parts = (int)std::min<long long>(64, std::max<long long>(1, rows_per / 32));
                         const dim3 gx((unsigned)((long long)kXcds * E * parts * ngrp));
-                        if (dtype == MOE_FP16)
-                            hipLaunchKernelGGL(scatter_static_group_kernel<F16>, gx, b, 0, st, a, spg, parts);
-                        else
-                            hipLaunchKernelGGL(scatter_static_group_kernel<BF16>, gx, b, 0, st, a, spg, parts);
+                        const bool two = h > 1024 * kXcds;     // two 16-element pieces per lane
+                        if (dtype == MOE_FP16) {
+                            if (two) hipLaunchKernelGGL((scatter_static_group_kernel<F16, 2>), gx, b, 0, st, a, spg, parts);
+                            else hipLaunchKernelGGL((scatter_static_group_kernel<F16, 1>), gx, b, 0, st, a, spg, parts);
+                        } else {
+                            if (two) hipLaunchKernelGGL((scatter_static_group_kernel<BF16, 2>), gx, b, 0, st, a, spg, parts);
+                            else hipLaunchKernelGGL((scatter_static_group_kernel<BF16, 1>), gx, b, 0, st, a, spg, parts);
+                        }
                     } else if (dtype == MOE_FP16) {
                         if (group_quant) launch_quant_wave<F16, MOE_QUANT_DYN_GROUP>(J, g, b, st, a);
                         else if (static_quant) launch_quant_wave<F16, MOE_QUANT_STATIC>(J, g, b, st, a);

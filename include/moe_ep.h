@@ -76,7 +76,7 @@ enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
  *      gives the static coefficient input (one coefficient, a smoothing vector
  *      shared by the experts, per-expert coefficients fused with smoothing);
  *      its formula is garbled, and multiplying is the reading taken. No
- *      dynamic_scales. Needs h % 16 == 0, h <= 8192, topk <= 64, 16-byte
+ *      dynamic_scales. Needs h % 16 == 0, h <= 16384, topk <= 64, 16-byte
  *      aligned x, expand_x and (for h or E*h values) quant_scales, and the
  *      token schedule.
  *  MOE_QUANT_DYN_TOKEN: int8 codes rint(x / s), s = max|x| / 127 over the token;
@@ -87,7 +87,7 @@ enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
  *      kept; an all-zero group has s = 0 and codes 0. dynamic_scales is fp32
  *      [ROWS, ceil(h/128)]. (The pages list the mode; its output types and group
  *      size are garbled, and these are the readings taken.) Needs h % 16 == 0,
- *      h <= 8192, topk <= 64, 16-byte aligned x and expand_x, and the token
+ *      h <= 16384, topk <= 64, 16-byte aligned x and expand_x, and the token
  *      schedule. */
 enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_STATIC = 1, MOE_QUANT_DYN_TOKEN = 2, MOE_QUANT_DYN_GROUP = 3 };
 

@@ -68,14 +68,16 @@ def _ws(*args):
     ((2, 4, 2, 16, 1, 1, 1), OK),             # static int8
     ((2, 4, 2, 16, 1, 0, 1), QUANT),          # int32 cannot be quantised
     ((2, 4, 2, 24, 1, 2, 1), QUANT),          # static needs h % 16 == 0
-    ((2, 4, 2, 8208, 1, 1, 1), QUANT),        # ... and h <= 8192
+    ((2, 4, 2, 16400, 1, 1, 1), QUANT),       # ... and h <= 16384
+    ((2, 4, 2, 16384, 1, 1, 1), OK),
     ((8, 4, 16, 64, 65, 1, 1), QUANT),        # ... and topk <= 64
     ((2, 4, 2, 16, 1, 1, -1), QUANT),
     ((2, 4, 2, 16, 1, 0, 2), QUANT),          # int32 cannot be quantised
     ((16, 256, 16, 7168, 8, 2, 3), OK),       # per-group FP8
     ((2, 4, 2, 16, 1, 0, 3), QUANT),
     ((2, 4, 2, 7176, 1, 2, 3), QUANT),        # per-group needs h % 16 == 0
-    ((2, 4, 2, 8208, 1, 2, 3), QUANT),        # ... and h <= 8192
+    ((2, 4, 2, 16400, 1, 2, 3), QUANT),       # ... and h <= 16384
+    ((2, 4, 2, 16384, 1, 2, 3), OK),
     ((8, 4, 16, 64, 65, 2, 3), QUANT),        # ... and topk <= 64
     ((2, 4, 2, 16, 1, 1, 4), QUANT),
 ])

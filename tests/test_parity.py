@@ -243,6 +243,10 @@ GROUP_QUANT = [
     wl.custom(4, 257, 8192, 2, 4, "bf16", "gauss_topk", quant_mode=3, name="h8192_j8"),
     wl.custom(65, 2, 256, 2, 4, "fp16", "gauss_topk", quant_mode=3, name="65_chunks_scanned_offsets"),
     wl.custom(2, 2, 128, 64, 40, "bf16", "gauss_topk", quant_mode=3, name="topk64"),
+    wl.custom(2, 40, 12288, 4, 4, "bf16", "gauss_topk", quant_mode=3, name="h12288_j12"),
+    wl.custom(2, 40, 16384, 4, 4, "fp16", "zipf_topk", quant_mode=3, name="h16384_j16"),
+    wl.custom(2, 40, 16384, 4, 4, "bf16", "gauss_topk", quant_mode=2, name="h16384_int8_j16"),
+    wl.custom(2, 40, 16400, 4, 4, "bf16", "gauss_topk", quant_mode=2, name="h16400_int8_block_kernel"),
 ]
 
 
@@ -294,6 +298,11 @@ STATIC_QUANT = [
     wl.custom(7, 300, 7168, 8, 4, "bf16", "gauss_topk", quant_mode=1, name="expert_ragged_groups"),
     wl.custom(2, 2048, 7168, 2, 2, "fp16", "gauss_topk", quant_mode=1, name="expert_32_parts_per_group"),
     wl.custom(8, 400, 4096, 8, 8, "bf16", "zipf_topk", quant_mode=1, name="expert_zipf_groups"),
+    # rows past 8192 elements: 12 and 16 pieces per lane, two pieces per lane in the source-group kernel
+    wl.custom(2, 40, 12288, 4, 4, "bf16", "gauss_topk", quant_mode=1, name="h12288_expert"),
+    wl.custom(2, 40, 16384, 4, 4, "fp16", "gauss_topk", quant_mode=1, name="h16384_expert"),
+    wl.custom(2, 40, 16384, 4, 4, "bf16", "gauss_topk", quant_mode=1, static_scales="column", name="h16384_column"),
+    wl.custom(2, 40, 8208, 4, 4, "bf16", "gauss_topk", quant_mode=1, name="h8208_expert_ragged_slices"),
 ]
 
 
