@@ -54,7 +54,9 @@ enum moe_status {
                               static or per-group quantiser does not take, or a static
                               coefficient count other than 1, h or E*h */
     MOE_ERR_WORKSPACE = 5, /* workspace smaller than the queried size */
-    MOE_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch */
+    MOE_ERR_LAUNCH = 6,    /* the HIP runtime refused a launch (a call reads and clears HIP's
+                              last-error state before its launches, so an earlier error that
+                              the caller has not collected is not reported as this one) */
     MOE_ERR_SCHEDULE = 7,  /* unknown schedule mode, or the segment schedule (or the
                               segment_is_large output) at W*S above 11264 */
     MOE_ERR_ALIGN = 8,     /* a pointer is not aligned to its element size (16 bytes for
