@@ -234,6 +234,8 @@ def main():
     ap.add_argument("--workload", default="w16_h7168_bf16_q8", choices=sorted(wl.BY_NAME))
     ap.add_argument("--bs", type=int, default=None,
                     help="tokens per rank for the main workload (same seed and recipe; default: the workload's)")
+    ap.add_argument("--h", type=int, default=None,
+                    help="hidden size for the main workload (same seed and recipe; default: the workload's)")
     ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf,w16_h7168_bf16_fp8g128,"
                                       "w16_h7168_bf16_static_q8",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
@@ -269,6 +271,8 @@ def main():
     w = wl.BY_NAME[args.workload]
     if args.bs is not None and args.bs != w.bs:
         w = dataclasses.replace(w, bs=args.bs, name="%s_bs%d" % (w.name, args.bs))
+    if args.h is not None and args.h != w.h:
+        w = dataclasses.replace(w, h=args.h, name="%s_h%d" % (w.name, args.h))
     r = measure(w, args.steps, args.warmup, flush, torch, moe)
     disp_b, comb_b = algorithmic_bytes(w)
     ms = r["step"]
