@@ -60,7 +60,8 @@ enum moe_status {
     MOE_ERR_SCHEDULE = 7,  /* unknown schedule mode, or the segment schedule (or the
                               segment_is_large output) at W*S above 11264 */
     MOE_ERR_ALIGN = 8,     /* a pointer is not aligned to its element size (16 bytes for
-                              the workspace) */
+                              the workspace, and for the inputs moe_quant lists under
+                              quant modes 1 and 3) */
     MOE_ERR_MASK = 9       /* unknown mask kind, or a mask pointer that does not match it */
 };
 
