@@ -165,6 +165,10 @@ EDGE = [
     wl.custom(2, 5, 16, 4, 2, "int32", name="topk_equals_experts"),
     wl.custom(4, 1, 24, 1, 1, "fp16", "gauss_topk", name="topk1_bs1"),
     wl.custom(3, 70, 7176, 5, 3, "bf16", "zipf_topk", name="bf16_h7176_ragged_tiles"),
+    # h = 1, the smallest hidden size: scalar copy, scalar gather and the block quantiser on one element
+    wl.custom(2, 4, 1, 2, 2, "int32", name="int32_h1"),
+    wl.custom(3, 5, 1, 2, 2, "fp16", "gauss_topk", name="fp16_h1"),
+    wl.custom(2, 7, 1, 3, 2, "bf16", "gauss_topk", quant_mode=2, name="bf16_q_h1_block_quant"),
     wl.custom(2, 3, 16, 70, 40, "int32", name="topk70_copy_lds_path"),
     wl.custom(2, 2, 32, 66, 40, "bf16", "gauss_topk", quant_mode=2, name="topk66_quant_block_path"),
     # the copy with one wavefront per token (from 1024 tokens): rows of 1, 14 and 16 pieces per lane, a row
