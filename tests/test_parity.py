@@ -302,6 +302,9 @@ STATIC_QUANT = [
     wl.custom(7, 300, 7168, 8, 4, "bf16", "gauss_topk", quant_mode=1, name="expert_ragged_groups"),
     wl.custom(2, 2048, 7168, 2, 2, "fp16", "gauss_topk", quant_mode=1, name="expert_32_parts_per_group"),
     wl.custom(8, 400, 4096, 8, 8, "bf16", "zipf_topk", quant_mode=1, name="expert_zipf_groups"),
+    # over 64 rows per wavefront (64 parts of 4 wavefronts per expert): the rows' assist_info entries are loaded
+    # 64 at a time, one per lane, so the wavefronts of the busier expert take a second batch
+    wl.custom(2, 20000, 16, 1, 1, "bf16", "zipf_topk", quant_mode=1, name="expert_over_64_rows_per_wave"),
     # rows past 8192 elements: 12 and 16 pieces per lane, two pieces per lane in the source-group kernel
     wl.custom(2, 40, 12288, 4, 4, "bf16", "gauss_topk", quant_mode=1, name="h12288_expert"),
     wl.custom(2, 40, 16384, 4, 4, "fp16", "gauss_topk", quant_mode=1, name="h16384_expert"),
