@@ -41,6 +41,7 @@
 #include <hip/hip_runtime.h>
 
 #include <stddef.h>
+#include <limits.h>
 #include <stdint.h>
 
 #include <algorithm>
@@ -60,6 +61,7 @@ constexpr int kDirectMaxChunks = 64;       // chunk count up to which blocks sum
 constexpr int kSegLdsMax = 11264;          // W*S limit for the LDS-resident segment counts
 constexpr long long kMaxTokens = (1ll << 24) - 1;   // N blocks of 256 threads stay below 2^32 items
 constexpr int kPlanRows = 8;               // rows per segment-schedule work item
+static_assert(kPlanRows <= 64, "a plan item's rows are held one per lane");
 constexpr int kSegGrid = 4096;             // blocks of the segment-major payload pass
 constexpr int64_t kReadmeLargeBytes = 2 * 1024 * 1024;
 
@@ -169,6 +171,30 @@ __device__ int block_excl_scan(int v, int *tmp, int *total)
     *total = tmp[32];
     __syncthreads();
     return res;
+}
+
+// Inclusive scan of one int per thread over the block, through buf
+// (blockDim.x ints of LDS): the max over this and lower threads, or (REV) the
+// min over this and higher threads. Shuffles inside each wavefront, then the
+// wavefront totals; buf holds every thread's result on return. Every thread
+// of the block calls it.
+template <bool REV>
+__device__ int block_incl_minmax(int v, int *buf)
+{
+    const int t = threadIdx.x, lane = t & 63, wid = t >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int y = REV ? __shfl_down(v, d, 64) : __shfl_up(v, d, 64);
+        if (REV ? lane + d < 64 : lane >= d) v = REV ? min(v, y) : max(v, y);
+    }
+    if (lane == (REV ? 0 : 63)) buf[wid] = v;        // the wavefront's total
+    __syncthreads();
+    for (int w = 0; w < nw; ++w)
+        if (REV ? w > wid : w < wid) v = REV ? min(v, buf[w]) : max(v, buf[w]);
+    __syncthreads();
+    buf[t] = v;
+    __syncthreads();
+    return v;
 }
 
 __device__ __forceinline__ int wave_sum_i(int v)
@@ -312,39 +338,6 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
 // scan (many chunks, or the segment schedule)
 // --------------------------------------------------------------------------
 
-// Walk rank r's segments in order and emit the work items of the segment
-// schedule: a large segment is cut into items of its own of at most `rows`
-// rows; runs of other segments are packed into items of exactly `rows` rows
-// (the last one shorter). Returns the number of items; writes them when
-// `plan` is non-null. The count pass and the write pass share this code.
-__device__ int plan_rank(const int32_t *segc, const uint8_t *flag, int S, int row0, int rows, int2 *plan)
-{
-    int n = 0, row = row0, pack_start = row0, run = 0;
-    for (int i = 0; i < S; ++i) {
-        const int c = segc[i];
-        if (flag[i]) {
-            if (run) { if (plan) plan[n] = make_int2(pack_start, row); ++n; run = 0; }
-            for (int q = 0; q < c; q += rows) {
-                if (plan) plan[n] = make_int2(row + q, row + min(c, q + rows));
-                ++n;
-            }
-            row += c;
-            pack_start = row;
-        } else {
-            run += c;
-            row += c;
-            while (run >= rows) {
-                if (plan) plan[n] = make_int2(pack_start, pack_start + rows);
-                ++n;
-                pack_start += rows;
-                run -= rows;
-            }
-        }
-    }
-    if (run) { if (plan) plan[n] = make_int2(pack_start, row); ++n; }
-    return n;
-}
-
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t *__restrict__ pc, const int32_t *__restrict__ pci, int W, int epr, int nbs, int h,
     int elem_bytes, int32_t *__restrict__ boff, int32_t *__restrict__ erc, int want_seg, long long large_bytes,
@@ -426,35 +419,106 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     if (!want_seg) return;
     __syncthreads();
     // segment counts: differences of consecutive inclusive counts within a rank
+    const int G = W * S;
     int32_t *segc = seg_lds;
-    uint8_t *flag = reinterpret_cast<uint8_t *>(seg_lds + (size_t)W * S);
-    for (int i = tid; i < W * S; i += blockDim.x) segc[i] = erc[i] - (i % S > 0 ? erc[i - 1] : 0);
+    uint8_t *flag = reinterpret_cast<uint8_t *>(seg_lds + (size_t)G);
+    for (int i = tid; i < G; i += blockDim.x) segc[i] = erc[i] - (i % S > 0 ? erc[i - 1] : 0);
+    // rows each rank receives from the other ranks (part[] is free from here on)
+    for (int r = tid; r < W; r += blockDim.x) part[r] = 0;
+    __syncthreads();
+    for (int i = tid; i < G; i += blockDim.x)
+        if ((i % S) % W != i / S && segc[i]) atomicAdd(&part[i / S], segc[i]);
     __syncthreads();
 
-    // large-segment predicate (combine_doubleplane README 方案设计), one rank per thread
-    if (tid < W) {
-        const int r = tid;
-        long long remote = 0;
-        for (int i = 0; i < S; ++i)
-            if (i % W != r) remote += segc[r * S + i];
-        const long long num = remote * h * elem_bytes;
-        const long long den = (long long)(W - 1 > 1 ? W - 1 : 1) * epr;
-        for (int i = 0; i < S; ++i) {
-            const long long c = segc[r * S + i];
-            const long long bytes = c * h * elem_bytes;
-            const int large = (i % W != r) && c > 0 && bytes >= large_bytes && bytes * den > num;
-            flag[r * S + i] = (uint8_t)large;
-            if (seg_flags) seg_flags[(size_t)r * S + i] = large;
-        }
+    // large-segment predicate (combine_doubleplane README 方案设计), one segment
+    // per thread: segment i of rank r comes from source rank i % W
+    const long long den = (long long)(W - 1 > 1 ? W - 1 : 1) * epr;
+    for (int g = tid; g < G; g += blockDim.x) {
+        const int r = g / S, i = g % S;
+        const long long c = segc[g], bytes = c * h * elem_bytes;
+        const long long num = (long long)part[r] * h * elem_bytes;
+        const int large = (i % W != r) && c > 0 && bytes >= large_bytes && bytes * den > num;
+        flag[g] = (uint8_t)large;
+        if (seg_flags) seg_flags[g] = large;
     }
     if (!plan) return;
     __syncthreads();
 
-    int items = 0;
-    if (tid < W) items = plan_rank(segc + tid * S, flag + tid * S, S, eoff[tid * epr], kPlanRows, nullptr);
+    // The plan. Every rank's rows fall into blocks: a block opens at the rank's
+    // first segment, at a large segment and at the segment after one, so a
+    // large segment is a block of its own and the others pack into blocks
+    // between them. Each block is cut into kPlanRows-row items from its start
+    // (the last one shorter). Items are numbered by start row, as walking each
+    // rank's segments in turn would emit them. Thread tid owns the segments
+    // [g0, g1); the start and the end of each segment's block come from
+    // block-wide max and min scans over the openers' row offsets, which grow
+    // with the segment index.
+    constexpr int PT = (kSegLdsMax + kScanThreads - 1) / kScanThreads;
+    const int per = (G + (int)blockDim.x - 1) / (int)blockDim.x;     // <= PT: G <= kSegLdsMax
+    const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
+    auto opener = [&](int g) { return g % S == 0 || flag[g] != 0 || flag[g - 1] != 0; };
+    int csum = 0;
+    for (int g = g0; g < g1; ++g) csum += segc[g];
+    int total_rows;
+    const int off0 = block_excl_scan(csum, tmp, &total_rows);        // row offset of segment g0
+    int o[PT];
+    int last = -1, first = INT_MAX;
+    {
+        int run = off0;
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const int g = g0 + k;
+            o[k] = run;
+            if (g < g1) {
+                if (opener(g)) {
+                    first = min(first, run);
+                    last = run;
+                }
+                run += segc[g];
+            }
+        }
+    }
+    block_incl_minmax<false>(last, part);
+    const int carry_f = tid > 0 ? part[tid - 1] : -1;                // last opener before g0
+    __syncthreads();
+    block_incl_minmax<true>(first, part);
+    const int carry_b = tid + 1 < (int)blockDim.x ? part[tid + 1] : INT_MAX;   // first opener after g1 - 1
+    int eb[PT];
+    {
+        int nxt = carry_b == INT_MAX ? total_rows : carry_b;
+#pragma unroll
+        for (int k = PT - 1; k >= 0; --k) {
+            const int g = g0 + k;
+            eb[k] = nxt;
+            if (g < g1 && opener(g)) nxt = o[k];
+        }
+    }
+    int sb[PT], nmine = 0;
+    {
+        int cur = carry_f;
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const int g = g0 + k;
+            if (g < g1 && opener(g)) cur = o[k];
+            sb[k] = cur;
+            if (g < g1) {
+                const int lo = o[k] - cur, hi = lo + segc[g];
+                nmine += (hi + kPlanRows - 1) / kPlanRows - (lo + kPlanRows - 1) / kPlanRows;
+            }
+        }
+    }
     int nitems;
-    const int first = block_excl_scan(items, tmp, &nitems);
-    if (tid < W) plan_rank(segc + tid * S, flag + tid * S, S, eoff[tid * epr], kPlanRows, plan + first);
+    int idx = block_excl_scan(nmine, tmp, &nitems);
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        const int g = g0 + k;
+        if (g >= g1) continue;
+        const int lo = o[k] - sb[k], hi = lo + segc[g];
+        for (int m = (lo + kPlanRows - 1) / kPlanRows; m < (hi + kPlanRows - 1) / kPlanRows; ++m) {
+            const int st = sb[k] + kPlanRows * m;
+            plan[idx++] = make_int2(st, min(st + kPlanRows, eb[k]));
+        }
+    }
     if (tid == 0) *nplan = nitems;
 }
 
@@ -1189,6 +1253,103 @@ __global__ __launch_bounds__(kBlockThreads) void segment_payload_kernel(Dispatch
     }
 }
 
+// Segment schedule, pass 2 on the wavefront path (rows of at most 16 KiB in
+// 16-byte pieces, or per-token int8 with h % 16 == 0 and h <= 16384): a
+// workgroup takes plan items, its lanes load the item's source tokens from
+// assist_info at once (one row per lane), and wavefront w fills rows lo + w,
+// lo + w + 4, ... with the token-major kernels' per-wavefront code (the
+// same stores, and for int8 the same codes and scale). 16 ranks x 256 bf16
+// tokens, int8: 132 us per dispatch (292 us with a workgroup walking its
+// item's rows one at a time), against 50 us for the token-major schedule,
+// which reads each token once instead of once per destination row.
+__device__ __forceinline__ int item_row_token(const DispatchArgs &a, int lo, int hi, int lane)
+{
+    int t = -1;
+    if (lane < hi - lo) {
+        const int row = lo + lane;
+        const int s = a.assist[(size_t)row * 3 + 0], tok = a.assist[(size_t)row * 3 + 1];
+        if ((unsigned)s < (unsigned)a.W && (unsigned)tok < (unsigned)a.bs) t = s * a.bs + tok;
+    }
+    return t;
+}
+
+template <int J>
+__global__ __launch_bounds__(kQuantThreads) void segment_copy_wave_kernel(DispatchArgs a)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n16 = (int)(a.rowbytes / 16), n = *a.nplan;
+    for (int item = blockIdx.x; item < n; item += gridDim.x) {
+        const int2 it = a.plan[item];
+        const int lo = max(it.x, 0), hi = min(it.y, a.R);
+        const int my_t = item_row_token(a, lo, hi, lane);
+        for (int i = wave; i < min(hi - lo, 64); i += kQuantThreads / 64) {
+            const int t = __builtin_amdgcn_readlane(my_t, i);
+            if (t < 0) continue;
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
+            uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)(lo + i) * a.rowbytes);
+            uint4 v[J];
+#pragma unroll
+            for (int j = 0; j < J; ++j) v[j] = src[min(lane + 64 * j, n16 - 1)];
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int c = lane + 64 * j;
+                if (c >= n16) continue;
+                if (j & 1) store_stream(dst + c, v[j]);    // the token-major copy's mix
+                else dst[c] = v[j];
+            }
+        }
+    }
+}
+
+template <class T, int J>
+__global__ __launch_bounds__(kQuantThreads) void segment_quant_wave_kernel(DispatchArgs a)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int noc = a.h / 16, n = *a.nplan;
+    DispatchArgs one = a;          // one destination row per token visit
+    one.K = 1;
+    for (int item = blockIdx.x; item < n; item += gridDim.x) {
+        const int2 it = a.plan[item];
+        const int lo = max(it.x, 0), hi = min(it.y, a.R);
+        const int my_t = item_row_token(a, lo, hi, lane);
+        for (int i = wave; i < min(hi - lo, 64); i += kQuantThreads / 64) {
+            const int t = __builtin_amdgcn_readlane(my_t, i);
+            if (t < 0) continue;
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
+            uint4 v[J][2];
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int oc = min(lane + 64 * j, noc - 1);
+                v[j][0] = src[2 * oc];
+                v[j][1] = src[2 * oc + 1];
+            }
+            quant_store_wave<T, J>(one, lane, v, lane == 0 ? lo + i : -1);
+        }
+    }
+}
+
+void launch_segment_copy_wave(int J, dim3 g, dim3 b, hipStream_t st, const DispatchArgs &a)
+{
+    if (J <= 1) hipLaunchKernelGGL((segment_copy_wave_kernel<1>), g, b, 0, st, a);
+    else if (J <= 2) hipLaunchKernelGGL((segment_copy_wave_kernel<2>), g, b, 0, st, a);
+    else if (J <= 4) hipLaunchKernelGGL((segment_copy_wave_kernel<4>), g, b, 0, st, a);
+    else if (J <= 8) hipLaunchKernelGGL((segment_copy_wave_kernel<8>), g, b, 0, st, a);
+    else if (J <= 14) hipLaunchKernelGGL((segment_copy_wave_kernel<14>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((segment_copy_wave_kernel<16>), g, b, 0, st, a);
+}
+
+template <class T>
+void launch_segment_quant_wave(int J, dim3 g, dim3 b, hipStream_t st, const DispatchArgs &a)
+{
+    if (J <= 1) hipLaunchKernelGGL((segment_quant_wave_kernel<T, 1>), g, b, 0, st, a);
+    else if (J <= 2) hipLaunchKernelGGL((segment_quant_wave_kernel<T, 2>), g, b, 0, st, a);
+    else if (J <= 4) hipLaunchKernelGGL((segment_quant_wave_kernel<T, 4>), g, b, 0, st, a);
+    else if (J <= 7) hipLaunchKernelGGL((segment_quant_wave_kernel<T, 7>), g, b, 0, st, a);
+    else if (J <= 8) hipLaunchKernelGGL((segment_quant_wave_kernel<T, 8>), g, b, 0, st, a);
+    else if (J <= 12) hipLaunchKernelGGL((segment_quant_wave_kernel<T, 12>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((segment_quant_wave_kernel<T, 16>), g, b, 0, st, a);
+}
+
 // --------------------------------------------------------------------------
 // combine
 // --------------------------------------------------------------------------
@@ -1667,7 +1828,14 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
             const int qm = !quant ? 0 : (dtype == MOE_FP16 ? 1 : 2);
             const bool vec = quant ? (h % 8 == 0 && aligned(x, 16) && aligned(expand_x, 8))
                                    : (rowbytes % 16 == 0 && aligned(x, 16) && aligned(expand_x, 16));
-            if (qm == 0) {
+            const int Jc = (int)((rowbytes / 16 + 63) / 64), Jq = (h / 16 + 63) / 64;
+            const dim3 gw(kSegGrid), bw(kQuantThreads);
+            if (qm == 0 && vec && Jc <= 16) {
+                launch_segment_copy_wave(Jc, gw, bw, st, a);
+            } else if (qm != 0 && wave) {
+                if (qm == 1) launch_segment_quant_wave<F16>(Jq, gw, bw, st, a);
+                else launch_segment_quant_wave<BF16>(Jq, gw, bw, st, a);
+            } else if (qm == 0) {
                 if (vec) hipLaunchKernelGGL((segment_payload_kernel<0, true>), g, b, 0, st, a);
                 else hipLaunchKernelGGL((segment_payload_kernel<0, false>), g, b, 0, st, a);
             } else if (qm == 1) {

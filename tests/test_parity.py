@@ -410,7 +410,15 @@ def test_empty_batch_writes_zero_counts():
 
 SCHED_CASES = [wl.WORKLOADS[1], wl.WORKLOADS[2], wl.WORKLOADS[3], wl.WORKLOADS[4],
                wl.custom(4, 192, 7168, 4, 2, "fp16", "zipf_topk", name="zipf_bs192_literal_rule_fires"),
-               wl.custom(3, 70, 7176, 5, 3, "bf16", "zipf_topk", quant_mode=2, name="bf16_q_ragged")]
+               wl.custom(3, 70, 7176, 5, 3, "bf16", "zipf_topk", quant_mode=2, name="bf16_q_ragged"),
+               # the segment payload's wavefront kernels at 16 pieces per lane and a ragged 2-piece row, the
+               # block kernel for rows that are not 16-byte pieces, and 104 ranks (10,816 segments: the most,
+               # 11, per thread of the plan's scans)
+               wl.custom(4, 100, 8192, 4, 4, "fp16", "zipf_topk", name="copy_h8192_j16"),
+               wl.custom(2, 40, 16384, 4, 4, "bf16", "gauss_topk", quant_mode=2, name="q8_h16384_j16"),
+               wl.custom(3, 300, 1040, 4, 3, "fp16", "zipf_topk", quant_mode=2, name="q8_h1040_j2"),
+               wl.custom(3, 20, 13, 3, 2, "int32", name="int32_h13_block_path"),
+               wl.custom(104, 3, 16, 2, 1, "bf16", "zipf_topk", name="w104_11_segments_per_thread")]
 
 
 @pytest.mark.parametrize("w", SCHED_CASES, ids=lambda w: w.name)
