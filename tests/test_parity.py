@@ -8,6 +8,8 @@ equality. Combine runs on the GPU's own dispatch outputs passed through the
 identity expert (for int8 rows: bf16(f32(q) * scale)), the oracle's on the
 oracle's; the two never exchange data.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -623,6 +625,32 @@ def test_random_configurations(w, kind):
         check(w)
     else:
         check_masked(w, kind)
+
+
+def random_segment_case(i):
+    """A random configuration through the segment schedule at a random large-segment threshold (the schedule
+    takes copies and per-token int8; its segment counts stay within the scan's LDS)."""
+    w, kind = random_case(i)
+    if w.quant_mode in (1, 3):
+        w = dataclasses.replace(w, quant_mode=2, copy_experts=w.copy_experts if w.dtype == "bf16" else 0)
+    while w.ep_world * w.ep_world * w.experts_per_rank > 11264:
+        w = dataclasses.replace(w, experts_per_rank=max(1, w.experts_per_rank // 2),
+                                topk=min(w.topk, w.ep_world * max(1, w.experts_per_rank // 2)))
+    T = int(np.random.default_rng(i).choice([0, 4096, 65536, -1]))
+    return w, kind, T
+
+
+RANDOM_SEGMENT_CASES = [random_segment_case(i) for i in range(100, 112)]
+
+
+@pytest.mark.parametrize("w,kind,T", RANDOM_SEGMENT_CASES,
+                         ids=lambda v: v if isinstance(v, (str, int)) else v.name)
+def test_random_configurations_segment_schedule(w, kind, T):
+    sched = moe.MoeSchedule(mode=moe.MOE_SCHED_SEGMENT, large_segment_bytes=T)
+    if kind == "none":
+        check(w, schedule=sched)
+    else:
+        check_masked(w, kind, schedule=sched)
 
 
 def random_large_case(i):
