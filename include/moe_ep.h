@@ -135,7 +135,10 @@ typedef struct moe_special_experts {
  *  MOE_SCHED_SEGMENT: workgroups walk expand_x in destination order; a segment
  *                     selected by the large-segment predicate gets whole
  *                     workgroups of its own (split by rows), the other
- *                     segments are packed together. */
+ *                     segments are packed together. Each token row is then
+ *                     read once per destination row rather than once, so
+ *                     this mode is slower (16 ranks x 256 bf16 tokens of
+ *                     7168, int8: 132 us per dispatch against 50 us). */
 enum moe_sched_mode { MOE_SCHED_TOKEN = 0, MOE_SCHED_SEGMENT = 1 };
 
 /* Optional dispatch schedule (host struct; pass NULL for the defaults).
