@@ -69,7 +69,8 @@ constexpr int kCopyThreads = 128;          // token-major copy: block = (token, 
 constexpr int kCopyUnroll = 2;             // 16-byte chunks per thread per slice
 constexpr int kCopyWaveMinTokens = 1024;   // from here on the copy runs one wavefront per token ...
 constexpr long long kCopyWaveMaxBytes = 640ll << 20;    // ... up to this much expand_x
-constexpr long long kMixedStoreMaxBytes = 384ll << 20;  // quantised expand_x up to which stores are mixed
+constexpr long long kMixedStoreMaxBytes = 320ll << 20;  // rows written up to which half the stores are plain
+constexpr long long kQuarterPlainMaxBytes = 512ll << 20; // ... a quarter of them; none beyond
 constexpr int kQuantThreads = 256;         // one wavefront per token
 constexpr int kQuantMaxK = 64;             // wavefront-per-token quantiser handles topk <= 64 ...
 constexpr int kQuantMaxH = 16384;          // ... and h <= 16384 (16 pieces of 16 elements per lane)
@@ -104,11 +105,20 @@ struct BF16 {
 // 16 ranks x 256 tokens, h = 7168 (294 MB moved) that kernel takes 45 us,
 // against 51 us with plain stores only and 55 us with non-temporal ones only;
 // a pure 235 MB scattered-row write reaches ~6.3 TB/s plain and ~4.8 TB/s
-// non-temporal. The mix is no slower on small outputs either. It holds while
-// the rows written fit in about the Infinity Cache (256 MB): at 16 ranks x
-// 512 tokens (470 MB of int8 rows) non-temporal stores alone take 111 us
-// against 126 us mixed, at 16 x 1024 tokens 199 us against 258 us, so larger
-// outputs store non-temporally only (nt_stores).
+// non-temporal. The mix is no slower on small outputs either. As the rows
+// written outgrow the Infinity Cache (256 MB) the plain share must shrink
+// (store_mix). The int8 dispatch at 16 ranks, h = 7168 takes:
+// - 384 tokens per rank (352 MB of rows): 76 us with a quarter of the stores
+//   plain, 82 us with half, 84 us with none;
+// - 512 tokens (470 MB): 102 / 125 / 112 us;
+// - 576 tokens (528 MB): 117 / 142 / 118 us;
+// - 640 tokens (587 MB): 134 us with a quarter, 130 us with none;
+// - 1024 tokens: 252 us with a quarter, 198 us with none.
+// So the quantisers keep half of their stores plain up to 320 MiB of rows, a
+// quarter up to 512 MiB, and none beyond. The wavefront copy (bf16 rows twice
+// as long) is best with half plain up to its 640 MiB limit: at 256 and 320
+// tokens per rank (470 and 587 MB) it takes 85 and 116 us that way, against
+// 91 and 139 us with a quarter or none.
 typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void store_stream(uint4 *p, uint4 v)
 {
@@ -547,8 +557,15 @@ struct DispatchArgs {
     long long rowbytes;       // bytes of one x row
     const float *qs;          // static quantisation coefficients
     int qkind;                // their shape: kStaticOne, kStaticColumn or kStaticExpert
-    int nt_stores;            // 1: every payload store non-temporal (large outputs), 0: the mixed pattern
+    int store_mix;            // wavefront scatters: 0 half the stores plain, 1 a quarter, 2 none
 };
+
+// Whether piece j of copy k of a wavefront scatter is stored non-temporally
+// (see store_stream): every other piece, every piece but one in four, or all.
+__device__ __forceinline__ bool stream_piece(const DispatchArgs &a, int j, int k)
+{
+    return a.store_mix == 2 || ((j + k) & (a.store_mix == 1 ? 3 : 1)) != 0;
+}
 
 // ep_recv_count[r][el*W + s] = (end row of segment (el, s) of rank r) - (first row of rank r),
 // from the chunk prefixes: first row of (chunk b, expert e) = sum_{b'<b} pci + sum_{b'>=b} pc.
@@ -803,7 +820,7 @@ __device__ __forceinline__ void quant_store_wave(const DispatchArgs &a, int lane
             const int row = __builtin_amdgcn_readlane(my_row, k);
             if (row < 0) continue;
             uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + lane + 64 * j;
-            if (a.nt_stores || ((j + k) & 1)) store_stream(dst, q);   // see store_stream
+            if (stream_piece(a, j, k)) store_stream(dst, q);   // see store_stream
             else *dst = q;
         }
     }
@@ -871,7 +888,7 @@ __device__ __forceinline__ void quant_store_wave_static(const DispatchArgs &a, i
             const int row = __builtin_amdgcn_readlane(my_row, k);
             if (row < 0) continue;
             uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + oc;
-            if (a.nt_stores || ((j + k) & 1)) store_stream(dst, q);
+            if (stream_piece(a, j, k)) store_stream(dst, q);
             else *dst = q;
         }
     }
@@ -906,7 +923,7 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_copy_wave_kernel(Dispat
                 const int row = __builtin_amdgcn_readlane(my_row, k);
                 if (row < 0) continue;
                 uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.rowbytes) + c;
-                if (a.nt_stores || ((j + k) & 1)) store_stream(dst, v[j]);
+                if (stream_piece(a, j, k)) store_stream(dst, v[j]);
                 else *dst = v[j];
             }
         }
@@ -989,7 +1006,7 @@ __device__ __forceinline__ void quant_store_wave_fp8(const DispatchArgs &a, int 
             const int row = __builtin_amdgcn_readlane(my_row, k);
             if (row < 0) continue;
             uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + c;
-            if (a.nt_stores || ((j + k) & 1)) store_stream(dst, q);   // see store_stream
+            if (stream_piece(a, j, k)) store_stream(dst, q);   // see store_stream
             else *dst = q;
         }
     }
@@ -1752,9 +1769,11 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         a.nsl = 1;
         a.qs = quant_scales;
         a.qkind = qkind;
-        // the mixed store pattern pays while the quantised rows fit in about the
-        // Infinity Cache; beyond that, non-temporal stores only
-        a.nt_stores = quant && (long long)N * K * h > kMixedStoreMaxBytes ? 1 : 0;
+        // the plain share of the quantisers' stores shrinks as the rows written
+        // outgrow the Infinity Cache; the wavefront copy keeps half of its
+        // stores plain up to its own limit (see store_stream)
+        const long long qbytes = N * K * (long long)h;
+        a.store_mix = !quant || qbytes <= kMixedStoreMaxBytes ? 0 : (qbytes <= kQuarterPlainMaxBytes ? 1 : 2);
         if (mode == MOE_SCHED_TOKEN) {
             const size_t kdsm = (size_t)4 * K * sizeof(int);
             if (!quant) {

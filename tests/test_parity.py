@@ -192,14 +192,15 @@ def test_edge_shapes(w):
     check(w)
 
 
-# outputs past the store-policy thresholds: quantised rows above 384 MiB store non-temporally only,
-# and a copy above 640 MiB of rows goes back to the (token, slice) blocks
+# outputs past the store-policy thresholds: quantised rows above 320 MiB keep a quarter of their stores plain,
+# above 512 MiB none, and a copy above 640 MiB of rows goes back to the (token, slice) blocks
 LARGE_OUTPUTS = [
-    wl.custom(16, 448, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2, index=4, name="int8_411MB_nt_stores"),
-    wl.custom(16, 448, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=3, index=4, name="fp8_411MB_nt_stores"),
+    wl.custom(16, 448, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2, index=4, name="int8_411MB_quarter_plain"),
+    wl.custom(16, 448, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=3, index=4, name="fp8_411MB_quarter_plain"),
     wl.custom(16, 448, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=1, index=4, name="static_411MB_nt_stores"),
     wl.custom(16, 448, 7168, 8, 16, "fp16", "zipf_topk", quant_mode=1, static_scales="column", index=4,
-              name="static_column_411MB_nt_stores"),
+              name="static_column_411MB_quarter_plain"),
+    wl.custom(16, 600, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2, index=4, name="int8_551MB_nt_stores"),
     wl.custom(16, 384, 7168, 8, 16, "bf16", "gauss_topk", index=4, name="copy_705MB_slices"),
 ]
 
