@@ -41,25 +41,42 @@ METRIC = "dispatch+combine effective HBM GB/s (and % roofline), tokens/s at h=71
 HBM_PEAK_GBPS = 8000.0
 
 
-def algorithmic_bytes(w: wl.Workload):
+def algorithmic_bytes(w: wl.Workload, inp=None):
     """Bytes the method must move, each array once.
 
-    dispatch: read x once + ids; write expand_x, assist_info, ep_recv_count
-              (+ dynamic_scales when quantising dynamically; + the static
-              coefficients read once for quantMode 1)
+    dispatch: read x once (tokens with a row) + ids (+ the mask); write
+              expand_x, assist_info, ep_recv_count (+ dynamic_scales when
+              quantising dynamically; + the static coefficients read once for
+              quantMode 1)
     combine:  read expand_x (expert output), scales, assist_info,
-              ep_recv_count, ids; write x_out
+              ep_recv_count, ids (+ the mask, + the token of each copy-expert
+              pair); write x_out
+
+    Only pairs that get a row move a row: with a token mask or special experts
+    the counts come from the inputs (made here when not given).
     """
     N, K, h, rows = w.num_tokens, w.topk, w.h, w.rows
     sx = 4 if w.dtype == "int32" else 2
     s_exp = 1 if w.quant_mode else sx             # int8 or E4M3 codes
     s_y = 2 if w.quant_mode else sx               # identity-expert output for quantised rows is bf16
     erc = w.ep_world * w.num_experts * 4
+    toks, copies, mask_b = N, 0, 0
+    if w.mask != "none" or w.zero_experts or w.copy_experts:
+        inp = inp if inp is not None else wl.make_inputs(w)
+        ids, E = inp["ids"], w.num_experts
+        act = np.ones((N, K), bool)
+        if "mask" in inp:
+            m = inp["mask"].astype(bool)
+            act = np.broadcast_to(m[:, None], (N, K)) if m.ndim == 1 else m
+            mask_b = inp["mask"].size
+        real = act & (ids < E)
+        rows, toks = int(real.sum()), int(real.any(axis=1).sum())
+        copies = int((act & (ids >= E + w.zero_experts) & (ids < E + w.zero_experts + w.copy_experts)).sum())
     n_scales = {2: rows, 3: rows * ((h + 127) // 128)}.get(w.quant_mode, 0)   # fp32 dynamic scales
     if w.quant_mode == 1:                         # fp32 static coefficients, read
         n_scales = {"scalar": 1, "column": h, "expert": w.num_experts * h}[w.static_scales]
-    disp = N * h * sx + N * K * 4 + rows * h * s_exp + rows * 12 + erc + n_scales * 4
-    comb = rows * h * s_y + N * K * 4 + rows * 12 + erc + N * K * 4 + N * h * s_y
+    disp = toks * h * sx + N * K * 4 + mask_b + rows * h * s_exp + rows * 12 + erc + n_scales * 4
+    comb = rows * h * s_y + copies * h * s_y + N * K * 4 + mask_b + rows * 12 + erc + N * K * 4 + N * h * s_y
     return disp, comb
 
 
@@ -89,7 +106,11 @@ def measure(w, steps, warmup, flush, torch, moe):
     W, epr = w.ep_world, w.experts_per_rank
     qs = torch.from_numpy(inp["quant_scales"]).cuda() if w.quant_mode == 1 else None
     buf = moe.DispatchBuffers(W, w.bs, epr, w.h, w.topk, tdt, w.quant_mode, "cuda")
-    moe.dispatch_into(buf, x, ids, quant_scales=qs)
+    # token mask and special experts (the copy experts' tokens: x itself, bf16 like the expert output)
+    extra = dict(x_active_mask=torch.from_numpy(inp["mask"]).cuda() if "mask" in inp else None,
+                 zero_experts=w.zero_experts, copy_experts=w.copy_experts)
+    ori = dict(ori_x=x) if w.copy_experts else {}
+    moe.dispatch_into(buf, x, ids, quant_scales=qs, **extra)
     if w.quant_mode == 1:                      # static codes: the expert sees bf16(q)
         y = buf.expand_x.to(torch.bfloat16)
     elif w.quant_mode == 2:
@@ -104,8 +125,8 @@ def measure(w, steps, warmup, flush, torch, moe):
     cws = moe.combine_workspace(W, w.bs, epr, w.h, w.topk, y.dtype)
 
     def step():
-        moe.dispatch_into(buf, x, ids, quant_scales=qs)
-        moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws)
+        moe.dispatch_into(buf, x, ids, quant_scales=qs, **extra)
+        moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws, **extra, **ori)
 
     def b2b(fn, n):
         """mean ms of n back-to-back calls between two events (one event bubble amortised over n)"""
@@ -124,8 +145,9 @@ def measure(w, steps, warmup, flush, torch, moe):
     # the timed region: exactly `steps` steps, synchronised on both sides
     ms_step = b2b(step, steps)
     # each half alone, back to back (the combine is the dominant launch sequence)
-    ms_disp = b2b(lambda: moe.dispatch_into(buf, x, ids, quant_scales=qs), steps)
-    ms_comb = b2b(lambda: moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws),
+    ms_disp = b2b(lambda: moe.dispatch_into(buf, x, ids, quant_scales=qs, **extra), steps)
+    ms_comb = b2b(lambda: moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws,
+                                           **extra, **ori),
                   steps)
     # cold: L2 and the Infinity Cache evicted (untimed 1 GiB read) before every step; each such
     # sample also holds one event-to-kernel bubble
@@ -238,7 +260,8 @@ def main():
     ap.add_argument("--h", type=int, default=None,
                     help="hidden size for the main workload (same seed and recipe; default: the workload's)")
     ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf,w16_h7168_bf16_fp8g128,"
-                                      "w16_h7168_bf16_static_q8",
+                                      "w16_h7168_bf16_static_q8,w16_h7168_bf16_q8_pair_mask,"
+                                      "w16_h7168_bf16_q8_zero_copy",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -299,6 +322,11 @@ def main():
                       "graph_ms_per_step": round(ra["graph"], 5),
                       "algorithmic_bytes": da + ca,
                       "quant": quant_label(wa)}
+        if wa.mask != "none":
+            also[name]["mask"] = {"pair": "per pair, 3/4 active",
+                                  "token_prefix": "per token, each rank's first 3/4"}[wa.mask]
+        if wa.zero_experts or wa.copy_experts:
+            also[name]["special_experts"] = {"zero": wa.zero_experts, "copy": wa.copy_experts}
 
     line = {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

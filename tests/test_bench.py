@@ -26,6 +26,35 @@ def test_algorithmic_bytes_of_the_workloads():
     assert c1 == c and d1 == 294273024 - 32768 * 4 + 256 * 7168 * 4
 
 
+def test_masked_and_special_bytes_count_only_rows_that_move():
+    # brute force over the pairs: a row moves for an active pair of a real expert; a copy-expert pair makes the
+    # combine read its token; x is read for tokens with a row; the mask is read by both calls
+    import numpy as np
+    for name in ("w16_h7168_bf16_q8_pair_mask", "w16_h7168_bf16_q8_zero_copy"):
+        w = wl.BY_NAME[name]
+        inp = wl.make_inputs(w)
+        N, K, h, E = w.num_tokens, w.topk, w.h, w.num_experts
+        rows = copies = toks = 0
+        for t in range(N):
+            has = False
+            for k in range(K):
+                on = True if "mask" not in inp else bool(inp["mask"][t, k] if inp["mask"].ndim == 2
+                                                           else inp["mask"][t])
+                e = int(inp["ids"][t, k])
+                if on and e < E:
+                    rows += 1
+                    has = True
+                if on and E + w.zero_experts <= e < E + w.zero_experts + w.copy_experts:
+                    copies += 1
+            toks += has
+        mb = inp["mask"].size if "mask" in inp else 0
+        erc = w.ep_world * E * 4
+        want_d = toks * h * 2 + N * K * 4 + mb + rows * h + rows * 12 + erc + rows * 4
+        want_c = rows * h * 2 + copies * h * 2 + N * K * 4 + mb + rows * 12 + erc + N * K * 4 + N * h * 2
+        assert bench.algorithmic_bytes(w, inp) == (want_d, want_c), name
+        assert 0 < rows < w.rows
+
+
 def test_code_hash_ignores_comments_and_spacing_only(tmp_path):
     a = tmp_path / "a.hip"
     a.write_text('const char *s = "x // y /* z */";  // note\nint f() { return 1; } /* block\ncomment */\n')

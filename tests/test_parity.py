@@ -151,6 +151,16 @@ def test_page_workloads_full_size(w):
     check(w)
 
 
+@pytest.mark.parametrize("name", ["w16_h7168_bf16_q8_pair_mask", "w16_h7168_bf16_q8_zero_copy"])
+def test_benchmarked_mask_and_special_expert_workloads_full_size(name):
+    """The bench's masked and zero/copy-expert lines, at their full size and with their own inputs."""
+    w = wl.BY_NAME[name]
+    if w.mask == "none":
+        check(w)
+    else:
+        check_masked(w, "workload")
+
+
 # --------------------------------------------------------------------------
 # edge cases
 # --------------------------------------------------------------------------
@@ -511,7 +521,7 @@ def _make_mask(kind, w, seed):
 
 def check_masked(w, kind, seed=1, schedule=None):
     inp = wl.make_inputs(w)
-    mask = _make_mask(kind, w, seed)
+    mask = inp["mask"].astype(bool) if kind == "workload" else _make_mask(kind, w, seed)
     print("parity case %s mask=%s seed=%d W=%d bs=%d h=%d K=%d %s q%d sched=%s" % (
         w.name, kind, seed, w.ep_world, w.bs, w.h, w.topk, w.dtype, w.quant_mode,
         None if schedule is None else schedule.mode), flush=True)

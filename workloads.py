@@ -64,6 +64,8 @@ class Workload:
     zero_experts: int = 0   # special experts after the E real ones: ids E .. E+zero-1
     copy_experts: int = 0   # then E+zero .. E+zero+copy-1
     static_scales: str = "expert"   # quantMode 1 coefficients: "scalar" | "column" | "expert"
+    mask: str = "none"      # token mask: "none" | "token_prefix" (each rank's first 3/4 of its tokens)
+                            # | "pair" (each pair active with probability 3/4)
 
     @property
     def num_experts(self) -> int:
@@ -91,6 +93,12 @@ EXTRA_WORKLOADS = [
     Workload("w16_h7168_bf16_fp8g128", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=3),
     # and with static int8 quantisation (quantMode 1), one coefficient per expert and column
     Workload("w16_h7168_bf16_static_q8", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=1),
+    # per-token int8 with a per-pair token mask (3/4 of the pairs active)
+    Workload("w16_h7168_bf16_q8_pair_mask", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2,
+             mask="pair"),
+    # per-token int8 with 16 zero and 16 copy experts beside the 256 real ones (the router picks among 288)
+    Workload("w16_h7168_bf16_q8_zero_copy", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2,
+             zero_experts=16, copy_experts=16),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
@@ -150,6 +158,8 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
       ids      [N, K]  int32
       scales   [N, K]  int32 for int32 tokens (uniform in [1, 4]), else fp32
       quant_scales     fp32 quantMode 1 coefficients (only for quantMode 1)
+      mask     uint8 [N] or [N, K] token mask (only when the workload has one;
+               drawn after everything else, so the other inputs do not change)
     """
     rng = np.random.default_rng(1234 + w.index if seed is None else seed)
     N, h = w.num_tokens, w.h
@@ -167,4 +177,13 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
     out = dict(x=x, ids=ids, scales=scales)
     if w.quant_mode == 1:
         out["quant_scales"] = static_scales(w)
+    if w.mask == "token_prefix":
+        m = np.zeros(N, np.uint8)
+        for s in range(w.ep_world):
+            m[s * w.bs: s * w.bs + (3 * w.bs) // 4] = 1
+        out["mask"] = m
+    elif w.mask == "pair":
+        out["mask"] = (rng.random((N, w.topk)) < 0.75).astype(np.uint8)
+    elif w.mask != "none":
+        raise ValueError(w.mask)
     return out
