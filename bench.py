@@ -100,7 +100,7 @@ def quant_label(w):
     return lab
 
 
-def measure(w, steps, warmup, flush, torch, moe):
+def measure(w, steps, warmup, flush, torch, moe, schedule=None):
     inp, x, ids, sc = _device_inputs(w, torch)
     tdt = {"int32": torch.int32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
     W, epr = w.ep_world, w.experts_per_rank
@@ -110,7 +110,8 @@ def measure(w, steps, warmup, flush, torch, moe):
     extra = dict(x_active_mask=torch.from_numpy(inp["mask"]).cuda() if "mask" in inp else None,
                  zero_experts=w.zero_experts, copy_experts=w.copy_experts)
     ori = dict(ori_x=x) if w.copy_experts else {}
-    moe.dispatch_into(buf, x, ids, quant_scales=qs, **extra)
+    dx = dict(extra, schedule=schedule) if schedule is not None else extra     # dispatch only
+    moe.dispatch_into(buf, x, ids, quant_scales=qs, **dx)
     if w.quant_mode == 1:                      # static codes: the expert sees bf16(q)
         y = buf.expand_x.to(torch.bfloat16)
     elif w.quant_mode == 2:
@@ -125,7 +126,7 @@ def measure(w, steps, warmup, flush, torch, moe):
     cws = moe.combine_workspace(W, w.bs, epr, w.h, w.topk, y.dtype)
 
     def step():
-        moe.dispatch_into(buf, x, ids, quant_scales=qs, **extra)
+        moe.dispatch_into(buf, x, ids, quant_scales=qs, **dx)
         moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws, **extra, **ori)
 
     def b2b(fn, n):
@@ -145,7 +146,7 @@ def measure(w, steps, warmup, flush, torch, moe):
     # the timed region: exactly `steps` steps, synchronised on both sides
     ms_step = b2b(step, steps)
     # each half alone, back to back (the combine is the dominant launch sequence)
-    ms_disp = b2b(lambda: moe.dispatch_into(buf, x, ids, quant_scales=qs, **extra), steps)
+    ms_disp = b2b(lambda: moe.dispatch_into(buf, x, ids, quant_scales=qs, **dx), steps)
     ms_comb = b2b(lambda: moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws,
                                            **extra, **ori),
                   steps)
@@ -257,6 +258,9 @@ def main():
     ap.add_argument("--workload", default="w16_h7168_bf16_q8", choices=sorted(wl.BY_NAME))
     ap.add_argument("--bs", type=int, default=None,
                     help="tokens per rank for the main workload (same seed and recipe; default: the workload's)")
+    ap.add_argument("--schedule", choices=["token", "segment"], default="token",
+                    help="dispatch schedule of the main workload: token-major (default) or the segment-major "
+                         "large-segment schedule (copies and per-token int8 only)")
     ap.add_argument("--h", type=int, default=None,
                     help="hidden size for the main workload (same seed and recipe; default: the workload's)")
     ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf,w16_h7168_bf16_fp8g128,"
@@ -297,7 +301,14 @@ def main():
         w = dataclasses.replace(w, bs=args.bs, name="%s_bs%d" % (w.name, args.bs))
     if args.h is not None and args.h != w.h:
         w = dataclasses.replace(w, h=args.h, name="%s_h%d" % (w.name, args.h))
-    r = measure(w, args.steps, args.warmup, flush, torch, moe)
+    sched = None
+    if args.schedule == "segment":
+        if w.quant_mode in (1, 3):
+            print("the segment schedule takes copies and per-token int8 only", file=sys.stderr)
+            sys.exit(2)
+        sched = moe.MoeSchedule(mode=moe.MOE_SCHED_SEGMENT, large_segment_bytes=-1)
+        w = dataclasses.replace(w, name="%s_segment_schedule" % w.name)
+    r = measure(w, args.steps, args.warmup, flush, torch, moe, sched)
     disp_b, comb_b = algorithmic_bytes(w)
     ms = r["step"]
     gbps = (disp_b + comb_b) / (ms * 1e-3) / 1e9
