@@ -935,8 +935,10 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_copy_wave_kernel(Dispat
 // one-step corrected |x| * inv) is clamped to 448 and converted, with x's sign,
 // by v_cvt_pk_fp8_f32 (OCP E4M3 on gfx950, round to nearest even). Two checks
 // make the codes those of the definition: for every 16-bit (x, group max) pair,
-// the corrected quotient rounded to E4M3 equals the E4M3 rounding of the exact
-// quotient (checked exhaustively on the CPU); and on gfx950 the instruction
+// the corrected quotient rounded to E4M3 equals the E4M3 rounding of the
+// correctly rounded binary32 quotient (checked exhaustively on the CPU; where
+// that quotient lands on an E4M3 midpoint it is that binary32 value, not the
+// exact rational one, whose tie decides); and on gfx950 the instruction
 // equals that rounding for every binary32 |v| <= 448 (all 2,277,507,074 such
 // values compared).
 template <class T, bool FAST>

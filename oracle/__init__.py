@@ -42,32 +42,37 @@ _lib = None
 def _load():
     global _lib
     if _lib is None:
-        lib = ctypes.CDLL(build())
-        P, I, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
-        lib.oracle_dispatch.argtypes = [P, P, P, I, I, I, I, I, I, I, P, LL, P, I, I, I, P, P, P, P, P]
-        lib.oracle_dispatch.restype = I
-        lib.oracle_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, I, I, P, P]
-        lib.oracle_combine.restype = I
-        lib.oracle_large_segments.argtypes = [P, I, I, I, I, LL, P]
-        lib.oracle_large_segments.restype = I
-        lib.oracle_identity_expert_dequant.argtypes = [P, P, LL, I, P]
-        lib.oracle_identity_expert_dequant.restype = None
-        lib.oracle_identity_expert_dequant_fp8.argtypes = [P, P, LL, I, P]
-        lib.oracle_identity_expert_dequant_fp8.restype = None
-        lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
-        lib.oracle_e4m3_to_f32.restype = ctypes.c_float
-        lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
-        lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
-        lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
-        lib.oracle_f16_to_f32.restype = ctypes.c_float
-        lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
-        lib.oracle_f32_to_f16.restype = ctypes.c_uint16
-        lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
-        lib.oracle_bf16_to_f32.restype = ctypes.c_float
-        lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
-        lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
-        _lib = lib
+        _lib = bind(ctypes.CDLL(build()))
     return _lib
+
+
+def bind(lib):
+    """Declare the C signatures on a loaded oracle library (the tests also bind
+    copies of it built from altered sources, to show that the pins catch them)."""
+    P, I, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
+    lib.oracle_dispatch.argtypes = [P, P, P, I, I, I, I, I, I, I, P, LL, P, I, I, I, P, P, P, P, P]
+    lib.oracle_dispatch.restype = I
+    lib.oracle_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, I, I, P, P]
+    lib.oracle_combine.restype = I
+    lib.oracle_large_segments.argtypes = [P, I, I, I, I, LL, P]
+    lib.oracle_large_segments.restype = I
+    lib.oracle_identity_expert_dequant.argtypes = [P, P, LL, I, P]
+    lib.oracle_identity_expert_dequant.restype = None
+    lib.oracle_identity_expert_dequant_fp8.argtypes = [P, P, LL, I, P]
+    lib.oracle_identity_expert_dequant_fp8.restype = None
+    lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
+    lib.oracle_e4m3_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_e4m3.restype = ctypes.c_uint8
+    lib.oracle_f16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_f16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_f16.restype = ctypes.c_uint16
+    lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f32.restype = ctypes.c_float
+    lib.oracle_f32_to_bf16.argtypes = [ctypes.c_float]
+    lib.oracle_f32_to_bf16.restype = ctypes.c_uint16
+    return lib
 
 
 class OracleError(RuntimeError):
