@@ -1,20 +1,22 @@
 #!/usr/bin/env python3
 """Dispatch + combine throughput on one MI355X.
 
-One step = moe_dispatch (route, scan, scatter with per-token int8
-quantisation) + moe_combine (gather + fp32 weighted reduce) over one batch of
-synthetic tokens, inputs resident in HBM. The expert between them is the
-identity expert; its output (bf16(q * scale) for int8 rows) is produced once,
-before timing, as an input of combine.
+One step = moe_dispatch (rows and payload, with per-token int8 quantisation
+on the default workload) + moe_combine (rows, gather and fp32 weighted
+reduce) over one batch of synthetic tokens, inputs resident in HBM. The
+expert between them is the identity expert; its output (bf16(q * scale) for
+int8 rows) is produced once, before timing, as an input of combine.
 
-Timing: exactly --steps steps run back to back between two HIP events on
-the stream the kernels run on, synchronised on both sides (launch gaps
-included). The 823 MB working set of the default workload is three times the
-256 MB Infinity Cache, so consecutive steps do not find each other's data in
-cache. Dispatch and combine are also timed alone the same way; the combine
-launch sequence (slot pass + gather) is the dominant one and gives the
-roofline figure. A cold figure (a 1 GiB read before every step, each step
-bracketed by its own events) is reported beside it.
+Timing (the measurement protocol of the pages' perf runs: warm-up, then
+timed loops): --warmup untimed steps, then exactly --steps timed steps. Before
+each timed step an untimed 1 GiB read evicts L2 and the 256 MB Infinity
+Cache; each step is bracketed by two HIP events on the stream the kernels run
+on (launch gaps included), and the loop is synchronised before and after.
+`value` is the algorithmic bytes over the median step. Reported beside it:
+the minimum, the same steps back to back without eviction (warm), each call
+alone back to back, the steps replayed from a HIP graph, and a 1 GiB
+device-to-device copy measured in the same process, as the practical
+ceiling. The combine is the dominant launch and gives the roofline figure.
 
     python bench.py [--steps 50] [--warmup 5] [--workload w16_h7168_bf16_q8]
 
@@ -61,7 +63,7 @@ def algorithmic_bytes(w: wl.Workload, inp=None):
     s_y = 2 if w.quant_mode else sx               # identity-expert output for quantised rows is bf16
     erc = w.ep_world * w.num_experts * 4
     toks, copies, mask_b = N, 0, 0
-    if w.mask != "none" or w.zero_experts or w.copy_experts:
+    if w.mask != "none" or w.zero_experts or w.copy_experts or w.const_experts:
         inp = inp if inp is not None else wl.make_inputs(w)
         ids, E = inp["ids"], w.num_experts
         act = np.ones((N, K), bool)
@@ -76,7 +78,9 @@ def algorithmic_bytes(w: wl.Workload, inp=None):
     if w.quant_mode == 1:                         # fp32 static coefficients, read
         n_scales = {"scalar": 1, "column": h, "expert": w.num_experts * h}[w.static_scales]
     disp = toks * h * sx + N * K * 4 + mask_b + rows * h * s_exp + rows * 12 + erc + n_scales * 4
-    comb = rows * h * s_y + copies * h * s_y + N * K * 4 + mask_b + rows * 12 + erc + N * K * 4 + N * h * s_y
+    consts = w.const_experts * h * s_y           # the const experts' outputs, read once
+    comb = (rows * h * s_y + copies * h * s_y + consts + N * K * 4 + mask_b + rows * 12 + erc + N * K * 4
+            + N * h * s_y)
     return disp, comb
 
 
@@ -87,6 +91,41 @@ def _device_inputs(w, torch):
     if bf:
         x = x.view(torch.bfloat16)
     return inp, x, torch.from_numpy(inp["ids"]).cuda(), torch.from_numpy(inp["scales"]).cuda()
+
+
+class StepEvents:
+    """Timing events for the per-step samples: HIP events created with hipEventDisableSystemFence,
+    recorded on torch's current stream. The timestamps are the same device clock as torch's events;
+    without the system-scope fence a pair around nothing reads 1.5 us less (5.4 against 3.9 us on
+    the GPU machine), overhead that would otherwise sit in every sample. `n` pairs; pairs(i) -> (a, b)."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, torch, n):
+        import ctypes
+        self.torch, self.ct = torch, ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.ev = []
+        for _ in range(2 * n):
+            e = ctypes.c_void_p()
+            if self.hip.hipEventCreateWithFlags(ctypes.byref(e), ctypes.c_uint(self.DISABLE_SYSTEM_FENCE)) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+            self.ev.append(e)
+
+    def record(self, i, which):
+        stream = self.ct.c_void_p(self.torch.cuda.current_stream().cuda_stream)
+        if self.hip.hipEventRecord(self.ev[2 * i + which], stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def ms(self, i):
+        out = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(out), self.ev[2 * i], self.ev[2 * i + 1]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return out.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
 
 
 QUANT_LABELS = {1: "static int8, one coefficient per %s", 2: "per-token dynamic int8",
@@ -106,10 +145,15 @@ def measure(w, steps, warmup, flush, torch, moe, schedule=None):
     W, epr = w.ep_world, w.experts_per_rank
     qs = torch.from_numpy(inp["quant_scales"]).cuda() if w.quant_mode == 1 else None
     buf = moe.DispatchBuffers(W, w.bs, epr, w.h, w.topk, tdt, w.quant_mode, "cuda")
-    # token mask and special experts (the copy experts' tokens: x itself, bf16 like the expert output)
+    # token mask and special experts (the copy experts' tokens: x itself, bf16 like the expert output;
+    # the const experts' outputs in the combine's dtype)
     extra = dict(x_active_mask=torch.from_numpy(inp["mask"]).cuda() if "mask" in inp else None,
-                 zero_experts=w.zero_experts, copy_experts=w.copy_experts)
+                 zero_experts=w.zero_experts, copy_experts=w.copy_experts, const_experts=w.const_experts)
     ori = dict(ori_x=x) if w.copy_experts else {}
+    if w.const_experts:
+        cx = torch.from_numpy(inp["const_x"].view(np.int16) if inp["const_x"].dtype == np.uint16
+                              else inp["const_x"]).cuda()
+        ori["const_x"] = cx.view(torch.bfloat16) if inp["const_x"].dtype == np.uint16 else cx
     dx = dict(extra, schedule=schedule) if schedule is not None else extra     # dispatch only
     moe.dispatch_into(buf, x, ids, quant_scales=qs, **dx)
     if w.quant_mode == 1:                      # static codes: the expert sees bf16(q)
@@ -143,24 +187,32 @@ def measure(w, steps, warmup, flush, torch, moe, schedule=None):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # the timed region: exactly `steps` steps, synchronised on both sides
+    # the timed region: exactly `steps` steps, each after an untimed eviction of L2 and the
+    # Infinity Cache (a 1 GiB read) and bracketed by its own events; synchronised on both sides
+    ev = StepEvents(torch, steps)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        flush.max()
+        ev.record(i, 0)
+        step()
+        ev.record(i, 1)
+    torch.cuda.synchronize()
+    cold = [ev.ms(i) for i in range(steps)]
+    # the same events around nothing after the same eviction: the overhead inside each sample
+    for i in range(steps):
+        flush.max()
+        ev.record(i, 0)
+        ev.record(i, 1)
+    torch.cuda.synchronize()
+    empty = statistics.median(ev.ms(i) for i in range(steps))
+    ev.close()
+    # warm: the same steps back to back between two events
     ms_step = b2b(step, steps)
-    # each half alone, back to back (the combine is the dominant launch sequence)
+    # each half alone, back to back (the combine is the dominant launch)
     ms_disp = b2b(lambda: moe.dispatch_into(buf, x, ids, quant_scales=qs, **dx), steps)
     ms_comb = b2b(lambda: moe.combine_into(x_out, y, buf.assist_info, buf.ep_recv_count, ids, sc, W, epr, cws,
                                            **extra, **ori),
                   steps)
-    # cold: L2 and the Infinity Cache evicted (untimed 1 GiB read) before every step; each such
-    # sample also holds one event-to-kernel bubble
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
-    torch.cuda.synchronize()
-    for i in range(steps):
-        flush.max()
-        ev[i][0].record()
-        step()
-        ev[i][1].record()
-    torch.cuda.synchronize()
-    cold = [a.elapsed_time(b) for a, b in ev]
     # the same steps captured once in a HIP graph and replayed (no host work per launch); reported
     # beside the eager figure, which stays the headline
     side = torch.cuda.Stream()
@@ -177,7 +229,7 @@ def measure(w, steps, warmup, flush, torch, moe, schedule=None):
     graph.replay()
     ms_graph = b2b(graph.replay, 3) / steps
     del graph
-    return dict(step=ms_step, disp=ms_disp, comb=ms_comb, cold=cold, graph=ms_graph)
+    return dict(step=ms_step, disp=ms_disp, comb=ms_comb, cold=cold, graph=ms_graph, empty=empty)
 
 
 def code_hash(path):
@@ -222,9 +274,40 @@ def counted_traffic(w):
     return rec["per_launch_bytes"]["moe_combine"]
 
 
-def cpu_baseline(w, reps=9):
-    """The oracle as it stands (single-threaded C), timed on the host."""
+def combine_kernel(w) -> str:
+    """The kernel(s) one moe_combine call launches for this workload's shape: the one-launch
+    combine up to 2^16 pairs and 1024 pairs per source rank (rows in 16-byte pieces, topk <= 16),
+    else the slot pass and the gather."""
+    dt = "BF16" if (w.dtype == "bf16" or w.quant_mode != 0) else ("F16" if w.dtype == "fp16" else "int")
+    es = 4 if dt == "int" else 2
+    if (w.h * es) % 16 == 0 and w.topk <= 16 and w.rows <= 65535 and w.bs * w.topk <= 1024:
+        pre = w.ep_world * w.num_experts <= 2048
+        return "combine_fused_kernel<%s,%d,%s>" % (dt, 8 if w.topk <= 8 else 16, "true" if pre else "false")
+    vec = (w.h * es) % 16 == 0
+    gather = ("combine_gather_i32_kernel<%s>" % ("true" if vec else "false") if dt == "int"
+              else "combine_gather_half_kernel<%s,%s>" % (dt, "true" if vec else "false"))
+    return "combine_slots_kernel + " + gather
+
+
+def cpu_model() -> str:
+    """The host CPU's model name from /proc/cpuinfo ("unknown" when absent)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, reps=5):
+    """The oracle as it stands (single-threaded C), timed on the host: 1 warm-up + the median
+    of `reps` full steps; beside it the all-cores C baseline (oracle/moe_cpu_threads.c, whose
+    outputs a CPU test checks against the oracle) on the same inputs, where it covers the
+    workload (copies and per-token int8)."""
     import oracle
+    from oracle import cpu_threads
 
     inp = wl.make_inputs(w)
     bf = w.dtype == "bf16"
@@ -234,20 +317,63 @@ def cpu_baseline(w, reps=9):
     y = oracle.identity_expert(d["expand_x"], d["dynamic_scales"] if w.quant_mode != 1
                                else np.ones(w.rows, np.float32))
     out_bf = bf or w.quant_mode != 0
-    times = []
-    for _ in range(reps):
-        t0 = time.perf_counter()
+
+    def one():
         d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode, bf16=bf,
                             quant_scales=qs)
         oracle.combine(y, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"], w.ep_world,
                        w.experts_per_rank, bf16=out_bf)
-        times.append(time.perf_counter() - t0)
+
+    def med(fn):
+        fn()
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            fn()
+            times.append(time.perf_counter() - t0)
+        return statistics.median(times)
+
     disp_b, comb_b = algorithmic_bytes(w)
-    t = statistics.median(times)
-    return {"value": round((disp_b + comb_b) / t / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "one full %s step (dispatch + combine, %d tokens), 1 warm-up + median of %d runs, "
-                      "single-threaded C oracle (gcc -O2), identity-expert dequantisation untimed; %.2f s/step"
-                      % (w.name, w.num_tokens, reps, t)}
+    t1 = med(one)
+    out = {"value": round((disp_b + comb_b) / t1 / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+           "sample": "one full %s step (dispatch + combine, %d tokens), 1 warm-up + median of %d, single-threaded "
+                     "C oracle (gcc -O2), identity-expert dequantisation untimed; %.3f s/step"
+                     % (w.name, w.num_tokens, reps, t1),
+           "cpu_model": cpu_model(), "cpu_count": os.cpu_count()}
+    if w.quant_mode in (0, 2) and w.mask == "none" and not (w.zero_experts or w.copy_experts or w.const_experts):
+        n = cpu_threads.default_threads()
+
+        def many():
+            c = cpu_threads.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode, bf16=bf,
+                                     threads=n)
+            cpu_threads.combine(y, c["assist_info"], inp["scales"], w.ep_world, bf16=out_bf, threads=n)
+
+        tn = med(many)
+        out["all_cores"] = {"value": round((disp_b + comb_b) / tn / 1e9, 3), "unit": "GB/s", "cores": n,
+                            "kind": "threaded C baseline (same arithmetic, checked against the oracle)",
+                            "sample": "the same step, payload and sums split over %d threads; %.3f s/step"
+                                      % (n, tn)}
+    return out
+
+
+def copy_ceiling(torch, n_bytes=1 << 30, reps=5):
+    """GB/s of a plain device-to-device copy of n_bytes (read + write counted), best of reps after
+    one warm-up copy: the practical ceiling that streaming kernels meet on this GPU."""
+    src = torch.empty(n_bytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    best = None
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    del src, dst
+    return 2 * n_bytes / (best * 1e-3) / 1e9
 
 
 def main():
@@ -265,7 +391,7 @@ def main():
                     help="hidden size for the main workload (same seed and recipe; default: the workload's)")
     ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf,w16_h7168_bf16_fp8g128,"
                                       "w16_h7168_bf16_static_q8,w16_h7168_bf16_q8_pair_mask,"
-                                      "w16_h7168_bf16_q8_zero_copy",
+                                      "w16_h7168_bf16_q8_special",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -310,34 +436,35 @@ def main():
         w = dataclasses.replace(w, name="%s_segment_schedule" % w.name)
     r = measure(w, args.steps, args.warmup, flush, torch, moe, sched)
     disp_b, comb_b = algorithmic_bytes(w)
-    ms = r["step"]
+    ms = statistics.median(r["cold"])                 # the protocol's figure: median of the timed steps
     gbps = (disp_b + comb_b) / (ms * 1e-3) / 1e9
     comb_ms = r["comb"]
     comb_gbps = comb_b / (comb_ms * 1e-3) / 1e9
-    kernel = "moe_combine = combine_slots_kernel + " + (
-        "combine_gather_half_kernel<BF16,true>" if (w.dtype == "bf16" or w.quant_mode != 0) else
-        ("combine_gather_half_kernel<F16,true>" if w.dtype == "fp16" else "combine_gather_i32_kernel<true>"))
 
     also = {}
     for name in [n for n in args.also.split(",") if n]:
         wa = wl.BY_NAME[name]
         ra = measure(wa, args.steps, args.warmup, flush, torch, moe)
         da, ca = algorithmic_bytes(wa)
-        msa = ra["step"]
+        msa = statistics.median(ra["cold"])
         also[name] = {"ms_per_step": round(msa, 5), "GB/s": round((da + ca) / (msa * 1e-3) / 1e9, 1),
                       "frac_of_hbm_peak": round((da + ca) / (msa * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
                       "tokens_per_s": round(wa.num_tokens / (msa * 1e-3), 1),
+                      "min_ms": round(min(ra["cold"]), 5),
+                      "empty_event_pair_ms": round(ra["empty"], 5),
+                      "warm_b2b_ms": round(ra["step"], 5),
+                      "warm_b2b_GB/s": round((da + ca) / (ra["step"] * 1e-3) / 1e9, 1),
                       "dispatch_ms": round(ra["disp"], 5), "combine_ms": round(ra["comb"], 5),
-                      "cold_median_ms": round(statistics.median(ra["cold"]), 5),
-                      "cold_GB/s": round((da + ca) / (statistics.median(ra["cold"]) * 1e-3) / 1e9, 1),
                       "graph_ms_per_step": round(ra["graph"], 5),
                       "algorithmic_bytes": da + ca,
                       "quant": quant_label(wa)}
         if wa.mask != "none":
             also[name]["mask"] = {"pair": "per pair, 3/4 active",
                                   "token_prefix": "per token, each rank's first 3/4"}[wa.mask]
-        if wa.zero_experts or wa.copy_experts:
-            also[name]["special_experts"] = {"zero": wa.zero_experts, "copy": wa.copy_experts}
+        if wa.zero_experts or wa.copy_experts or wa.const_experts:
+            also[name]["special_experts"] = {"zero": wa.zero_experts, "copy": wa.copy_experts,
+                                             "const": wa.const_experts}
+    ceiling = copy_ceiling(torch)
 
     line = {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -353,20 +480,29 @@ def main():
                    "algorithmic_bytes": disp_b + comb_b},
         "tokens_per_s": round(w.num_tokens / (ms * 1e-3), 1),
         "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "frac_of_copy_ceiling": round(gbps / ceiling, 4),
         "roofline": {"bound": "hbm", "achieved": round(comb_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(comb_gbps / HBM_PEAK_GBPS, 4), "traffic": counted_traffic(w), "kernel": kernel,
+                     "frac": round(comb_gbps / HBM_PEAK_GBPS, 4), "traffic": counted_traffic(w),
+                     "kernel": combine_kernel(w), "scope": "one moe_combine call (the dominant launch), "
+                                                           "timed back to back",
                      "bytes_per_launch": comb_b, "avg_launch_ms": round(comb_ms, 5)},
-        "timing": {"protocol": "%d steps back to back between two HIP events on the kernels' stream, "
-                               "synchronised before and after" % args.steps,
+        "timing": {"protocol": "%d warm-up steps, then %d timed steps, each after an untimed 1 GiB read that "
+                               "evicts L2 and the Infinity Cache and bracketed by two HIP events on the kernels' "
+                               "stream; synchronised before and after; value = median" % (args.warmup, args.steps),
+                   "median_ms": round(ms, 5), "min_ms": round(min(r["cold"]), 5),
+                   "empty_event_pair_ms": round(r["empty"], 5),
+                   "event_note": "HIP events without the system-scope fence; empty_event_pair_ms is the median of "
+                                 "the same event pair around nothing after the same eviction, included in every "
+                                 "sample",
+                   "warm_b2b_ms": round(r["step"], 5),
+                   "warm_b2b_GB/s": round((disp_b + comb_b) / (r["step"] * 1e-3) / 1e9, 1),
+                   "warm_note": "the same steps back to back between two events, no eviction",
                    "dispatch_ms": round(r["disp"], 5), "combine_ms": round(comb_ms, 5),
-                   "cold_median_ms": round(statistics.median(r["cold"]), 5), "cold_min_ms": round(min(r["cold"]), 5),
-                   "cold_GB/s": round((disp_b + comb_b) / (statistics.median(r["cold"]) * 1e-3) / 1e9, 1),
-                   "cold_note": "1 GiB read before each step evicts L2 and the Infinity Cache; each cold sample "
-                                "includes one event-to-kernel bubble",
                    "graph_ms_per_step": round(r["graph"], 5),
                    "graph_note": "the same %d steps captured once in a HIP graph, replayed twice untimed, then "
-                                 "3 timed replays (mean; no host work per launch); the headline value is the "
-                                 "eager figure" % args.steps},
+                                 "3 timed replays (mean; no host work per launch)" % args.steps,
+                   "copy_ceiling_GB/s": round(ceiling, 1),
+                   "copy_note": "1 GiB device-to-device copy (read + write), best of 5"},
         "also": also,
     }
     if not args.no_cpu_baseline:

@@ -42,15 +42,19 @@ class MoeError(RuntimeError):
 
 class MoeSpecialExperts(ctypes.Structure):
     _fields_ = [("zero_expert_num", ctypes.c_int32), ("copy_expert_num", ctypes.c_int32),
-                ("const_expert_num", ctypes.c_int32), ("reserved", ctypes.c_int32), ("ori_x", ctypes.c_void_p)]
+                ("const_expert_num", ctypes.c_int32), ("reserved", ctypes.c_int32), ("ori_x", ctypes.c_void_p),
+                ("const_x", ctypes.c_void_p)]
 
 
-def _special(zero_experts: int, copy_experts: int, ori_x: Optional[torch.Tensor] = None):
+def _special(zero_experts: int, copy_experts: int, ori_x: Optional[torch.Tensor] = None, const_experts: int = 0,
+             const_x: Optional[torch.Tensor] = None):
     """byref(moe_special_experts) or None when there are no special experts."""
-    if not zero_experts and not copy_experts:
+    if not zero_experts and not copy_experts and not const_experts:
         return None
     sp = MoeSpecialExperts(zero_expert_num=int(zero_experts), copy_expert_num=int(copy_experts),
-                           ori_x=None if ori_x is None else ori_x.data_ptr())
+                           const_expert_num=int(const_experts),
+                           ori_x=None if ori_x is None else ori_x.data_ptr(),
+                           const_x=None if const_x is None else const_x.data_ptr())
     return ctypes.byref(sp)
 
 
@@ -236,7 +240,7 @@ def _quant_scales_args(qs: Optional[torch.Tensor], device):
 def dispatch_into(buf: DispatchBuffers, x: torch.Tensor, expert_ids: torch.Tensor,
                   expert_scales: Optional[torch.Tensor] = None, schedule: Optional[MoeSchedule] = None,
                   x_active_mask: Optional[torch.Tensor] = None, zero_experts: int = 0, copy_experts: int = 0,
-                  quant_scales: Optional[torch.Tensor] = None):
+                  quant_scales: Optional[torch.Tensor] = None, const_experts: int = 0):
     """moe_dispatch into preallocated buffers on the current stream. quant_scales: the static
     quantiser's coefficients (quantMode 1 only): 1, h or E*h fp32 values. The C ABI sees only
     pointers, so the tensors' shapes, dtypes and device are checked here against buf."""
@@ -251,7 +255,8 @@ def dispatch_into(buf: DispatchBuffers, x: torch.Tensor, expert_ids: torch.Tenso
     mp, mk = _mask_args(x_active_mask, W * bs, K, dev)
     qp, qn = _quant_scales_args(quant_scales, dev)
     rc = library().moe_dispatch(
-        _ptr(x), _ptr(expert_ids), _ptr(expert_scales), mp, mk, _special(zero_experts, copy_experts), W, bs, epr,
+        _ptr(x), _ptr(expert_ids), _ptr(expert_scales), mp, mk, _special(zero_experts, copy_experts, None,
+                                                                         const_experts), W, bs, epr,
         h, K, dtype_code(buf.dtype),
         buf.quant_mode, qp, ctypes.c_int64(qn),
         _ptr(buf.expand_x), _ptr(buf.dynamic_scales), _ptr(buf.assist_info), _ptr(buf.ep_recv_count),
@@ -264,7 +269,8 @@ def dispatch_into(buf: DispatchBuffers, x: torch.Tensor, expert_ids: torch.Tenso
 def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_per_rank: int,
              quant_mode: int = MOE_QUANT_NONE, expert_scales: Optional[torch.Tensor] = None,
              schedule: Optional[MoeSchedule] = None, x_active_mask: Optional[torch.Tensor] = None,
-             zero_experts: int = 0, copy_experts: int = 0, quant_scales: Optional[torch.Tensor] = None):
+             zero_experts: int = 0, copy_experts: int = 0, quant_scales: Optional[torch.Tensor] = None,
+             const_experts: int = 0):
     """Dispatch tokens into expert-grouped rows.
 
     x: [ep_world*bs, h] int32/fp16/bf16 on a GPU; expert_ids: [ep_world*bs, topk]
@@ -272,7 +278,8 @@ def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_p
     and, when expert_scales is given, a fifth item expand_scales. With a token
     mask (bool/uint8 [N] or [N, topk]) only the first ep_recv_count[:, -1].sum()
     rows of the row-indexed outputs are written; the same holds with special
-    experts (ids E.. for zero_experts, then copy_experts), whose pairs get no row.
+    experts (ids E.. for zero_experts, then copy_experts, then const_experts), whose
+    pairs get no row.
     quant_mode 1 (static int8) takes its coefficients in quant_scales (fp32, 1, h or
     E*h values) and returns no dynamic scales.
     """
@@ -292,7 +299,7 @@ def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_p
         buf.expand_scales = torch.empty((N * K,), dtype=getattr(expert_scales, "dtype", torch.float32),
                                         device=dev)
     dispatch_into(buf, x, expert_ids, expert_scales, schedule, x_active_mask, zero_experts, copy_experts,
-                  quant_scales)
+                  quant_scales, const_experts)
     out = (buf.expand_x, buf.dynamic_scales, buf.assist_info, buf.ep_recv_count)
     return out + (buf.expand_scales,) if expert_scales is not None else out
 
@@ -301,10 +308,12 @@ def combine_into(x_out: torch.Tensor, expand_x: torch.Tensor, assist_info: torch
                  ep_recv_count: torch.Tensor, expert_ids: torch.Tensor, expert_scales: torch.Tensor,
                  ep_world: int, experts_per_rank: int, workspace: Optional[torch.Tensor] = None,
                  x_active_mask: Optional[torch.Tensor] = None, zero_experts: int = 0, copy_experts: int = 0,
-                 ori_x: Optional[torch.Tensor] = None):
+                 ori_x: Optional[torch.Tensor] = None, const_experts: int = 0,
+                 const_x: Optional[torch.Tensor] = None):
     """moe_combine into a preallocated x_out on the current stream. Copy experts need ori_x,
-    the tokens given to dispatch, in expand_x's dtype. The C ABI sees only pointers, so the
-    tensors' shapes, dtypes and device are checked here."""
+    the tokens given to dispatch, and const experts const_x [const_experts, h], their fixed
+    outputs, both in expand_x's dtype. The C ABI sees only pointers, so the tensors' shapes,
+    dtypes and device are checked here."""
     dev = _gpu_device("expand_x", expand_x)
     _gpu_device("expert_ids", expert_ids)
     if expand_x.dim() != 2 or expert_ids.dim() != 2:
@@ -325,6 +334,10 @@ def combine_into(x_out: torch.Tensor, expand_x: torch.Tensor, assist_info: torch
         if ori_x is None:
             raise MoeError("moe_combine", MOE_ERR_NULLPTR, "copy experts need ori_x, the tokens given to dispatch")
         _check_tensor("ori_x", ori_x, expand_x.dtype, (N, h), dev)
+    if const_experts:
+        if const_x is None:
+            raise MoeError("moe_combine", MOE_ERR_NULLPTR, "const experts need const_x, their outputs")
+        _check_tensor("const_x", const_x, expand_x.dtype, (int(const_experts), h), dev)
     dt = dtype_code(expand_x.dtype)
     if workspace is None:
         workspace = combine_workspace(ep_world, N // ep_world, experts_per_rank, h, K, expand_x.dtype, dev)
@@ -332,7 +345,8 @@ def combine_into(x_out: torch.Tensor, expand_x: torch.Tensor, assist_info: torch
         _check_tensor("workspace", workspace, torch.uint8, (workspace.numel(),), dev)
     rc = library().moe_combine(
         _ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_count), _ptr(expert_ids), _ptr(expert_scales), mp, mk,
-        _special(zero_experts, copy_experts, ori_x), ep_world, N // ep_world, experts_per_rank, h, K, dt,
+        _special(zero_experts, copy_experts, ori_x, const_experts, const_x), ep_world, N // ep_world,
+        experts_per_rank, h, K, dt,
         _ptr(x_out), _ptr(workspace), workspace.numel(), _stream_ptr(dev))
     _check("moe_combine", rc)
     return x_out
@@ -347,7 +361,7 @@ def combine_workspace(ep_world, bs, experts_per_rank, h, topk, dtype: torch.dtyp
 def combine(expand_x: torch.Tensor, assist_info: torch.Tensor, ep_recv_count: torch.Tensor,
             expert_ids: torch.Tensor, expert_scales: torch.Tensor, ep_world: int, experts_per_rank: int,
             x_active_mask: Optional[torch.Tensor] = None, zero_experts: int = 0, copy_experts: int = 0,
-            ori_x: Optional[torch.Tensor] = None):
+            ori_x: Optional[torch.Tensor] = None, const_experts: int = 0, const_x: Optional[torch.Tensor] = None):
     """x_out[t] = sum over active k of expand_x[row(t,k)] * expert_scales[t,k] (fp32 accumulation);
     x_active_mask: the dispatch's."""
     dev = _gpu_device("expand_x", expand_x)
@@ -357,4 +371,4 @@ def combine(expand_x: torch.Tensor, assist_info: torch.Tensor, ep_recv_count: to
     x_out = torch.empty((expert_ids.shape[0], expand_x.shape[1]), dtype=expand_x.dtype, device=dev)
     return combine_into(x_out, expand_x, assist_info, ep_recv_count, expert_ids, expert_scales, ep_world,
                         experts_per_rank, x_active_mask=x_active_mask, zero_experts=zero_experts,
-                        copy_experts=copy_experts, ori_x=ori_x)
+                        copy_experts=copy_experts, ori_x=ori_x, const_experts=const_experts, const_x=const_x)

@@ -45,6 +45,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "moe_ep.h"
 
@@ -78,6 +79,7 @@ constexpr int kBlockThreads = 256;         // generic block-per-token kernels
 constexpr int kGatherThreads = 128;        // combine: block = (token, 128-chunk slice)
 constexpr int kSlotThreads = 256;
 constexpr int kCopySlot = -2;             // slot of a copy-expert pair: the token itself
+constexpr int kConstSlot0 = -3;           // slot of a pair of const expert j: kConstSlot0 - j
 // shapes of the static quantisation coefficients: 1, h or E*h values
 constexpr int kStaticOne = 0, kStaticColumn = 1, kStaticExpert = 2;
 constexpr int kXcds = 8;                   // gfx950 XCDs; consecutive workgroups go to consecutive XCDs
@@ -558,6 +560,8 @@ struct DispatchArgs {
     const float *qs;          // static quantisation coefficients
     int qkind;                // their shape: kStaticOne, kStaticColumn or kStaticExpert
     int store_mix;            // wavefront scatters: 0 half the stores plain, 1 a quarter, 2 none
+    const uint8_t *mask;      // token mask (one-launch dispatch; the route kernel takes its own)
+    int mask_kind;
 };
 
 // Whether piece j of copy k of a wavefront scatter is stored non-temporally
@@ -1369,6 +1373,191 @@ void launch_segment_quant_wave(int J, dim3 g, dim3 b, hipStream_t st, const Disp
     else hipLaunchKernelGGL((segment_quant_wave_kernel<T, 16>), g, b, 0, st, a);
 }
 
+
+// --------------------------------------------------------------------------
+// one launch per call for small batches
+// --------------------------------------------------------------------------
+//
+// Rows by counting. Rows are ordered by expert, then source rank, then token,
+// and for pairs of one expert that is the order of their flat index p = t*K + k
+// (a token names each expert once). With key(p) = e*N*K + p for a pair that is
+// exchanged (active, routed to one of the E real experts), the row of pair p is
+// the number of exchanged pairs whose key is smaller. A workgroup that needs
+// the rows of token t's K pairs reads every pair's expert id (N*K int32, in L2
+// after the first workgroups), compares those keys with its K targets (two VALU
+// operations per key and target) and sums the counts over the workgroup. The
+// dispatch then needs no route launch and the combine no slot pass; at 8 ranks
+// x 32 tokens, top-8, a dispatch thread compares 8 keys. The combine counts
+// less: the first row of a pair's segment comes from ep_recv_count, so it only
+// counts the same source rank's earlier pairs of the same expert.
+
+constexpr int kFusedThreads = 256;        // one-launch dispatch: workgroup = (token, slice)
+constexpr int kFusedUnroll = 2;           // 16-byte chunks per thread: a slice is 8 KiB
+constexpr int kFusedMaxPairs = 4096;      // N*K up to which dispatch runs as one launch
+constexpr int kFusedMaxCounts = 4096;     // W*E segment counts of its ep_recv_count workgroup (LDS)
+constexpr int kFusedMaxK = 16;
+constexpr int kFusedCombinePairs = 65535; // one-launch combine: N*K (16-bit counts) ...
+constexpr int kFusedCombineSrcPairs = 1024;   // ... and bs*K (pairs a workgroup may count)
+constexpr int kFusedCombineLdsCounts = 2048;  // W*E up to which a workgroup stages ep_recv_count in LDS
+
+// Expert of pair p if the pair is exchanged (active, and routed to one of the
+// E real experts), else -1. The id of an inactive pair is loaded with its mask
+// byte, so that both loads are in flight together, and then ignored.
+__device__ __forceinline__ int exchanged_expert(const int32_t *ids, const uint8_t *mask, int mask_kind, int p, int K,
+                                                float rK, int E)
+{
+    int e = ids[p];
+    if (mask_kind == MOE_MASK_TOKEN) {
+        if (!mask[div_small(p, K, rK)]) e = -1;
+    } else if (mask_kind == MOE_MASK_PAIR) {
+        if (!mask[p]) e = -1;
+    }
+    return (unsigned)e < (unsigned)E ? e : -1;
+}
+
+// Workgroup-wide sums of KW words that hold two 16-bit counts each; every
+// thread gets the totals. red: KW ints of LDS per wavefront.
+template <int KW>
+__device__ __forceinline__ void block_sum_packed(int (&w)[KW], int *red)
+{
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) w[i] = __builtin_amdgcn_readlane(wave_incl_scan(w[i]), 63);
+    if (lane == 0) {
+#pragma unroll
+        for (int i = 0; i < KW; ++i) red[wid * KW + i] = w[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+        int v = 0;
+        for (int q = 0; q < nw; ++q) v += red[q * KW + i];
+        w[i] = v;
+    }
+}
+
+// Count k (16 bits) of the packed words.
+template <int KW>
+__device__ __forceinline__ int packed_count(const int (&w)[KW], int k)
+{
+    return (w[k >> 1] >> (16 * (k & 1))) & 0xffff;
+}
+
+// ep_recv_count workgroup of the one-launch dispatch: segment counts by LDS
+// atomics over every exchanged pair, one exclusive scan over all W*E segments
+// in (rank, el*W + s) order, and per rank that scan minus its value at the
+// rank's first segment (a rank has S = E segments).
+__device__ void fused_counts(const DispatchArgs &a)
+{
+    extern __shared__ int cnt[];                 // [W * E]
+    __shared__ int tmp[40];
+    const int G = a.W * a.E, NK = a.R, tid = threadIdx.x, nt = blockDim.x;
+    const float rK = 1.0f / a.K, rbs = 1.0f / a.bs, repr = 1.0f / a.epr, rE = 1.0f / a.E;
+    for (int i = tid; i < G; i += nt) cnt[i] = 0;
+    __syncthreads();
+    for (int p = tid; p < NK; p += nt) {
+        const int e = exchanged_expert(a.ids, a.mask, a.mask_kind, p, a.K, rK, a.E);
+        if (e < 0) continue;
+        const int s = div_small(div_small(p, a.K, rK), a.bs, rbs);
+        const int r = div_small(e, a.epr, repr);
+        atomicAdd(&cnt[r * a.E + (e - r * a.epr) * a.W + s], 1);
+    }
+    __syncthreads();
+    const int per = (G + nt - 1) / nt;
+    const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
+    int sum = 0;
+    for (int g = g0; g < g1; ++g) sum += cnt[g];
+    int total;
+    int run = block_excl_scan(sum, tmp, &total);
+    for (int g = g0; g < g1; ++g) {
+        run += cnt[g];
+        cnt[g] = run;                            // inclusive prefix over all segments
+    }
+    __syncthreads();
+    for (int g = tid; g < G; g += nt) {
+        const int r = div_small(g, a.E, rE);
+        a.erc[g] = cnt[g] - (r > 0 ? cnt[r * a.E - 1] : 0);
+    }
+}
+
+// One-launch dispatch (copies): workgroups (token t, 8 KiB slice) plus one
+// ep_recv_count workgroup at the end of the grid. Each thread loads its slice
+// chunks first, then L of the N*K expert ids (L * kFusedThreads >= N*K); lane k
+// of every wavefront holds the key of token t's pair k. After the count, every
+// thread stores its chunks to the K rows; slice 0 writes assist_info and
+// expand_scales. Needs rows in 16-byte pieces, K <= KT and N*K <= L * 256.
+template <int KT, int L>
+__global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(DispatchArgs a)
+{
+    constexpr int KW = KT / 2;
+    __shared__ int red[kFusedThreads / 64 * KW];
+    const int N = a.W * a.bs, NK = a.R;
+    if ((int)blockIdx.x >= N * a.nsl) {
+        fused_counts(a);
+        return;
+    }
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int t = blockIdx.x / a.nsl, sl = blockIdx.x - t * a.nsl;
+    const float rK = 1.0f / a.K;
+    const int nc = (int)(a.rowbytes / 16), c0 = sl * (kFusedThreads * kFusedUnroll) + tid;
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
+    uint4 v[kFusedUnroll];
+#pragma unroll
+    for (int u = 0; u < kFusedUnroll; ++u) v[u] = src[min(c0 + u * kFusedThreads, nc - 1)];
+    int key[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const int p = tid + j * kFusedThreads;
+        const int e = p < NK ? exchanged_expert(a.ids, a.mask, a.mask_kind, p, a.K, rK, a.E) : -1;
+        key[j] = e >= 0 ? e * NK + p : INT_MAX;
+    }
+    const int pt = t * a.K + (lane < a.K ? lane : 0);
+    const int et = exchanged_expert(a.ids, a.mask, a.mask_kind, pt, a.K, rK, a.E);
+    const int tkey = lane < a.K && et >= 0 ? et * NK + pt : INT_MAX;
+    int w[KW];
+#pragma unroll
+    for (int i = 0; i < KW; ++i) w[i] = 0;
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        const int tk = __builtin_amdgcn_readlane(tkey, k);
+        int c = 0;
+#pragma unroll
+        for (int j = 0; j < L; ++j) c += key[j] < tk;
+        w[k >> 1] += c << (16 * (k & 1));
+    }
+    block_sum_packed<KW>(w, red);
+    int rows[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        const bool has = k < a.K && __builtin_amdgcn_readlane(tkey, k) != INT_MAX;
+        const int row = packed_count<KW>(w, k);
+        rows[k] = has && row < a.R ? row : -1;
+    }
+    if (sl == 0 && tid < a.K) {
+        int row = -1;
+#pragma unroll
+        for (int k = 0; k < KT; ++k)
+            if (tid == k) row = rows[k];
+        if (row >= 0) {
+            const int s = t / a.bs;
+            a.assist[(size_t)row * 3 + 0] = s;
+            a.assist[(size_t)row * 3 + 1] = t - s * a.bs;
+            a.assist[(size_t)row * 3 + 2] = tid;
+            if (a.esc_out) a.esc_out[row] = a.esc_in[pt];
+        }
+    }
+#pragma unroll
+    for (int u = 0; u < kFusedUnroll; ++u) {
+        const int c = c0 + u * kFusedThreads;
+        if (c >= nc) continue;
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            if (rows[k] < 0) continue;
+            store_stream(reinterpret_cast<uint4 *>(a.expand_x + (size_t)rows[k] * a.rowbytes) + c, v[u]);
+        }
+    }
+}
+
 // --------------------------------------------------------------------------
 // combine
 // --------------------------------------------------------------------------
@@ -1384,10 +1573,12 @@ struct CombineArgs {
     const uint8_t *mask;
     const int32_t *ids;       // expert_ids [N, K]: special experts are recognised by id
     const char *ori_x;        // [N, h]: the tokens, for copy experts
+    const char *const_x;      // [const experts, h]: the const experts' outputs
     int mask_kind;
     int pair_pass;            // a mask or special experts: mark pairs that have no row
-    int E, zero_end, copy_end; // special ids: [E, zero_end) zero, [zero_end, copy_end) copy
-    int W, bs, h, K, R, S, nsl;
+    // special ids: [E, zero_end) zero, [zero_end, copy_end) copy, [copy_end, const_end) const
+    int E, zero_end, copy_end, const_end;
+    int W, bs, h, K, R, S, nsl, epr;
     long long rowbytes;
 };
 
@@ -1395,8 +1586,9 @@ struct CombineArgs {
 // (src_token, topk_id) of source rank src_rank. Only its index travels.
 // Under a token mask or with special experts only the first A rows exist (A =
 // sum over ranks of the last inclusive count). A pair without a row gets slot
-// -1 (inactive, or a zero expert: the gather skips it) or -2 (a copy expert:
-// the gather reads the token itself). A thread handles row i and pair i.
+// -1 (inactive, or a zero expert: the gather skips it), -2 (a copy expert:
+// the gather reads the token itself) or -3 - j (const expert j: the gather
+// reads row j of the const table). A thread handles row i and pair i.
 __global__ __launch_bounds__(kSlotThreads) void combine_slots_kernel(CombineArgs a)
 {
     __shared__ int tmp[40];
@@ -1412,7 +1604,8 @@ __global__ __launch_bounds__(kSlotThreads) void combine_slots_kernel(CombineArgs
             if (a.mask_kind == MOE_MASK_PAIR) on = a.mask[i] != 0;
             const int e = a.ids[i];
             if (!on || (e >= a.E && e < a.zero_end)) a.slot_out[i] = -1;
-            else if (e >= a.zero_end && e < a.copy_end) a.slot_out[i] = -2;
+            else if (e >= a.zero_end && e < a.copy_end) a.slot_out[i] = kCopySlot;
+            else if (e >= a.copy_end && e < a.const_end) a.slot_out[i] = kConstSlot0 - (e - a.copy_end);
         }
     }
     if (i >= rows || i >= a.R) return;
@@ -1426,18 +1619,23 @@ __device__ __forceinline__ void gather_prologue(const CombineArgs &a, int t, int
     for (int k = threadIdx.x; k < a.K; k += blockDim.x) {
         const size_t p = (size_t)t * a.K + k;
         const int row = a.slot[p];
-        // -2 (copy expert) is honoured only when this call has copy experts, so a
-        // stale or foreign slot never sends the gather to a missing ori_x
-        rows[k] = (unsigned)row < (unsigned)a.R ? row : (row == kCopySlot && a.ori_x ? kCopySlot : -1);
+        // -2 (copy expert) and -3 - j (const expert j) are honoured only when this
+        // call has such experts, so a stale or foreign slot never sends the gather
+        // to a missing ori_x or past the const table
+        const bool cst = row <= kConstSlot0 && a.const_x && kConstSlot0 - row < a.const_end - a.copy_end;
+        rows[k] = (unsigned)row < (unsigned)a.R ? row : ((row == kCopySlot && a.ori_x) || cst ? row : -1);
         sc[k] = reinterpret_cast<const uint32_t *>(a.scales)[p];
     }
     __syncthreads();
 }
 
-// The row a slot names: an expand_x row, or (copy expert) token t of ori_x.
+// The row a slot names: an expand_x row, token t of ori_x (copy expert) or
+// row j of the const table (const expert j).
 __device__ __forceinline__ const char *slot_row(const CombineArgs &a, int t, int row)
 {
-    return row >= 0 ? a.expand_x + (size_t)row * a.rowbytes : a.ori_x + (size_t)t * a.rowbytes;
+    if (row >= 0) return a.expand_x + (size_t)row * a.rowbytes;
+    if (row == kCopySlot) return a.ori_x + (size_t)t * a.rowbytes;
+    return a.const_x + (size_t)(kConstSlot0 - row) * a.rowbytes;
 }
 
 // fp16 / bf16: block = (token, slice of kGatherThreads 16-byte chunks)
@@ -1534,6 +1732,152 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_i32_kernel(Comb
     }
 }
 
+
+// One-launch combine: workgroup = (token t, slice of kGatherThreads 16-byte
+// chunks), with the gather and the fp32 weighted sum of the gather kernels
+// above. The slot of token t's pair k is found in the workgroup (lane k of
+// every wavefront holds it): a real expert's row is the first row of its
+// segment, from ep_recv_count (the rows of all lower ranks, plus the rank's
+// inclusive count before segment (el, s)), plus the pairs of source rank s's
+// earlier tokens routed to the same expert, counted over those tokens' ids. A
+// copy expert reads token t, const expert j row j of the const table. PRE
+// stages ep_recv_count in LDS (W*E <= kFusedCombineLdsCounts), so that the
+// segment start needs no second dependent load. Needs rows in 16-byte pieces,
+// K <= KT and N*K < 2^16.
+template <class T, int KT, bool PRE>
+__global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineArgs a)
+{
+    constexpr int KW = KT / 2;
+    extern __shared__ int erc_lds[];              // PRE: ep_recv_count [W * S]
+    __shared__ int red[kGatherThreads / 64 * KW];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int t = blockIdx.x / a.nsl, sl = blockIdx.x - t * a.nsl;
+    const int K = a.K;
+    const int s = t / a.bs;
+    const float rK = 1.0f / K;
+    // lane k: pair k of token t
+    const int pt = t * K + (lane < K ? lane : 0);
+    const int e = a.ids[pt];
+    bool on = lane < K;
+    if (a.mask_kind == MOE_MASK_TOKEN) on = on && a.mask[t] != 0;
+    else if (a.mask_kind == MOE_MASK_PAIR) on = on && a.mask[pt] != 0;
+    const uint32_t wbits = reinterpret_cast<const uint32_t *>(a.scales)[pt];
+    const bool real = on && (unsigned)e < (unsigned)a.E;
+    const int r = real ? div_small(e, a.epr, 1.0f / a.epr) : -1;
+    const int seg = real ? (e - r * a.epr) * a.W + s : 0;     // segment (el, s) inside rank r
+    if (PRE) {
+        for (int i = tid; i < a.W * a.S; i += kGatherThreads) erc_lds[i] = a.erc[i];
+    }
+    int base = 0;
+    if (!PRE && real && seg > 0) base = a.erc[(size_t)r * a.S + seg - 1];
+    const int ek = real ? e : INT_MIN;             // an inactive pair below reads as -1, never INT_MIN
+    // Every lane's values that other lanes need are read here, with the whole
+    // wavefront active: a lane that is switched off inside the loops below may
+    // not hold them there.
+    int ek_u[KT], rk_u[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        ek_u[k] = __builtin_amdgcn_readlane(ek, k);
+        rk_u[k] = __builtin_amdgcn_readlane(r, k);
+    }
+    int w[KW];
+#pragma unroll
+    for (int i = 0; i < KW; ++i) w[i] = 0;
+    // rows of the ranks below r
+    for (int q = tid; q < a.W; q += kGatherThreads) {
+        const int tot = a.erc[(size_t)q * a.S + a.S - 1];
+#pragma unroll
+        for (int k = 0; k < KT; ++k) w[k >> 1] += (q < rk_u[k] ? tot : 0) << (16 * (k & 1));
+    }
+    // pairs of source rank s's earlier tokens routed to the same expert, four ids per thread at a time
+    const int p1 = t * K;
+    for (int p0 = s * a.bs * K + tid; p0 < p1; p0 += 4 * kGatherThreads) {
+        int ep[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int p = p0 + u * kGatherThreads;
+            ep[u] = p < p1 ? exchanged_expert(a.ids, a.mask, a.mask_kind, p, K, rK, a.E) : -1;
+        }
+#pragma unroll
+        for (int k = 0; k < KT; ++k) {
+            int c = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) c += ep[u] == ek_u[k];
+            w[k >> 1] += c << (16 * (k & 1));
+        }
+    }
+    block_sum_packed<KW>(w, red);                 // (its barrier also publishes erc_lds)
+    if (PRE && real && seg > 0) base = erc_lds[r * a.S + seg - 1];
+    int cnt = 0;
+#pragma unroll
+    for (int k = 0; k < KT; ++k)
+        if (lane == k) cnt = packed_count<KW>(w, k);
+    // the slot of lane k's pair: a row, kCopySlot, kConstSlot0 - j, or -1 (nothing to add)
+    int slot = -1;
+    if (real) {
+        slot = cnt + base;
+        if ((unsigned)slot >= (unsigned)a.R) slot = -1;
+    } else if (on && e >= a.zero_end && e < a.copy_end && a.ori_x) {
+        slot = kCopySlot;
+    } else if (on && e >= a.copy_end && e < a.const_end && a.const_x) {
+        slot = kConstSlot0 - (e - a.copy_end);
+    }
+    int slot_u[KT];
+    uint32_t w_u[KT];
+#pragma unroll
+    for (int k = 0; k < KT; ++k) {
+        slot_u[k] = k < K ? __builtin_amdgcn_readlane(slot, k) : -1;
+        w_u[k] = __builtin_amdgcn_readlane(wbits, k);
+    }
+    constexpr bool I32 = std::is_same<T, int32_t>::value;
+    const int nch = I32 ? a.h / 4 : a.h / 8, c = sl * kGatherThreads + tid;
+    if (c >= nch) return;
+    constexpr int KB = 8;
+    float acc[8];
+    uint32_t iacc[4];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) iacc[i] = 0u;
+#pragma unroll
+    for (int kb = 0; kb < KT; kb += KB) {
+        if (kb >= K) break;
+        uint4 v[KB];
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            const int k = kb + kk;
+            v[kk] = slot_u[k] != -1 ? load_stream(reinterpret_cast<const uint4 *>(slot_row(a, t, slot_u[k])) + c)
+                                    : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int kk = 0; kk < KB; ++kk) {
+            const int k = kb + kk;
+            if (slot_u[k] == -1) continue;
+            const uint32_t wk = w_u[k];
+            const uint32_t q[4] = {v[kk].x, v[kk].y, v[kk].z, v[kk].w};
+            if constexpr (I32) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) iacc[i] += q[i] * wk;
+            } else {
+                const float wgt = __uint_as_float(wk);
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    acc[i] = __builtin_fmaf(T::load((uint16_t)(q[i >> 1] >> ((i & 1) * 16))), wgt, acc[i]);
+            }
+        }
+    }
+    uint4 out;
+    if constexpr (I32) {
+        out = make_uint4(iacc[0], iacc[1], iacc[2], iacc[3]);
+    } else {
+        uint32_t o[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (uint32_t)T::store(acc[2 * i]) | ((uint32_t)T::store(acc[2 * i + 1]) << 16);
+        out = make_uint4(o[0], o[1], o[2], o[3]);
+    }
+    store_stream(reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes) + c, out);
+}
+
 // --------------------------------------------------------------------------
 // host side
 // --------------------------------------------------------------------------
@@ -1558,12 +1902,13 @@ int check_scalars(int W, int bs, int epr, int h, int K, int dtype)
     return MOE_OK;
 }
 
-// Special experts: counts >= 0, no const experts, ids below 2^31.
+// Special experts: counts >= 0, every id below 2^31.
 int check_special(const moe_special_experts *sp, long long E)
 {
     if (!sp) return MOE_OK;
-    if (sp->zero_expert_num < 0 || sp->copy_expert_num < 0 || sp->const_expert_num != 0) return MOE_ERR_SHAPE;
-    if (E + sp->zero_expert_num + sp->copy_expert_num >= (1ll << 31)) return MOE_ERR_SHAPE;
+    if (sp->zero_expert_num < 0 || sp->copy_expert_num < 0 || sp->const_expert_num < 0) return MOE_ERR_SHAPE;
+    if (E + sp->zero_expert_num + sp->copy_expert_num + (long long)sp->const_expert_num >= (1ll << 31))
+        return MOE_ERR_SHAPE;
     return MOE_OK;
 }
 
@@ -1728,7 +2073,54 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     // plan is needed); otherwise one scan block forms every offset first
     const bool direct = N > 0 && mode == MOE_SCHED_TOKEN && L.NB <= kDirectMaxChunks;
 
+    DispatchArgs a;
+    a.x = static_cast<const char *>(x);
+    a.ids = expert_ids;
+    a.esc_in = static_cast<const int32_t *>(expert_scales);
+    a.expand_x = static_cast<char *>(expand_x);
+    a.dyn = dynamic_scales;
+    a.assist = assist_info;
+    a.esc_out = static_cast<int32_t *>(expand_scales);
+    a.erc = ep_recv_count;
+    a.lr = lr;
+    a.pc = pc;
+    a.pci = pci;
+    a.boff = boff;
+    a.plan = plan;
+    a.nplan = nplan;
+    a.W = W; a.bs = bs; a.epr = epr; a.h = h; a.K = K; a.nbs = L.nbs; a.R = (int)(N * K);
+    a.E = E; a.S = (int)S; a.NB = L.NB;
+    // with a scan block present it also wrote ep_recv_count
+    a.direct = (direct && !want_seg) ? 1 : 0;
+    a.rowbytes = (long long)rowbytes;
+    a.nsl = 1;
+    a.qs = quant_scales;
+    a.qkind = qkind;
+    a.mask = x_active_mask;
+    a.mask_kind = mask_kind;
+    // the plain share of the quantisers' stores shrinks as the rows written
+    // outgrow the Infinity Cache; the wavefront copy keeps half of its
+    // stores plain up to its own limit (see store_stream)
+    const long long qbytes = N * K * (long long)h;
+    a.store_mix = !quant || qbytes <= kMixedStoreMaxBytes ? 0 : (qbytes <= kQuarterPlainMaxBytes ? 1 : 2);
+
     (void)hipGetLastError();
+    // Small batches of copies: one launch (rows by counting, see dispatch_fused_kernel)
+    const bool vec16 = rowbytes % 16 == 0 && aligned(x, 16) && aligned(expand_x, 16);
+    if (N > 0 && !quant && mode == MOE_SCHED_TOKEN && !want_seg && vec16 && K <= kFusedMaxK &&
+        N * K <= kFusedMaxPairs && (long long)W * E <= kFusedMaxCounts) {
+        const int sc = kFusedThreads * kFusedUnroll;
+        a.nsl = (int)(((long long)rowbytes / 16 + sc - 1) / sc);
+        const dim3 g((unsigned)(N * a.nsl + 1)), b(kFusedThreads);
+        const size_t lds = (size_t)W * E * sizeof(int);
+        const bool k8 = K <= 8, l8 = N * K <= 8 * kFusedThreads;
+        if (k8 && l8) hipLaunchKernelGGL((dispatch_fused_kernel<8, 8>), g, b, lds, st, a);
+        else if (k8) hipLaunchKernelGGL((dispatch_fused_kernel<8, 16>), g, b, lds, st, a);
+        else if (l8) hipLaunchKernelGGL((dispatch_fused_kernel<16, 8>), g, b, lds, st, a);
+        else hipLaunchKernelGGL((dispatch_fused_kernel<16, 16>), g, b, lds, st, a);
+        return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+    }
+
     const int elem_out = quant ? 1 : (int)xs;
     if (N > 0) {
         const dim3 g(L.NB), b(kRouteThreads);
@@ -1748,34 +2140,6 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                            W, epr, L.nbs, h, elem_out, boff, ep_recv_count, want_seg ? 1 : 0, large, seg_flags,
                            (mode == MOE_SCHED_SEGMENT && N > 0) ? plan : nullptr, nplan);
     if (N > 0) {
-        DispatchArgs a;
-        a.x = static_cast<const char *>(x);
-        a.ids = expert_ids;
-        a.esc_in = static_cast<const int32_t *>(expert_scales);
-        a.expand_x = static_cast<char *>(expand_x);
-        a.dyn = dynamic_scales;
-        a.assist = assist_info;
-        a.esc_out = static_cast<int32_t *>(expand_scales);
-        a.erc = ep_recv_count;
-        a.lr = lr;
-        a.pc = pc;
-        a.pci = pci;
-        a.boff = boff;
-        a.plan = plan;
-        a.nplan = nplan;
-        a.W = W; a.bs = bs; a.epr = epr; a.h = h; a.K = K; a.nbs = L.nbs; a.R = (int)(N * K);
-        a.E = E; a.S = (int)S; a.NB = L.NB;
-        // with a scan block present it also wrote ep_recv_count
-        a.direct = (direct && !want_seg) ? 1 : 0;
-        a.rowbytes = (long long)rowbytes;
-        a.nsl = 1;
-        a.qs = quant_scales;
-        a.qkind = qkind;
-        // the plain share of the quantisers' stores shrinks as the rows written
-        // outgrow the Infinity Cache; the wavefront copy keeps half of its
-        // stores plain up to its own limit (see store_stream)
-        const long long qbytes = N * K * (long long)h;
-        a.store_mix = !quant || qbytes <= kMixedStoreMaxBytes ? 0 : (qbytes <= kQuarterPlainMaxBytes ? 1 : 2);
         if (mode == MOE_SCHED_TOKEN) {
             const size_t kdsm = (size_t)4 * K * sizeof(int);
             if (!quant) {
@@ -1810,7 +2174,12 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                         const int spg = (int)std::max<long long>(1, std::min<long long>(W, gtok / std::max(bs, 1)));
                         const int ngrp = (W + spg - 1) / spg;
                         const long long rows_per = std::max<long long>(1, N * K / ((long long)E * ngrp));
-                        const int parts = (int)std::min<long long>(64, std::max<long long>(1, rows_per / 32));
+                        // parts: workgroups per (slice, expert, group); any count >= 1 covers the rows.
+                        // Capped so that the grid stays below 2^32 work-items (8 * E * ngrp < 2^24 always
+                        // holds: E <= 1024, ngrp <= W <= 768), which matters past ~6.7e7 pairs.
+                        const long long max_parts = ((1ll << 32) / kQuantThreads - 1) / ((long long)kXcds * E * ngrp);
+                        const int parts = (int)std::max<long long>(
+                            1, std::min<long long>({64, std::max<long long>(1, rows_per / 32), max_parts}));
                         const dim3 gx((unsigned)((long long)kXcds * E * parts * ngrp));
                         const bool two = h > 1024 * kXcds;     // two 16-element pieces per lane
                         if (dtype == MOE_FP16) {
@@ -1899,13 +2268,16 @@ int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t 
     if (mask_kind == MOE_MASK_NONE && x_active_mask) return MOE_ERR_MASK;
     if ((rc = check_special(special, (long long)W * experts_per_rank))) return rc;
     const int zero_n = special ? special->zero_expert_num : 0, copy_n = special ? special->copy_expert_num : 0;
+    const int const_n = special ? special->const_expert_num : 0;
     const void *ori_x = copy_n > 0 ? special->ori_x : nullptr;
+    const void *const_x = const_n > 0 ? special->const_x : nullptr;
     if (copy_n > 0 && N > 0 && !ori_x) return MOE_ERR_NULLPTR;
+    if (const_n > 0 && N > 0 && !const_x) return MOE_ERR_NULLPTR;
     if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
     const size_t xs = elem_size(dtype);
     if (!aligned(expand_x, xs) || !aligned(assist_info, 4) || !aligned(ep_recv_count, 4) ||
         !aligned(expert_ids, 4) || !aligned(expert_scales, 4) || !aligned(x_out, xs) || !aligned(workspace, 16) ||
-        !aligned(ori_x, xs))
+        !aligned(ori_x, xs) || !aligned(const_x, xs))
         return MOE_ERR_ALIGN;
     if (N == 0) return MOE_OK;
 
@@ -1921,20 +2293,40 @@ int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t 
     a.mask_kind = mask_kind;
     a.ids = expert_ids;
     a.ori_x = static_cast<const char *>(ori_x);
+    a.const_x = static_cast<const char *>(const_x);
     a.E = W * experts_per_rank;
     a.zero_end = a.E + zero_n;
     a.copy_end = a.zero_end + copy_n;
-    a.pair_pass = (mask_kind != MOE_MASK_NONE || zero_n + copy_n > 0) ? 1 : 0;
+    a.const_end = a.copy_end + const_n;
+    a.pair_pass = (mask_kind != MOE_MASK_NONE || zero_n + copy_n + const_n > 0) ? 1 : 0;
     a.W = W; a.bs = bs; a.h = h; a.K = K; a.R = (int)(N * K); a.S = experts_per_rank * W;
+    a.epr = experts_per_rank;
     a.rowbytes = (long long)((size_t)h * xs);
     const bool vec = (size_t)a.rowbytes % 16 == 0 && aligned(expand_x, 16) && aligned(x_out, 16) &&
-                     aligned(ori_x, 16);
+                     aligned(ori_x, 16) && aligned(const_x, 16);
     const long long n = vec ? a.rowbytes / 16 : h;
     a.nsl = (int)((n + kGatherThreads - 1) / kGatherThreads);
     hipStream_t st = static_cast<hipStream_t>(stream);
     const size_t kdsm = (size_t)2 * K * sizeof(int);
     const dim3 g((unsigned)(N * a.nsl)), b(kGatherThreads);
     (void)hipGetLastError();
+    // One launch: slots found in each workgroup (see combine_fused_kernel)
+    if (vec && K <= kFusedMaxK && N * K <= kFusedCombinePairs && (long long)bs * K <= kFusedCombineSrcPairs) {
+        const bool pre = (long long)W * a.S <= kFusedCombineLdsCounts, k8 = K <= 8;
+        const size_t lds = pre ? (size_t)W * a.S * sizeof(int) : 0;
+#define MOE_FUSED_COMBINE(T)                                                                        \
+        do {                                                                                        \
+            if (pre && k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, true>), g, b, lds, st, a);        \
+            else if (pre) hipLaunchKernelGGL((combine_fused_kernel<T, 16, true>), g, b, lds, st, a);       \
+            else if (k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, false>), g, b, lds, st, a);        \
+            else hipLaunchKernelGGL((combine_fused_kernel<T, 16, false>), g, b, lds, st, a);               \
+        } while (0)
+        if (dtype == MOE_INT32) MOE_FUSED_COMBINE(int32_t);
+        else if (dtype == MOE_FP16) MOE_FUSED_COMBINE(F16);
+        else MOE_FUSED_COMBINE(BF16);
+#undef MOE_FUSED_COMBINE
+        return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+    }
     hipLaunchKernelGGL(combine_slots_kernel, dim3((unsigned)((a.R + kSlotThreads - 1) / kSlotThreads)),
                        dim3(kSlotThreads), 0, st, a);
     if (dtype == MOE_INT32) {

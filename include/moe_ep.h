@@ -103,7 +103,8 @@ enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_STATIC = 1, MOE_QUANT_DYN_TOKEN =
  *                  The pages ask each rank's active tokens to come first;
  *                  any pattern is accepted here.
  *  MOE_MASK_PAIR:  uint8 [N, K]; pair (t, k) is sent iff its byte is nonzero.
- * An inactive pair gets no row and no count, and its expert id is never read.
+ * An inactive pair gets no row and no count, and its expert id is ignored (a
+ * kernel may load it together with the mask byte; its value never matters).
  * The A active pairs fill expand_x rows 0..A-1 in the usual order, with
  * A = sum over ranks r of ep_recv_count[r][S-1]; later rows of the N*K-row
  * buffers are left untouched. Dispatch and combine take the same mask. */
@@ -111,20 +112,25 @@ enum moe_mask { MOE_MASK_NONE = 0, MOE_MASK_TOKEN = 1, MOE_MASK_PAIR = 2 };
 
 /* Special experts: zeroExpertNum / copyExpertNum / constExpertNum of
  * aclnnMoeDistributeDispatchV4 (参数说明), id ranges after the E real experts:
- * zero experts [E, E + zero), copy experts [E + zero, E + zero + copy). The
- * pages give only the ranges; here a pair routed to a special expert is not
- * exchanged (no row, no count, like an inactive pair), and in the combine a
- * zero expert adds nothing while a copy expert adds ori_x[t] * weight at its
- * place in the k order. Const experts are not supported (const_expert_num
- * must be 0, as the page's current version asks). Pass NULL for none.
- *  ori_x: DEVICE [N, h], the tokens given to dispatch, in the combine's dtype;
- *         read by moe_combine when copy_expert_num > 0, ignored by dispatch. */
+ * zero experts [E, E + zero), copy experts [E + zero, E + zero + copy), const
+ * experts [E + zero + copy, E + zero + copy + const). The pages give only the
+ * ranges; here a pair routed to a special expert is not exchanged (no row, no
+ * count, like an inactive pair), and in the combine, at the pair's place in
+ * the k order, a zero expert adds nothing, a copy expert adds ori_x[t] * weight
+ * and const expert j adds const_x[j] * weight (a const expert's output is one
+ * fixed vector, the same for every token). Pass NULL for none.
+ *  ori_x:   DEVICE [N, h], the tokens given to dispatch, in the combine's dtype;
+ *           read by moe_combine when copy_expert_num > 0, ignored by dispatch.
+ *  const_x: DEVICE [const_expert_num, h] in the combine's dtype, caller-owned;
+ *           read by moe_combine when const_expert_num > 0, ignored by dispatch.
+ * The counts are >= 0 and E + zero + copy + const < 2^31 (else MOE_ERR_SHAPE). */
 typedef struct moe_special_experts {
     int32_t zero_expert_num;
     int32_t copy_expert_num;
     int32_t const_expert_num;
     int32_t reserved;
     const void *ori_x;
+    const void *const_x;
 } moe_special_experts;
 
 /* How dispatch assigns its payload copies to workgroups. Both modes produce
@@ -171,7 +177,7 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
  *
  *  x              [N, h] dtype           tokens; rows s*bs..s*bs+bs-1 are rank s's
  *  expert_ids     [N, K] int32           global expert ids in [0, E), distinct per token
- *                                        (only active pairs' ids are read)
+ *                                        (inactive pairs' ids are ignored)
  *  expert_scales  [N, K] 4-byte or NULL  only read when expand_scales is given
  *  x_active_mask  uint8 [N] or [N, K]    see moe_mask; NULL with MOE_MASK_NONE
  *  mask_kind      moe_mask

@@ -50,9 +50,9 @@ def bind(lib):
     """Declare the C signatures on a loaded oracle library (the tests also bind
     copies of it built from altered sources, to show that the pins catch them)."""
     P, I, LL = ctypes.c_void_p, ctypes.c_int, ctypes.c_longlong
-    lib.oracle_dispatch.argtypes = [P, P, P, I, I, I, I, I, I, I, P, LL, P, I, I, I, P, P, P, P, P]
+    lib.oracle_dispatch.argtypes = [P, P, P, I, I, I, I, I, I, I, P, LL, P, I, I, I, I, P, P, P, P, P]
     lib.oracle_dispatch.restype = I
-    lib.oracle_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, I, I, P, P]
+    lib.oracle_combine.argtypes = [P, P, P, P, P, I, I, I, I, I, I, P, I, I, I, I, P, P, P]
     lib.oracle_combine.restype = I
     lib.oracle_large_segments.argtypes = [P, I, I, I, I, LL, P]
     lib.oracle_large_segments.restype = I
@@ -106,13 +106,13 @@ def _mask(mask, N, K):
 
 
 def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=None, bf16=False, mask=None,
-             zero_experts=0, copy_experts=0, quant_scales=None):
+             zero_experts=0, copy_experts=0, quant_scales=None, const_experts=0):
     """Counting-sort dispatch. Returns dict with expand_x, dynamic_scales,
     assist_info, ep_recv_count, rows (the number of rows written: N*K, or the
     active pairs under a mask) and (when scales are given) expand_scales.
     mask: None, per-token [N] or per-pair [N, K] (nonzero = active).
-    zero_experts / copy_experts: special expert ids E.. (zero) and E+zero.. (copy);
-    their pairs are not exchanged.
+    zero_experts / copy_experts / const_experts: special expert ids E.. (zero), E+zero..
+    (copy) and E+zero+copy.. (const); their pairs are not exchanged.
     quant_scales: quantMode 1's fp32 coefficients, 1, h or E*h values (q = sat8(rint(x * c)), the
     exact product rounded once)."""
     x = np.ascontiguousarray(x)
@@ -148,7 +148,7 @@ def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=Non
     m, mk = _mask(mask, N, K)
     rc = _load().oracle_dispatch(_ptr(x), _ptr(ids), _ptr(expert_scales), W, bs, epr, h, K, dt,
                                  int(quant_mode), _ptr(qs), 0 if qs is None else qs.size, _ptr(m), mk,
-                                 int(zero_experts), int(copy_experts),
+                                 int(zero_experts), int(copy_experts), int(const_experts),
                                  _ptr(expand_x), _ptr(dyn), _ptr(assist),
                                  _ptr(erc), _ptr(esc))
     if rc != 0:
@@ -161,11 +161,12 @@ def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=Non
 
 
 def combine(expand_x, assist_info, ep_recv_count, ids, expert_scales, ep_world, experts_per_rank,
-            bf16=False, mask=None, zero_experts=0, copy_experts=0, ori_x=None):
+            bf16=False, mask=None, zero_experts=0, copy_experts=0, ori_x=None, const_experts=0, const_x=None):
     """Push-style combine: x_out[t] = sum over active k of expand_x[row(t,k)] * scales[t,k]
     (0 for a token with no active pair); mask as for dispatch. A copy expert adds
-    ori_x[t] * weight (ori_x: the dispatch's x, same dtype as expand_x); a zero
-    expert adds nothing."""
+    ori_x[t] * weight (ori_x: the dispatch's x, same dtype as expand_x); const expert j
+    adds const_x[j] * weight (const_x [const_experts, h], same dtype); a zero expert adds
+    nothing."""
     expand_x = np.ascontiguousarray(expand_x)
     assist_info = np.ascontiguousarray(assist_info, dtype=np.int32)
     ep_recv_count = np.ascontiguousarray(ep_recv_count, dtype=np.int32)
@@ -184,9 +185,12 @@ def combine(expand_x, assist_info, ep_recv_count, ids, expert_scales, ep_world, 
     ox = None if ori_x is None else np.ascontiguousarray(ori_x)   # kept alive across the call
     if ox is not None:
         assert ox.shape == (N, h) and ox.dtype.itemsize == expand_x.dtype.itemsize
+    cx = None if const_x is None else np.ascontiguousarray(const_x)
+    if cx is not None:
+        assert cx.shape == (int(const_experts), h) and cx.dtype.itemsize == expand_x.dtype.itemsize
     rc = _load().oracle_combine(_ptr(expand_x), _ptr(assist_info), _ptr(ep_recv_count), _ptr(ids),
                                 _ptr(expert_scales), W, bs, epr, h, K, dt, _ptr(m), mk, int(zero_experts),
-                                int(copy_experts), _ptr(ox), _ptr(x_out))
+                                int(copy_experts), int(const_experts), _ptr(ox), _ptr(cx), _ptr(x_out))
     if rc != 0:
         raise OracleError("oracle_combine returned %d" % rc)
     return x_out

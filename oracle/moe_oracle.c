@@ -204,13 +204,15 @@ static size_t elem_size(int dtype) { return dtype == OR_INT32 ? 4 : 2; }
  * accepted.
  */
 /*
- * Special experts ([P3] 参数说明, zeroExpertNum / copyExpertNum): ids in
- * [E, E + zero) are zero experts, ids in [E + zero, E + zero + copy) copy
- * experts. The pages give only the id ranges; reading taken: a special pair is
- * not exchanged (no row, no count); in the combine a zero expert contributes
- * nothing and a copy expert contributes the token itself, ori_x[t] * weight,
- * at its place in the k order. (constExpertNum is not supported, as in the
- * page's current version.)
+ * Special experts ([P3] 参数说明, zeroExpertNum / copyExpertNum /
+ * constExpertNum): ids in [E, E + zero) are zero experts, ids in
+ * [E + zero, E + zero + copy) copy experts, ids in
+ * [E + zero + copy, E + zero + copy + const) const experts. The pages give only
+ * the id ranges; reading taken: a special pair is not exchanged (no row, no
+ * count); in the combine, at the pair's place in the k order, a zero expert
+ * contributes nothing, a copy expert the token itself, ori_x[t] * weight, and
+ * const expert j a fixed vector, const_x[j] * weight (the same for every
+ * token: the plainest meaning of an expert whose output is constant).
  */
 static int pair_active(const uint8_t *mask, int mask_kind, long long t, int k, int K)
 {
@@ -236,13 +238,13 @@ static int pair_active(const uint8_t *mask, int mask_kind, long long t, int k, i
 int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales,
                     int W, int bs, int epr, int h, int K, int dtype, int quant,
                     const float *qscale, long long qscale_n, const uint8_t *mask, int mask_kind, int zero_num,
-                    int copy_num,
+                    int copy_num, int const_num,
                     void *expand_x, float *dyn_scales, int32_t *assist,
                     int32_t *ep_recv_count, void *expand_scales)
 {
     if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
     if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0) != (mask != NULL)) return OR_BAD_ARG;
-    if (zero_num < 0 || copy_num < 0) return OR_BAD_ARG;
+    if (zero_num < 0 || copy_num < 0 || const_num < 0) return OR_BAD_ARG;
     if (quant < 0 || quant > 3) return OR_BAD_ARG;
     if (quant != 0 && dtype == OR_INT32) return OR_BAD_ARG;
     const int G = (h + 127) / 128;                     /* quantMode 3 groups per row */
@@ -257,7 +259,7 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
         for (int k = 0; k < K; ++k) {
             if (!pair_active(mask, mask_kind, t, k, K)) continue;
             int32_t e = ids[t * K + k];
-            if (e < 0 || (long long)e >= E + zero_num + copy_num) { free(cnt); return OR_BAD_ID; }
+            if (e < 0 || (long long)e >= E + zero_num + copy_num + const_num) { free(cnt); return OR_BAD_ID; }
             for (int j = 0; j < k; ++j)
                 if (pair_active(mask, mask_kind, t, j, K) && ids[t * K + j] == e) { free(cnt); return OR_DUP_ID; }
             if (e >= E) continue;                      /* special expert: not exchanged */
@@ -376,6 +378,15 @@ static int is_copy(const int32_t *ids, const uint8_t *mask, int mask_kind, long 
     return pair_active(mask, mask_kind, t, k, K) && e >= E + zero_num && e < E + zero_num + copy_num;
 }
 
+/* Index j of the const expert of pair (t, k), or -1 when it is not an active
+ * const-expert pair. */
+static long long const_index(const int32_t *ids, const uint8_t *mask, int mask_kind, long long t, int k, int K,
+                             long long E, int zero_num, int copy_num, int const_num)
+{
+    long long e = ids[t * K + k], c0 = E + zero_num + copy_num;
+    return pair_active(mask, mask_kind, t, k, K) && e >= c0 && e < c0 + const_num ? e - c0 : -1;
+}
+
 /*
  * Push-style, as [P1] 实现逻辑 describes it: every expert-output row is
  * returned to slot (src_token, topk_id) of its source rank's window; the
@@ -388,16 +399,18 @@ static int is_copy(const int32_t *ids, const uint8_t *mask, int mask_kind, long 
  * slot must be filled exactly once and no inactive one (same mask as the
  * dispatch). The sum runs over the active pairs in ascending k; a token with
  * none gets 0 (reading: the pages say nothing about the output of a token
- * that was not exchanged).
+ * that was not exchanged). Special experts contribute as described above
+ * (ori_x [N, h] and const_x [const_num, h], in the dtype of expand_x).
  */
 int oracle_combine(const void *expand_x, const int32_t *assist, const int32_t *ep_recv_count,
                    const int32_t *ids, const void *scales, int W, int bs, int epr, int h, int K,
-                   int dtype, const uint8_t *mask, int mask_kind, int zero_num, int copy_num,
-                   const void *ori_x, void *x_out)
+                   int dtype, const uint8_t *mask, int mask_kind, int zero_num, int copy_num, int const_num,
+                   const void *ori_x, const void *const_x, void *x_out)
 {
     if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
     if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0) != (mask != NULL)) return OR_BAD_ARG;
     if (zero_num < 0 || copy_num < 0 || (copy_num > 0 && !ori_x)) return OR_BAD_ARG;
+    if (const_num < 0 || (const_num > 0 && !const_x)) return OR_BAD_ARG;
     const long long N = (long long)W * bs, S = (long long)epr * W, E = (long long)W * epr;
 
     long long rows = 0, active = 0;
@@ -436,11 +449,14 @@ int oracle_combine(const void *expand_x, const int32_t *assist, const int32_t *e
                 uint32_t acc = 0;
                 for (int k = 0; k < K; ++k) {
                     int32_t sc = ((const int32_t *)scales)[t * K + k];
+                    long long cj = const_index(ids, mask, mask_kind, t, k, K, E, zero_num, copy_num, const_num);
                     if (slot[t * K + k] >= 0) {
                         const int32_t *y = (const int32_t *)expand_x + (size_t)slot[t * K + k] * h;
                         acc += (uint32_t)y[j] * (uint32_t)sc;
                     } else if (is_copy(ids, mask, mask_kind, t, k, K, E, zero_num, copy_num)) {
                         acc += (uint32_t)((const int32_t *)ori_x)[t * h + j] * (uint32_t)sc;
+                    } else if (cj >= 0) {
+                        acc += (uint32_t)((const int32_t *)const_x)[cj * h + j] * (uint32_t)sc;
                     }
                 }
                 ((int32_t *)x_out)[t * h + j] = (int32_t)acc;
@@ -448,10 +464,13 @@ int oracle_combine(const void *expand_x, const int32_t *assist, const int32_t *e
                 float acc = 0.0f;
                 for (int k = 0; k < K; ++k) {
                     float sc = ((const float *)scales)[t * K + k];
+                    long long cj = const_index(ids, mask, mask_kind, t, k, K, E, zero_num, copy_num, const_num);
                     if (slot[t * K + k] >= 0)
                         acc = fmaf(load_f32(expand_x, (size_t)slot[t * K + k] * h + j, dtype), sc, acc);
                     else if (is_copy(ids, mask, mask_kind, t, k, K, E, zero_num, copy_num))
                         acc = fmaf(load_f32(ori_x, (size_t)(t * h + j), dtype), sc, acc);
+                    else if (cj >= 0)
+                        acc = fmaf(load_f32(const_x, (size_t)(cj * h + j), dtype), sc, acc);
                 }
                 ((uint16_t *)x_out)[t * h + j] = store_16(acc, dtype);
             }

@@ -28,9 +28,10 @@ def test_algorithmic_bytes_of_the_workloads():
 
 def test_masked_and_special_bytes_count_only_rows_that_move():
     # brute force over the pairs: a row moves for an active pair of a real expert; a copy-expert pair makes the
-    # combine read its token; x is read for tokens with a row; the mask is read by both calls
+    # combine read its token; x is read for tokens with a row; the mask is read by both calls; the const
+    # experts' table is read once
     import numpy as np
-    for name in ("w16_h7168_bf16_q8_pair_mask", "w16_h7168_bf16_q8_zero_copy"):
+    for name in ("w16_h7168_bf16_q8_pair_mask", "w16_h7168_bf16_q8_special"):
         w = wl.BY_NAME[name]
         inp = wl.make_inputs(w)
         N, K, h, E = w.num_tokens, w.topk, w.h, w.num_experts
@@ -50,7 +51,9 @@ def test_masked_and_special_bytes_count_only_rows_that_move():
         mb = inp["mask"].size if "mask" in inp else 0
         erc = w.ep_world * E * 4
         want_d = toks * h * 2 + N * K * 4 + mb + rows * h + rows * 12 + erc + rows * 4
-        want_c = rows * h * 2 + copies * h * 2 + N * K * 4 + mb + rows * 12 + erc + N * K * 4 + N * h * 2
+        # the const experts' outputs are read once
+        want_c = (rows * h * 2 + copies * h * 2 + w.const_experts * h * 2 + N * K * 4 + mb + rows * 12 + erc
+                  + N * K * 4 + N * h * 2)
         assert bench.algorithmic_bytes(w, inp) == (want_d, want_c), name
         assert 0 < rows < w.rows
 

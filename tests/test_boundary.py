@@ -159,8 +159,9 @@ def _dispatch(**kw):
     (dict(quant=1, qs=8 * A, qn=1, sched=moe.MoeSchedule(mode=1)), SCHEDULE),   # token schedule only
     (dict(quant=1, qs=8 * A, qn=1, x=A + 2), ALIGN),           # 16-byte rows
     (dict(sp=moe.MoeSpecialExperts(zero_expert_num=-1)), SHAPE),
-    (dict(sp=moe.MoeSpecialExperts(const_expert_num=1)), SHAPE),        # const experts are not supported
+    (dict(sp=moe.MoeSpecialExperts(const_expert_num=-1)), SHAPE),
     (dict(sp=moe.MoeSpecialExperts(zero_expert_num=2 ** 31 - 4)), SHAPE),   # E + zero = 2^31
+    (dict(sp=moe.MoeSpecialExperts(copy_expert_num=2 ** 30, const_expert_num=2 ** 30 - 4)), SHAPE),   # 2^31 ids
     (dict(mk=3, mask=8 * A), MASK),                                     # unknown mask kind
     (dict(mk=1), MASK),                                                 # a kind without a mask
     (dict(mask=8 * A), MASK),                                           # a mask without a kind
@@ -201,7 +202,10 @@ def _combine(**kw):
     (dict(bs=0), OK),                                # empty batch: nothing to launch
     (dict(sp=moe.MoeSpecialExperts(copy_expert_num=2)), NULLPTR),      # copy experts need ori_x
     (dict(sp=moe.MoeSpecialExperts(copy_expert_num=2, ori_x=8 * A + 1)), ALIGN),
-    (dict(sp=moe.MoeSpecialExperts(const_expert_num=3)), SHAPE),
+    (dict(sp=moe.MoeSpecialExperts(const_expert_num=3)), NULLPTR),     # const experts need their outputs
+    (dict(sp=moe.MoeSpecialExperts(const_expert_num=3, const_x=8 * A + 1)), ALIGN),
+    (dict(sp=moe.MoeSpecialExperts(const_expert_num=-1, const_x=8 * A)), SHAPE),
+    (dict(sp=moe.MoeSpecialExperts(zero_expert_num=1, const_expert_num=2 ** 31 - 5, const_x=8 * A)), SHAPE),
     (dict(mk=-1), MASK),
     (dict(mk=2), MASK),                              # a kind without a mask
     (dict(mask=8 * A), MASK),                        # a mask without a kind

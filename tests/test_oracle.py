@@ -674,15 +674,18 @@ def test_group_quantiser_properties():
 def test_special_experts_match_a_dispatch_without_those_pairs():
     """Pairs routed to a zero or copy expert behave exactly like pairs switched
     off by a per-pair mask (a different code path in the oracle)."""
-    for w in (wl.custom(3, 7, 5, 3, 2, "int32", zero_experts=2, copy_experts=2, name="int32_special"),
+    for w in (wl.custom(3, 7, 5, 3, 2, "int32", zero_experts=2, copy_experts=2, const_experts=2,
+                        name="int32_special"),
               wl.custom(4, 9, 16, 4, 3, "bf16", "zipf_topk", quant_mode=2, zero_experts=3, copy_experts=1,
-                        name="bf16_special")):
+                        const_experts=2, name="bf16_special")):
         inp = wl.make_inputs(w)
         E = w.num_experts
         special = inp["ids"] >= E
         assert special.any() and (~special).any()
+        assert (inp["ids"] >= E + w.zero_experts + w.copy_experts).any()      # some const pairs
         d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
-                            bf16=w.dtype == "bf16", zero_experts=w.zero_experts, copy_experts=w.copy_experts)
+                            bf16=w.dtype == "bf16", zero_experts=w.zero_experts, copy_experts=w.copy_experts,
+                            const_experts=w.const_experts)
         ids_masked = np.where(special, 0, inp["ids"]).astype(np.int32)
         m = oracle.dispatch(inp["x"], ids_masked, w.ep_world, w.experts_per_rank, w.quant_mode,
                             bf16=w.dtype == "bf16", mask=~special)
@@ -690,10 +693,10 @@ def test_special_experts_match_a_dispatch_without_those_pairs():
             assert d[key].tobytes() == m[key].tobytes(), (w.name, key)
         # ids beyond the special ranges are still an error
         bad = inp["ids"].copy()
-        bad[0, 0] = E + w.zero_experts + w.copy_experts
+        bad[0, 0] = E + w.zero_experts + w.copy_experts + w.const_experts
         with pytest.raises(oracle.OracleError):
             oracle.dispatch(inp["x"], bad, w.ep_world, w.experts_per_rank, w.quant_mode, bf16=w.dtype == "bf16",
-                            zero_experts=w.zero_experts, copy_experts=w.copy_experts)
+                            zero_experts=w.zero_experts, copy_experts=w.copy_experts, const_experts=w.const_experts)
 
 
 def test_special_experts_int32_combine_closed_form():
@@ -711,6 +714,69 @@ def test_special_experts_int32_combine_closed_form():
     ssum = (inp["scales"].astype(np.int64) * counted).sum(axis=1)
     want = ((inp["x"].astype(np.int64) * ssum[:, None]) & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
     assert (out == want).all()
+
+
+def test_const_experts_int32_combine_closed_form():
+    """Identity expert, int32, with const experts ("aclnnMoeDistributeDispatchV4" 参数说明,
+    constExpertNum; reading: const expert j outputs the fixed row const_x[j]):
+    x_out[t] = x[t] * (sum of real and copy weights) + sum over const pairs of
+    const_x[j] * weight, in wrapping 32-bit arithmetic; zero experts add nothing."""
+    w = wl.custom(4, 11, 6, 4, 2, "int32", zero_experts=2, copy_experts=2, const_experts=3,
+                  name="int32_const_combine")
+    inp = wl.make_inputs(w)
+    E, Z, C, Q = w.num_experts, w.zero_experts, w.copy_experts, w.const_experts
+    ids, sc, cx = inp["ids"], inp["scales"].astype(np.int64), inp["const_x"].astype(np.int64)
+    assert cx.shape == (Q, w.h)
+    d = oracle.dispatch(inp["x"], ids, w.ep_world, w.experts_per_rank, zero_experts=Z, copy_experts=C,
+                        const_experts=Q)
+    out = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], ids, inp["scales"], w.ep_world,
+                         w.experts_per_rank, zero_experts=Z, copy_experts=C, ori_x=inp["x"], const_experts=Q,
+                         const_x=inp["const_x"])
+    is_const = (ids >= E + Z + C) & (ids < E + Z + C + Q)
+    assert is_const.any() and ((ids >= E) & (ids < E + Z)).any()
+    token_w = (sc * ((ids < E) | ((ids >= E + Z) & (ids < E + Z + C)))).sum(axis=1)
+    want = inp["x"].astype(np.int64) * token_w[:, None]
+    for t, k in zip(*np.nonzero(is_const)):
+        want[t] += cx[ids[t, k] - (E + Z + C)] * sc[t, k]
+    want = (want & 0xFFFFFFFF).astype(np.uint32).view(np.int32)
+    assert (out == want).all()
+    # a zero table makes const experts zero experts
+    zero = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], ids, inp["scales"], w.ep_world,
+                          w.experts_per_rank, zero_experts=Z, copy_experts=C, ori_x=inp["x"], const_experts=Q,
+                          const_x=np.zeros_like(inp["const_x"]))
+    as_zero = np.where(is_const, E, ids).astype(np.int32)        # E is the first zero expert
+    ref = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], as_zero, inp["scales"], w.ep_world,
+                         w.experts_per_rank, zero_experts=Z, copy_experts=C, ori_x=inp["x"])
+    assert (zero == ref).all()
+
+
+def test_const_expert_adds_its_row_in_k_order():
+    """fp16/bf16: a const pair's term is fma(const_x[j], w, acc) at its own k; the same sum
+    is obtained when the pair goes to an unused real expert whose output row is const_x[j]."""
+    for dt in ("fp16", "bf16"):
+        w = wl.custom(3, 13, 24, 4, 3, dt, "gauss_topk", const_experts=3, name="const_" + dt)
+        inp = wl.make_inputs(w)
+        E, bf = w.num_experts, dt == "bf16"
+        ids, cx = inp["ids"], inp["const_x"]
+        assert (ids >= E).any()
+        d = oracle.dispatch(inp["x"], ids, w.ep_world, w.experts_per_rank, bf16=bf, const_experts=3)
+        got = oracle.combine(d["expand_x"], d["assist_info"], d["ep_recv_count"], ids, inp["scales"], w.ep_world,
+                             w.experts_per_rank, bf16=bf, const_experts=3, const_x=cx)
+        real = ids.copy()
+        for t in range(w.num_tokens):
+            free = [e for e in range(E) if e not in set(ids[t].tolist())]
+            for k in range(w.topk):
+                if real[t, k] >= E:
+                    real[t, k] = free.pop()
+        r = oracle.dispatch(inp["x"], real, w.ep_world, w.experts_per_rank, bf16=bf)
+        rows = r["expand_x"].copy()
+        for i, (s, tok, k) in enumerate(r["assist_info"].tolist()):   # the expert's output for those pairs
+            t = s * w.bs + tok
+            if ids[t, k] >= E:
+                rows[i] = cx[ids[t, k] - E]
+        want = oracle.combine(rows, r["assist_info"], r["ep_recv_count"], real, inp["scales"], w.ep_world,
+                              w.experts_per_rank, bf16=bf)
+        assert got.view(np.uint16).tobytes() == want.view(np.uint16).tobytes(), dt
 
 
 def test_copy_expert_adds_the_token_in_k_order():

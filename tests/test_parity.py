@@ -56,17 +56,32 @@ def gpu_quant_scales(w, inp):
     return to_dev(inp["quant_scales"]) if w.quant_mode == 1 else None
 
 
+def special_args(w):
+    """The workload's special-expert counts (dispatch and combine take the same)."""
+    return dict(zero_experts=w.zero_experts, copy_experts=w.copy_experts, const_experts=w.const_experts)
+
+
+def gpu_combine_special(w, inp, x):
+    """Combine's special-expert inputs on the GPU: the tokens for copy experts (the combine's dtype:
+    bf16 tokens for quantised runs) and the const experts' outputs."""
+    cbf = w.dtype == "bf16" or w.quant_mode != 0
+    return dict(special_args(w), ori_x=x if w.copy_experts else None,
+                const_x=to_dev(inp["const_x"], cbf) if w.const_experts else None)
+
+
+def oracle_combine_special(w, inp):
+    return dict(special_args(w), ori_x=inp["x"] if w.copy_experts else None,
+                const_x=inp["const_x"] if w.const_experts else None)
+
+
 def run_gpu(w, inp, schedule=None):
     bf = w.dtype == "bf16"
     x, ids, sc = to_dev(inp["x"], bf), to_dev(inp["ids"]), to_dev(inp["scales"])
-    special = dict(zero_experts=w.zero_experts, copy_experts=w.copy_experts)
     ex, dyn, assist, erc, esc = moe.dispatch(x, ids, w.ep_world, w.experts_per_rank, w.quant_mode,
                                              expert_scales=sc, schedule=schedule,
-                                             quant_scales=gpu_quant_scales(w, inp), **special)
+                                             quant_scales=gpu_quant_scales(w, inp), **special_args(w))
     y = gpu_identity_expert(ex, dyn if w.quant_mode != 1 else torch.ones(ex.shape[0], device=DEV))
-    # copy experts read the tokens in the combine's dtype (bf16 tokens for quantised runs)
-    xo = moe.combine(y, assist, erc, ids, sc, w.ep_world, w.experts_per_rank,
-                     ori_x=x if w.copy_experts else None, **special)
+    xo = moe.combine(y, assist, erc, ids, sc, w.ep_world, w.experts_per_rank, **gpu_combine_special(w, inp, x))
     torch.cuda.synchronize()
     return dict(expand_x=to_np(ex), dynamic_scales=None if dyn is None else to_np(dyn),
                 assist_info=to_np(assist), ep_recv_count=to_np(erc), expand_scales=to_np(esc),
@@ -75,15 +90,14 @@ def run_gpu(w, inp, schedule=None):
 
 def run_oracle(w, inp):
     bf = w.dtype == "bf16"
-    special = dict(zero_experts=w.zero_experts, copy_experts=w.copy_experts)
     d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
-                        expert_scales=inp["scales"], bf16=bf, quant_scales=inp.get("quant_scales"), **special)
+                        expert_scales=inp["scales"], bf16=bf, quant_scales=inp.get("quant_scales"),
+                        **special_args(w))
     y = oracle.identity_expert(d["expand_x"], d["dynamic_scales"] if w.quant_mode != 1
                                else np.ones(w.rows, np.float32))
     out_bf = bf or w.quant_mode != 0
     d["x_out"] = oracle.combine(y, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"],
-                                w.ep_world, w.experts_per_rank, bf16=out_bf,
-                                ori_x=inp["x"] if w.copy_experts else None, **special)
+                                w.ep_world, w.experts_per_rank, bf16=out_bf, **oracle_combine_special(w, inp))
     d["y"] = y
     return d
 
@@ -151,9 +165,9 @@ def test_page_workloads_full_size(w):
     check(w)
 
 
-@pytest.mark.parametrize("name", ["w16_h7168_bf16_q8_pair_mask", "w16_h7168_bf16_q8_zero_copy"])
+@pytest.mark.parametrize("name", ["w16_h7168_bf16_q8_pair_mask", "w16_h7168_bf16_q8_special"])
 def test_benchmarked_mask_and_special_expert_workloads_full_size(name):
-    """The bench's masked and zero/copy-expert lines, at their full size and with their own inputs."""
+    """The bench's masked and special-expert lines, at their full size and with their own inputs."""
     w = wl.BY_NAME[name]
     if w.mask == "none":
         check(w)
@@ -380,6 +394,14 @@ SPECIAL = [
     wl.custom(8, 16, 64, 4, 2, "fp16", "gauss_topk", copy_experts=40, name="fp16_mostly_copy"),
     wl.custom(8, 128, 1024, 8, 4, "bf16", "zipf_topk", zero_experts=8, copy_experts=8, name="bf16_copy_wave"),
     wl.custom(2, 6, 32, 2, 1, "fp16", "gauss_topk", zero_experts=30, name="fp16_mostly_zero"),
+    # const experts (constExpertNum): const expert j adds row j of the const table
+    wl.custom(4, 9, 16, 3, 2, "int32", zero_experts=1, copy_experts=1, const_experts=3, name="int32_const"),
+    wl.custom(3, 7, 13, 3, 2, "int32", const_experts=2, name="int32_const_scalar_path"),
+    wl.custom(4, 33, 7168, 8, 4, "bf16", "gauss_topk", quant_mode=2, zero_experts=4, copy_experts=4,
+              const_experts=4, name="bf16_q8_zero_copy_const"),
+    wl.custom(8, 32, 7168, 8, 8, "fp16", "gauss_topk", const_experts=8, name="fp16_w8_const"),
+    wl.custom(2, 1100, 64, 8, 4, "bf16", "zipf_topk", zero_experts=2, copy_experts=2, const_experts=2,
+              name="bf16_slot_path_special"),
 ]
 
 
@@ -393,6 +415,40 @@ def test_special_experts(w):
 def test_special_experts_with_a_mask_and_the_segment_schedule(kind):
     w = wl.custom(4, 40, 512, 4, 3, "bf16", "zipf_topk", zero_experts=3, copy_experts=3, name="special_masked")
     check_masked(w, kind, schedule=moe.MoeSchedule(mode=moe.MOE_SCHED_SEGMENT, large_segment_bytes=1024))
+
+
+# --------------------------------------------------------------------------
+# one launch per call (rows by counting) against the route / slot-pass paths:
+# shapes on both sides of each threshold (dispatch: N*K <= 4096, K <= 16,
+# W*E <= 4096; combine: bs*K <= 1024, K <= 16, N*K < 2^16, ep_recv_count in
+# LDS for W*E <= 2048)
+# --------------------------------------------------------------------------
+
+FUSED = [
+    wl.custom(8, 64, 2048, 8, 8, "fp16", "gauss_topk", name="fused_nk4096_k8"),
+    wl.custom(4, 16, 1024, 16, 8, "bf16", "zipf_topk", name="fused_k16_nk1024"),
+    wl.custom(4, 48, 1024, 16, 8, "bf16", "gauss_topk", name="fused_k16_nk3072"),
+    wl.custom(2, 257, 512, 8, 4, "fp16", "zipf_topk", name="route_nk4112_fused_combine"),
+    wl.custom(4, 8, 256, 17, 8, "bf16", "gauss_topk", name="k17_no_fused_path"),
+    wl.custom(64, 2, 64, 4, 2, "bf16", "zipf_topk", name="w64_e128_counts_past_lds"),
+    wl.custom(16, 16, 512, 8, 16, "fp16", "gauss_topk", name="w16_e256_combine_erc_global"),
+    wl.custom(2, 1025, 128, 8, 4, "bf16", "gauss_topk", name="bsk8200_slot_pass"),
+    wl.custom(4, 128, 256, 8, 4, "fp16", "zipf_topk", name="bsk1024_last_fused_combine"),
+    wl.custom(4, 129, 256, 8, 4, "fp16", "zipf_topk", name="bsk1032_slot_pass"),
+    wl.custom(5, 3, 8, 7, 3, "int32", name="int32_h8_two_chunks"),
+    wl.custom(2, 1, 16, 1, 1, "int32", name="one_token_per_rank_top1"),
+]
+
+
+@pytest.mark.parametrize("w", FUSED, ids=lambda w: w.name)
+def test_one_launch_paths_and_their_thresholds(w):
+    check(w)
+
+
+@pytest.mark.parametrize("kind", ["token_any", "pair"])
+@pytest.mark.parametrize("w", [FUSED[0], FUSED[2], FUSED[7]], ids=lambda w: w.name)
+def test_one_launch_paths_with_a_mask(w, kind):
+    check_masked(w, kind)
 
 
 def test_int32_combine_wraps_like_the_oracle():
@@ -528,22 +584,21 @@ def check_masked(w, kind, seed=1, schedule=None):
     bf = w.dtype == "bf16"
     x, ids, sc = to_dev(inp["x"], bf), to_dev(inp["ids"]), to_dev(inp["scales"])
     m = torch.from_numpy(mask).to(DEV)
-    special = dict(zero_experts=w.zero_experts, copy_experts=w.copy_experts)
     ex, dyn, assist, erc, esc = moe.dispatch(x, ids, w.ep_world, w.experts_per_rank, w.quant_mode,
                                              expert_scales=sc, schedule=schedule, x_active_mask=m,
-                                             quant_scales=gpu_quant_scales(w, inp), **special)
+                                             quant_scales=gpu_quant_scales(w, inp), **special_args(w))
     y = gpu_identity_expert(ex, dyn if w.quant_mode != 1 else torch.ones(ex.shape[0], device=DEV))
     xo = moe.combine(y, assist, erc, ids, sc, w.ep_world, w.experts_per_rank, x_active_mask=m,
-                     ori_x=x if w.copy_experts else None, **special)
+                     **gpu_combine_special(w, inp, x))
     torch.cuda.synchronize()
     d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode,
                         expert_scales=inp["scales"], bf16=bf, mask=mask, quant_scales=inp.get("quant_scales"),
-                        **special)
+                        **special_args(w))
     yo = oracle.identity_expert(d["expand_x"], d["dynamic_scales"] if w.quant_mode != 1
                                 else np.ones(w.rows, np.float32))
     xo_o = oracle.combine(yo, d["assist_info"], d["ep_recv_count"], inp["ids"], inp["scales"], w.ep_world,
                           w.experts_per_rank, bf16=bf or w.quant_mode != 0, mask=mask,
-                          ori_x=inp["x"] if w.copy_experts else None, **special)
+                          **oracle_combine_special(w, inp))
     A = d["rows"]
     assert (to_np(erc) == d["ep_recv_count"]).all(), "ep_recv_count"
     assert (to_np(assist)[:A] == d["assist_info"][:A]).all(), "assist_info"
@@ -556,7 +611,7 @@ def check_masked(w, kind, seed=1, schedule=None):
         assert (g == xo_o).all(), "x_out"
     else:
         assert g.view(np.uint16).tobytes() == xo_o.view(np.uint16).tobytes(), "x_out bits"
-    if w.dtype != "int32" and not (w.zero_experts or w.copy_experts):
+    if w.dtype != "int32" and not (w.zero_experts or w.copy_experts or w.const_experts):
         # and the tolerance metric over the active pairs
         act = np.repeat(mask[:, None], w.topk, axis=1) if mask.ndim == 1 else mask
         yf = as_f32(yo, True if (bf or w.quant_mode != 0) else False)

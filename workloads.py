@@ -63,6 +63,7 @@ class Workload:
     zipf_s: float = 1.2
     zero_experts: int = 0   # special experts after the E real ones: ids E .. E+zero-1
     copy_experts: int = 0   # then E+zero .. E+zero+copy-1
+    const_experts: int = 0  # then E+zero+copy .. E+zero+copy+const-1
     static_scales: str = "expert"   # quantMode 1 coefficients: "scalar" | "column" | "expert"
     mask: str = "none"      # token mask: "none" | "token_prefix" (each rank's first 3/4 of its tokens)
                             # | "pair" (each pair active with probability 3/4)
@@ -96,21 +97,23 @@ EXTRA_WORKLOADS = [
     # per-token int8 with a per-pair token mask (3/4 of the pairs active)
     Workload("w16_h7168_bf16_q8_pair_mask", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2,
              mask="pair"),
-    # per-token int8 with 16 zero and 16 copy experts beside the 256 real ones (the router picks among 288)
-    Workload("w16_h7168_bf16_q8_zero_copy", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2,
-             zero_experts=16, copy_experts=16),
+    # per-token int8 with 16 zero, 16 copy and 16 const experts beside the 256 real ones (the router
+    # picks among 304)
+    Workload("w16_h7168_bf16_q8_special", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=2,
+             zero_experts=16, copy_experts=16, const_experts=16),
 ]
 BY_NAME = {w.name: w for w in WORKLOADS + EXTRA_WORKLOADS}
 
 
 def custom(ep_world, bs, h, topk, experts_per_rank, dtype="int32", routing="uniform_distinct",
            quant_mode=0, x_lo=-1000, x_hi=1000, name="custom", index=100, zero_experts=0, copy_experts=0,
-           static_scales="expert"):
-    """A workload of arbitrary shape, for edge-case tests. zero_experts / copy_experts add
-    special expert ids after the E real ones, drawn by the routing like any other."""
+           static_scales="expert", const_experts=0):
+    """A workload of arbitrary shape, for edge-case tests. zero_experts / copy_experts /
+    const_experts add special expert ids after the E real ones, drawn by the routing like
+    any other."""
     return Workload(name, index, ep_world, bs, h, topk, experts_per_rank, dtype, routing,
                     quant_mode=quant_mode, x_lo=x_lo, x_hi=x_hi, zero_experts=zero_experts,
-                    copy_experts=copy_experts, static_scales=static_scales)
+                    copy_experts=copy_experts, static_scales=static_scales, const_experts=const_experts)
 
 
 def static_scales(w: Workload) -> np.ndarray:
@@ -130,7 +133,7 @@ def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
 
 def _routing(w: Workload, rng: np.random.Generator):
     N, K = w.num_tokens, w.topk
-    E = w.num_experts + w.zero_experts + w.copy_experts     # every id the router can pick
+    E = w.num_experts + w.zero_experts + w.copy_experts + w.const_experts   # every id the router can pick
     if w.routing == "uniform_distinct":
         ids = np.stack([rng.permutation(E)[:K] for _ in range(N)]).astype(np.int32) if N else \
             np.zeros((0, K), np.int32)
@@ -160,6 +163,9 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
       quant_scales     fp32 quantMode 1 coefficients (only for quantMode 1)
       mask     uint8 [N] or [N, K] token mask (only when the workload has one;
                drawn after everything else, so the other inputs do not change)
+      const_x  [const_experts, h] the const experts' outputs, in the combine's dtype
+               (the token dtype, or bf16 bits when dispatch quantises): int32 in the
+               token range, else N(0,1); drawn last (only with const experts)
     """
     rng = np.random.default_rng(1234 + w.index if seed is None else seed)
     N, h = w.num_tokens, w.h
@@ -186,4 +192,11 @@ def make_inputs(w: Workload, seed: Optional[int] = None) -> dict:
         out["mask"] = (rng.random((N, w.topk)) < 0.75).astype(np.uint8)
     elif w.mask != "none":
         raise ValueError(w.mask)
+    if w.const_experts:
+        shape = (w.const_experts, h)
+        if w.dtype == "int32":
+            out["const_x"] = rng.integers(w.x_lo, w.x_hi + 1, size=shape, dtype=np.int64).astype(np.int32)
+        else:
+            g = rng.standard_normal(shape).astype(np.float32)
+            out["const_x"] = g.astype(np.float16) if (w.dtype == "fp16" and not w.quant_mode) else f32_to_bf16_bits(g)
     return out
