@@ -30,8 +30,9 @@ MOE_QUANT_NONE, MOE_QUANT_STATIC, MOE_QUANT_DYN_TOKEN, MOE_QUANT_DYN_GROUP = 0, 
 MOE_SCHED_TOKEN, MOE_SCHED_SEGMENT = 0, 1
 MOE_MASK_NONE, MOE_MASK_TOKEN, MOE_MASK_PAIR = 0, 1, 2
 
-EXPORTS = ("moe_dispatch_workspace_size", "moe_dispatch", "moe_combine_workspace_size", "moe_combine",
-           "moe_status_str")
+EXPORTS = ("moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_noalloc", "moe_combine_workspace_size",
+           "moe_combine", "moe_status_str")
+NOALLOC_SCRATCH_BYTES = 32 << 20      # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class MoeError(RuntimeError):
@@ -80,6 +81,9 @@ def library() -> ctypes.CDLL:
     lib.moe_dispatch.argtypes = [P, P, P, P, I, ctypes.POINTER(MoeSpecialExperts), I, I, I, I, I, I, I, P,
                                  ctypes.c_int64, P, P, P, P, P, ctypes.POINTER(MoeSchedule), P, SZ, P]
     lib.moe_dispatch.restype = I
+    lib.moe_dispatch_noalloc.argtypes = [P, P, P, P, I, ctypes.POINTER(MoeSpecialExperts), I, I, I, I, I, I, I, P,
+                                         ctypes.c_int64, P, P, P, P, P, ctypes.POINTER(MoeSchedule), P]
+    lib.moe_dispatch_noalloc.restype = I
     lib.moe_combine_workspace_size.argtypes = [I, I, I, I, I, I, ctypes.POINTER(SZ)]
     lib.moe_combine_workspace_size.restype = I
     lib.moe_combine.argtypes = [P, P, P, P, P, P, I, ctypes.POINTER(MoeSpecialExperts), I, I, I, I, I, I, P, P,
@@ -263,6 +267,34 @@ def dispatch_into(buf: DispatchBuffers, x: torch.Tensor, expert_ids: torch.Tenso
         _ptr(buf.expand_scales), ctypes.byref(schedule) if schedule is not None else None,
         _ptr(buf.workspace), buf.workspace.numel(), _stream_ptr(dev))
     _check("moe_dispatch", rc)
+    return buf
+
+
+def dispatch_noalloc_into(buf: DispatchBuffers, x: torch.Tensor, expert_ids: torch.Tensor,
+                          expert_scales: Optional[torch.Tensor] = None, schedule: Optional[MoeSchedule] = None,
+                          x_active_mask: Optional[torch.Tensor] = None, zero_experts: int = 0,
+                          copy_experts: int = 0, quant_scales: Optional[torch.Tensor] = None,
+                          const_experts: int = 0):
+    """moe_dispatch_noalloc into preallocated buffers on the current stream: the same outputs as
+    dispatch_into, with the library's own per-GPU scratch in place of buf.workspace (which is not
+    used). The same checks run first."""
+    W, bs, epr, h, K = buf.shape
+    dev = buf.check()
+    _check_tensor("x", x, buf.dtype, (W * bs, h), dev)
+    _check_tensor("expert_ids", expert_ids, torch.int32, (W * bs, K), dev)
+    if expert_scales is not None:
+        _check_tensor("expert_scales", expert_scales,
+                      torch.int32 if getattr(expert_scales, "dtype", None) == torch.int32 else torch.float32,
+                      (W * bs, K), dev)
+    mp, mk = _mask_args(x_active_mask, W * bs, K, dev)
+    qp, qn = _quant_scales_args(quant_scales, dev)
+    rc = library().moe_dispatch_noalloc(
+        _ptr(x), _ptr(expert_ids), _ptr(expert_scales), mp, mk, _special(zero_experts, copy_experts, None,
+                                                                         const_experts), W, bs, epr,
+        h, K, dtype_code(buf.dtype), buf.quant_mode, qp, ctypes.c_int64(qn),
+        _ptr(buf.expand_x), _ptr(buf.dynamic_scales), _ptr(buf.assist_info), _ptr(buf.ep_recv_count),
+        _ptr(buf.expand_scales), ctypes.byref(schedule) if schedule is not None else None, _stream_ptr(dev))
+    _check("moe_dispatch_noalloc", rc)
     return buf
 
 

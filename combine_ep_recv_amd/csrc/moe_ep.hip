@@ -45,6 +45,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 
 #include "moe_ep.h"
@@ -1957,6 +1958,32 @@ void launch_quant_wave(int J, dim3 g, dim3 b, hipStream_t st, const DispatchArgs
     else hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 16, QM>), g, b, 0, st, a);
 }
 
+// ---- scratch of the allocation-free dispatch (moe_dispatch_noalloc) ----
+// One file-scope device array: every GPU the library runs on holds its own
+// copy, at its own address, until the process ends. Host code must not use
+// the array's name as a device address (on the host it names a stand-in): the
+// address is looked up per device with hipGetSymbolAddress and kept here.
+constexpr size_t kScratchBytes = MOE_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];             // device address of `scratch` per device, once looked up
+
+// The scratch's device address on the current device (looked up on the first
+// call there, with that device current), or nullptr when the lookup fails.
+void *scratch_on_current_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 extern "C" {
@@ -2238,6 +2265,30 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         }
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
+}
+
+int moe_dispatch_noalloc(const void *x, const int32_t *expert_ids, const void *expert_scales,
+                         const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
+                         int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype, int quant_mode,
+                         const float *quant_scales, int64_t quant_scales_numel, void *expand_x,
+                         float *dynamic_scales, int32_t *assist_info, int32_t *ep_recv_count, void *expand_scales,
+                         const moe_schedule *schedule, void *stream)
+{
+    size_t need = 0;
+    int rc = moe_dispatch_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype, quant_mode, &need);
+    if (rc) return rc;
+    if (need > kScratchBytes) return MOE_ERR_WORKSPACE;
+    void *ws = scratch_on_current_device();
+    if (!ws) {
+        (void)hipGetLastError();
+        return MOE_ERR_LAUNCH;
+    }
+    // Every dispatch kernel writes the workspace words it reads (chunk counts, ranks, offsets, the
+    // plan and its length) before reading them, so nothing in the scratch must start at zero.
+    return moe_dispatch(x, expert_ids, expert_scales, x_active_mask, mask_kind, special, ep_world, bs,
+                        experts_per_rank, h, topk, dtype, quant_mode, quant_scales, quant_scales_numel, expand_x,
+                        dynamic_scales, assist_info, ep_recv_count, expand_scales, schedule, ws, kScratchBytes,
+                        stream);
 }
 
 int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype,

@@ -214,6 +214,33 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                  int32_t *ep_recv_count, void *expand_scales, const moe_schedule *schedule,
                  void *workspace, size_t workspace_bytes, void *stream);
 
+/* Scratch of moe_dispatch_noalloc, per GPU (bytes). */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * Dispatch without a workspace argument, for callers that cannot allocate:
+ * code under HIP graph capture, tight serving loops, and harnesses that forbid
+ * hipMalloc. Same arguments, outputs and validation as moe_dispatch, less the
+ * workspace. It allocates nothing: its scratch is a file-scope device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (32 MiB) that each GPU the library runs on holds
+ * until the process ends; its address on the current device (hipGetDevice) is
+ * looked up on the first call there, and `stream` must belong to that device.
+ * A shape whose moe_dispatch_workspace_size exceeds the scratch returns
+ * MOE_ERR_WORKSPACE before anything is launched (16 ranks x 256 tokens, top-8,
+ * needs about 0.3 MiB; the limit lies near 6 million (token, expert) pairs);
+ * a failed lookup returns MOE_ERR_LAUNCH. Every call on one GPU shares that
+ * GPU's array, which keeps the last call's contents (none of which a call
+ * needs to find zeroed): calls that overlap on one GPU, on different streams
+ * or host threads, race and must be ordered by the caller.
+ */
+int moe_dispatch_noalloc(const void *x, const int32_t *expert_ids, const void *expert_scales,
+                         const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
+                         int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype,
+                         int quant_mode, const float *quant_scales, int64_t quant_scales_numel,
+                         void *expand_x, float *dynamic_scales, int32_t *assist_info,
+                         int32_t *ep_recv_count, void *expand_scales, const moe_schedule *schedule,
+                         void *stream);
+
 /* Phase one of combine: validates the scalars and writes the workspace size
  * (N*K int32 slots, rounded up to 256 bytes). */
 int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h, int topk,
