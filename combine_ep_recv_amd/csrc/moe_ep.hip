@@ -1073,7 +1073,12 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(Dispa
 
 // Rows, assist_info, expand_scales (and, on the direct path, ep_recv_count)
 // without the payload: one wavefront per token. It runs before a payload pass
-// that walks expand_x in row order.
+// that walks expand_x in expert-major order, and also reads its token once,
+// contiguously, so that the payload pass's scattered re-reads of token slices
+// find them in the Infinity Cache instead of HBM. At 16 ranks x 256 bf16 tokens
+// with per-expert static coefficients that read takes a timed step (after the
+// 1 GiB eviction) from 192.7 to 169.5 us; back to back, with the tokens
+// already cached, it costs 6 us (157 -> 163 us).
 __global__ __launch_bounds__(kQuantThreads) void dispatch_meta_kernel(DispatchArgs a)
 {
     const int lane = threadIdx.x & 63;
@@ -1084,6 +1089,14 @@ __global__ __launch_bounds__(kQuantThreads) void dispatch_meta_kernel(DispatchAr
     if (t >= N) return;
     const size_t pk = (size_t)t * K + (lane < K ? lane : 0);
     lane_pair_row(a, t, lane, a.ids[pk], a.lr[pk], true);
+    const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
+    const int nc = (int)(a.rowbytes / 16);
+    uint32_t sink = 0;
+    for (int c = lane; c < nc; c += 64) {
+        const uint4 v = src[c];
+        sink ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    asm volatile("" ::"v"(sink));      // keeps the loads: their only purpose is to leave the lines cached
 }
 
 // Static quantisation with one coefficient per expert and column, expert-major

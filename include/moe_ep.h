@@ -201,10 +201,14 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
  *
  * Ranges: ep_world in [2, 768], experts_per_rank >= 1, E <= 1024,
  * 1 <= topk <= E, bs >= 0 (bs == 0 writes zero counts and nothing else),
- * h >= 1, N*K < 2^31, N < 2^24, N*ceil(h/128) < 2^25, E + zero + copy experts < 2^31.
- * Active ids outside [0, E + zero + copy) or repeated within a token are a
- * precondition violation: the kernels stay in bounds but the outputs are
+ * h >= 1, N*K < 2^31, N < 2^24, N*ceil(h/128) < 2^25, E + special experts < 2^31.
+ * Active ids outside [0, E + zero + copy + const) or repeated within a token
+ * are a precondition violation: the kernels stay in bounds but the outputs are
  * unspecified. Outputs are bitwise deterministic.
+ * Copies of up to 4096 (token, expert) pairs with rows in 16-byte pieces and
+ * topk <= 16 run as one kernel, which counts each pair's row in the workgroup
+ * that writes it; other calls launch the route kernel first. Both give the same
+ * outputs; the workspace is required either way.
  */
 int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales,
                  const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
@@ -260,20 +264,24 @@ int moe_combine_workspace_size(int ep_world, int bs, int experts_per_rank, int h
  *
  *  expand_x       [ROWS, h] dtype (fp16, bf16 or int32; the expert outputs)
  *  assist_info    [ROWS, 3]: dispatch's, unchanged
- *  ep_recv_count  [W, S]: dispatch's, unchanged (checked for presence and alignment;
- *                 the rows are located through assist_info)
+ *  ep_recv_count  [W, S]: dispatch's, unchanged (the slot pass locates rows through
+ *                 assist_info; the one-launch combine reads segment starts from here)
  *  expert_ids     [N, K] int32: the ids given to dispatch (checked likewise)
  *  expert_scales  [N, K] fp32 for fp16/bf16, int32 for int32 data
  *  x_active_mask, mask_kind: the dispatch's. The sum then runs over the
  *                 active pairs only (k ascending); a token with none gets 0.
  *  special        the dispatch's (NULL for none); needs ori_x when copy experts
- *                 exist. With a mask or special experts, ep_recv_count is read
- *                 to find the row total.
+ *                 exist and const_x when const experts exist. With a mask or
+ *                 special experts, ep_recv_count is read to find the row total.
  *  x_out          [N, h] dtype
  *  workspace      device scratch of at least the queried size
  * The scalars must equal those given to dispatch. Rows that assist_info does
  * not name leave their slot undefined; the kernels stay in bounds but the
- * affected outputs are unspecified.
+ * affected outputs are unspecified. Up to 1024 pairs per source rank (bs*K),
+ * fewer than 2^16 pairs in all, rows in 16-byte pieces and topk <= 16, the
+ * combine is one kernel that finds each pair's row from ep_recv_count (its
+ * segment's start) and the source's earlier expert ids, instead of a slot pass
+ * over assist_info; the outputs are the same.
  */
 int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t *ep_recv_count,
                 const int32_t *expert_ids, const void *expert_scales,

@@ -693,6 +693,38 @@ def test_random_configurations(w, kind):
         check_masked(w, kind)
 
 
+def random_small_case(i):
+    """Small batches, mostly on the one-launch paths (dispatch: copies with N*K <= 4096, K <= 16;
+    combine: bs*K <= 1024), with const experts beside zero and copy ones."""
+    rng = np.random.default_rng(1900 + i)
+    W = int(rng.choice([2, 3, 4, 5, 8, 12]))
+    K = int(rng.integers(1, 17))
+    epr = int(rng.integers(max(1, -(-K // W)), 9))
+    bs = int(rng.integers(1, max(2, min(1024 // K, 4096 // (W * K)) + 1)))
+    dtype = str(rng.choice(["int32", "fp16", "bf16"]))
+    quant = 0 if dtype == "int32" else int(rng.choice([0, 0, 0, 2]))
+    step = 4 if dtype == "int32" else 8                # 16-byte rows, except now and then
+    h = step * int(rng.integers(1, 400)) if rng.random() < 0.85 else int(rng.integers(1, 300))
+    routing = "uniform_distinct" if dtype == "int32" else str(rng.choice(["gauss_topk", "zipf_topk"]))
+    zero, const = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+    copy = 0 if (quant and dtype != "bf16") else int(rng.integers(0, 3))
+    kind = str(rng.choice(["none", "token_any", "pair"]))
+    w = wl.custom(W, bs, h, K, epr, dtype, routing, quant_mode=quant, zero_experts=zero, copy_experts=copy,
+                  const_experts=const, index=1300 + i, name="small%d" % i)
+    return w, kind
+
+
+RANDOM_SMALL_CASES = [random_small_case(i) for i in range(24)]
+
+
+@pytest.mark.parametrize("w,kind", RANDOM_SMALL_CASES, ids=lambda v: v if isinstance(v, str) else v.name)
+def test_random_small_batches(w, kind):
+    if kind == "none":
+        check(w)
+    else:
+        check_masked(w, kind)
+
+
 def random_segment_case(i):
     """A random configuration through the segment schedule at a random large-segment threshold (the schedule
     takes copies and per-token int8; its segment counts stay within the scan's LDS)."""
