@@ -1414,19 +1414,38 @@ constexpr int kFusedCombinePairs = 65535; // one-launch combine: N*K (16-bit cou
 constexpr int kFusedCombineSrcPairs = 1024;   // ... and bs*K (pairs a workgroup may count)
 constexpr int kFusedCombineLdsCounts = 2048;  // W*E up to which a workgroup stages ep_recv_count in LDS
 
-// Expert of pair p if the pair is exchanged (active, and routed to one of the
-// E real experts), else -1. The id of an inactive pair is loaded with its mask
-// byte, so that both loads are in flight together, and then ignored.
-__device__ __forceinline__ int exchanged_expert(const int32_t *ids, const uint8_t *mask, int mask_kind, int p, int K,
-                                                float rK, int E)
+// Expert ids and mask bytes of L pairs p[j], in two phases: pair_loads issues
+// every load before any value is used, so that the L latencies overlap, and
+// pair_experts then keeps the expert of each pair that is exchanged (below n,
+// active, routed to one of the E real experts) and writes -1 for the others.
+// The loads are the same whatever the mask kind, with no branch between them:
+// a mask test between two id loads makes the compiler wait for the first
+// before it issues the second, and loads on some paths only make it drain
+// every load at the first wait. Without a mask the "mask bytes" are bytes of
+// the ids (same cache lines), ignored. Pairs at or past n are read at n - 1
+// (at 0 if n is 0: the caller guarantees one pair).
+template <int L>
+__device__ __forceinline__ void pair_loads(const int32_t *ids, const uint8_t *mask, int mask_kind, const int (&p)[L],
+                                           int n, int K, float rK, int (&e)[L], int (&m)[L])
 {
-    int e = ids[p];
-    if (mask_kind == MOE_MASK_TOKEN) {
-        if (!mask[div_small(p, K, rK)]) e = -1;
-    } else if (mask_kind == MOE_MASK_PAIR) {
-        if (!mask[p]) e = -1;
+    const int last = n > 0 ? n - 1 : 0;
+    const uint8_t *mb = mask_kind == MOE_MASK_NONE ? reinterpret_cast<const uint8_t *>(ids) : mask;
+#pragma unroll
+    for (int j = 0; j < L; ++j) e[j] = ids[min(p[j], last)];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+        const int q = min(p[j], last);
+        m[j] = mb[mask_kind == MOE_MASK_TOKEN ? div_small(q, K, rK) : q];
     }
-    return (unsigned)e < (unsigned)E ? e : -1;
+}
+
+template <int L>
+__device__ __forceinline__ void pair_experts(int mask_kind, const int (&p)[L], int n, int E, int (&e)[L],
+                                             const int (&m)[L])
+{
+#pragma unroll
+    for (int j = 0; j < L; ++j)
+        e[j] = p[j] < n && (mask_kind == MOE_MASK_NONE || m[j] != 0) && (unsigned)e[j] < (unsigned)E ? e[j] : -1;
 }
 
 // Workgroup-wide sums of KW words that hold two 16-bit counts each; every
@@ -1469,12 +1488,20 @@ __device__ void fused_counts(const DispatchArgs &a)
     const float rK = 1.0f / a.K, rbs = 1.0f / a.bs, repr = 1.0f / a.epr, rE = 1.0f / a.E;
     for (int i = tid; i < G; i += nt) cnt[i] = 0;
     __syncthreads();
-    for (int p = tid; p < NK; p += nt) {
-        const int e = exchanged_expert(a.ids, a.mask, a.mask_kind, p, a.K, rK, a.E);
-        if (e < 0) continue;
-        const int s = div_small(div_small(p, a.K, rK), a.bs, rbs);
-        const int r = div_small(e, a.epr, repr);
-        atomicAdd(&cnt[r * a.E + (e - r * a.epr) * a.W + s], 1);
+    constexpr int CL = 8;                        // pairs per thread and pass, loads first
+    for (int p0 = tid; p0 < NK; p0 += CL * nt) {
+        int p[CL], e[CL], m[CL];
+#pragma unroll
+        for (int j = 0; j < CL; ++j) p[j] = p0 + j * nt;
+        pair_loads<CL>(a.ids, a.mask, a.mask_kind, p, NK, a.K, rK, e, m);
+        pair_experts<CL>(a.mask_kind, p, NK, a.E, e, m);
+#pragma unroll
+        for (int j = 0; j < CL; ++j) {
+            if (e[j] < 0) continue;
+            const int s = div_small(div_small(p[j], a.K, rK), a.bs, rbs);
+            const int r = div_small(e[j], a.epr, repr);
+            atomicAdd(&cnt[r * a.E + (e[j] - r * a.epr) * a.W + s], 1);
+        }
     }
     __syncthreads();
     const int per = (G + nt - 1) / nt;
@@ -1495,9 +1522,10 @@ __device__ void fused_counts(const DispatchArgs &a)
 }
 
 // One-launch dispatch (copies): workgroups (token t, 8 KiB slice) plus one
-// ep_recv_count workgroup at the end of the grid. Each thread loads its slice
-// chunks first, then L of the N*K expert ids (L * kFusedThreads >= N*K); lane k
-// of every wavefront holds the key of token t's pair k. After the count, every
+// ep_recv_count workgroup at the end of the grid. Each thread issues the loads
+// of L of the N*K expert ids (L * kFusedThreads >= N*K) and of token t's pair
+// `lane` first, then those of its slice chunks, so that the count waits for the
+// ids only; lane k of every wavefront holds the key of token t's pair k. After the count, every
 // thread stores its chunks to the K rows; slice 0 writes assist_info and
 // expand_scales. Needs rows in 16-byte pieces, K <= KT and N*K <= L * 256.
 template <int KT, int L>
@@ -1515,19 +1543,21 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(DispatchA
     const float rK = 1.0f / a.K;
     const int nc = (int)(a.rowbytes / 16), c0 = sl * (kFusedThreads * kFusedUnroll) + tid;
     const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
+    int p[L + 1], e[L + 1], m[L + 1];            // [L]: pair `lane` of token t
+#pragma unroll
+    for (int j = 0; j < L; ++j) p[j] = tid + j * kFusedThreads;
+    p[L] = t * a.K + (lane < a.K ? lane : 0);
+    pair_loads<L + 1>(a.ids, a.mask, a.mask_kind, p, NK, a.K, rK, e, m);
     uint4 v[kFusedUnroll];
 #pragma unroll
     for (int u = 0; u < kFusedUnroll; ++u) v[u] = src[min(c0 + u * kFusedThreads, nc - 1)];
+    __builtin_amdgcn_sched_barrier(0);           // keep the slice loads above the waits for the ids
+    pair_experts<L + 1>(a.mask_kind, p, NK, a.E, e, m);
     int key[L];
 #pragma unroll
-    for (int j = 0; j < L; ++j) {
-        const int p = tid + j * kFusedThreads;
-        const int e = p < NK ? exchanged_expert(a.ids, a.mask, a.mask_kind, p, a.K, rK, a.E) : -1;
-        key[j] = e >= 0 ? e * NK + p : INT_MAX;
-    }
-    const int pt = t * a.K + (lane < a.K ? lane : 0);
-    const int et = exchanged_expert(a.ids, a.mask, a.mask_kind, pt, a.K, rK, a.E);
-    const int tkey = lane < a.K && et >= 0 ? et * NK + pt : INT_MAX;
+    for (int j = 0; j < L; ++j) key[j] = e[j] >= 0 ? e[j] * NK + p[j] : INT_MAX;
+    const int pt = p[L];
+    const int tkey = lane < a.K && e[L] >= 0 ? e[L] * NK + pt : INT_MAX;
     int w[KW];
 #pragma unroll
     for (int i = 0; i < KW; ++i) w[i] = 0;
@@ -1769,19 +1799,39 @@ __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineAr
     const int K = a.K;
     const int s = t / a.bs;
     const float rK = 1.0f / K;
-    // lane k: pair k of token t
+    // Every load of the prologue that depends on no other is issued first, in
+    // this order, and only then is any value used, so that their latencies
+    // overlap: lane k's pair k of token t (id, weight, mask byte), the rank
+    // totals, the first SB source pairs of each thread, and (PRE) the
+    // ep_recv_count values the thread stages. These loads are issued whatever
+    // the sizes, at clamped indices, and the values not needed are ignored: a
+    // load under a condition makes the compiler's waits assume the path
+    // without it, and the first wait would then drain every load.
     const int pt = t * K + (lane < K ? lane : 0);
     const int e = a.ids[pt];
-    bool on = lane < K;
-    if (a.mask_kind == MOE_MASK_TOKEN) on = on && a.mask[t] != 0;
-    else if (a.mask_kind == MOE_MASK_PAIR) on = on && a.mask[pt] != 0;
     const uint32_t wbits = reinterpret_cast<const uint32_t *>(a.scales)[pt];
+    const uint8_t *mp = a.mask_kind == MOE_MASK_TOKEN  ? a.mask + t
+                        : a.mask_kind == MOE_MASK_PAIR ? a.mask + pt
+                                                       : reinterpret_cast<const uint8_t *>(a.ids + pt);
+    const int mb = *mp;                            // (without a mask: any byte, ignored)
+    const int tot0 = a.erc[(size_t)min(tid, a.W - 1) * a.S + a.S - 1];
+    constexpr int SB = 4;                          // source pairs per thread and pass
+    const int p1 = t * K;                          // token t's first pair
+    int sp[SB], se[SB], sm[SB];
+#pragma unroll
+    for (int u = 0; u < SB; ++u) sp[u] = s * a.bs * K + tid + u * kGatherThreads;
+    pair_loads<SB>(a.ids, a.mask, a.mask_kind, sp, p1, K, rK, se, sm);
+    constexpr int PS = kFusedCombineLdsCounts / kGatherThreads;
+    const int WS = a.W * a.S;
+    int ercv[PRE ? PS : 1];
+    if (PRE) {
+#pragma unroll
+        for (int u = 0; u < PS; ++u) ercv[u] = a.erc[min(tid + u * kGatherThreads, WS - 1)];
+    }
+    const bool on = lane < K && (a.mask_kind == MOE_MASK_NONE || mb != 0);
     const bool real = on && (unsigned)e < (unsigned)a.E;
     const int r = real ? div_small(e, a.epr, 1.0f / a.epr) : -1;
     const int seg = real ? (e - r * a.epr) * a.W + s : 0;     // segment (el, s) inside rank r
-    if (PRE) {
-        for (int i = tid; i < a.W * a.S; i += kGatherThreads) erc_lds[i] = a.erc[i];
-    }
     int base = 0;
     if (!PRE && real && seg > 0) base = a.erc[(size_t)r * a.S + seg - 1];
     const int ek = real ? e : INT_MIN;             // an inactive pair below reads as -1, never INT_MIN
@@ -1799,25 +1849,31 @@ __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineAr
     for (int i = 0; i < KW; ++i) w[i] = 0;
     // rows of the ranks below r
     for (int q = tid; q < a.W; q += kGatherThreads) {
-        const int tot = a.erc[(size_t)q * a.S + a.S - 1];
+        const int tot = q == tid ? tot0 : a.erc[(size_t)q * a.S + a.S - 1];
 #pragma unroll
         for (int k = 0; k < KT; ++k) w[k >> 1] += (q < rk_u[k] ? tot : 0) << (16 * (k & 1));
     }
-    // pairs of source rank s's earlier tokens routed to the same expert, four ids per thread at a time
-    const int p1 = t * K;
-    for (int p0 = s * a.bs * K + tid; p0 < p1; p0 += 4 * kGatherThreads) {
-        int ep[4];
+    // pairs of source rank s's earlier tokens routed to the same expert, SB ids per thread and pass
+    for (int p0 = s * a.bs * K + tid; p0 < p1; p0 += SB * kGatherThreads) {
+        if (p0 != sp[0]) {                        // the first pass's loads were issued above
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int p = p0 + u * kGatherThreads;
-            ep[u] = p < p1 ? exchanged_expert(a.ids, a.mask, a.mask_kind, p, K, rK, a.E) : -1;
+            for (int u = 0; u < SB; ++u) sp[u] = p0 + u * kGatherThreads;
+            pair_loads<SB>(a.ids, a.mask, a.mask_kind, sp, p1, K, rK, se, sm);
         }
+        pair_experts<SB>(a.mask_kind, sp, p1, a.E, se, sm);
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
             int c = 0;
 #pragma unroll
-            for (int u = 0; u < 4; ++u) c += ep[u] == ek_u[k];
+            for (int u = 0; u < SB; ++u) c += se[u] == ek_u[k];
             w[k >> 1] += c << (16 * (k & 1));
+        }
+    }
+    if (PRE) {
+#pragma unroll
+        for (int u = 0; u < PS; ++u) {
+            const int i = tid + u * kGatherThreads;
+            if (i < WS) erc_lds[i] = ercv[u];
         }
     }
     block_sum_packed<KW>(w, red);                 // (its barrier also publishes erc_lds)
