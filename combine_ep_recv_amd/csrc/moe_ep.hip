@@ -60,6 +60,7 @@ constexpr int kRouteWords = kRouteTokens / 64;
 constexpr int kMaxExperts = 1024;          // moeExpertNum upper bound
 constexpr int kMinWorld = 2, kMaxWorld = 768;   // epWorldSize range
 constexpr int kDirectMaxChunks = 64;       // chunk count up to which blocks sum the prefixes themselves
+constexpr int kChunkBatch = 16;            // chunk counts such a sum loads at once
 constexpr int kSegLdsMax = 11264;          // W*S limit for the LDS-resident segment counts
 constexpr long long kMaxTokens = (1ll << 24) - 1;   // N blocks of 256 threads stay below 2^32 items
 constexpr int kPlanRows = 8;               // rows per segment-schedule work item
@@ -581,10 +582,21 @@ __device__ void write_erc_direct(const DispatchArgs &a, size_t gtid, size_t nthr
         const int r = (int)(q / a.S), i = (int)(q % a.S), el = i / a.W, s = i % a.W;
         const int e = r * a.epr + el, e0 = r * a.epr, bend = (s + 1) * a.nbs;
         int end = 0, base = 0;
-#pragma unroll 8
-        for (int b = 0; b < a.NB; ++b) {
-            end += (b < bend ? a.pci : a.pc)[(size_t)b * a.E + e];
-            base += a.pc[(size_t)b * a.E + e0];
+        // every chunk count of a pass is loaded before any is added (clamped
+        // indices, the extra values dropped), so a pass costs one round trip
+        for (int b0 = 0; b0 < a.NB; b0 += kChunkBatch) {
+            int ve[kChunkBatch], vb[kChunkBatch];
+#pragma unroll
+            for (int j = 0; j < kChunkBatch; ++j) {
+                const int b = min(b0 + j, a.NB - 1);
+                ve[j] = (b < bend ? a.pci : a.pc)[(size_t)b * a.E + e];
+                vb[j] = a.pc[(size_t)b * a.E + e0];
+            }
+#pragma unroll
+            for (int j = 0; j < kChunkBatch; ++j) {
+                end += b0 + j < a.NB ? ve[j] : 0;
+                base += b0 + j < a.NB ? vb[j] : 0;
+            }
         }
         a.erc[q] = end - base;
     }
@@ -653,8 +665,17 @@ __device__ __forceinline__ int lane_pair_row(const DispatchArgs &a, int t, int l
         const int bt = s * a.nbs + tok / kRouteTokens;
         int off = 0;
         if (a.direct) {
-#pragma unroll 8
-            for (int b = 0; b < a.NB; ++b) off += (b < bt ? a.pci : a.pc)[(size_t)b * a.E + e];
+            // all chunk counts of a pass loaded before any is added: one round trip per pass
+            for (int b0 = 0; b0 < a.NB; b0 += kChunkBatch) {
+                int v[kChunkBatch];
+#pragma unroll
+                for (int j = 0; j < kChunkBatch; ++j) {
+                    const int b = min(b0 + j, a.NB - 1);
+                    v[j] = (b < bt ? a.pci : a.pc)[(size_t)b * a.E + e];
+                }
+#pragma unroll
+                for (int j = 0; j < kChunkBatch; ++j) off += b0 + j < a.NB ? v[j] : 0;
+            }
         } else {
             off = a.boff[(size_t)bt * a.E + e];
         }
@@ -1055,7 +1076,10 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(Dispa
     const int nwaves = gridDim.x * (kQuantThreads / 64);
     for (int t = blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6); t < N; t += nwaves) {
         const size_t pk = (size_t)t * K + (lane < K ? lane : 0);
+        // the pair loads go out before the token's, and the row resolution waits for
+        // them alone: its chunk-count loads then overlap the token loads
         const int e = a.ids[pk], l = a.lr[pk];
+        __builtin_amdgcn_sched_barrier(0);
         const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
         uint4 v[J][2];
 #pragma unroll
@@ -1064,6 +1088,7 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(Dispa
             v[j][0] = src[2 * oc];
             v[j][1] = src[2 * oc + 1];
         }
+        __builtin_amdgcn_sched_barrier(0);
         const int my_row = lane_pair_row(a, t, lane, e, l, true);
         if constexpr (QM == MOE_QUANT_DYN_GROUP) quant_store_wave_fp8<T, J>(a, lane, v, my_row);
         else if constexpr (QM == MOE_QUANT_STATIC) quant_store_wave_static<T, J>(a, lane, v, my_row);
