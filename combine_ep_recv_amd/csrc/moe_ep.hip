@@ -1423,8 +1423,10 @@ void launch_segment_quant_wave(int J, dim3 g, dim3 b, hipStream_t st, const Disp
 // exchanged (active, routed to one of the E real experts), the row of pair p is
 // the number of exchanged pairs whose key is smaller. A workgroup that needs
 // the rows of token t's K pairs reads every pair's expert id (N*K int32, in L2
-// after the first workgroups), compares those keys with its K targets (two VALU
-// operations per key and target) and sums the counts over the workgroup. The
+// after the first workgroups), compares those keys with its K targets and sums
+// the counts over the workgroup: a wavefront counts with one ballot per key and
+// target (the population of the lane mask is the wavefront's count, so nothing
+// is summed across lanes), and the workgroup adds its wavefronts' counts. The
 // dispatch then needs no route launch and the combine no slot pass; at 8 ranks
 // x 32 tokens, top-8, a dispatch thread compares 8 keys. The combine counts
 // less: the first row of a pair's segment comes from ep_recv_count, so it only
@@ -1435,7 +1437,7 @@ constexpr int kFusedUnroll = 2;           // 16-byte chunks per thread: a slice 
 constexpr int kFusedMaxPairs = 4096;      // N*K up to which dispatch runs as one launch
 constexpr int kFusedMaxCounts = 4096;     // W*E segment counts of its ep_recv_count workgroup (LDS)
 constexpr int kFusedMaxK = 16;
-constexpr int kFusedCombinePairs = 65535; // one-launch combine: N*K (16-bit counts) ...
+constexpr int kFusedCombinePairs = 65535; // one-launch combine: N*K (the range its tests cover) ...
 constexpr int kFusedCombineSrcPairs = 1024;   // ... and bs*K (pairs a workgroup may count)
 constexpr int kFusedCombineLdsCounts = 2048;  // W*E up to which a workgroup stages ep_recv_count in LDS
 
@@ -1471,34 +1473,6 @@ __device__ __forceinline__ void pair_experts(int mask_kind, const int (&p)[L], i
 #pragma unroll
     for (int j = 0; j < L; ++j)
         e[j] = p[j] < n && (mask_kind == MOE_MASK_NONE || m[j] != 0) && (unsigned)e[j] < (unsigned)E ? e[j] : -1;
-}
-
-// Workgroup-wide sums of KW words that hold two 16-bit counts each; every
-// thread gets the totals. red: KW ints of LDS per wavefront.
-template <int KW>
-__device__ __forceinline__ void block_sum_packed(int (&w)[KW], int *red)
-{
-    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-#pragma unroll
-    for (int i = 0; i < KW; ++i) w[i] = __builtin_amdgcn_readlane(wave_incl_scan(w[i]), 63);
-    if (lane == 0) {
-#pragma unroll
-        for (int i = 0; i < KW; ++i) red[wid * KW + i] = w[i];
-    }
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KW; ++i) {
-        int v = 0;
-        for (int q = 0; q < nw; ++q) v += red[q * KW + i];
-        w[i] = v;
-    }
-}
-
-// Count k (16 bits) of the packed words.
-template <int KW>
-__device__ __forceinline__ int packed_count(const int (&w)[KW], int k)
-{
-    return (w[k >> 1] >> (16 * (k & 1))) & 0xffff;
 }
 
 // ep_recv_count workgroup of the one-launch dispatch: segment counts by LDS
@@ -1556,8 +1530,8 @@ __device__ void fused_counts(const DispatchArgs &a)
 template <int KT, int L>
 __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(DispatchArgs a)
 {
-    constexpr int KW = KT / 2;
-    __shared__ int red[kFusedThreads / 64 * KW];
+    constexpr int NW = kFusedThreads / 64;
+    __shared__ int red[NW * 64];
     const int N = a.W * a.bs, NK = a.R;
     if ((int)blockIdx.x >= N * a.nsl) {
         fused_counts(a);
@@ -1583,23 +1557,29 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(DispatchA
     for (int j = 0; j < L; ++j) key[j] = e[j] >= 0 ? e[j] * NK + p[j] : INT_MAX;
     const int pt = p[L];
     const int tkey = lane < a.K && e[L] >= 0 ? e[L] * NK + pt : INT_MAX;
-    int w[KW];
-#pragma unroll
-    for (int i = 0; i < KW; ++i) w[i] = 0;
+    // every thread is active here: the ballots see the whole wavefront. Lane k
+    // keeps the wavefront's count for target k, selected as each is formed; every
+    // lane writes its slot (only the first KT are read), since a write under a
+    // lane test lets the compiler sink the counts into it and keep all L * KT lane
+    // masks live until then.
+    int mine = 0;
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
         const int tk = __builtin_amdgcn_readlane(tkey, k);
         int c = 0;
 #pragma unroll
-        for (int j = 0; j < L; ++j) c += key[j] < tk;
-        w[k >> 1] += c << (16 * (k & 1));
+        for (int j = 0; j < L; ++j) c += __popcll(__builtin_amdgcn_ballot_w64(key[j] < tk));
+        mine = lane == k ? c : mine;
     }
-    block_sum_packed<KW>(w, red);
+    red[tid] = mine;
+    __syncthreads();
     int rows[KT];
 #pragma unroll
     for (int k = 0; k < KT; ++k) {
+        int row = 0;
+#pragma unroll
+        for (int q = 0; q < NW; ++q) row += red[q * 64 + k];
         const bool has = k < a.K && __builtin_amdgcn_readlane(tkey, k) != INT_MAX;
-        const int row = packed_count<KW>(w, k);
         rows[k] = has && row < a.R ? row : -1;
     }
     if (sl == 0 && tid < a.K) {
@@ -1816,9 +1796,9 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_i32_kernel(Comb
 template <class T, int KT, bool PRE>
 __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineArgs a)
 {
-    constexpr int KW = KT / 2;
+    constexpr int NW = kGatherThreads / 64;
     extern __shared__ int erc_lds[];              // PRE: ep_recv_count [W * S]
-    __shared__ int red[kGatherThreads / 64 * KW];
+    __shared__ int red[kGatherThreads];
     const int tid = threadIdx.x, lane = tid & 63;
     const int t = blockIdx.x / a.nsl, sl = blockIdx.x - t * a.nsl;
     const int K = a.K;
@@ -1826,8 +1806,8 @@ __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineAr
     const float rK = 1.0f / K;
     // Every load of the prologue that depends on no other is issued first, in
     // this order, and only then is any value used, so that their latencies
-    // overlap: lane k's pair k of token t (id, weight, mask byte), the rank
-    // totals, the first SB source pairs of each thread, and (PRE) the
+    // overlap: lane k's pair k of token t (id, weight, mask byte), the first 64
+    // rank totals, the first SB source pairs of each thread, and (PRE) the
     // ep_recv_count values the thread stages. These loads are issued whatever
     // the sizes, at clamped indices, and the values not needed are ignored: a
     // load under a condition makes the compiler's waits assume the path
@@ -1839,7 +1819,7 @@ __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineAr
                         : a.mask_kind == MOE_MASK_PAIR ? a.mask + pt
                                                        : reinterpret_cast<const uint8_t *>(a.ids + pt);
     const int mb = *mp;                            // (without a mask: any byte, ignored)
-    const int tot0 = a.erc[(size_t)min(tid, a.W - 1) * a.S + a.S - 1];
+    const int tot0 = a.erc[(size_t)min(lane, a.W - 1) * a.S + a.S - 1];
     constexpr int SB = 4;                          // source pairs per thread and pass
     const int p1 = t * K;                          // token t's first pair
     int sp[SB], se[SB], sm[SB];
@@ -1863,26 +1843,32 @@ __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineAr
     // Every lane's values that other lanes need are read here, with the whole
     // wavefront active: a lane that is switched off inside the loops below may
     // not hold them there.
-    int ek_u[KT], rk_u[KT];
+    int ek_u[KT];
 #pragma unroll
-    for (int k = 0; k < KT; ++k) {
-        ek_u[k] = __builtin_amdgcn_readlane(ek, k);
-        rk_u[k] = __builtin_amdgcn_readlane(r, k);
+    for (int k = 0; k < KT; ++k) ek_u[k] = __builtin_amdgcn_readlane(ek, k);
+    // Rows of the ranks below lane k's rank r: every wavefront scans the W rank
+    // totals, 64 at a time (the first 64 loaded above), and lane k reads the
+    // prefix before r from the scan (ds_bpermute). Loop bounds are uniform.
+    int below = 0;
+    for (int q0 = 0; q0 < a.W; q0 += 64) {
+        const int q = q0 + lane;
+        const int tot = q0 == 0 ? (lane < a.W ? tot0 : 0)
+                                : (q < a.W ? a.erc[(size_t)q * a.S + a.S - 1] : 0);
+        const int sc = wave_incl_scan(tot);
+        const int n = min(r - q0, 64);           // ranks of this chunk below r (r = -1: none)
+        const int got = __builtin_amdgcn_ds_bpermute(max(n - 1, 0) << 2, sc);
+        below += n > 0 ? got : 0;
     }
-    int w[KW];
+    // Pairs of source rank s's earlier tokens routed to the same expert: every
+    // wavefront counts its share with one ballot per pair slot and target, lane
+    // k keeps target k's count, and the workgroup adds its wavefronts' counts.
+    // The loop is uniform, so the ballots see every lane.
+    int mine = 0;
+    const int pfirst = s * a.bs * K;
+    for (int pb = pfirst; pb < p1; pb += SB * kGatherThreads) {
+        if (pb != pfirst) {                       // the first pass's loads were issued above
 #pragma unroll
-    for (int i = 0; i < KW; ++i) w[i] = 0;
-    // rows of the ranks below r
-    for (int q = tid; q < a.W; q += kGatherThreads) {
-        const int tot = q == tid ? tot0 : a.erc[(size_t)q * a.S + a.S - 1];
-#pragma unroll
-        for (int k = 0; k < KT; ++k) w[k >> 1] += (q < rk_u[k] ? tot : 0) << (16 * (k & 1));
-    }
-    // pairs of source rank s's earlier tokens routed to the same expert, SB ids per thread and pass
-    for (int p0 = s * a.bs * K + tid; p0 < p1; p0 += SB * kGatherThreads) {
-        if (p0 != sp[0]) {                        // the first pass's loads were issued above
-#pragma unroll
-            for (int u = 0; u < SB; ++u) sp[u] = p0 + u * kGatherThreads;
+            for (int u = 0; u < SB; ++u) sp[u] = pb + tid + u * kGatherThreads;
             pair_loads<SB>(a.ids, a.mask, a.mask_kind, sp, p1, K, rK, se, sm);
         }
         pair_experts<SB>(a.mask_kind, sp, p1, a.E, se, sm);
@@ -1890,8 +1876,8 @@ __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineAr
         for (int k = 0; k < KT; ++k) {
             int c = 0;
 #pragma unroll
-            for (int u = 0; u < SB; ++u) c += se[u] == ek_u[k];
-            w[k >> 1] += c << (16 * (k & 1));
+            for (int u = 0; u < SB; ++u) c += __popcll(__builtin_amdgcn_ballot_w64(se[u] == ek_u[k]));
+            mine += lane == k ? c : 0;
         }
     }
     if (PRE) {
@@ -1901,12 +1887,12 @@ __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineAr
             if (i < WS) erc_lds[i] = ercv[u];
         }
     }
-    block_sum_packed<KW>(w, red);                 // (its barrier also publishes erc_lds)
+    red[tid] = mine;                              // every lane (only the first KT are read): see dispatch_fused_kernel
+    __syncthreads();                              // (also publishes erc_lds)
     if (PRE && real && seg > 0) base = erc_lds[r * a.S + seg - 1];
-    int cnt = 0;
+    int cnt = below;
 #pragma unroll
-    for (int k = 0; k < KT; ++k)
-        if (lane == k) cnt = packed_count<KW>(w, k);
+    for (int q = 0; q < NW; ++q) cnt += red[q * 64 + lane];
     // the slot of lane k's pair: a row, kCopySlot, kConstSlot0 - j, or -1 (nothing to add)
     int slot = -1;
     if (real) {
