@@ -782,6 +782,56 @@ def test_random_large_configurations(w, kind):
         check_masked(w, kind)
 
 
+def random_sweep_case(i):
+    """A wider random draw than the lists above: up to 768 ranks with tiny batches, the one-launch region, topk
+    up to 64, ragged h, every quantiser, mask kind and special-expert kind, and now and then the segment schedule
+    (copies and per-token int8) at a random threshold. Sized so the oracle stays fast."""
+    rng = np.random.default_rng(50000 + i)
+    region = rng.random()
+    if region < 0.15:
+        W, bs, epr = int(rng.choice([96, 128, 200, 384, 768])), int(rng.integers(1, 4)), 1
+    elif region < 0.5:
+        W = int(rng.choice([2, 3, 4, 6, 8, 16, 32, 64, 65]))
+        bs = int(rng.integers(1, max(2, 4096 // (W * 4))))
+        epr = int(rng.integers(1, max(2, min(9, 1024 // W))))
+    else:
+        W = int(rng.choice([2, 3, 4, 5, 8, 16, 24]))
+        bs = int(rng.integers(1, 700 // max(1, W // 4)))
+        epr = int(rng.integers(1, max(2, min(17, 1024 // W))))
+    K = int(rng.integers(1, min(W * epr, 64 if rng.random() < 0.1 else 16) + 1))
+    dtype = str(rng.choice(["int32", "fp16", "bf16"]))
+    quant = 0 if dtype == "int32" else int(rng.choice([0, 0, 1, 2, 2, 3]))
+    if quant in (1, 3):
+        h = 16 * int(rng.integers(1, 200))
+    else:
+        h = int(rng.choice([8, 16, 24, 64, 1024, 7168])) if rng.random() < 0.6 else int(rng.integers(1, 2000))
+    routing = "uniform_distinct" if dtype == "int32" else str(rng.choice(["gauss_topk", "zipf_topk"]))
+    zero, const = int(rng.integers(0, 3)), int(rng.integers(0, 3))
+    copy = 0 if (quant and dtype != "bf16") else int(rng.integers(0, 3))
+    sk = str(rng.choice(["scalar", "column", "expert"]))
+    kind = str(rng.choice(["none", "none", "token_any", "token_prefix", "pair"]))
+    w = wl.custom(W, bs, h, K, epr, dtype, routing, quant_mode=quant, zero_experts=zero, copy_experts=copy,
+                  const_experts=const, static_scales=sk, index=20000 + i, name="sweep%d" % i)
+    T = None
+    if quant in (0, 2) and rng.random() < 0.2 and W * W * epr <= 11264:
+        T = int(rng.choice([0, 4096, 65536, -1]))
+    return w, kind, T
+
+
+RANDOM_SWEEP_CASES = [c for c in (random_sweep_case(i) for i in range(170))
+                      if c[0].num_tokens * c[0].topk * c[0].h <= 6e7][:150]
+
+
+@pytest.mark.parametrize("w,kind,T", RANDOM_SWEEP_CASES,
+                         ids=lambda v: v if isinstance(v, (str, int)) or v is None else v.name)
+def test_random_sweep(w, kind, T):
+    sched = None if T is None else moe.MoeSchedule(mode=moe.MOE_SCHED_SEGMENT, large_segment_bytes=T)
+    if kind == "none":
+        check(w, schedule=sched)
+    else:
+        check_masked(w, kind, seed=int(w.name[5:]), schedule=sched)
+
+
 # --------------------------------------------------------------------------
 # determinism (aclnnMoeDistributeDispatchV4 约束说明: deterministic by default)
 # --------------------------------------------------------------------------
