@@ -282,27 +282,34 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
     // An inactive pair (token masks) is routed nowhere: its id reads as -1, so
     // it sets no bit, is not counted and gets rank -1, and no kernel after this
     // one writes a row for it.
+    // A pass loads U ids, then (with a mask) their U mask bytes, at clamped
+    // indices (npairs >= 1), and only then tests them: a mask test between two
+    // loads makes the compiler wait for each pair before issuing the next.
     const size_t tok_base = (size_t)s * bs + tok0;
-    auto load_pair = [&](int p, int &eu, int &tlu) {
-        tlu = div_small(p, K, rK);
-        eu = -1;
-        if (p < npairs) {
-            eu = ids[pair0 + p];
-            if constexpr (MK == MOE_MASK_TOKEN) if (!mask[tok_base + tlu]) eu = -1;
-            if constexpr (MK == MOE_MASK_PAIR) if (!mask[pair0 + p]) eu = -1;
+    int e[U], tl[U], mk[U];
+    auto load_pass = [&](int p0) {
+#pragma unroll
+        for (int u = 0; u < U; ++u) e[u] = ids[pair0 + min(p0 + u * kRouteThreads, npairs - 1)];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = min(p0 + u * kRouteThreads, npairs - 1);
+            if constexpr (MK == MOE_MASK_TOKEN) mk[u] = mask[tok_base + div_small(p, K, rK)];
+            if constexpr (MK == MOE_MASK_PAIR) mk[u] = mask[pair0 + p];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int p = p0 + u * kRouteThreads;
+            tl[u] = div_small(p, K, rK);
+            if (p >= npairs) e[u] = -1;
+            if constexpr (MK != MOE_MASK_NONE) if (!mk[u]) e[u] = -1;
         }
     };
-    int e[U], tl[U];
     const bool one_pass = npairs <= kRouteThreads * U;
-#pragma unroll
-    for (int u = 0; u < U; ++u) load_pair(threadIdx.x + u * kRouteThreads, e[u], tl[u]);
+    load_pass(threadIdx.x);
     for (int i = threadIdx.x; i < E * kRouteWords; i += blockDim.x) bm[i] = 0ull;
     __syncthreads();
     for (int p0 = threadIdx.x; p0 < npairs; p0 += kRouteThreads * U) {
-        if (p0 != (int)threadIdx.x) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) load_pair(p0 + u * kRouteThreads, e[u], tl[u]);
-        }
+        if (p0 != (int)threadIdx.x) load_pass(p0);
 #pragma unroll
         for (int u = 0; u < U; ++u)
             if ((unsigned)e[u] < (unsigned)E) atomicOr(&bm[e[u] * kRouteWords + (tl[u] >> 6)], 1ull << (tl[u] & 63));
@@ -335,10 +342,7 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
     }
 
     for (int p0 = threadIdx.x; p0 < npairs; p0 += kRouteThreads * U) {
-        if (!one_pass) {
-#pragma unroll
-            for (int u = 0; u < U; ++u) load_pair(p0 + u * kRouteThreads, e[u], tl[u]);
-        }
+        if (!one_pass) load_pass(p0);
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             const int p = p0 + u * kRouteThreads;
@@ -1642,23 +1646,30 @@ __global__ __launch_bounds__(kSlotThreads) void combine_slots_kernel(CombineArgs
 {
     __shared__ int tmp[40];
     const int i = blockIdx.x * kSlotThreads + threadIdx.x;
+    // Row i's assist_info entry, and in the pair pass pair i's id, its mask byte
+    // and the first rank totals, are loaded first, unconditionally, at clamped
+    // indices (R >= 1, W >= 1): none depends on another, and loads on some paths
+    // only would make the compiler's first wait drain them all.
+    const size_t ic = (size_t)min(i, a.R - 1);
+    const int s = a.assist[ic * 3 + 0], tok = a.assist[ic * 3 + 1], k = a.assist[ic * 3 + 2];
     int rows = a.R;
     if (a.pair_pass) {
-        int part = 0;
-        for (int r = threadIdx.x; r < a.W; r += kSlotThreads) part += a.erc[(size_t)r * a.S + a.S - 1];
+        const int e = a.ids[ic];
+        const int tot0 = a.erc[(size_t)min((int)threadIdx.x, a.W - 1) * a.S + a.S - 1];
+        const uint8_t *mp = a.mask_kind == MOE_MASK_TOKEN  ? a.mask + ic / a.K
+                            : a.mask_kind == MOE_MASK_PAIR ? a.mask + ic
+                                                           : reinterpret_cast<const uint8_t *>(a.ids + ic);
+        const int mb = a.mask_kind == MOE_MASK_NONE ? 1 : *mp;
+        int part = (int)threadIdx.x < a.W ? tot0 : 0;
+        for (int r = threadIdx.x + kSlotThreads; r < a.W; r += kSlotThreads) part += a.erc[(size_t)r * a.S + a.S - 1];
         block_excl_scan(part, tmp, &rows);
         if (i < a.R) {
-            bool on = true;
-            if (a.mask_kind == MOE_MASK_TOKEN) on = a.mask[i / a.K] != 0;
-            if (a.mask_kind == MOE_MASK_PAIR) on = a.mask[i] != 0;
-            const int e = a.ids[i];
-            if (!on || (e >= a.E && e < a.zero_end)) a.slot_out[i] = -1;
+            if (mb == 0 || (e >= a.E && e < a.zero_end)) a.slot_out[i] = -1;
             else if (e >= a.zero_end && e < a.copy_end) a.slot_out[i] = kCopySlot;
             else if (e >= a.copy_end && e < a.const_end) a.slot_out[i] = kConstSlot0 - (e - a.copy_end);
         }
     }
     if (i >= rows || i >= a.R) return;
-    const int s = a.assist[(size_t)i * 3 + 0], tok = a.assist[(size_t)i * 3 + 1], k = a.assist[(size_t)i * 3 + 2];
     if ((unsigned)s < (unsigned)a.W && (unsigned)tok < (unsigned)a.bs && (unsigned)k < (unsigned)a.K)
         a.slot_out[((size_t)s * a.bs + tok) * a.K + k] = i;
 }
