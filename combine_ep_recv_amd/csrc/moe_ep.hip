@@ -1444,6 +1444,7 @@ constexpr int kFusedMaxK = 16;
 constexpr int kFusedCombinePairs = 65535; // one-launch combine: N*K (the range its tests cover) ...
 constexpr int kFusedCombineSrcPairs = 1024;   // ... and bs*K (pairs a workgroup may count)
 constexpr int kFusedCombineLdsCounts = 2048;  // W*E up to which a workgroup stages ep_recv_count in LDS
+static_assert(kFusedCombineLdsCounts == 16 * kGatherThreads, "the deepest staging loads 16 counts per thread");
 
 // Expert ids and mask bytes of L pairs p[j], in two phases: pair_loads issues
 // every load before any value is used, so that the L latencies overlap, and
@@ -1800,13 +1801,15 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_i32_kernel(Comb
 // segment, from ep_recv_count (the rows of all lower ranks, plus the rank's
 // inclusive count before segment (el, s)), plus the pairs of source rank s's
 // earlier tokens routed to the same expert, counted over those tokens' ids. A
-// copy expert reads token t, const expert j row j of the const table. PRE
-// stages ep_recv_count in LDS (W*E <= kFusedCombineLdsCounts), so that the
-// segment start needs no second dependent load. Needs rows in 16-byte pieces,
-// K <= KT and N*K < 2^16.
-template <class T, int KT, bool PRE>
+// copy expert reads token t, const expert j row j of the const table. With
+// PS > 0 the workgroup stages ep_recv_count in LDS, PS values per thread
+// (W*E <= PS * kGatherThreads), so that the segment start needs no second
+// dependent load; PS is 4 or 16 so that small tables do not pay for 16 loads
+// per thread. Needs rows in 16-byte pieces, K <= KT and N*K < 2^16.
+template <class T, int KT, int PS>
 __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineArgs a)
 {
+    constexpr bool PRE = PS > 0;
     constexpr int NW = kGatherThreads / 64;
     extern __shared__ int erc_lds[];              // PRE: ep_recv_count [W * S]
     __shared__ int red[kGatherThreads];
@@ -1837,7 +1840,6 @@ __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineAr
 #pragma unroll
     for (int u = 0; u < SB; ++u) sp[u] = s * a.bs * K + tid + u * kGatherThreads;
     pair_loads<SB>(a.ids, a.mask, a.mask_kind, sp, p1, K, rK, se, sm);
-    constexpr int PS = kFusedCombineLdsCounts / kGatherThreads;
     const int WS = a.W * a.S;
     int ercv[PRE ? PS : 1];
     if (PRE) {
@@ -2454,14 +2456,18 @@ int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t 
     (void)hipGetLastError();
     // One launch: slots found in each workgroup (see combine_fused_kernel)
     if (vec && K <= kFusedMaxK && N * K <= kFusedCombinePairs && (long long)bs * K <= kFusedCombineSrcPairs) {
-        const bool pre = (long long)W * a.S <= kFusedCombineLdsCounts, k8 = K <= 8;
-        const size_t lds = pre ? (size_t)W * a.S * sizeof(int) : 0;
+        const long long ws = (long long)W * a.S;
+        const int ps = ws <= 4 * kGatherThreads ? 4 : ws <= kFusedCombineLdsCounts ? 16 : 0;
+        const bool k8 = K <= 8;
+        const size_t lds = ps ? (size_t)ws * sizeof(int) : 0;
 #define MOE_FUSED_COMBINE(T)                                                                        \
         do {                                                                                        \
-            if (pre && k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, true>), g, b, lds, st, a);        \
-            else if (pre) hipLaunchKernelGGL((combine_fused_kernel<T, 16, true>), g, b, lds, st, a);       \
-            else if (k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, false>), g, b, lds, st, a);        \
-            else hipLaunchKernelGGL((combine_fused_kernel<T, 16, false>), g, b, lds, st, a);               \
+            if (ps == 4 && k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, 4>), g, b, lds, st, a);       \
+            else if (ps == 4) hipLaunchKernelGGL((combine_fused_kernel<T, 16, 4>), g, b, lds, st, a);       \
+            else if (ps && k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, 16>), g, b, lds, st, a);      \
+            else if (ps) hipLaunchKernelGGL((combine_fused_kernel<T, 16, 16>), g, b, lds, st, a);          \
+            else if (k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, 0>), g, b, lds, st, a);            \
+            else hipLaunchKernelGGL((combine_fused_kernel<T, 16, 0>), g, b, lds, st, a);                   \
         } while (0)
         if (dtype == MOE_INT32) MOE_FUSED_COMBINE(int32_t);
         else if (dtype == MOE_FP16) MOE_FUSED_COMBINE(F16);

@@ -432,6 +432,9 @@ FUSED = [
     wl.custom(4, 8, 256, 17, 8, "bf16", "gauss_topk", name="k17_no_fused_path"),
     wl.custom(64, 2, 64, 4, 2, "bf16", "zipf_topk", name="w64_e128_counts_past_lds"),
     wl.custom(16, 16, 512, 8, 16, "fp16", "gauss_topk", name="w16_e256_combine_erc_global"),
+    # 1024 ep_recv_count values: the combine's deeper LDS staging (more than 512, at most 2048)
+    wl.custom(8, 16, 512, 8, 16, "fp16", "gauss_topk", name="w8_e128_combine_erc_lds16"),
+    wl.custom(16, 8, 256, 16, 4, "bf16", "zipf_topk", name="w16_e64_k16_combine_erc_lds16"),
     wl.custom(2, 1025, 128, 8, 4, "bf16", "gauss_topk", name="bsk8200_slot_pass"),
     wl.custom(4, 128, 256, 8, 4, "fp16", "zipf_topk", name="bsk1024_last_fused_combine"),
     wl.custom(4, 129, 256, 8, 4, "fp16", "zipf_topk", name="bsk1032_slot_pass"),
