@@ -1450,40 +1450,41 @@ static_assert(kFusedCombineLdsCounts == 16 * kGatherThreads, "the deepest stagin
 // every load before any value is used, so that the L latencies overlap, and
 // pair_experts then keeps the expert of each pair that is exchanged (below n,
 // active, routed to one of the E real experts) and writes -1 for the others.
-// The loads are the same whatever the mask kind, with no branch between them:
-// a mask test between two id loads makes the compiler wait for the first
-// before it issues the second, and loads on some paths only make it drain
-// every load at the first wait. Without a mask the "mask bytes" are bytes of
-// the ids (same cache lines), ignored. Pairs at or past n are read at n - 1
-// (at 0 if n is 0: the caller guarantees one pair).
-template <int L>
+// MASKED (a token or pair mask) is a template parameter: without a mask no
+// mask byte is loaded, and with one the loads are the same for both kinds,
+// with no branch between them (a mask test between two id loads makes the
+// compiler wait for the first before it issues the second, and loads on some
+// paths only make it drain every load at the first wait). Pairs at or past n
+// are read at n - 1 (at 0 if n is 0: the caller guarantees one pair).
+template <int L, bool MASKED>
 __device__ __forceinline__ void pair_loads(const int32_t *ids, const uint8_t *mask, int mask_kind, const int (&p)[L],
                                            int n, int K, float rK, int (&e)[L], int (&m)[L])
 {
     const int last = n > 0 ? n - 1 : 0;
-    const uint8_t *mb = mask_kind == MOE_MASK_NONE ? reinterpret_cast<const uint8_t *>(ids) : mask;
 #pragma unroll
     for (int j = 0; j < L; ++j) e[j] = ids[min(p[j], last)];
+    if constexpr (MASKED) {
 #pragma unroll
-    for (int j = 0; j < L; ++j) {
-        const int q = min(p[j], last);
-        m[j] = mb[mask_kind == MOE_MASK_TOKEN ? div_small(q, K, rK) : q];
+        for (int j = 0; j < L; ++j) {
+            const int q = min(p[j], last);
+            m[j] = mask[mask_kind == MOE_MASK_TOKEN ? div_small(q, K, rK) : q];
+        }
     }
 }
 
-template <int L>
-__device__ __forceinline__ void pair_experts(int mask_kind, const int (&p)[L], int n, int E, int (&e)[L],
-                                             const int (&m)[L])
+template <int L, bool MASKED>
+__device__ __forceinline__ void pair_experts(const int (&p)[L], int n, int E, int (&e)[L], const int (&m)[L])
 {
 #pragma unroll
     for (int j = 0; j < L; ++j)
-        e[j] = p[j] < n && (mask_kind == MOE_MASK_NONE || m[j] != 0) && (unsigned)e[j] < (unsigned)E ? e[j] : -1;
+        e[j] = p[j] < n && (!MASKED || m[j] != 0) && (unsigned)e[j] < (unsigned)E ? e[j] : -1;
 }
 
 // ep_recv_count workgroup of the one-launch dispatch: segment counts by LDS
 // atomics over every exchanged pair, one exclusive scan over all W*E segments
 // in (rank, el*W + s) order, and per rank that scan minus its value at the
 // rank's first segment (a rank has S = E segments).
+template <bool MASKED>
 __device__ void fused_counts(const DispatchArgs &a)
 {
     extern __shared__ int cnt[];                 // [W * E]
@@ -1497,8 +1498,8 @@ __device__ void fused_counts(const DispatchArgs &a)
         int p[CL], e[CL], m[CL];
 #pragma unroll
         for (int j = 0; j < CL; ++j) p[j] = p0 + j * nt;
-        pair_loads<CL>(a.ids, a.mask, a.mask_kind, p, NK, a.K, rK, e, m);
-        pair_experts<CL>(a.mask_kind, p, NK, a.E, e, m);
+        pair_loads<CL, MASKED>(a.ids, a.mask, a.mask_kind, p, NK, a.K, rK, e, m);
+        pair_experts<CL, MASKED>(p, NK, a.E, e, m);
 #pragma unroll
         for (int j = 0; j < CL; ++j) {
             if (e[j] < 0) continue;
@@ -1532,14 +1533,14 @@ __device__ void fused_counts(const DispatchArgs &a)
 // ids only; lane k of every wavefront holds the key of token t's pair k. After the count, every
 // thread stores its chunks to the K rows; slice 0 writes assist_info and
 // expand_scales. Needs rows in 16-byte pieces, K <= KT and N*K <= L * 256.
-template <int KT, int L>
+template <int KT, int L, bool MASKED>
 __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(DispatchArgs a)
 {
     constexpr int NW = kFusedThreads / 64;
     __shared__ int red[NW * 64];
     const int N = a.W * a.bs, NK = a.R;
     if ((int)blockIdx.x >= N * a.nsl) {
-        fused_counts(a);
+        fused_counts<MASKED>(a);
         return;
     }
     const int tid = threadIdx.x, lane = tid & 63;
@@ -1551,12 +1552,12 @@ __global__ __launch_bounds__(kFusedThreads) void dispatch_fused_kernel(DispatchA
 #pragma unroll
     for (int j = 0; j < L; ++j) p[j] = tid + j * kFusedThreads;
     p[L] = t * a.K + (lane < a.K ? lane : 0);
-    pair_loads<L + 1>(a.ids, a.mask, a.mask_kind, p, NK, a.K, rK, e, m);
+    pair_loads<L + 1, MASKED>(a.ids, a.mask, a.mask_kind, p, NK, a.K, rK, e, m);
     uint4 v[kFusedUnroll];
 #pragma unroll
     for (int u = 0; u < kFusedUnroll; ++u) v[u] = src[min(c0 + u * kFusedThreads, nc - 1)];
     __builtin_amdgcn_sched_barrier(0);           // keep the slice loads above the waits for the ids
-    pair_experts<L + 1>(a.mask_kind, p, NK, a.E, e, m);
+    pair_experts<L + 1, MASKED>(p, NK, a.E, e, m);
     int key[L];
 #pragma unroll
     for (int j = 0; j < L; ++j) key[j] = e[j] >= 0 ? e[j] * NK + p[j] : INT_MAX;
@@ -1806,7 +1807,7 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_i32_kernel(Comb
 // (W*E <= PS * kGatherThreads), so that the segment start needs no second
 // dependent load; PS is 4 or 16 so that small tables do not pay for 16 loads
 // per thread. Needs rows in 16-byte pieces, K <= KT and N*K < 2^16.
-template <class T, int KT, int PS>
+template <class T, int KT, int PS, bool MASKED>
 __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineArgs a)
 {
     constexpr bool PRE = PS > 0;
@@ -1829,24 +1830,21 @@ __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineAr
     const int pt = t * K + (lane < K ? lane : 0);
     const int e = a.ids[pt];
     const uint32_t wbits = reinterpret_cast<const uint32_t *>(a.scales)[pt];
-    const uint8_t *mp = a.mask_kind == MOE_MASK_TOKEN  ? a.mask + t
-                        : a.mask_kind == MOE_MASK_PAIR ? a.mask + pt
-                                                       : reinterpret_cast<const uint8_t *>(a.ids + pt);
-    const int mb = *mp;                            // (without a mask: any byte, ignored)
+    const int mb = MASKED ? a.mask[a.mask_kind == MOE_MASK_TOKEN ? (size_t)t : (size_t)pt] : 1;
     const int tot0 = a.erc[(size_t)min(lane, a.W - 1) * a.S + a.S - 1];
     constexpr int SB = 4;                          // source pairs per thread and pass
     const int p1 = t * K;                          // token t's first pair
     int sp[SB], se[SB], sm[SB];
 #pragma unroll
     for (int u = 0; u < SB; ++u) sp[u] = s * a.bs * K + tid + u * kGatherThreads;
-    pair_loads<SB>(a.ids, a.mask, a.mask_kind, sp, p1, K, rK, se, sm);
+    pair_loads<SB, MASKED>(a.ids, a.mask, a.mask_kind, sp, p1, K, rK, se, sm);
     const int WS = a.W * a.S;
     int ercv[PRE ? PS : 1];
     if (PRE) {
 #pragma unroll
         for (int u = 0; u < PS; ++u) ercv[u] = a.erc[min(tid + u * kGatherThreads, WS - 1)];
     }
-    const bool on = lane < K && (a.mask_kind == MOE_MASK_NONE || mb != 0);
+    const bool on = lane < K && mb != 0;
     const bool real = on && (unsigned)e < (unsigned)a.E;
     const int r = real ? div_small(e, a.epr, 1.0f / a.epr) : -1;
     const int seg = real ? (e - r * a.epr) * a.W + s : 0;     // segment (el, s) inside rank r
@@ -1882,9 +1880,9 @@ __global__ __launch_bounds__(kGatherThreads) void combine_fused_kernel(CombineAr
         if (pb != pfirst) {                       // the first pass's loads were issued above
 #pragma unroll
             for (int u = 0; u < SB; ++u) sp[u] = pb + tid + u * kGatherThreads;
-            pair_loads<SB>(a.ids, a.mask, a.mask_kind, sp, p1, K, rK, se, sm);
+            pair_loads<SB, MASKED>(a.ids, a.mask, a.mask_kind, sp, p1, K, rK, se, sm);
         }
-        pair_experts<SB>(a.mask_kind, sp, p1, a.E, se, sm);
+        pair_experts<SB, MASKED>(sp, p1, a.E, se, sm);
 #pragma unroll
         for (int k = 0; k < KT; ++k) {
             int c = 0;
@@ -2234,10 +2232,16 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         const dim3 g((unsigned)(N * a.nsl + 1)), b(kFusedThreads);
         const size_t lds = (size_t)W * E * sizeof(int);
         const bool k8 = K <= 8, l8 = N * K <= 8 * kFusedThreads;
-        if (k8 && l8) hipLaunchKernelGGL((dispatch_fused_kernel<8, 8>), g, b, lds, st, a);
-        else if (k8) hipLaunchKernelGGL((dispatch_fused_kernel<8, 16>), g, b, lds, st, a);
-        else if (l8) hipLaunchKernelGGL((dispatch_fused_kernel<16, 8>), g, b, lds, st, a);
-        else hipLaunchKernelGGL((dispatch_fused_kernel<16, 16>), g, b, lds, st, a);
+#define MOE_FUSED_DISPATCH(M)                                                                       \
+        do {                                                                                        \
+            if (k8 && l8) hipLaunchKernelGGL((dispatch_fused_kernel<8, 8, M>), g, b, lds, st, a);           \
+            else if (k8) hipLaunchKernelGGL((dispatch_fused_kernel<8, 16, M>), g, b, lds, st, a);          \
+            else if (l8) hipLaunchKernelGGL((dispatch_fused_kernel<16, 8, M>), g, b, lds, st, a);          \
+            else hipLaunchKernelGGL((dispatch_fused_kernel<16, 16, M>), g, b, lds, st, a);                 \
+        } while (0)
+        if (a.mask_kind == MOE_MASK_NONE) MOE_FUSED_DISPATCH(false);
+        else MOE_FUSED_DISPATCH(true);
+#undef MOE_FUSED_DISPATCH
         return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
     }
 
@@ -2460,19 +2464,25 @@ int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t 
         const int ps = ws <= 4 * kGatherThreads ? 4 : ws <= kFusedCombineLdsCounts ? 16 : 0;
         const bool k8 = K <= 8;
         const size_t lds = ps ? (size_t)ws * sizeof(int) : 0;
+#define MOE_FUSED_COMBINE_M(T, M)                                                                   \
+        do {                                                                                        \
+            if (ps == 4 && k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, 4, M>), g, b, lds, st, a);    \
+            else if (ps == 4) hipLaunchKernelGGL((combine_fused_kernel<T, 16, 4, M>), g, b, lds, st, a);    \
+            else if (ps && k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, 16, M>), g, b, lds, st, a);   \
+            else if (ps) hipLaunchKernelGGL((combine_fused_kernel<T, 16, 16, M>), g, b, lds, st, a);       \
+            else if (k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, 0, M>), g, b, lds, st, a);         \
+            else hipLaunchKernelGGL((combine_fused_kernel<T, 16, 0, M>), g, b, lds, st, a);                \
+        } while (0)
 #define MOE_FUSED_COMBINE(T)                                                                        \
         do {                                                                                        \
-            if (ps == 4 && k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, 4>), g, b, lds, st, a);       \
-            else if (ps == 4) hipLaunchKernelGGL((combine_fused_kernel<T, 16, 4>), g, b, lds, st, a);       \
-            else if (ps && k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, 16>), g, b, lds, st, a);      \
-            else if (ps) hipLaunchKernelGGL((combine_fused_kernel<T, 16, 16>), g, b, lds, st, a);          \
-            else if (k8) hipLaunchKernelGGL((combine_fused_kernel<T, 8, 0>), g, b, lds, st, a);            \
-            else hipLaunchKernelGGL((combine_fused_kernel<T, 16, 0>), g, b, lds, st, a);                   \
+            if (a.mask_kind == MOE_MASK_NONE) MOE_FUSED_COMBINE_M(T, false);                           \
+            else MOE_FUSED_COMBINE_M(T, true);                                                      \
         } while (0)
         if (dtype == MOE_INT32) MOE_FUSED_COMBINE(int32_t);
         else if (dtype == MOE_FP16) MOE_FUSED_COMBINE(F16);
         else MOE_FUSED_COMBINE(BF16);
 #undef MOE_FUSED_COMBINE
+#undef MOE_FUSED_COMBINE_M
         return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
     }
     hipLaunchKernelGGL(combine_slots_kernel, dim3((unsigned)((a.R + kSlotThreads - 1) / kSlotThreads)),
