@@ -97,7 +97,7 @@ class StepEvents:
     """Timing events for the per-step samples: HIP events created with hipEventDisableSystemFence,
     recorded on torch's current stream. The timestamps are the same device clock as torch's events;
     without the system-scope fence a pair around nothing reads 1.5 us less (5.4 against 3.9 us on
-    the GPU machine), overhead that would otherwise sit in every sample. `n` pairs; pairs(i) -> (a, b)."""
+    an MI355X), overhead that would otherwise sit in every sample. `n` pairs; pairs(i) -> (a, b)."""
     DISABLE_SYSTEM_FENCE = 0x20000000
 
     def __init__(self, torch, n):

@@ -44,7 +44,7 @@ def _load():
 
 
 def default_threads() -> int:
-    """The host cores this process may use, at most 16 (a GPU machine's share for one GPU)."""
+    """The host cores this process may use, at most 16 (a host's share for one GPU)."""
     try:
         n = len(os.sched_getaffinity(0))
     except (AttributeError, OSError):
