@@ -102,8 +102,8 @@ struct BF16 {
 };
 
 // Streaming (non-temporal) 16-byte accesses for data that is touched once. They
-// pay where reads dominate (the combine's gather and its x_out stores) and in
-// the (token, slice) copy. The write-dominated wavefront scatters (the
+// pay where reads dominate (the combine's gather; its x_out stores are
+// device-scope, see store_device) and in the (token, slice) copy. The write-dominated wavefront scatters (the
 // quantisers, the wavefront copy) split their stores: a checkerboard over
 // (1 KiB chunk, copy) goes non-temporal, the rest plain. At
 // 16 ranks x 256 tokens, h = 7168 (294 MB moved) that kernel takes 45 us,
@@ -128,6 +128,24 @@ __device__ __forceinline__ void store_stream(uint4 *p, uint4 v)
 {
     u32x4_t t = {v.x, v.y, v.z, v.w};
     __builtin_nontemporal_store(t, reinterpret_cast<u32x4_t *>(p));
+}
+// Device-scope 16-byte store (sc1): the line is written through the XCD's L2
+// rather than left dirty there for the launch's closing writeback. The
+// combine's x_out is written once and read by no later wave of the launch, so
+// that writeback is pure wait at the end of the kernel: at 16 ranks x 256
+// tokens, h = 7168 (58.7 MB of x_out) the cold dispatch + combine step takes
+// ~142.4 us with it against ~146 us with non-temporal stores, back to back
+// unchanged. The dispatch's scatter is not helped: sc1 on its non-temporal
+// half takes the back-to-back step from 141 to 165 us, on its plain half it
+// changes nothing. There is no clang builtin for the scope bits, hence the
+// asm; the s_nop covers the wait states a VALU write to the store's data
+// registers needs after a 128-bit store, which the compiler does not see
+// across an asm statement. The store is a kernel's last memory access (no
+// later load's vmcnt wait miscounts it).
+__device__ __forceinline__ void store_device(uint4 *p, uint4 v)
+{
+    const u32x4_t t = {v.x, v.y, v.z, v.w};
+    asm volatile("global_store_dwordx4 %0, %1, off sc1\n\ts_nop 1" ::"v"(p), "v"(t) : "memory");
 }
 __device__ __forceinline__ uint4 load_stream(const uint4 *p)
 {
@@ -1741,7 +1759,7 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_half_kernel(Com
         uint32_t o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (uint32_t)T::store(acc[2 * i]) | ((uint32_t)T::store(acc[2 * i + 1]) << 16);
-        store_stream(reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes) + c,
+        store_device(reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes) + c,
                      make_uint4(o[0], o[1], o[2], o[3]));
     } else {
         const int j = sl * kGatherThreads + threadIdx.x;
