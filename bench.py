@@ -384,9 +384,12 @@ def main():
     ap.add_argument("--workload", default="w16_h7168_bf16_q8", choices=sorted(wl.BY_NAME))
     ap.add_argument("--bs", type=int, default=None,
                     help="tokens per rank for the main workload (same seed and recipe; default: the workload's)")
-    ap.add_argument("--schedule", choices=["token", "segment"], default="token",
-                    help="dispatch schedule of the main workload: token-major (default) or the segment-major "
-                         "large-segment schedule (copies and per-token int8 only)")
+    ap.add_argument("--schedule", choices=["adaptive", "token", "segment"], default="adaptive",
+                    help="dispatch schedule of the main workload: adaptive (the library's default: token-major, "
+                         "with whole workgroups for the large segments), token-major only, or segment-major "
+                         "(the last two large-segment forms take copies and per-token int8 only)")
+    ap.add_argument("--large-bytes", type=int, default=-1,
+                    help="large-segment threshold T in bytes for the main workload (default: the README's 2 MiB)")
     ap.add_argument("--h", type=int, default=None,
                     help="hidden size for the main workload (same seed and recipe; default: the workload's)")
     ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf,w16_h7168_bf16_fp8g128,"
@@ -428,12 +431,15 @@ def main():
     if args.h is not None and args.h != w.h:
         w = dataclasses.replace(w, h=args.h, name="%s_h%d" % (w.name, args.h))
     sched = None
-    if args.schedule == "segment":
-        if w.quant_mode in (1, 3):
-            print("the segment schedule takes copies and per-token int8 only", file=sys.stderr)
-            sys.exit(2)
-        sched = moe.MoeSchedule(mode=moe.MOE_SCHED_SEGMENT, large_segment_bytes=-1)
-        w = dataclasses.replace(w, name="%s_segment_schedule" % w.name)
+    if args.schedule == "segment" and w.quant_mode in (1, 3):
+        print("the segment schedule takes copies and per-token int8 only", file=sys.stderr)
+        sys.exit(2)
+    if args.schedule != "adaptive" or args.large_bytes >= 0:
+        mode = {"adaptive": moe.MOE_SCHED_ADAPTIVE, "token": moe.MOE_SCHED_TOKEN,
+                "segment": moe.MOE_SCHED_SEGMENT}[args.schedule]
+        sched = moe.MoeSchedule(mode=mode, large_segment_bytes=args.large_bytes)
+        w = dataclasses.replace(w, name="%s_%s_schedule%s" % (
+            w.name, args.schedule, "" if args.large_bytes < 0 else "_T%d" % args.large_bytes))
     r = measure(w, args.steps, args.warmup, flush, torch, moe, sched)
     disp_b, comb_b = algorithmic_bytes(w)
     ms = statistics.median(r["cold"])                 # the protocol's figure: median of the timed steps

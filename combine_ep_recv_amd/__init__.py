@@ -27,7 +27,7 @@ MOE_OK = 0
  MOE_ERR_ALIGN, MOE_ERR_MASK) = range(1, 10)
 MOE_INT32, MOE_FP16, MOE_BF16 = 0, 1, 2
 MOE_QUANT_NONE, MOE_QUANT_STATIC, MOE_QUANT_DYN_TOKEN, MOE_QUANT_DYN_GROUP = 0, 1, 2, 3
-MOE_SCHED_TOKEN, MOE_SCHED_SEGMENT = 0, 1
+MOE_SCHED_TOKEN, MOE_SCHED_SEGMENT, MOE_SCHED_ADAPTIVE = 0, 1, 2
 MOE_MASK_NONE, MOE_MASK_TOKEN, MOE_MASK_PAIR = 0, 1, 2
 
 EXPORTS = ("moe_dispatch_workspace_size", "moe_dispatch", "moe_dispatch_noalloc", "moe_combine_workspace_size",
@@ -60,8 +60,13 @@ def _special(zero_experts: int, copy_experts: int, ori_x: Optional[torch.Tensor]
 
 
 class MoeSchedule(ctypes.Structure):
+    """moe_schedule; by default the adaptive mode with the README's 2 MiB threshold (what a NULL schedule
+    selects)."""
     _fields_ = [("mode", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("large_segment_bytes", ctypes.c_int64), ("segment_is_large", ctypes.c_void_p)]
+
+    def __init__(self, mode=MOE_SCHED_ADAPTIVE, large_segment_bytes=-1, segment_is_large=None, reserved=0):
+        super().__init__(mode, reserved, large_segment_bytes, segment_is_large)
 
 
 _lib = None

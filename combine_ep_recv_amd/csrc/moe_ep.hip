@@ -64,8 +64,10 @@ constexpr int kChunkBatch = 16;            // chunk counts such a sum loads at o
 constexpr int kSegLdsMax = 11264;          // W*S limit for the LDS-resident segment counts
 constexpr long long kMaxTokens = (1ll << 24) - 1;   // N blocks of 256 threads stay below 2^32 items
 constexpr int kPlanRows = 8;               // rows per segment-schedule work item
+static_assert(kSegLdsMax <= 11 * kScanThreads, "the large-segment plan takes at most 11 segments per thread");
 static_assert(kPlanRows <= 64, "a plan item's rows are held one per lane");
 constexpr int kSegGrid = 4096;             // blocks of the segment-major payload pass
+constexpr int kAdaptiveSegGrid = 1024;     // blocks of the adaptive schedule's large-segment pass
 constexpr int64_t kReadmeLargeBytes = 2 * 1024 * 1024;
 
 constexpr int kCopyThreads = 128;          // token-major copy: block = (token, slice)
@@ -374,6 +376,20 @@ __global__ __launch_bounds__(kRouteThreads) void route_kernel(const int32_t *__r
 // scan (many chunks, or the segment schedule)
 // --------------------------------------------------------------------------
 
+// The large-segment predicate (combine_doubleplane README, 方案设计): segment
+// (el, s) of rank r with c rows is large iff it comes from another rank, is
+// non-empty, its payload c*h*elem_bytes reaches T, and that payload exceeds
+// the mean payload r receives per remote segment, num / den with num = (rows r
+// receives from other ranks)*h*elem_bytes and den = max(W-1, 1)*epr. The last
+// test is evaluated as c*den > remote rows: both sides of payload*den > num
+// carry the factor h*elem_bytes > 0, and without it no product can leave 64
+// bits.
+__device__ __forceinline__ bool segment_large(bool from_other_rank, long long c, long long remote_rows,
+                                              long long row_bytes, long long large_bytes, long long den)
+{
+    return from_other_rank && c > 0 && c * row_bytes >= large_bytes && c * den > remote_rows;
+}
+
 __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const int32_t *__restrict__ pc, const int32_t *__restrict__ pci, int W, int epr, int nbs, int h,
     int elem_bytes, int32_t *__restrict__ boff, int32_t *__restrict__ erc, int want_seg, long long large_bytes,
@@ -471,9 +487,7 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
     const long long den = (long long)(W - 1 > 1 ? W - 1 : 1) * epr;
     for (int g = tid; g < G; g += blockDim.x) {
         const int r = g / S, i = g % S;
-        const long long c = segc[g], bytes = c * h * elem_bytes;
-        const long long num = (long long)part[r] * h * elem_bytes;
-        const int large = (i % W != r) && c > 0 && bytes >= large_bytes && bytes * den > num;
+        const int large = segment_large(i % W != r, segc[g], part[r], (long long)h * elem_bytes, large_bytes, den);
         flag[g] = (uint8_t)large;
         if (seg_flags) seg_flags[g] = large;
     }
@@ -562,6 +576,114 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 // dispatch payload
 // --------------------------------------------------------------------------
 
+// Adaptive schedule: the large-segment flags, and work items for the large
+// segments only (the token-major scatter writes every other row), in one
+// block. Thread tid owns the consecutive segments [g0, g1) of the W*S in
+// ep_recv_count's order, which is also the order of their rows in expand_x,
+// so block-wide scans of the owned counts give each segment's first row and,
+// read at each rank's first segment, the rows each rank receives from the
+// other ranks. A segment's count sums its source rank's route chunks for its
+// expert, one load pass per two chunks of a source rank (per chunk at 11
+// segments per thread). Each large segment is cut
+// into kPlanRows-row items from its first row; items are numbered by start
+// row. PT >= ceil(W*S / kScanThreads) segments per thread.
+template <int PT>
+__global__ __launch_bounds__(kScanThreads) void large_plan_kernel(
+    const int32_t *__restrict__ pc, const int32_t *__restrict__ pci, int W, int epr, int nbs, int h,
+    int elem_bytes, long long large_bytes, int32_t *__restrict__ flags, int2 *__restrict__ plan,
+    int32_t *__restrict__ nplan)
+{
+    static_assert(PT <= 32, "owned segments are tracked in 32-bit masks");
+    __shared__ int32_t tmp[40];
+    __shared__ int32_t rstart[kMaxWorld + 1];     // remote rows received by the ranks before r
+    const int E = W * epr, S = E, G = W * S, tid = threadIdx.x;
+    const int per = (G + kScanThreads - 1) / kScanThreads;
+    const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
+
+    // owned segments (g = r*S + el*W + s, stepped from g0): rank, source rank,
+    // their expert's column in the chunk tables, and which ones open a rank
+    int rk[PT], sk[PT], col[PT];
+    unsigned first = 0;
+    {
+        int r = g0 / S, i = g0 - (g0 / S) * S;
+        int el = i / W, sr = i - (i / W) * W;
+#pragma unroll
+        for (int k = 0; k < PT; ++k) {
+            const bool in = g0 + k < g1;
+            rk[k] = in ? r : 0;
+            sk[k] = in ? sr : 0;
+            col[k] = in ? r * epr + el : 0;          // out of range: expert 0, source 0 (dropped)
+            if (in && el == 0 && sr == 0) first |= 1u << k;
+            if (++sr == W) {
+                sr = 0;
+                if (++el == epr) { el = 0; ++r; }
+            }
+        }
+    }
+    int c[PT];
+#pragma unroll
+    for (int k = 0; k < PT; ++k) c[k] = 0;
+    constexpr int CB = PT <= 8 ? 2 : 1;                // chunks per pass (11 segments: 1, within 128 VGPRs)
+    for (int j0 = 0; j0 < nbs; j0 += CB) {             // clamped loads, the extra dropped
+        int vi[CB][PT], vx[CB][PT];
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+#pragma unroll
+            for (int k = 0; k < PT; ++k) {
+                const size_t idx = (size_t)(sk[k] * nbs + min(j0 + u, nbs - 1)) * E + col[k];
+                vi[u][k] = pci[idx];
+                vx[u][k] = pc[idx];
+            }
+#pragma unroll
+        for (int u = 0; u < CB; ++u)
+#pragma unroll
+            for (int k = 0; k < PT; ++k) c[k] += g0 + k < g1 && j0 + u < nbs ? vi[u][k] - vx[u][k] : 0;
+    }
+    int csum = 0, rsum = 0;
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        csum += c[k];
+        rsum += sk[k] != rk[k] ? c[k] : 0;
+    }
+    int total_rows, total_remote;
+    const int row0 = block_excl_scan(csum, tmp, &total_rows);      // first row of segment g0
+    int run = block_excl_scan(rsum, tmp, &total_remote);
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        if ((first >> k) & 1u) rstart[rk[k]] = run;
+        run += sk[k] != rk[k] ? c[k] : 0;
+    }
+    if (tid == 0) rstart[W] = total_remote;
+    __syncthreads();
+
+    const long long den = (long long)(W - 1 > 1 ? W - 1 : 1) * epr, row_bytes = (long long)h * elem_bytes;
+    unsigned big = 0;
+    int nmine = 0;
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        if (g0 + k >= g1) continue;
+        const int remote = rstart[rk[k] + 1] - rstart[rk[k]];
+        const bool large = segment_large(sk[k] != rk[k], c[k], remote, row_bytes, large_bytes, den);
+        flags[g0 + k] = large ? 1 : 0;
+        if (large) {
+            big |= 1u << k;
+            nmine += (c[k] + kPlanRows - 1) / kPlanRows;
+        }
+    }
+    int nitems;
+    int idx = block_excl_scan(nmine, tmp, &nitems);
+    int row = row0;
+#pragma unroll
+    for (int k = 0; k < PT; ++k) {
+        if (g0 + k >= g1) continue;
+        if ((big >> k) & 1u)
+            for (int m = 0; m < c[k]; m += kPlanRows)
+                plan[idx++] = make_int2(row + m, row + min(m + kPlanRows, c[k]));
+        row += c[k];
+    }
+    if (tid == 0) *nplan = nitems;
+}
+
 struct DispatchArgs {
     const char *x;
     const int32_t *ids;
@@ -586,6 +708,7 @@ struct DispatchArgs {
     int store_mix;            // wavefront scatters: 0 half the stores plain, 1 a quarter, 2 none
     const uint8_t *mask;      // token mask (one-launch dispatch; the route kernel takes its own)
     int mask_kind;
+    const int32_t *skip;      // adaptive schedule: large-segment flags [W, S]; their rows get no payload here
 };
 
 // Whether piece j of copy k of a wavefront scatter is stored non-temporally
@@ -656,6 +779,7 @@ __device__ __forceinline__ void pairs_sum(const DispatchArgs &a, int t, const in
 }
 
 // Final rows (-1 for an invalid pair); optionally writes assist_info / expand_scales.
+template <bool SKIP = false>
 __device__ __forceinline__ void pairs_finish(const DispatchArgs &a, int t, const int *ek, const int *lk,
                                              const int *off, int *rows, bool meta, int lt, int nthr)
 {
@@ -673,18 +797,29 @@ __device__ __forceinline__ void pairs_finish(const DispatchArgs &a, int t, const
             a.assist[(size_t)row * 3 + 2] = k;
             if (a.esc_out) a.esc_out[row] = a.esc_in[(size_t)t * a.K + k];
         }
+        if constexpr (SKIP) {        // a large segment's row: meta here, payload by its own workgroups
+            if (row >= 0) {
+                const int r = ek[k] / a.epr;
+                if (a.skip[(size_t)r * a.S + (size_t)(ek[k] - r * a.epr) * a.W + s]) rows[k] = -1;
+            }
+        }
     }
 }
 
 // Row of pair (t, lane) for lanes < K (-1 for other lanes and invalid pairs), from
 // registers only: the chunk prefixes are summed by the lane itself (direct path)
 // or read from the scan's table. Writes assist_info / expand_scales when asked.
+template <bool SKIP = false>
 __device__ __forceinline__ int lane_pair_row(const DispatchArgs &a, int t, int lane, int e, int l, bool meta)
 {
     const int s = t / a.bs, tok = t - s * a.bs;
-    int row = -1;
+    int row = -1, big = 0;
     if (lane < a.K && (unsigned)e < (unsigned)a.E && l >= 0) {
         const int bt = s * a.nbs + tok / kRouteTokens;
+        if constexpr (SKIP) {
+            const int r = e / a.epr;
+            big = a.skip[(size_t)r * a.S + (size_t)(e - r * a.epr) * a.W + s];
+        }
         int off = 0;
         if (a.direct) {
             // all chunk counts of a pass loaded before any is added: one round trip per pass
@@ -710,14 +845,14 @@ __device__ __forceinline__ int lane_pair_row(const DispatchArgs &a, int t, int l
         a.assist[(size_t)row * 3 + 2] = lane;
         if (a.esc_out) a.esc_out[row] = a.esc_in[(size_t)t * a.K + lane];
     }
-    return row;
+    return SKIP && big ? -1 : row;     // a large segment's row: meta here, payload by its own workgroups
 }
 
 // Token-major copy: block = (token, slice of kCopyThreads * kCopyUnroll chunks).
 // For topk <= 64 each wavefront resolves the K rows in its own lanes (pair k in
 // lane k, loaded before the payload) and reads them back with readlane: no LDS and
 // no barrier; larger topk goes through LDS.
-template <bool VEC>
+template <bool VEC, bool SKIP = false>
 __global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(DispatchArgs a)
 {
     extern __shared__ int dsm[];                  // ek, lk, off, rows: 4 * K ints (topk > 64 only)
@@ -747,7 +882,7 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(DispatchArgs
     }
 
     if (small_k) {
-        const int my_row = lane_pair_row(a, t, lane, e, l, sl == 0 && tid < 64);
+        const int my_row = lane_pair_row<SKIP>(a, t, lane, e, l, sl == 0 && tid < 64);
 #pragma unroll
         for (int u = 0; u < kCopyUnroll; ++u) {
             const int c = c0 + u * kCopyThreads;
@@ -767,7 +902,7 @@ __global__ __launch_bounds__(kCopyThreads) void scatter_copy_kernel(DispatchArgs
     __syncthreads();
     pairs_sum(a, t, ek, off, tid, kCopyThreads);
     __syncthreads();
-    pairs_finish(a, t, ek, lk, off, rows, sl == 0, tid, kCopyThreads);
+    pairs_finish<SKIP>(a, t, ek, lk, off, rows, sl == 0, tid, kCopyThreads);
     __syncthreads();
 #pragma unroll
     for (int u = 0; u < kCopyUnroll; ++u) {
@@ -947,7 +1082,7 @@ __device__ __forceinline__ void quant_store_wave_static(const DispatchArgs &a, i
 // quantising scatter, with the same checkerboard of plain and non-temporal
 // stores (at 16 ranks x 256 tokens of bf16: 84 us; 109 us all non-temporal,
 // 130 us all plain).
-template <int J>
+template <int J, bool SKIP = false>
 __global__ __launch_bounds__(kQuantThreads) void scatter_copy_wave_kernel(DispatchArgs a)
 {
     const int lane = threadIdx.x & 63;
@@ -962,7 +1097,7 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_copy_wave_kernel(Dispat
         uint4 v[J];
 #pragma unroll
         for (int j = 0; j < J; ++j) v[j] = load_stream(src + min(lane + 64 * j, nc - 1));
-        const int my_row = lane_pair_row(a, t, lane, e, l, true);
+        const int my_row = lane_pair_row<SKIP>(a, t, lane, e, l, true);
 #pragma unroll
         for (int j = 0; j < J; ++j) {
             const int c = lane + 64 * j;
@@ -1088,7 +1223,7 @@ __device__ __forceinline__ void quant_store_wave_fp8(const DispatchArgs &a, int 
 // in-chunk rank before the row's 16-byte loads, so both are in flight together;
 // rows reach the store loop through readlane. No LDS, no barrier. Needs
 // h % 16 == 0, h <= 1024 * J, topk <= kQuantMaxK.
-template <class T, int J, int QM>
+template <class T, int J, int QM, bool SKIP = false>
 __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(DispatchArgs a)
 {
     const int lane = threadIdx.x & 63;
@@ -1111,7 +1246,7 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(Dispa
             v[j][1] = src[2 * oc + 1];
         }
         __builtin_amdgcn_sched_barrier(0);
-        const int my_row = lane_pair_row(a, t, lane, e, l, true);
+        const int my_row = lane_pair_row<SKIP>(a, t, lane, e, l, true);
         if constexpr (QM == MOE_QUANT_DYN_GROUP) quant_store_wave_fp8<T, J>(a, lane, v, my_row);
         else if constexpr (QM == MOE_QUANT_STATIC) quant_store_wave_static<T, J>(a, lane, v, my_row);
         else quant_store_wave<T, J>(a, lane, v, my_row);
@@ -1258,7 +1393,7 @@ __device__ float quant_row_block(const uint16_t *__restrict__ src, int8_t *__res
     return scale;
 }
 
-template <class T, bool VEC>
+template <class T, bool VEC, bool SKIP = false>
 __global__ __launch_bounds__(kBlockThreads) void scatter_quant_block_kernel(DispatchArgs a)
 {
     extern __shared__ int dsm[];
@@ -1271,7 +1406,7 @@ __global__ __launch_bounds__(kBlockThreads) void scatter_quant_block_kernel(Disp
     __syncthreads();
     pairs_sum(a, t, ek, off, threadIdx.x, kBlockThreads);
     __syncthreads();
-    pairs_finish(a, t, ek, lk, off, rows, true, threadIdx.x, kBlockThreads);
+    pairs_finish<SKIP>(a, t, ek, lk, off, rows, true, threadIdx.x, kBlockThreads);
     __syncthreads();
     const float scale = quant_row_block<T, VEC>(reinterpret_cast<const uint16_t *>(a.x) + (size_t)t * a.h,
                                                 reinterpret_cast<int8_t *>(a.expand_x), rows, a.K, a.h, red);
@@ -2024,7 +2159,7 @@ int check_special(const moe_special_experts *sp, long long E)
 
 struct DispatchLayout {
     int nbs, NB;
-    size_t pc, pci, boff, lr, plan, nplan, total;
+    size_t pc, pci, boff, lr, plan, nplan, flags, total;
 };
 
 DispatchLayout dispatch_layout(int W, int bs, int epr, int K)
@@ -2041,30 +2176,32 @@ DispatchLayout dispatch_layout(int W, int bs, int epr, int K)
     L.lr = off;    off = round_up(off + N * K * 4, 256);
     L.plan = off;  off = round_up(off + plan_cap * 8, 256);
     L.nplan = off; off = round_up(off + 4, 256);
+    L.flags = off; off = round_up(off + (W * S <= (size_t)kSegLdsMax ? W * S * 4 : 0), 256);
     L.total = off;
     return L;
 }
 
+template <bool SKIP>
 void launch_copy_wave(int J, dim3 g, dim3 b, hipStream_t st, const DispatchArgs &a)
 {
-    if (J <= 1) hipLaunchKernelGGL((scatter_copy_wave_kernel<1>), g, b, 0, st, a);
-    else if (J <= 2) hipLaunchKernelGGL((scatter_copy_wave_kernel<2>), g, b, 0, st, a);
-    else if (J <= 4) hipLaunchKernelGGL((scatter_copy_wave_kernel<4>), g, b, 0, st, a);
-    else if (J <= 8) hipLaunchKernelGGL((scatter_copy_wave_kernel<8>), g, b, 0, st, a);
-    else if (J <= 14) hipLaunchKernelGGL((scatter_copy_wave_kernel<14>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((scatter_copy_wave_kernel<16>), g, b, 0, st, a);
+    if (J <= 1) hipLaunchKernelGGL((scatter_copy_wave_kernel<1, SKIP>), g, b, 0, st, a);
+    else if (J <= 2) hipLaunchKernelGGL((scatter_copy_wave_kernel<2, SKIP>), g, b, 0, st, a);
+    else if (J <= 4) hipLaunchKernelGGL((scatter_copy_wave_kernel<4, SKIP>), g, b, 0, st, a);
+    else if (J <= 8) hipLaunchKernelGGL((scatter_copy_wave_kernel<8, SKIP>), g, b, 0, st, a);
+    else if (J <= 14) hipLaunchKernelGGL((scatter_copy_wave_kernel<14, SKIP>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((scatter_copy_wave_kernel<16, SKIP>), g, b, 0, st, a);
 }
 
-template <class T, int QM>
+template <class T, int QM, bool SKIP = false>
 void launch_quant_wave(int J, dim3 g, dim3 b, hipStream_t st, const DispatchArgs &a)
 {
-    if (J <= 1) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 1, QM>), g, b, 0, st, a);
-    else if (J <= 2) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 2, QM>), g, b, 0, st, a);
-    else if (J <= 4) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 4, QM>), g, b, 0, st, a);
-    else if (J <= 7) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 7, QM>), g, b, 0, st, a);
-    else if (J <= 8) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 8, QM>), g, b, 0, st, a);
-    else if (J <= 12) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 12, QM>), g, b, 0, st, a);
-    else hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 16, QM>), g, b, 0, st, a);
+    if (J <= 1) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 1, QM, SKIP>), g, b, 0, st, a);
+    else if (J <= 2) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 2, QM, SKIP>), g, b, 0, st, a);
+    else if (J <= 4) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 4, QM, SKIP>), g, b, 0, st, a);
+    else if (J <= 7) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 7, QM, SKIP>), g, b, 0, st, a);
+    else if (J <= 8) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 8, QM, SKIP>), g, b, 0, st, a);
+    else if (J <= 12) hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 12, QM, SKIP>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((scatter_quant_wave_kernel<T, 16, QM, SKIP>), g, b, 0, st, a);
 }
 
 // ---- scratch of the allocation-free dispatch (moe_dispatch_noalloc) ----
@@ -2172,17 +2309,23 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     if ((rc = check_special(special, (long long)W * epr))) return rc;
     if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
 
-    const int mode = schedule ? schedule->mode : MOE_SCHED_TOKEN;
+    const int mode = schedule ? schedule->mode : MOE_SCHED_ADAPTIVE;
     long long large = schedule ? schedule->large_segment_bytes : -1;
     if (large < 0) large = kReadmeLargeBytes;
     int32_t *seg_flags = schedule ? schedule->segment_is_large : nullptr;
-    if (mode != MOE_SCHED_TOKEN && mode != MOE_SCHED_SEGMENT) return MOE_ERR_SCHEDULE;
+    if (mode != MOE_SCHED_TOKEN && mode != MOE_SCHED_SEGMENT && mode != MOE_SCHED_ADAPTIVE) return MOE_ERR_SCHEDULE;
     const long long S = (long long)epr * W;
-    const bool want_seg = mode == MOE_SCHED_SEGMENT || seg_flags;
+    const size_t xs = elem_size(dtype);
+    const int elem_out = quant ? 1 : (int)xs;
+    // The adaptive schedule runs its large-segment pass only where a segment
+    // can be large: a segment holds at most bs rows (ids are distinct per
+    // token), so bs * h * elem_out < T rules every segment out.
+    const bool adaptive = mode == MOE_SCHED_ADAPTIVE && N > 0 && (!quant || quant_mode == MOE_QUANT_DYN_TOKEN) &&
+                          (long long)W * S <= kSegLdsMax && (long long)bs * h * elem_out >= large;
+    const bool want_seg = mode == MOE_SCHED_SEGMENT || (seg_flags && !adaptive);
     if (want_seg && (long long)W * S > kSegLdsMax) return MOE_ERR_SCHEDULE;
     if ((group_quant || static_quant) && mode == MOE_SCHED_SEGMENT) return MOE_ERR_SCHEDULE;
 
-    const size_t xs = elem_size(dtype);
     const size_t rowbytes = (size_t)h * xs;
     if (!aligned(x, xs) || !aligned(expert_ids, 4) || !aligned(expert_scales, 4) ||
         !aligned(expand_x, quant ? 1 : xs) || !aligned(dynamic_scales, 4) || !aligned(assist_info, 4) ||
@@ -2207,7 +2350,8 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     const int E = W * epr;
     // blocks sum the chunk prefixes themselves unless there are many chunks (or a
     // plan is needed); otherwise one scan block forms every offset first
-    const bool direct = N > 0 && mode == MOE_SCHED_TOKEN && L.NB <= kDirectMaxChunks;
+    const bool direct = N > 0 && mode != MOE_SCHED_SEGMENT && L.NB <= kDirectMaxChunks;
+    int32_t *flags = seg_flags ? seg_flags : reinterpret_cast<int32_t *>(ws + L.flags);
 
     DispatchArgs a;
     a.x = static_cast<const char *>(x);
@@ -2224,6 +2368,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     a.boff = boff;
     a.plan = plan;
     a.nplan = nplan;
+    a.skip = adaptive ? flags : nullptr;
     a.W = W; a.bs = bs; a.epr = epr; a.h = h; a.K = K; a.nbs = L.nbs; a.R = (int)(N * K);
     a.E = E; a.S = (int)S; a.NB = L.NB;
     // with a scan block present it also wrote ep_recv_count
@@ -2243,7 +2388,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     (void)hipGetLastError();
     // Small batches of copies: one launch (rows by counting, see dispatch_fused_kernel)
     const bool vec16 = rowbytes % 16 == 0 && aligned(x, 16) && aligned(expand_x, 16);
-    if (N > 0 && !quant && mode == MOE_SCHED_TOKEN && !want_seg && vec16 && K <= kFusedMaxK &&
+    if (N > 0 && !quant && mode != MOE_SCHED_SEGMENT && !adaptive && !want_seg && vec16 && K <= kFusedMaxK &&
         N * K <= kFusedMaxPairs && (long long)W * E <= kFusedMaxCounts) {
         const int sc = kFusedThreads * kFusedUnroll;
         a.nsl = (int)(((long long)rowbytes / 16 + sc - 1) / sc);
@@ -2263,7 +2408,6 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;
     }
 
-    const int elem_out = quant ? 1 : (int)xs;
     if (N > 0) {
         const dim3 g(L.NB), b(kRouteThreads);
         const size_t lds = (size_t)E * kRouteWords * 8;
@@ -2281,8 +2425,42 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), want_seg ? (size_t)W * S * 5 : 0, st, pc, pci,
                            W, epr, L.nbs, h, elem_out, boff, ep_recv_count, want_seg ? 1 : 0, large, seg_flags,
                            (mode == MOE_SCHED_SEGMENT && N > 0) ? plan : nullptr, nplan);
+    if (adaptive) {
+        const long long per = ((long long)W * S + kScanThreads - 1) / kScanThreads;    // <= 11
+#define MOE_LARGE_PLAN(P) hipLaunchKernelGGL(large_plan_kernel<P>, dim3(1), dim3(kScanThreads), 0, st, pc, pci, W, \
+                                             epr, L.nbs, h, elem_out, large, flags, plan, nplan)
+        if (per <= 1) MOE_LARGE_PLAN(1);
+        else if (per <= 2) MOE_LARGE_PLAN(2);
+        else if (per <= 4) MOE_LARGE_PLAN(4);
+        else if (per <= 8) MOE_LARGE_PLAN(8);
+        else MOE_LARGE_PLAN(11);
+#undef MOE_LARGE_PLAN
+    }
+    // the payload pass over a plan's items (segment-major, or the adaptive schedule's large segments)
+    auto segment_payload = [&](unsigned blocks) {
+        const int qm = !quant ? 0 : (dtype == MOE_FP16 ? 1 : 2);
+        const bool vec = quant ? (h % 8 == 0 && aligned(x, 16) && aligned(expand_x, 8))
+                               : (rowbytes % 16 == 0 && aligned(x, 16) && aligned(expand_x, 16));
+        const int Jc = (int)((rowbytes / 16 + 63) / 64), Jq = (h / 16 + 63) / 64;
+        const dim3 g(blocks), b(kBlockThreads), bw(kQuantThreads);
+        if (qm == 0 && vec && Jc <= 16) {
+            launch_segment_copy_wave(Jc, g, bw, st, a);
+        } else if (qm != 0 && wave) {
+            if (qm == 1) launch_segment_quant_wave<F16>(Jq, g, bw, st, a);
+            else launch_segment_quant_wave<BF16>(Jq, g, bw, st, a);
+        } else if (qm == 0) {
+            if (vec) hipLaunchKernelGGL((segment_payload_kernel<0, true>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((segment_payload_kernel<0, false>), g, b, 0, st, a);
+        } else if (qm == 1) {
+            if (vec) hipLaunchKernelGGL((segment_payload_kernel<1, true>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((segment_payload_kernel<1, false>), g, b, 0, st, a);
+        } else {
+            if (vec) hipLaunchKernelGGL((segment_payload_kernel<2, true>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((segment_payload_kernel<2, false>), g, b, 0, st, a);
+        }
+    };
     if (N > 0) {
-        if (mode == MOE_SCHED_TOKEN) {
+        if (mode != MOE_SCHED_SEGMENT) {
             const size_t kdsm = (size_t)4 * K * sizeof(int);
             if (!quant) {
                 const bool vec = rowbytes % 16 == 0 && aligned(x, 16) && aligned(expand_x, 16);
@@ -2297,12 +2475,18 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                 if (vec && K <= kQuantMaxK && Jc <= 16 && N >= kCopyWaveMinTokens &&
                     (long long)N * K * (long long)rowbytes <= kCopyWaveMaxBytes) {
                     const dim3 g((unsigned)((N + 3) / 4)), b(kQuantThreads);
-                    launch_copy_wave(Jc, g, b, st, a);
+                    if (adaptive) launch_copy_wave<true>(Jc, g, b, st, a);
+                    else launch_copy_wave<false>(Jc, g, b, st, a);
                 } else {
                     a.nsl = (int)((n + sc - 1) / sc);
                     const dim3 g((unsigned)(N * a.nsl)), b(kCopyThreads);
-                    if (vec) hipLaunchKernelGGL(scatter_copy_kernel<true>, g, b, kdsm, st, a);
-                    else hipLaunchKernelGGL(scatter_copy_kernel<false>, g, b, kdsm, st, a);
+                    if (adaptive) {
+                        if (vec) hipLaunchKernelGGL((scatter_copy_kernel<true, true>), g, b, kdsm, st, a);
+                        else hipLaunchKernelGGL((scatter_copy_kernel<false, true>), g, b, kdsm, st, a);
+                    } else {
+                        if (vec) hipLaunchKernelGGL((scatter_copy_kernel<true, false>), g, b, kdsm, st, a);
+                        else hipLaunchKernelGGL((scatter_copy_kernel<false, false>), g, b, kdsm, st, a);
+                    }
                 }
             } else {
                 if (wave) {
@@ -2334,49 +2518,39 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                     } else if (dtype == MOE_FP16) {
                         if (group_quant) launch_quant_wave<F16, MOE_QUANT_DYN_GROUP>(J, g, b, st, a);
                         else if (static_quant) launch_quant_wave<F16, MOE_QUANT_STATIC>(J, g, b, st, a);
+                        else if (adaptive) launch_quant_wave<F16, MOE_QUANT_DYN_TOKEN, true>(J, g, b, st, a);
                         else launch_quant_wave<F16, MOE_QUANT_DYN_TOKEN>(J, g, b, st, a);
                     } else {
                         if (group_quant) launch_quant_wave<BF16, MOE_QUANT_DYN_GROUP>(J, g, b, st, a);
                         else if (static_quant) launch_quant_wave<BF16, MOE_QUANT_STATIC>(J, g, b, st, a);
+                        else if (adaptive) launch_quant_wave<BF16, MOE_QUANT_DYN_TOKEN, true>(J, g, b, st, a);
                         else launch_quant_wave<BF16, MOE_QUANT_DYN_TOKEN>(J, g, b, st, a);
                     }
                 } else {
                     const bool vec = h % 8 == 0 && aligned(x, 16) && aligned(expand_x, 8);
                     const dim3 g((unsigned)N), b(kBlockThreads);
+#define MOE_QUANT_BLOCK(T, S)                                                                      \
+                    do {                                                                           \
+                        if (vec) hipLaunchKernelGGL((scatter_quant_block_kernel<T, true, S>), g, b, kdsm, st, a);   \
+                        else hipLaunchKernelGGL((scatter_quant_block_kernel<T, false, S>), g, b, kdsm, st, a);      \
+                    } while (0)
                     if (dtype == MOE_FP16) {
-                        if (vec) hipLaunchKernelGGL((scatter_quant_block_kernel<F16, true>), g, b, kdsm, st, a);
-                        else hipLaunchKernelGGL((scatter_quant_block_kernel<F16, false>), g, b, kdsm, st, a);
+                        if (adaptive) MOE_QUANT_BLOCK(F16, true);
+                        else MOE_QUANT_BLOCK(F16, false);
                     } else {
-                        if (vec) hipLaunchKernelGGL((scatter_quant_block_kernel<BF16, true>), g, b, kdsm, st, a);
-                        else hipLaunchKernelGGL((scatter_quant_block_kernel<BF16, false>), g, b, kdsm, st, a);
+                        if (adaptive) MOE_QUANT_BLOCK(BF16, true);
+                        else MOE_QUANT_BLOCK(BF16, false);
                     }
+#undef MOE_QUANT_BLOCK
                 }
             }
+            // adaptive schedule: the large segments' rows, whole workgroups per item
+            if (adaptive) segment_payload(kAdaptiveSegGrid);
         } else {
             const long long npairs = N * K;
             hipLaunchKernelGGL(segment_meta_kernel, dim3((unsigned)((npairs + kBlockThreads - 1) / kBlockThreads)),
                                dim3(kBlockThreads), 0, st, a);
-            const dim3 g(kSegGrid), b(kBlockThreads);
-            const int qm = !quant ? 0 : (dtype == MOE_FP16 ? 1 : 2);
-            const bool vec = quant ? (h % 8 == 0 && aligned(x, 16) && aligned(expand_x, 8))
-                                   : (rowbytes % 16 == 0 && aligned(x, 16) && aligned(expand_x, 16));
-            const int Jc = (int)((rowbytes / 16 + 63) / 64), Jq = (h / 16 + 63) / 64;
-            const dim3 gw(kSegGrid), bw(kQuantThreads);
-            if (qm == 0 && vec && Jc <= 16) {
-                launch_segment_copy_wave(Jc, gw, bw, st, a);
-            } else if (qm != 0 && wave) {
-                if (qm == 1) launch_segment_quant_wave<F16>(Jq, gw, bw, st, a);
-                else launch_segment_quant_wave<BF16>(Jq, gw, bw, st, a);
-            } else if (qm == 0) {
-                if (vec) hipLaunchKernelGGL((segment_payload_kernel<0, true>), g, b, 0, st, a);
-                else hipLaunchKernelGGL((segment_payload_kernel<0, false>), g, b, 0, st, a);
-            } else if (qm == 1) {
-                if (vec) hipLaunchKernelGGL((segment_payload_kernel<1, true>), g, b, 0, st, a);
-                else hipLaunchKernelGGL((segment_payload_kernel<1, false>), g, b, 0, st, a);
-            } else {
-                if (vec) hipLaunchKernelGGL((segment_payload_kernel<2, true>), g, b, 0, st, a);
-                else hipLaunchKernelGGL((segment_payload_kernel<2, false>), g, b, 0, st, a);
-            }
+            segment_payload(kSegGrid);
         }
     }
     return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_LAUNCH;

@@ -80,8 +80,9 @@ enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
  *      shared by the experts, per-expert coefficients fused with smoothing);
  *      its formula is garbled, and multiplying is the reading taken. No
  *      dynamic_scales. Needs h % 16 == 0, h <= 16384, topk <= 64, 16-byte
- *      aligned x, expand_x and (for h or E*h values) quant_scales, and the
- *      token schedule.
+ *      aligned x, expand_x and (for h or E*h values) quant_scales, and a
+ *      token-major schedule (not MOE_SCHED_SEGMENT; the adaptive one runs
+ *      this mode token-major).
  *  MOE_QUANT_DYN_TOKEN: int8 codes rint(x / s), s = max|x| / 127 over the token;
  *      dynamic_scales holds one fp32 scale per row.
  *  MOE_QUANT_DYN_GROUP: OCP FP8 E4M3 ("fn") codes per group of 128 elements of
@@ -90,8 +91,9 @@ enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
  *      kept; an all-zero group has s = 0 and codes 0. dynamic_scales is fp32
  *      [ROWS, ceil(h/128)]. (The pages list the mode; its output types and group
  *      size are garbled, and these are the readings taken.) Needs h % 16 == 0,
- *      h <= 16384, topk <= 64, 16-byte aligned x and expand_x, and the token
- *      schedule. */
+ *      h <= 16384, topk <= 64, 16-byte aligned x and expand_x, and a
+ *      token-major schedule (not MOE_SCHED_SEGMENT; the adaptive one runs
+ *      this mode token-major). */
 enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_STATIC = 1, MOE_QUANT_DYN_TOKEN = 2, MOE_QUANT_DYN_GROUP = 3 };
 
 /* Token masks: xActiveMaskOptional of aclnnMoeDistributeDispatchV4 (参数说明):
@@ -137,17 +139,31 @@ typedef struct moe_special_experts {
  * bitwise identical outputs (the combine_doubleplane README requires the same
  * x_out whichever return path a segment takes).
  *  MOE_SCHED_TOKEN:   one workgroup per source token reads the row once and
- *                     writes its K copies (default).
+ *                     writes its K copies; the predicate is not consulted.
  *  MOE_SCHED_SEGMENT: workgroups walk expand_x in destination order; a segment
  *                     selected by the large-segment predicate gets whole
  *                     workgroups of its own (split by rows), the other
  *                     segments are packed together. Each token row is then
  *                     read once per destination row rather than once, so
  *                     this mode is slower (16 ranks x 256 bf16 tokens of
- *                     7168, int8: 132 us per dispatch against 50 us). */
-enum moe_sched_mode { MOE_SCHED_TOKEN = 0, MOE_SCHED_SEGMENT = 1 };
+ *                     7168, int8: 132 us per dispatch against 50 us).
+ *  MOE_SCHED_ADAPTIVE (the default when schedule is NULL): the token
+ *                     schedule for every segment the predicate does not
+ *                     select; the rows of each selected segment are written
+ *                     by whole workgroups of their own, split by rows (each
+ *                     such row reads its token once more). A segment holds at
+ *                     most bs rows (ids are distinct per token), so when
+ *                     bs*h*elem_bytes < T no segment can be selected and this
+ *                     mode runs exactly the token schedule; with the README's
+ *                     2 MiB that holds at 16 ranks x 256 tokens of 7168 int8.
+ *                     It covers copies and per-token int8 (quant_mode 0 and
+ *                     2) with W*S <= 11264; other quant modes and larger
+ *                     segment tables take the token schedule. */
+enum moe_sched_mode { MOE_SCHED_TOKEN = 0, MOE_SCHED_SEGMENT = 1, MOE_SCHED_ADAPTIVE = 2 };
 
-/* Optional dispatch schedule (host struct; pass NULL for the defaults).
+/* Optional dispatch schedule (host struct; pass NULL for the defaults:
+ * MOE_SCHED_ADAPTIVE with the README's 2 MiB).
+ *  mode: a moe_sched_mode.
  *  large_segment_bytes: threshold T of the predicate (README 方案设计): a
  *      segment (el, s) of rank r is large iff s != r, it is non-empty, its
  *      payload count*h*elem_bytes is >= T, and count*h*elem_bytes*den > num

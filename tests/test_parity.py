@@ -494,11 +494,17 @@ SCHED_CASES = [wl.WORKLOADS[1], wl.WORKLOADS[2], wl.WORKLOADS[3], wl.WORKLOADS[4
                wl.custom(2, 40, 16384, 4, 4, "bf16", "gauss_topk", quant_mode=2, name="q8_h16384_j16"),
                wl.custom(3, 300, 1040, 4, 3, "fp16", "zipf_topk", quant_mode=2, name="q8_h1040_j2"),
                wl.custom(3, 20, 13, 3, 2, "int32", name="int32_h13_block_path"),
-               wl.custom(104, 3, 16, 2, 1, "bf16", "zipf_topk", name="w104_11_segments_per_thread")]
+               wl.custom(104, 3, 16, 2, 1, "bf16", "zipf_topk", name="w104_11_segments_per_thread"),
+               # topk > 64 (the token-major kernels' LDS row path), and 66 route chunks (offsets from the
+               # scan block instead of per-pair chunk sums)
+               wl.custom(2, 24, 64, 70, 40, "fp16", "zipf_topk", name="copy_k70_lds_rows"),
+               wl.custom(2, 24, 64, 70, 40, "bf16", "gauss_topk", quant_mode=2, name="q8_k70_block_kernel"),
+               wl.custom(2, 8300, 32, 2, 2, "bf16", "zipf_topk", quant_mode=2, name="q8_66_chunks_scan_offsets")]
 
 
 @pytest.mark.parametrize("w", SCHED_CASES, ids=lambda w: w.name)
-@pytest.mark.parametrize("mode", [moe.MOE_SCHED_TOKEN, moe.MOE_SCHED_SEGMENT], ids=["token", "segment"])
+@pytest.mark.parametrize("mode", [moe.MOE_SCHED_TOKEN, moe.MOE_SCHED_SEGMENT, moe.MOE_SCHED_ADAPTIVE],
+                         ids=["token", "segment", "adaptive"])
 @pytest.mark.parametrize("T", [-1, 0, 64 * 1024, 1 << 40], ids=["T2MiB", "T0", "T64KiB", "Tinf"])
 def test_schedules_are_result_neutral_and_flag_the_right_segments(w, mode, T):
     inp = wl.make_inputs(w)
@@ -511,6 +517,16 @@ def test_schedules_are_result_neutral_and_flag_the_right_segments(w, mode, T):
     assert (to_np(flags) == want.astype(np.int32)).all()
     if T < 0 and w.name != "zipf_bs192_literal_rule_fires":
         assert want.sum() == 0     # the README's 2 MiB never fires on the page workloads
+
+
+def test_default_schedule_splits_off_the_segments_the_literal_rule_selects():
+    """With no schedule the dispatch is adaptive at the README's 2 MiB: on this shape (192 tokens per rank of 7168
+    fp16, Zipf routing) a segment can reach 2 MiB, so the large-segment pass runs, and some segments are large."""
+    w = SCHED_CASES[4]
+    assert w.name == "zipf_bs192_literal_rule_fires"
+    inp = wl.make_inputs(w)
+    _, o = check(w, inp, None)
+    assert oracle.large_segments(o["ep_recv_count"], w.ep_world, w.experts_per_rank, w.h, 2, TWO_MIB).sum() > 0
 
 
 # --------------------------------------------------------------------------
@@ -746,12 +762,23 @@ def random_segment_case(i):
 
 
 RANDOM_SEGMENT_CASES = [random_segment_case(i) for i in range(100, 112)]
+RANDOM_ADAPTIVE_CASES = [random_segment_case(i) for i in range(112, 124)]
 
 
 @pytest.mark.parametrize("w,kind,T", RANDOM_SEGMENT_CASES,
                          ids=lambda v: v if isinstance(v, (str, int)) else v.name)
 def test_random_configurations_segment_schedule(w, kind, T):
     sched = moe.MoeSchedule(mode=moe.MOE_SCHED_SEGMENT, large_segment_bytes=T)
+    if kind == "none":
+        check(w, schedule=sched)
+    else:
+        check_masked(w, kind, schedule=sched)
+
+
+@pytest.mark.parametrize("w,kind,T", RANDOM_ADAPTIVE_CASES,
+                         ids=lambda v: v if isinstance(v, (str, int)) else v.name)
+def test_random_configurations_adaptive_schedule(w, kind, T):
+    sched = moe.MoeSchedule(mode=moe.MOE_SCHED_ADAPTIVE, large_segment_bytes=T)
     if kind == "none":
         check(w, schedule=sched)
     else:
