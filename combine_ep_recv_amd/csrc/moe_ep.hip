@@ -64,10 +64,9 @@ constexpr int kChunkBatch = 16;            // chunk counts such a sum loads at o
 constexpr int kSegLdsMax = 11264;          // W*S limit for the LDS-resident segment counts
 constexpr long long kMaxTokens = (1ll << 24) - 1;   // N blocks of 256 threads stay below 2^32 items
 constexpr int kPlanRows = 8;               // rows per segment-schedule work item
-static_assert(kSegLdsMax <= 11 * kScanThreads, "the large-segment plan takes at most 11 segments per thread");
 static_assert(kPlanRows <= 64, "a plan item's rows are held one per lane");
 constexpr int kSegGrid = 4096;             // blocks of the segment-major payload pass
-constexpr int kAdaptiveSegGrid = 1024;     // blocks of the adaptive schedule's large-segment pass
+constexpr int kAdaptiveSegGrid = 1024;     // most blocks of the adaptive schedule's large-segment pass
 constexpr int64_t kReadmeLargeBytes = 2 * 1024 * 1024;
 
 constexpr int kCopyThreads = 128;          // token-major copy: block = (token, slice)
@@ -576,114 +575,6 @@ __global__ __launch_bounds__(kScanThreads) void scan_kernel(
 // dispatch payload
 // --------------------------------------------------------------------------
 
-// Adaptive schedule: the large-segment flags, and work items for the large
-// segments only (the token-major scatter writes every other row), in one
-// block. Thread tid owns the consecutive segments [g0, g1) of the W*S in
-// ep_recv_count's order, which is also the order of their rows in expand_x,
-// so block-wide scans of the owned counts give each segment's first row and,
-// read at each rank's first segment, the rows each rank receives from the
-// other ranks. A segment's count sums its source rank's route chunks for its
-// expert, one load pass per two chunks of a source rank (per chunk at 11
-// segments per thread). Each large segment is cut
-// into kPlanRows-row items from its first row; items are numbered by start
-// row. PT >= ceil(W*S / kScanThreads) segments per thread.
-template <int PT>
-__global__ __launch_bounds__(kScanThreads) void large_plan_kernel(
-    const int32_t *__restrict__ pc, const int32_t *__restrict__ pci, int W, int epr, int nbs, int h,
-    int elem_bytes, long long large_bytes, int32_t *__restrict__ flags, int2 *__restrict__ plan,
-    int32_t *__restrict__ nplan)
-{
-    static_assert(PT <= 32, "owned segments are tracked in 32-bit masks");
-    __shared__ int32_t tmp[40];
-    __shared__ int32_t rstart[kMaxWorld + 1];     // remote rows received by the ranks before r
-    const int E = W * epr, S = E, G = W * S, tid = threadIdx.x;
-    const int per = (G + kScanThreads - 1) / kScanThreads;
-    const int g0 = min(tid * per, G), g1 = min(g0 + per, G);
-
-    // owned segments (g = r*S + el*W + s, stepped from g0): rank, source rank,
-    // their expert's column in the chunk tables, and which ones open a rank
-    int rk[PT], sk[PT], col[PT];
-    unsigned first = 0;
-    {
-        int r = g0 / S, i = g0 - (g0 / S) * S;
-        int el = i / W, sr = i - (i / W) * W;
-#pragma unroll
-        for (int k = 0; k < PT; ++k) {
-            const bool in = g0 + k < g1;
-            rk[k] = in ? r : 0;
-            sk[k] = in ? sr : 0;
-            col[k] = in ? r * epr + el : 0;          // out of range: expert 0, source 0 (dropped)
-            if (in && el == 0 && sr == 0) first |= 1u << k;
-            if (++sr == W) {
-                sr = 0;
-                if (++el == epr) { el = 0; ++r; }
-            }
-        }
-    }
-    int c[PT];
-#pragma unroll
-    for (int k = 0; k < PT; ++k) c[k] = 0;
-    constexpr int CB = PT <= 8 ? 2 : 1;                // chunks per pass (11 segments: 1, within 128 VGPRs)
-    for (int j0 = 0; j0 < nbs; j0 += CB) {             // clamped loads, the extra dropped
-        int vi[CB][PT], vx[CB][PT];
-#pragma unroll
-        for (int u = 0; u < CB; ++u)
-#pragma unroll
-            for (int k = 0; k < PT; ++k) {
-                const size_t idx = (size_t)(sk[k] * nbs + min(j0 + u, nbs - 1)) * E + col[k];
-                vi[u][k] = pci[idx];
-                vx[u][k] = pc[idx];
-            }
-#pragma unroll
-        for (int u = 0; u < CB; ++u)
-#pragma unroll
-            for (int k = 0; k < PT; ++k) c[k] += g0 + k < g1 && j0 + u < nbs ? vi[u][k] - vx[u][k] : 0;
-    }
-    int csum = 0, rsum = 0;
-#pragma unroll
-    for (int k = 0; k < PT; ++k) {
-        csum += c[k];
-        rsum += sk[k] != rk[k] ? c[k] : 0;
-    }
-    int total_rows, total_remote;
-    const int row0 = block_excl_scan(csum, tmp, &total_rows);      // first row of segment g0
-    int run = block_excl_scan(rsum, tmp, &total_remote);
-#pragma unroll
-    for (int k = 0; k < PT; ++k) {
-        if ((first >> k) & 1u) rstart[rk[k]] = run;
-        run += sk[k] != rk[k] ? c[k] : 0;
-    }
-    if (tid == 0) rstart[W] = total_remote;
-    __syncthreads();
-
-    const long long den = (long long)(W - 1 > 1 ? W - 1 : 1) * epr, row_bytes = (long long)h * elem_bytes;
-    unsigned big = 0;
-    int nmine = 0;
-#pragma unroll
-    for (int k = 0; k < PT; ++k) {
-        if (g0 + k >= g1) continue;
-        const int remote = rstart[rk[k] + 1] - rstart[rk[k]];
-        const bool large = segment_large(sk[k] != rk[k], c[k], remote, row_bytes, large_bytes, den);
-        flags[g0 + k] = large ? 1 : 0;
-        if (large) {
-            big |= 1u << k;
-            nmine += (c[k] + kPlanRows - 1) / kPlanRows;
-        }
-    }
-    int nitems;
-    int idx = block_excl_scan(nmine, tmp, &nitems);
-    int row = row0;
-#pragma unroll
-    for (int k = 0; k < PT; ++k) {
-        if (g0 + k >= g1) continue;
-        if ((big >> k) & 1u)
-            for (int m = 0; m < c[k]; m += kPlanRows)
-                plan[idx++] = make_int2(row + m, row + min(m + kPlanRows, c[k]));
-        row += c[k];
-    }
-    if (tid == 0) *nplan = nitems;
-}
-
 struct DispatchArgs {
     const char *x;
     const int32_t *ids;
@@ -708,7 +599,11 @@ struct DispatchArgs {
     int store_mix;            // wavefront scatters: 0 half the stores plain, 1 a quarter, 2 none
     const uint8_t *mask;      // token mask (one-launch dispatch; the route kernel takes its own)
     int mask_kind;
-    const int32_t *skip;      // adaptive schedule: large-segment flags [W, S]; their rows get no payload here
+    // adaptive schedule: per expand_x row, its token if the row's segment is large (written by the
+    // token-major kernels, which leave that row's payload out) and -1 otherwise; the threshold T, the
+    // bytes of an expand_x row and max(W-1, 1)*epr for the predicate
+    int32_t *lq;
+    long long large, out_row_bytes, den;
 };
 
 // Whether piece j of copy k of a wavefront scatter is stored non-temporally
@@ -745,6 +640,43 @@ __device__ void write_erc_direct(const DispatchArgs &a, size_t gtid, size_t nthr
         }
         a.erc[q] = end - base;
     }
+}
+
+// Rows of segment (expert e, source rank s): its source's route chunks' counts
+// for e. The first four chunks' counts (all of them up to 1024 tokens per
+// rank) are loaded together, so the caller can issue them with its other
+// loads; further chunks take a loop.
+__device__ __forceinline__ int segment_rows(const DispatchArgs &a, int e, int s)
+{
+    const int b0 = s * a.nbs, last = b0 + a.nbs - 1;
+    int vi[4], vx[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        const size_t idx = (size_t)min(b0 + u, last) * a.E + e;
+        vi[u] = a.pci[idx];
+        vx[u] = a.pc[idx];
+    }
+    int c = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) c += u < a.nbs ? vi[u] - vx[u] : 0;
+    for (int b = b0 + 4; b <= last; ++b) c += a.pci[(size_t)b * a.E + e] - a.pc[(size_t)b * a.E + e];
+    return c;
+}
+
+// The large-segment predicate (segment_large) for the segment of expert e
+// from source rank s with c rows, from the route's chunk counts. Only a
+// segment that passes the size test sums the rows its rank receives from the
+// other ranks: over every route chunk of another source, that chunk's pairs to
+// the rank's experts (an inclusive minus an exclusive prefix over experts).
+__device__ bool pair_segment_large(const DispatchArgs &a, int e, int s, int c)
+{
+    const int r = e / a.epr;
+    if (r == s || c <= 0 || (long long)c * a.out_row_bytes < a.large) return false;
+    const int e0 = r * a.epr, e1 = e0 + a.epr - 1;
+    long long remote = 0;
+    for (int b = 0; b < a.NB; ++b)
+        if (b / a.nbs != r) remote += a.pci[(size_t)b * a.E + e1] - a.pc[(size_t)b * a.E + e0];
+    return segment_large(true, c, remote, a.out_row_bytes, a.large, a.den);
 }
 
 // Rows of the K pairs of token t, cooperatively over the calling threads
@@ -790,18 +722,16 @@ __device__ __forceinline__ void pairs_finish(const DispatchArgs &a, int t, const
             row = off[k] + lk[k];
             if ((unsigned)row >= (unsigned)a.R) row = -1;
         }
-        rows[k] = row;
+        bool big = false;
+        if constexpr (SKIP)
+            if (row >= 0) big = pair_segment_large(a, ek[k], s, segment_rows(a, ek[k], s));
+        rows[k] = big ? -1 : row;    // a large segment's row: meta here, payload by its own wavefronts
         if (meta && row >= 0) {
             a.assist[(size_t)row * 3 + 0] = s;
             a.assist[(size_t)row * 3 + 1] = tok;
             a.assist[(size_t)row * 3 + 2] = k;
             if (a.esc_out) a.esc_out[row] = a.esc_in[(size_t)t * a.K + k];
-        }
-        if constexpr (SKIP) {        // a large segment's row: meta here, payload by its own workgroups
-            if (row >= 0) {
-                const int r = ek[k] / a.epr;
-                if (a.skip[(size_t)r * a.S + (size_t)(ek[k] - r * a.epr) * a.W + s]) rows[k] = -1;
-            }
+            if constexpr (SKIP) a.lq[row] = big ? t : -1;
         }
     }
 }
@@ -813,13 +743,12 @@ template <bool SKIP = false>
 __device__ __forceinline__ int lane_pair_row(const DispatchArgs &a, int t, int lane, int e, int l, bool meta)
 {
     const int s = t / a.bs, tok = t - s * a.bs;
-    int row = -1, big = 0;
+    int row = -1;
+    bool big = false;
     if (lane < a.K && (unsigned)e < (unsigned)a.E && l >= 0) {
         const int bt = s * a.nbs + tok / kRouteTokens;
-        if constexpr (SKIP) {
-            const int r = e / a.epr;
-            big = a.skip[(size_t)r * a.S + (size_t)(e - r * a.epr) * a.W + s];
-        }
+        int c = 0;
+        if constexpr (SKIP) c = segment_rows(a, e, s);    // loaded with the offsets below
         int off = 0;
         if (a.direct) {
             // all chunk counts of a pass loaded before any is added: one round trip per pass
@@ -838,14 +767,16 @@ __device__ __forceinline__ int lane_pair_row(const DispatchArgs &a, int t, int l
         }
         row = off + l;
         if ((unsigned)row >= (unsigned)a.R) row = -1;
+        if constexpr (SKIP) big = row >= 0 && pair_segment_large(a, e, s, c);
     }
     if (meta && row >= 0) {
         a.assist[(size_t)row * 3 + 0] = s;
         a.assist[(size_t)row * 3 + 1] = tok;
         a.assist[(size_t)row * 3 + 2] = lane;
         if (a.esc_out) a.esc_out[row] = a.esc_in[(size_t)t * a.K + lane];
+        if constexpr (SKIP) a.lq[row] = big ? t : -1;
     }
-    return SKIP && big ? -1 : row;     // a large segment's row: meta here, payload by its own workgroups
+    return big ? -1 : row;       // a large segment's row: meta here, payload by its own wavefronts
 }
 
 // Token-major copy: block = (token, slice of kCopyThreads * kCopyUnroll chunks).
@@ -1547,6 +1478,138 @@ __global__ __launch_bounds__(kQuantThreads) void segment_quant_wave_kernel(Dispa
     }
 }
 
+// Adaptive schedule, after the token-major scatter: the rows of the large
+// segments. A large segment's rows are consecutive in expand_x, so each
+// wavefront takes windows of kPlanRows consecutive rows and fills every row of
+// its window that the token-major kernels left out (lq >= 0: the row's token),
+// in row order, with their per-wavefront copy or quantiser.
+// Rows at and past the active total (the ranks' ep_recv_count totals) were
+// not written by this call and are not read.
+__device__ __forceinline__ int active_rows(const DispatchArgs &a, int lane)
+{
+    int v = 0;
+    for (int r = lane; r < a.W; r += 64) v += a.erc[(size_t)r * a.S + a.S - 1];
+    return min(wave_sum_i(v), a.R);
+}
+
+// Lane i of window w0 (W rows): lq of row w0 + i, loaded at a clamped index
+// without waiting for the active total; window_token then drops rows at and
+// past it (and anything that is not a token index).
+template <int WR>
+__device__ __forceinline__ int window_load(const DispatchArgs &a, int w0, int lane)
+{
+    return a.lq[min(w0 + (lane < WR ? lane : 0), a.R - 1)];
+}
+
+template <int WR>
+__device__ __forceinline__ int window_token(const DispatchArgs &a, int v, int w0, int A, int lane)
+{
+    return lane < WR && w0 + lane < A && (unsigned)v < (unsigned)(a.W * a.bs) ? v : -1;
+}
+
+template <int J>
+__global__ __launch_bounds__(kQuantThreads) void large_copy_wave_kernel(DispatchArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6), nw = gridDim.x * (kQuantThreads / 64);
+    const int n16 = (int)(a.rowbytes / 16);
+    const int v0 = window_load<kPlanRows>(a, gw * kPlanRows, lane), A = active_rows(a, lane);
+    for (int w0 = gw * kPlanRows; w0 < A; w0 += nw * kPlanRows) {
+        const int my_t = window_token<kPlanRows>(a, w0 == gw * kPlanRows ? v0 : window_load<kPlanRows>(a, w0, lane),
+                                                 w0, A, lane);
+        for (unsigned long long m = __builtin_amdgcn_ballot_w64(my_t >= 0); m; m &= m - 1) {
+            const int i = __builtin_ctzll(m);
+            const int t = __builtin_amdgcn_readlane(my_t, i);
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
+            uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)(w0 + i) * a.rowbytes);
+            uint4 v[J];
+#pragma unroll
+            for (int j = 0; j < J; ++j) v[j] = src[min(lane + 64 * j, n16 - 1)];
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int c = lane + 64 * j;
+                if (c >= n16) continue;
+                if (j & 1) store_stream(dst + c, v[j]);    // the token-major copy's mix
+                else dst[c] = v[j];
+            }
+        }
+    }
+}
+
+template <class T, int J>
+__global__ __launch_bounds__(kQuantThreads) void large_quant_wave_kernel(DispatchArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int gw = blockIdx.x * (kQuantThreads / 64) + (threadIdx.x >> 6), nw = gridDim.x * (kQuantThreads / 64);
+    const int noc = a.h / 16;
+    const int v0 = window_load<kPlanRows>(a, gw * kPlanRows, lane), A = active_rows(a, lane);
+    DispatchArgs one = a;          // one destination row per token visit
+    one.K = 1;
+    for (int w0 = gw * kPlanRows; w0 < A; w0 += nw * kPlanRows) {
+        const int my_t = window_token<kPlanRows>(a, w0 == gw * kPlanRows ? v0 : window_load<kPlanRows>(a, w0, lane),
+                                                 w0, A, lane);
+        for (unsigned long long m = __builtin_amdgcn_ballot_w64(my_t >= 0); m; m &= m - 1) {
+            const int i = __builtin_ctzll(m);
+            const int t = __builtin_amdgcn_readlane(my_t, i);
+            const uint4 *src = reinterpret_cast<const uint4 *>(a.x + (size_t)t * a.rowbytes);
+            uint4 v[J][2];
+#pragma unroll
+            for (int j = 0; j < J; ++j) {
+                const int oc = min(lane + 64 * j, noc - 1);
+                v[j][0] = src[2 * oc];
+                v[j][1] = src[2 * oc + 1];
+            }
+            quant_store_wave<T, J>(one, lane, v, lane == 0 ? w0 + i : -1);
+        }
+    }
+}
+
+// The same for rows off the wavefront path: the block takes windows, and fills
+// each left-out row with the whole block.
+template <int MODE, bool VEC>   // MODE 0: copy, 1: quant fp16, 2: quant bf16
+__global__ __launch_bounds__(kBlockThreads) void large_payload_block_kernel(DispatchArgs a)
+{
+    __shared__ int one[1], win[kPlanRows], act[1];
+    __shared__ float red[kBlockThreads / 64];
+    if (threadIdx.x < 64) {
+        const int A = active_rows(a, threadIdx.x);
+        if (threadIdx.x == 0) act[0] = A;
+    }
+    __syncthreads();
+    const int A = act[0];
+    for (int w0 = blockIdx.x * kPlanRows; w0 < A; w0 += gridDim.x * kPlanRows) {
+        if (threadIdx.x < kPlanRows)
+            win[threadIdx.x] = window_token<kPlanRows>(a, window_load<kPlanRows>(a, w0, threadIdx.x), w0, A, threadIdx.x);
+        __syncthreads();
+        for (int i = 0; i < kPlanRows; ++i) {
+            const int t = win[i];
+            if (t < 0) continue;
+            const int row = w0 + i;
+            if (threadIdx.x == 0) one[0] = row;
+            __syncthreads();
+            if (MODE == 0) {
+                const char *src = a.x + (size_t)t * a.rowbytes;
+                char *dst = a.expand_x + (size_t)row * a.rowbytes;
+                if (VEC) {
+                    for (int c = threadIdx.x; c < (int)(a.rowbytes / 16); c += kBlockThreads)
+                        reinterpret_cast<uint4 *>(dst)[c] = reinterpret_cast<const uint4 *>(src)[c];
+                } else {
+                    for (int c = threadIdx.x; c < (int)(a.rowbytes / 2); c += kBlockThreads)
+                        reinterpret_cast<uint16_t *>(dst)[c] = reinterpret_cast<const uint16_t *>(src)[c];
+                }
+            } else {
+                const uint16_t *src = reinterpret_cast<const uint16_t *>(a.x) + (size_t)t * a.h;
+                int8_t *dst = reinterpret_cast<int8_t *>(a.expand_x);
+                const float scale = MODE == 1 ? quant_row_block<F16, VEC>(src, dst, one, 1, a.h, red)
+                                              : quant_row_block<BF16, VEC>(src, dst, one, 1, a.h, red);
+                if (threadIdx.x == 0) a.dyn[row] = scale;
+            }
+            __syncthreads();
+        }
+        __syncthreads();
+    }
+}
+
 void launch_segment_copy_wave(int J, dim3 g, dim3 b, hipStream_t st, const DispatchArgs &a)
 {
     if (J <= 1) hipLaunchKernelGGL((segment_copy_wave_kernel<1>), g, b, 0, st, a);
@@ -1567,6 +1630,28 @@ void launch_segment_quant_wave(int J, dim3 g, dim3 b, hipStream_t st, const Disp
     else if (J <= 8) hipLaunchKernelGGL((segment_quant_wave_kernel<T, 8>), g, b, 0, st, a);
     else if (J <= 12) hipLaunchKernelGGL((segment_quant_wave_kernel<T, 12>), g, b, 0, st, a);
     else hipLaunchKernelGGL((segment_quant_wave_kernel<T, 16>), g, b, 0, st, a);
+}
+
+void launch_large_copy_wave(int J, dim3 g, dim3 b, hipStream_t st, const DispatchArgs &a)
+{
+    if (J <= 1) hipLaunchKernelGGL((large_copy_wave_kernel<1>), g, b, 0, st, a);
+    else if (J <= 2) hipLaunchKernelGGL((large_copy_wave_kernel<2>), g, b, 0, st, a);
+    else if (J <= 4) hipLaunchKernelGGL((large_copy_wave_kernel<4>), g, b, 0, st, a);
+    else if (J <= 8) hipLaunchKernelGGL((large_copy_wave_kernel<8>), g, b, 0, st, a);
+    else if (J <= 14) hipLaunchKernelGGL((large_copy_wave_kernel<14>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((large_copy_wave_kernel<16>), g, b, 0, st, a);
+}
+
+template <class T>
+void launch_large_quant_wave(int J, dim3 g, dim3 b, hipStream_t st, const DispatchArgs &a)
+{
+    if (J <= 1) hipLaunchKernelGGL((large_quant_wave_kernel<T, 1>), g, b, 0, st, a);
+    else if (J <= 2) hipLaunchKernelGGL((large_quant_wave_kernel<T, 2>), g, b, 0, st, a);
+    else if (J <= 4) hipLaunchKernelGGL((large_quant_wave_kernel<T, 4>), g, b, 0, st, a);
+    else if (J <= 7) hipLaunchKernelGGL((large_quant_wave_kernel<T, 7>), g, b, 0, st, a);
+    else if (J <= 8) hipLaunchKernelGGL((large_quant_wave_kernel<T, 8>), g, b, 0, st, a);
+    else if (J <= 12) hipLaunchKernelGGL((large_quant_wave_kernel<T, 12>), g, b, 0, st, a);
+    else hipLaunchKernelGGL((large_quant_wave_kernel<T, 16>), g, b, 0, st, a);
 }
 
 
@@ -2159,7 +2244,7 @@ int check_special(const moe_special_experts *sp, long long E)
 
 struct DispatchLayout {
     int nbs, NB;
-    size_t pc, pci, boff, lr, plan, nplan, flags, total;
+    size_t pc, pci, boff, lr, plan, nplan, lq, total;
 };
 
 DispatchLayout dispatch_layout(int W, int bs, int epr, int K)
@@ -2176,7 +2261,7 @@ DispatchLayout dispatch_layout(int W, int bs, int epr, int K)
     L.lr = off;    off = round_up(off + N * K * 4, 256);
     L.plan = off;  off = round_up(off + plan_cap * 8, 256);
     L.nplan = off; off = round_up(off + 4, 256);
-    L.flags = off; off = round_up(off + (W * S <= (size_t)kSegLdsMax ? W * S * 4 : 0), 256);
+    L.lq = off;    off = round_up(off + N * K * 4, 256);
     L.total = off;
     return L;
 }
@@ -2321,8 +2406,8 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     // can be large: a segment holds at most bs rows (ids are distinct per
     // token), so bs * h * elem_out < T rules every segment out.
     const bool adaptive = mode == MOE_SCHED_ADAPTIVE && N > 0 && (!quant || quant_mode == MOE_QUANT_DYN_TOKEN) &&
-                          (long long)W * S <= kSegLdsMax && (long long)bs * h * elem_out >= large;
-    const bool want_seg = mode == MOE_SCHED_SEGMENT || (seg_flags && !adaptive);
+                          (long long)bs * h * elem_out >= large;
+    const bool want_seg = mode == MOE_SCHED_SEGMENT || seg_flags;
     if (want_seg && (long long)W * S > kSegLdsMax) return MOE_ERR_SCHEDULE;
     if ((group_quant || static_quant) && mode == MOE_SCHED_SEGMENT) return MOE_ERR_SCHEDULE;
 
@@ -2351,7 +2436,6 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     // blocks sum the chunk prefixes themselves unless there are many chunks (or a
     // plan is needed); otherwise one scan block forms every offset first
     const bool direct = N > 0 && mode != MOE_SCHED_SEGMENT && L.NB <= kDirectMaxChunks;
-    int32_t *flags = seg_flags ? seg_flags : reinterpret_cast<int32_t *>(ws + L.flags);
 
     DispatchArgs a;
     a.x = static_cast<const char *>(x);
@@ -2368,7 +2452,10 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     a.boff = boff;
     a.plan = plan;
     a.nplan = nplan;
-    a.skip = adaptive ? flags : nullptr;
+    a.lq = adaptive ? reinterpret_cast<int32_t *>(ws + L.lq) : nullptr;
+    a.large = large;
+    a.out_row_bytes = (long long)h * elem_out;
+    a.den = (long long)(W - 1 > 1 ? W - 1 : 1) * epr;
     a.W = W; a.bs = bs; a.epr = epr; a.h = h; a.K = K; a.nbs = L.nbs; a.R = (int)(N * K);
     a.E = E; a.S = (int)S; a.NB = L.NB;
     // with a scan block present it also wrote ep_recv_count
@@ -2425,17 +2512,6 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(kScanThreads), want_seg ? (size_t)W * S * 5 : 0, st, pc, pci,
                            W, epr, L.nbs, h, elem_out, boff, ep_recv_count, want_seg ? 1 : 0, large, seg_flags,
                            (mode == MOE_SCHED_SEGMENT && N > 0) ? plan : nullptr, nplan);
-    if (adaptive) {
-        const long long per = ((long long)W * S + kScanThreads - 1) / kScanThreads;    // <= 11
-#define MOE_LARGE_PLAN(P) hipLaunchKernelGGL(large_plan_kernel<P>, dim3(1), dim3(kScanThreads), 0, st, pc, pci, W, \
-                                             epr, L.nbs, h, elem_out, large, flags, plan, nplan)
-        if (per <= 1) MOE_LARGE_PLAN(1);
-        else if (per <= 2) MOE_LARGE_PLAN(2);
-        else if (per <= 4) MOE_LARGE_PLAN(4);
-        else if (per <= 8) MOE_LARGE_PLAN(8);
-        else MOE_LARGE_PLAN(11);
-#undef MOE_LARGE_PLAN
-    }
     // the payload pass over a plan's items (segment-major, or the adaptive schedule's large segments)
     auto segment_payload = [&](unsigned blocks) {
         const int qm = !quant ? 0 : (dtype == MOE_FP16 ? 1 : 2);
@@ -2457,6 +2533,31 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
         } else {
             if (vec) hipLaunchKernelGGL((segment_payload_kernel<2, true>), g, b, 0, st, a);
             else hipLaunchKernelGGL((segment_payload_kernel<2, false>), g, b, 0, st, a);
+        }
+    };
+    // the adaptive schedule's pass over the rows the token-major kernels left out
+    auto large_payload = [&]() {
+        const int qm = !quant ? 0 : (dtype == MOE_FP16 ? 1 : 2);
+        const bool vec = quant ? (h % 8 == 0 && aligned(x, 16) && aligned(expand_x, 8))
+                               : (rowbytes % 16 == 0 && aligned(x, 16) && aligned(expand_x, 16));
+        const int Jc = (int)((rowbytes / 16 + 63) / 64), Jq = (h / 16 + 63) / 64;
+        const long long windows = (N * K + kPlanRows - 1) / kPlanRows;
+        const dim3 gw((unsigned)std::min<long long>(kAdaptiveSegGrid, (windows + 3) / 4)), bw(kQuantThreads);
+        const dim3 g((unsigned)std::min<long long>(kAdaptiveSegGrid, windows)), b(kBlockThreads);
+        if (qm == 0 && vec && Jc <= 16) {
+            launch_large_copy_wave(Jc, gw, bw, st, a);
+        } else if (qm != 0 && wave) {
+            if (qm == 1) launch_large_quant_wave<F16>(Jq, gw, bw, st, a);
+            else launch_large_quant_wave<BF16>(Jq, gw, bw, st, a);
+        } else if (qm == 0) {
+            if (vec) hipLaunchKernelGGL((large_payload_block_kernel<0, true>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((large_payload_block_kernel<0, false>), g, b, 0, st, a);
+        } else if (qm == 1) {
+            if (vec) hipLaunchKernelGGL((large_payload_block_kernel<1, true>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((large_payload_block_kernel<1, false>), g, b, 0, st, a);
+        } else {
+            if (vec) hipLaunchKernelGGL((large_payload_block_kernel<2, true>), g, b, 0, st, a);
+            else hipLaunchKernelGGL((large_payload_block_kernel<2, false>), g, b, 0, st, a);
         }
     };
     if (N > 0) {
@@ -2544,8 +2645,8 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
 #undef MOE_QUANT_BLOCK
                 }
             }
-            // adaptive schedule: the large segments' rows, whole workgroups per item
-            if (adaptive) segment_payload(kAdaptiveSegGrid);
+            // adaptive schedule: the large segments' rows, by wavefronts of their own
+            if (adaptive) large_payload();
         } else {
             const long long npairs = N * K;
             hipLaunchKernelGGL(segment_meta_kernel, dim3((unsigned)((npairs + kBlockThreads - 1) / kBlockThreads)),

@@ -149,16 +149,17 @@ typedef struct moe_special_experts {
  *                     7168, int8: 132 us per dispatch against 50 us).
  *  MOE_SCHED_ADAPTIVE (the default when schedule is NULL): the token
  *                     schedule for every segment the predicate does not
- *                     select; the rows of each selected segment are written
- *                     by whole workgroups of their own, split by rows (each
- *                     such row reads its token once more). A segment holds at
- *                     most bs rows (ids are distinct per token), so when
- *                     bs*h*elem_bytes < T no segment can be selected and this
- *                     mode runs exactly the token schedule; with the README's
- *                     2 MiB that holds at 16 ranks x 256 tokens of 7168 int8.
- *                     It covers copies and per-token int8 (quant_mode 0 and
- *                     2) with W*S <= 11264; other quant modes and larger
- *                     segment tables take the token schedule. */
+ *                     select; the token-major pass leaves out the rows of
+ *                     the selected segments, and a second pass writes them
+ *                     in windows of 8 consecutive expand_x rows, each window
+ *                     by a wavefront of its own (each such row reads its
+ *                     token once more). A segment holds at most bs rows (ids
+ *                     are distinct per token), so when bs*h*elem_bytes < T no
+ *                     segment can be selected and this mode runs exactly the
+ *                     token schedule; with the README's 2 MiB that holds at
+ *                     16 ranks x 256 tokens of 7168 int8. It covers copies
+ *                     and per-token int8 (quant_mode 0 and 2); the other
+ *                     quant modes take the token schedule. */
 enum moe_sched_mode { MOE_SCHED_TOKEN = 0, MOE_SCHED_SEGMENT = 1, MOE_SCHED_ADAPTIVE = 2 };
 
 /* Optional dispatch schedule (host struct; pass NULL for the defaults:
