@@ -599,10 +599,10 @@ struct DispatchArgs {
     int store_mix;            // wavefront scatters: 0 half the stores plain, 1 a quarter, 2 none
     const uint8_t *mask;      // token mask (one-launch dispatch; the route kernel takes its own)
     int mask_kind;
-    // adaptive schedule: per expand_x row, its token if the row's segment is large (written by the
-    // token-major kernels, which leave that row's payload out) and -1 otherwise; the threshold T, the
-    // bytes of an expand_x row and max(W-1, 1)*epr for the predicate
-    int32_t *lq;
+    // adaptive schedule: per expand_x row, 1 if the row's segment is large (written by the token-major
+    // kernels, which leave that row's payload out) and 0 otherwise; the threshold T, the bytes of an
+    // expand_x row and max(W-1, 1)*epr for the predicate
+    uint8_t *lflag;
     long long large, out_row_bytes, den;
 };
 
@@ -731,7 +731,7 @@ __device__ __forceinline__ void pairs_finish(const DispatchArgs &a, int t, const
             a.assist[(size_t)row * 3 + 1] = tok;
             a.assist[(size_t)row * 3 + 2] = k;
             if (a.esc_out) a.esc_out[row] = a.esc_in[(size_t)t * a.K + k];
-            if constexpr (SKIP) a.lq[row] = big ? t : -1;
+            if constexpr (SKIP) a.lflag[row] = big ? 1 : 0;
         }
     }
 }
@@ -774,7 +774,7 @@ __device__ __forceinline__ int lane_pair_row(const DispatchArgs &a, int t, int l
         a.assist[(size_t)row * 3 + 1] = tok;
         a.assist[(size_t)row * 3 + 2] = lane;
         if (a.esc_out) a.esc_out[row] = a.esc_in[(size_t)t * a.K + lane];
-        if constexpr (SKIP) a.lq[row] = big ? t : -1;
+        if constexpr (SKIP) a.lflag[row] = big ? 1 : 0;
     }
     return big ? -1 : row;       // a large segment's row: meta here, payload by its own wavefronts
 }
@@ -1481,8 +1481,9 @@ __global__ __launch_bounds__(kQuantThreads) void segment_quant_wave_kernel(Dispa
 // Adaptive schedule, after the token-major scatter: the rows of the large
 // segments. A large segment's rows are consecutive in expand_x, so each
 // wavefront takes windows of kPlanRows consecutive rows and fills every row of
-// its window that the token-major kernels left out (lq >= 0: the row's token),
-// in row order, with their per-wavefront copy or quantiser.
+// its window that the token-major kernels left out (flagged), in row order,
+// from the token its assist_info names, with their per-wavefront copy or
+// quantiser.
 // Rows at and past the active total (the ranks' ep_recv_count totals) were
 // not written by this call and are not read.
 __device__ __forceinline__ int active_rows(const DispatchArgs &a, int lane)
@@ -1492,19 +1493,25 @@ __device__ __forceinline__ int active_rows(const DispatchArgs &a, int lane)
     return min(wave_sum_i(v), a.R);
 }
 
-// Lane i of window w0 (W rows): lq of row w0 + i, loaded at a clamped index
-// without waiting for the active total; window_token then drops rows at and
-// past it (and anything that is not a token index).
+// Lane i of window w0 (WR rows): the flag of row w0 + i, loaded at a clamped
+// index without waiting for the active total; window_token then drops rows at
+// and past it, and reads the token of each flagged row from assist_info.
 template <int WR>
 __device__ __forceinline__ int window_load(const DispatchArgs &a, int w0, int lane)
 {
-    return a.lq[min(w0 + (lane < WR ? lane : 0), a.R - 1)];
+    return a.lflag[min(w0 + (lane < WR ? lane : 0), a.R - 1)];
 }
 
 template <int WR>
 __device__ __forceinline__ int window_token(const DispatchArgs &a, int v, int w0, int A, int lane)
 {
-    return lane < WR && w0 + lane < A && (unsigned)v < (unsigned)(a.W * a.bs) ? v : -1;
+    int t = -1;
+    if (lane < WR && w0 + lane < A && v != 0) {
+        const size_t row = (size_t)(w0 + lane);
+        const int s = a.assist[row * 3 + 0], tok = a.assist[row * 3 + 1];
+        if ((unsigned)s < (unsigned)a.W && (unsigned)tok < (unsigned)a.bs) t = s * a.bs + tok;
+    }
+    return t;
 }
 
 template <int J>
@@ -2244,7 +2251,7 @@ int check_special(const moe_special_experts *sp, long long E)
 
 struct DispatchLayout {
     int nbs, NB;
-    size_t pc, pci, boff, lr, plan, nplan, lq, total;
+    size_t pc, pci, boff, lr, plan, nplan, total;
 };
 
 DispatchLayout dispatch_layout(int W, int bs, int epr, int K)
@@ -2253,7 +2260,9 @@ DispatchLayout dispatch_layout(int W, int bs, int epr, int K)
     const size_t E = (size_t)W * epr, N = (size_t)W * bs, S = (size_t)epr * W;
     L.nbs = (bs + kRouteTokens - 1) / kRouteTokens;
     L.NB = W * L.nbs;
+    // plan items of the segment schedule; the adaptive schedule keeps its per-row flags (N * K bytes) there
     const size_t plan_cap = N * K / kPlanRows + 2 * (size_t)W * S + W + 1;
+    static_assert(kPlanRows == 8, "the plan region holds one byte per row");
     size_t off = 0;
     L.pc = off;    off = round_up(off + (size_t)L.NB * E * 4, 256);
     L.pci = off;   off = round_up(off + (size_t)L.NB * E * 4, 256);
@@ -2261,7 +2270,6 @@ DispatchLayout dispatch_layout(int W, int bs, int epr, int K)
     L.lr = off;    off = round_up(off + N * K * 4, 256);
     L.plan = off;  off = round_up(off + plan_cap * 8, 256);
     L.nplan = off; off = round_up(off + 4, 256);
-    L.lq = off;    off = round_up(off + N * K * 4, 256);
     L.total = off;
     return L;
 }
@@ -2452,7 +2460,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     a.boff = boff;
     a.plan = plan;
     a.nplan = nplan;
-    a.lq = adaptive ? reinterpret_cast<int32_t *>(ws + L.lq) : nullptr;
+    a.lflag = adaptive ? reinterpret_cast<uint8_t *>(ws + L.plan) : nullptr;   // the segment plan's region
     a.large = large;
     a.out_row_bytes = (long long)h * elem_out;
     a.den = (long long)(W - 1 > 1 ? W - 1 : 1) * epr;
