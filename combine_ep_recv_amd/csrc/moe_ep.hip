@@ -66,6 +66,7 @@ constexpr long long kMaxTokens = (1ll << 24) - 1;   // N blocks of 256 threads s
 constexpr int kPlanRows = 8;               // rows per segment-schedule work item
 static_assert(kPlanRows <= 64, "a plan item's rows are held one per lane");
 constexpr int kSegGrid = 4096;             // blocks of the segment-major payload pass
+constexpr size_t kDeviceStoreBytes = 64ull << 20;   // gather: the tail of x_out stored device-scope
 constexpr int kAdaptiveSegGrid = 1024;     // most blocks of the adaptive schedule's large-segment pass
 constexpr int64_t kReadmeLargeBytes = 2 * 1024 * 1024;
 
@@ -136,7 +137,11 @@ __device__ __forceinline__ void store_stream(uint4 *p, uint4 v)
 // that writeback is pure wait at the end of the kernel: at 16 ranks x 256
 // tokens, h = 7168 (58.7 MB of x_out) the cold dispatch + combine step takes
 // ~142.4 us with it against ~146 us with non-temporal stores, back to back
-// unchanged. The dispatch's scatter is not helped: sc1 on its non-temporal
+// unchanged. The lines stay in the Infinity Cache, though, and a larger
+// output written this way evicts what the next launch would find there (at
+// 512 tokens per rank: back to back 335 against 289 us, and 302 against 298
+// us timed), so only the last 64 MiB of x_out (all of it up to that size) is
+// stored device-scope, the rest non-temporally: 298 and 309 us there. The dispatch's scatter is not helped: sc1 on its non-temporal
 // half takes the back-to-back step from 141 to 165 us, on its plain half it
 // changes nothing. There is no clang builtin for the scope bits, hence the
 // asm; the s_nop covers the wait states a VALU write to the store's data
@@ -1880,6 +1885,7 @@ struct CombineArgs {
     int E, zero_end, copy_end, const_end;
     int W, bs, h, K, R, S, nsl, epr;
     long long rowbytes;
+    int dev_from;             // gather: tokens from here on store x_out device-scope (see store_device)
 };
 
 // Return path (README 实现逻辑): row i of expand_x belongs to slot
@@ -1986,8 +1992,9 @@ __global__ __launch_bounds__(kGatherThreads) void combine_gather_half_kernel(Com
         uint32_t o[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) o[i] = (uint32_t)T::store(acc[2 * i]) | ((uint32_t)T::store(acc[2 * i + 1]) << 16);
-        store_device(reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes) + c,
-                     make_uint4(o[0], o[1], o[2], o[3]));
+        uint4 *dst = reinterpret_cast<uint4 *>(a.x_out + (size_t)t * a.rowbytes) + c;
+        if (t >= a.dev_from) store_device(dst, make_uint4(o[0], o[1], o[2], o[3]));
+        else store_stream(dst, make_uint4(o[0], o[1], o[2], o[3]));
     } else {
         const int j = sl * kGatherThreads + threadIdx.x;
         if (j >= a.h) return;
@@ -2751,6 +2758,8 @@ int moe_combine(const void *expand_x, const int32_t *assist_info, const int32_t 
     a.W = W; a.bs = bs; a.h = h; a.K = K; a.R = (int)(N * K); a.S = experts_per_rank * W;
     a.epr = experts_per_rank;
     a.rowbytes = (long long)((size_t)h * xs);
+    // the last kDeviceStoreBytes of x_out (all of it up to that size) go device-scope
+    a.dev_from = (int)std::max<long long>(0, N - (long long)(kDeviceStoreBytes / std::max<size_t>(1, (size_t)h * xs)));
     const bool vec = (size_t)a.rowbytes % 16 == 0 && aligned(expand_x, 16) && aligned(x_out, 16) &&
                      aligned(ori_x, 16) && aligned(const_x, 16);
     const long long n = vec ? a.rowbytes / 16 : h;
