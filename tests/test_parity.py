@@ -519,6 +519,55 @@ def test_schedules_are_result_neutral_and_flag_the_right_segments(w, mode, T):
         assert want.sum() == 0     # the README's 2 MiB never fires on the page workloads
 
 
+ADAPTIVE_FLAG_CASES = [SCHED_CASES[i] for i in (2, 3, 4, 5, 6, 9, 12, 13)]
+
+
+def adaptive_row_flags(w, workspace):
+    """The adaptive schedule's per-row flags, read from the dispatch workspace (white box): one byte per row in
+    the segment plan's region, which follows pc, pci and boff ([NB, E] int32 each) and lr ([N*K] int32), each
+    region 256-byte aligned."""
+    nb = w.ep_world * ((w.bs + 255) // 256)
+    r256 = lambda n: (n + 255) // 256 * 256
+    off = 3 * r256(nb * w.num_experts * 4) + r256(w.rows * 4)
+    return to_np(workspace[off:off + w.rows])
+
+
+@pytest.mark.parametrize("w", ADAPTIVE_FLAG_CASES, ids=lambda w: w.name)
+@pytest.mark.parametrize("T", [0, 64 * 1024, -1], ids=["T0", "T64KiB", "T2MiB"])
+def test_adaptive_schedule_leaves_out_exactly_the_rows_of_large_segments(w, T):
+    """The token-major kernels evaluate the predicate per pair and flag the rows they leave to the second pass;
+    the flagged rows are exactly the rows of the segments the oracle's predicate selects (outputs alone cannot
+    show this: either pass writes the same bytes)."""
+    elem = 1 if w.quant_mode != 0 else (4 if w.dtype == "int32" else 2)
+    thr = TWO_MIB if T < 0 else T
+    if w.bs * w.h * elem < thr:
+        pytest.skip("no segment can reach the threshold: the adaptive pass is not engaged")
+    inp = wl.make_inputs(w)
+    bf = w.dtype == "bf16"
+    x, ids, sc = to_dev(inp["x"], bf), to_dev(inp["ids"]), to_dev(inp["scales"])
+    tdt = {"int32": torch.int32, "fp16": torch.float16, "bf16": torch.bfloat16}[w.dtype]
+    print("adaptive flags case %s T=%d" % (w.name, thr), flush=True)
+    buf = moe.DispatchBuffers(w.ep_world, w.bs, w.experts_per_rank, w.h, w.topk, tdt, w.quant_mode, DEV)
+    moe.dispatch_into(buf, x, ids, expert_scales=sc,
+                      schedule=moe.MoeSchedule(mode=moe.MOE_SCHED_ADAPTIVE, large_segment_bytes=T))
+    torch.cuda.synchronize()
+    o = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, w.quant_mode, bf16=bf)
+    erc = o["ep_recv_count"]
+    large = oracle.large_segments(erc, w.ep_world, w.experts_per_rank, w.h, elem, thr)
+    want = np.zeros(w.rows, np.uint8)
+    base = 0
+    for r in range(w.ep_world):
+        for g in range(erc.shape[1]):
+            lo = base + (erc[r, g - 1] if g else 0)
+            if large[r, g]:
+                want[lo:base + erc[r, g]] = 1
+        base += erc[r, -1]
+    got = adaptive_row_flags(w, buf.workspace)
+    assert (got[:base] == want[:base]).all(), (int(got[:base].sum()), int(want[:base].sum()))
+    if T == 0:
+        assert want.sum() > 0      # the case exercises the second pass
+
+
 def test_default_schedule_splits_off_the_segments_the_literal_rule_selects():
     """With no schedule the dispatch is adaptive at the README's 2 MiB: on this shape (192 tokens per rank of 7168
     fp16, Zipf routing) a segment can reach 2 MiB, so the large-segment pass runs, and some segments are large."""
