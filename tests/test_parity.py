@@ -935,22 +935,32 @@ def test_repeat_runs_are_bitwise_identical():
 # the eager result (checked after eager work between replays)
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("w", [wl.WORKLOADS[2], wl.custom(4, 64, 1024, 8, 4, "bf16", "gauss_topk", quant_mode=2,
-                                                             name="bf16_q8_graph")], ids=lambda w: w.name)
-def test_graph_replay_matches_eager(w):
+GRAPH_CASES = [
+    (wl.WORKLOADS[2], None),
+    (wl.custom(4, 64, 1024, 8, 4, "bf16", "gauss_topk", quant_mode=2, name="bf16_q8_graph"), None),
+    # the adaptive schedule's second pass and the segment-major schedule's scan and plan, both engaged at T = 0
+    (wl.custom(4, 64, 1024, 8, 4, "bf16", "zipf_topk", quant_mode=2, name="bf16_q8_graph_adaptive_T0"),
+     (moe.MOE_SCHED_ADAPTIVE, 0)),
+    (wl.custom(4, 64, 1024, 8, 4, "fp16", "zipf_topk", name="fp16_copy_graph_segment_T0"), (moe.MOE_SCHED_SEGMENT, 0)),
+]
+
+
+@pytest.mark.parametrize("w,sched", GRAPH_CASES, ids=lambda v: v.name if hasattr(v, "name") else str(v))
+def test_graph_replay_matches_eager(w, sched):
     print("parity case %s graph replay" % w.name, flush=True)
+    schedule = None if sched is None else moe.MoeSchedule(mode=sched[0], large_segment_bytes=sched[1])
     inp = wl.make_inputs(w)
     bf = w.dtype == "bf16"
     x, ids, sc = to_dev(inp["x"], bf), to_dev(inp["ids"]), to_dev(inp["scales"])
     tdt = torch.bfloat16 if bf else torch.float16
     buf = moe.DispatchBuffers(w.ep_world, w.bs, w.experts_per_rank, w.h, w.topk, tdt, w.quant_mode, DEV)
-    moe.dispatch_into(buf, x, ids)
-    y = gpu_identity_expert(buf.expand_x, buf.dynamic_scales)
+    moe.dispatch_into(buf, x, ids, schedule=schedule)
+    y = gpu_identity_expert(buf.expand_x, buf.dynamic_scales)   # for copies: expand_x itself, rewritten each step
     out = torch.empty((w.num_tokens, w.h), dtype=y.dtype, device=DEV)
     cws = moe.combine_workspace(w.ep_world, w.bs, w.experts_per_rank, w.h, w.topk, y.dtype, DEV)
 
     def step():
-        moe.dispatch_into(buf, x, ids)
+        moe.dispatch_into(buf, x, ids, schedule=schedule)
         moe.combine_into(out, y, buf.assist_info, buf.ep_recv_count, ids, sc, w.ep_world, w.experts_per_rank, cws)
 
     def snapshot():
