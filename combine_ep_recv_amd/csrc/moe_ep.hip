@@ -716,6 +716,8 @@ __device__ __forceinline__ void pairs_sum(const DispatchArgs &a, int t, const in
 }
 
 // Final rows (-1 for an invalid pair); optionally writes assist_info / expand_scales.
+// SKIP (adaptive schedule): a pair in a large segment also gets -1, after its
+// meta, and its row's flag; the large-segment pass writes its payload.
 template <bool SKIP = false>
 __device__ __forceinline__ void pairs_finish(const DispatchArgs &a, int t, const int *ek, const int *lk,
                                              const int *off, int *rows, bool meta, int lt, int nthr)
@@ -744,6 +746,7 @@ __device__ __forceinline__ void pairs_finish(const DispatchArgs &a, int t, const
 // Row of pair (t, lane) for lanes < K (-1 for other lanes and invalid pairs), from
 // registers only: the chunk prefixes are summed by the lane itself (direct path)
 // or read from the scan's table. Writes assist_info / expand_scales when asked.
+// SKIP (adaptive schedule): as pairs_finish.
 template <bool SKIP = false>
 __device__ __forceinline__ int lane_pair_row(const DispatchArgs &a, int t, int lane, int e, int l, bool meta)
 {
