@@ -60,6 +60,8 @@ def bind(lib):
     lib.oracle_identity_expert_dequant.restype = None
     lib.oracle_identity_expert_dequant_fp8.argtypes = [P, P, LL, I, P]
     lib.oracle_identity_expert_dequant_fp8.restype = None
+    lib.oracle_identity_expert_dequant_mx.argtypes = [P, P, LL, I, P]
+    lib.oracle_identity_expert_dequant_mx.restype = None
     lib.oracle_e4m3_to_f32.argtypes = [ctypes.c_uint8]
     lib.oracle_e4m3_to_f32.restype = ctypes.c_float
     lib.oracle_f32_to_e4m3.argtypes = [ctypes.c_float]
@@ -135,6 +137,9 @@ def dispatch(x, ids, ep_world, experts_per_rank, quant_mode=0, expert_scales=Non
     elif quant_mode == 3:                     # E4M3 codes, ceil(h/128) group scales per row
         expand_x = np.zeros((rows, h), np.uint8)
         dyn = np.zeros((rows, (h + 127) // 128), np.float32)
+    elif quant_mode == 4:                     # MXFP8: E4M3 codes, ceil(h/32) E8M0 scale bytes per row
+        expand_x = np.zeros((rows, h), np.uint8)
+        dyn = np.zeros((rows, (h + 31) // 32), np.uint8)
     else:
         expand_x = np.zeros((rows, h), x.dtype)
         dyn = None
@@ -225,10 +230,18 @@ def f32_to_bf16(v: float) -> int:
 def identity_expert(expand_x, dynamic_scales=None):
     """The harness's identity expert (not part of the method): returns expand_x
     unchanged, or the dequantised rows bf16(f32(q) * scale) as uint16 bits (one
-    fp32 product, one rounding): int8 rows with one scale per row, or E4M3 rows
-    (uint8) with one scale per 128-element group."""
+    fp32 product, one rounding): int8 rows with one scale per row, E4M3 rows
+    (uint8) with one fp32 scale per 128-element group, or E4M3 rows with one
+    E8M0 byte (uint8, the scale 2^(byte - 127)) per 32-element block."""
     if dynamic_scales is None:
         return expand_x
+    if np.asarray(dynamic_scales).dtype == np.uint8:
+        q = np.ascontiguousarray(expand_x, dtype=np.uint8)
+        sc = np.ascontiguousarray(dynamic_scales)
+        assert sc.shape == (q.shape[0], (q.shape[1] + 31) // 32)
+        y = np.zeros(q.shape, np.uint16)
+        _load().oracle_identity_expert_dequant_mx(_ptr(q), _ptr(sc), q.shape[0], q.shape[1], _ptr(y))
+        return y
     if np.asarray(dynamic_scales).ndim == 2:
         q = np.ascontiguousarray(expand_x, dtype=np.uint8)
         sc = np.ascontiguousarray(dynamic_scales, dtype=np.float32)

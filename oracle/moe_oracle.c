@@ -55,6 +55,20 @@
  *    x / scale, ties to even, after clamping the quotient to [-448, 448]; the
  *    code keeps the sign of x (so -0 gives 0x80); an all-zero group gets
  *    scale 0 and codes 0x00; G = ceil(h / 128) scales per expand_x row;
+ *  - quantMode 4 ("mx" dynamic quantisation; [P3] lists it with four output
+ *    types, a garbled scale shape and no scale input; the two types that need
+ *    an even H are the 4-bit ones): the OCP Microscaling (MX) format v1.0
+ *    with E4M3 elements (MXFP8), the 8-bit member that quantMode 3 already
+ *    fixes the element encoding for. Blocks of 32 consecutive elements of a
+ *    token (the last one shorter when 32 does not divide h); per block the
+ *    shared exponent is floor(log2(max|x|)) - 8 (8 = the exponent of E4M3's
+ *    largest normal, 448 = 1.75 * 2^8), clamped to E8M0's range [-127, 127]
+ *    (-127 for an all-zero block); the scale byte is that exponent + 127
+ *    (E8M0: the value 2^(byte - 127)); code = the E4M3 value nearest to
+ *    x * 2^-shared (exact in binary64), ties to even, after clamping to
+ *    [-448, 448], with the sign of x (-0 gives 0x80 in every block);
+ *    B = ceil(h / 32) scale bytes per expand_x row. Inputs are finite; the
+ *    other three element types are not built;
  *  - combine accumulates in fp32 with one fused multiply-add per k, k
  *    ascending from 0.0f, and rounds once (to nearest even) to the output
  *    type; int32 data combine in wrapping 32-bit integer arithmetic.
@@ -65,6 +79,7 @@
 #include <string.h>
 
 enum { OR_INT32 = 0, OR_FP16 = 1, OR_BF16 = 2 };
+enum { MX_BLOCK = 32 };                    /* elements per quantMode 4 scale block */
 enum { OR_OK = 0, OR_BAD_ARG = -1, OR_BAD_ID = -2, OR_DUP_ID = -3, OR_BAD_ASSIST = -4 };
 
 /* ------------------------------------------------------------------------ */
@@ -225,9 +240,10 @@ static int pair_active(const uint8_t *mask, int mask_kind, long long t, int k, i
  * x            [W*bs, h] dtype           tokens, source rank s owns rows s*bs..s*bs+bs-1
  * ids          [W*bs, K] int32           global expert ids, distinct per token
  * qscale       fp32 [qscale_n]           quant == 1 only: qscale_n is 1, h or E*h
- * expand_x     [W*bs*K, h]               dtype; int8 when quant is 1 or 2; E4M3 bytes when 3
+ * expand_x     [W*bs*K, h]               dtype; int8 when quant is 1 or 2; E4M3 bytes when 3 or 4
  * dyn_scales   [W*bs*K] fp32             quant == 2: one scale per row;
  *              [W*bs*K, G] fp32          quant == 3: G = ceil(h / 128) group scales per row
+ *              [W*bs*K, B] uint8         quant == 4: B = ceil(h / 32) E8M0 block scales per row
  * assist       [W*bs*K, 3] int32         (src_rank, src_token, topk_id) per row
  * ep_recv_count[W, epr*W] int32          inclusive per-rank segment counts
  * expand_scales[W*bs*K] fp32|int32|NULL  expert_scales[t,k] moved to row(t,k)
@@ -239,15 +255,16 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
                     int W, int bs, int epr, int h, int K, int dtype, int quant,
                     const float *qscale, long long qscale_n, const uint8_t *mask, int mask_kind, int zero_num,
                     int copy_num, int const_num,
-                    void *expand_x, float *dyn_scales, int32_t *assist,
+                    void *expand_x, void *dyn_scales, int32_t *assist,
                     int32_t *ep_recv_count, void *expand_scales)
 {
     if (W < 1 || bs < 0 || epr < 1 || h < 1 || K < 1) return OR_BAD_ARG;
     if (mask_kind < 0 || mask_kind > 2 || (mask_kind != 0) != (mask != NULL)) return OR_BAD_ARG;
     if (zero_num < 0 || copy_num < 0 || const_num < 0) return OR_BAD_ARG;
-    if (quant < 0 || quant > 3) return OR_BAD_ARG;
+    if (quant < 0 || quant > 4) return OR_BAD_ARG;
     if (quant != 0 && dtype == OR_INT32) return OR_BAD_ARG;
     const int G = (h + 127) / 128;                     /* quantMode 3 groups per row */
+    const int B = (h + MX_BLOCK - 1) / MX_BLOCK;       /* quantMode 4 blocks per row */
     const long long E = (long long)W * epr, N = (long long)W * bs, S = (long long)epr * W;
     if (K > E) return OR_BAD_ARG;
     if (quant == 1 && (!qscale || (qscale_n != 1 && qscale_n != h && qscale_n != E * h))) return OR_BAD_ARG;
@@ -346,7 +363,33 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
                         if (n < -448.0f) n = -448.0f;
                         q[j] = oracle_f32_to_e4m3(n);
                     }
-                    dyn_scales[row * G + g] = gs;
+                    ((float *)dyn_scales)[row * G + g] = gs;
+                }
+            } else if (quant == 4) {
+                uint8_t *q = (uint8_t *)expand_x + (size_t)row * h;
+                uint8_t *sb = (uint8_t *)dyn_scales + (size_t)row * B;
+                for (int b = 0; b < B; ++b) {
+                    int j0 = b * MX_BLOCK, j1 = j0 + MX_BLOCK < h ? j0 + MX_BLOCK : h;
+                    double amax = 0.0;
+                    for (int j = j0; j < j1; ++j) {
+                        double v = fabs((double)load_f32(x, (size_t)(t * h + j), dtype));
+                        if (v > amax) amax = v;
+                    }
+                    int shared = -127;                 /* all-zero block */
+                    if (amax > 0.0) {
+                        int e2;
+                        frexp(amax, &e2);              /* amax in [2^(e2-1), 2^e2) */
+                        shared = (e2 - 1) - 8;
+                        if (shared < -127) shared = -127;
+                        if (shared > 127) shared = 127;
+                    }
+                    sb[b] = (uint8_t)(shared + 127);
+                    for (int j = j0; j < j1; ++j) {
+                        double n = ldexp((double)load_f32(x, (size_t)(t * h + j), dtype), -shared);
+                        if (n > 448.0) n = 448.0;
+                        if (n < -448.0) n = -448.0;
+                        q[j] = oracle_f32_to_e4m3((float)n);
+                    }
                 }
             } else {
                 int8_t *q = (int8_t *)expand_x + (size_t)row * h;
@@ -357,7 +400,7 @@ int oracle_dispatch(const void *x, const int32_t *ids, const void *expert_scales
                     if (n < -127.0f) n = -127.0f;
                     q[j] = (int8_t)n;
                 }
-                dyn_scales[row] = scale;
+                ((float *)dyn_scales)[row] = scale;
             }
         }
     }
@@ -527,6 +570,19 @@ void oracle_identity_expert_dequant_fp8(const uint8_t *q, const float *scale, lo
     for (long long i = 0; i < rows; ++i)
         for (int j = 0; j < h; ++j)
             y[i * h + j] = oracle_f32_to_bf16(oracle_e4m3_to_f32(q[i * h + j]) * scale[i * G + j / 128]);
+}
+
+/* The same for MX rows: bf16(f32(e4m3) * 2^(byte - 127)), one E8M0 byte per
+ * block of 32 (the product is exact in binary32 for the bytes a finite 16-bit
+ * token can produce, so the bf16 conversion is the one rounding). */
+void oracle_identity_expert_dequant_mx(const uint8_t *q, const uint8_t *scale, long long rows, int h,
+                                       uint16_t *y)
+{
+    const int B = (h + MX_BLOCK - 1) / MX_BLOCK;
+    for (long long i = 0; i < rows; ++i)
+        for (int j = 0; j < h; ++j)
+            y[i * h + j] = oracle_f32_to_bf16(ldexpf(oracle_e4m3_to_f32(q[i * h + j]),
+                                                     (int)scale[i * B + j / MX_BLOCK] - 127));
 }
 
 void oracle_identity_expert_dequant(const int8_t *q, const float *scale, long long rows, int h,

@@ -666,6 +666,72 @@ def test_group_quantiser_properties():
 
 
 # --------------------------------------------------------------------------
+# quantMode 4 ("mx" dynamic quantisation, reading: OCP MXFP8, E4M3 elements,
+# blocks of 32, one E8M0 scale byte per block)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_mx_quantiser_against_frexp_and_torch_e4m3(dtype):
+    """Per block of 32 (the last one ragged): byte = clip(e - 1 - 8, -127, 127) + 127 with e from numpy's
+    frexp of the block max (0 for an all-zero block); codes equal torch's float8_e4m3fn cast of
+    clip(x * 2^-shared, -448, 448); the block max lands in [256, 448] after scaling; -0 keeps its sign."""
+    import torch
+
+    h = 32 * 5 + 8
+    rng = np.random.default_rng(8)
+    g = rng.standard_normal((8, h)) * 2.0 ** rng.integers(-30, 30, size=(8, 1))
+    g[2, 32:64] = 0.0                                    # an all-zero block
+    g[3, 7] = -0.0
+    g[5, 160:] *= 2.0 ** -12                             # a ragged block far below the others
+    if dtype == "fp16":
+        g = np.clip(g, -60000, 60000)
+        x = g.astype(np.float16)
+        xf = x.astype(np.float32)
+    else:
+        x = wl.f32_to_bf16_bits(g.astype(np.float32))
+        xf = (x.astype(np.uint32) << 16).view(np.float32)
+    ids = np.arange(8, dtype=np.int32)[:, None] % 2
+    d = oracle.dispatch(x, ids, 2, 1, quant_mode=4, bf16=dtype == "bf16")
+    B = (h + 31) // 32
+    assert d["expand_x"].dtype == np.uint8 and d["dynamic_scales"].dtype == np.uint8
+    assert d["dynamic_scales"].shape == (8, B)
+    row_of = {tuple(a): i for i, a in enumerate(d["assist_info"].tolist())}
+    dec = torch.from_numpy(np.arange(256, dtype=np.uint8)).view(torch.float8_e4m3fn).float().numpy()
+    for t in range(8):
+        i = row_of[(t // 4, t % 4, 0)]
+        q, sb = d["expand_x"][i], d["dynamic_scales"][i]
+        for b in range(B):
+            seg = slice(32 * b, min(h, 32 * b + 32))
+            amax = np.abs(xf[t, seg]).max()
+            shared = -127 if amax == 0 else int(np.clip(np.frexp(np.float64(amax))[1] - 1 - 8, -127, 127))
+            assert sb[b] == shared + 127, (t, b)
+            n = np.clip(xf[t, seg].astype(np.float64) * 2.0 ** -shared, -448, 448).astype(np.float32)
+            want = torch.from_numpy(n).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+            assert (q[seg] == want).all(), (t, b)
+            if amax > 0:
+                assert 256 <= np.abs(dec[q[seg]]).max() <= 448
+    assert d["expand_x"][row_of[(0, 3, 0)], 7] == 0x80
+    assert (d["dynamic_scales"][row_of[(0, 2, 0)], 1] == 0)
+
+
+def test_mx_identity_expert_matches_torch():
+    """bf16(e4m3(q) * 2^(byte - 127)) per 32-element block, against torch's float8_e4m3fn decoding, fp32
+    multiply by a power of two and round-to-nearest-even bfloat16 cast."""
+    import torch
+
+    rng = np.random.default_rng(43)
+    rows, h = 29, 200
+    codes = rng.integers(0, 256, size=(rows, h)).astype(np.uint8)
+    codes[(codes & 0x7f) == 0x7f] = 0                  # the NaN codes are not produced by the quantiser
+    sb = rng.integers(0, 247, size=(rows, (h + 31) // 32)).astype(np.uint8)
+    got = oracle.identity_expert(codes, sb)
+    dec = torch.from_numpy(codes).view(torch.float8_e4m3fn).float()
+    full = torch.exp2(torch.from_numpy(sb.astype(np.float32) - 127.0)).repeat_interleave(32, dim=1)[:, :h]
+    want = (dec * full).bfloat16().view(torch.int16).numpy()
+    assert got.view(np.int16).tobytes() == want.tobytes()
+
+
+# --------------------------------------------------------------------------
 # special experts (aclnnMoeDistributeDispatchV4 参数说明, zeroExpertNum /
 # copyExpertNum: id ranges after the E real experts). Reading: not exchanged;
 # a zero expert adds nothing, a copy expert adds the token itself

@@ -1,11 +1,14 @@
 """Pins of the oracle's arithmetic readings (CPU only).
 
-Three hand-worked fixtures under tests/golden/ fix the readings that decide
+Four hand-worked fixtures under tests/golden/ fix the readings that decide
 single bits of the outputs:
   * quant_int8_quotient.json -- quantMode 2 ("aclnnMoeDistributeDispatchV4",
     参数说明): q = rint(RN32(x / scale)), scale = RN32(max|x| / 127);
   * quant_fp8_quotient.json  -- quantMode 3 (same page): E4M3 of RN32(|x| / scale),
     scale = RN32(group max / 448);
+  * quant_mx_e8m0.json       -- quantMode 4 (same page, "mx"): OCP MXFP8, blocks of 32,
+    E8M0 byte = clamp(floor(log2 block max) - 8, -127, 127) + 127, E4M3 codes
+    of x * 2^-shared;
   * combine_fma_order.json   -- the check formula of the combine_doubleplane
     README (功能说明), summed in fp32 with one fused multiply-add per k, k
     ascending, one rounding to the output type.
@@ -164,6 +167,43 @@ def run_fp8_fixture(dtype):
     return bad
 
 
+def mx_fixture_tokens(dtype):
+    """Dense [tokens, h] float32 inputs of the MX fixture (elements not listed are 0; "-0" is -0.0)."""
+    g = _golden("quant_mx_e8m0.json")
+    rows = []
+    for tok in g[dtype]["x"]:
+        r = np.zeros(g["h"], np.float32)
+        for j, v in tok.items():
+            r[int(j)] = -0.0 if v == "-0" else v
+        rows.append(r)
+    return g, np.stack(rows)
+
+
+def mx_fixture_codes(g, dtype):
+    out = np.zeros((len(g[dtype]["codes"]), g["h"]), np.int64)
+    for t, tok in enumerate(g[dtype]["codes"]):
+        for j, c in tok.items():
+            out[t, int(j)] = c
+    return out
+
+
+def run_mx_fixture(dtype):
+    g, xf = mx_fixture_tokens(dtype)
+    x = to_bits(xf, dtype)
+    ids = np.zeros((xf.shape[0], 1), np.int32)
+    out = oracle.dispatch(x, ids, g["ep_world"], g["experts_per_rank"], quant_mode=4, bf16=dtype == "bf16")
+    want_codes = mx_fixture_codes(g, dtype)
+    bad = []
+    for row, (s, tok, k) in enumerate(out["assist_info"].tolist()):
+        codes = out["expand_x"][row].tolist()
+        if codes != want_codes[tok].tolist():
+            bad.append(("codes of token %d" % tok, codes, want_codes[tok].tolist()))
+        sc = out["dynamic_scales"][row].tolist()
+        if sc != g[dtype]["scales"][tok]:
+            bad.append(("scale bytes of token %d" % tok, sc, g[dtype]["scales"][tok]))
+    return bad
+
+
 def combine_fixture_inputs(dtype):
     g = _golden("combine_fma_order.json")
     d = g[dtype]
@@ -193,6 +233,8 @@ FIXTURES = {
     "int8_bf16": lambda: run_int8_fixture("bf16"),
     "fp8_fp16": lambda: run_fp8_fixture("fp16"),
     "fp8_bf16": lambda: run_fp8_fixture("bf16"),
+    "mx_fp16": lambda: run_mx_fixture("fp16"),
+    "mx_bf16": lambda: run_mx_fixture("bf16"),
     "combine_fp16": lambda: run_combine_fixture("fp16"),
     "combine_bf16": lambda: run_combine_fixture("bf16"),
 }
@@ -241,6 +283,55 @@ def test_fp8_fixture_follows_from_exact_arithmetic(dtype):
         assert codes == g["codes"][t], t
 
 
+def floor_log2(a: Fr) -> int:
+    e = 0
+    while a >= 2:
+        a /= 2
+        e += 1
+    while a < 1:
+        a *= 2
+        e -= 1
+    return e
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_mx_fixture_follows_from_exact_arithmetic(dtype):
+    """Every stored byte and code from the OCP MX definition in exact rationals: per block of 32, the shared
+    exponent floor(log2 max|x|) - 8 clamped to [-127, 127], byte = shared + 127, and the E4M3 rounding of
+    x * 2^-shared clamped to 448, the sign taken from x's sign bit."""
+    g, xf = mx_fixture_tokens(dtype)
+    rn = rn16 if dtype == "fp16" else rnbf16
+    want_codes = mx_fixture_codes(g, dtype)
+    h = g["h"]
+    for t in range(xf.shape[0]):
+        xs = [Fr(float(v)) for v in xf[t]]
+        assert all(rn(v) == v for v in xs), "token %d is not exactly representable" % t
+        bytes_, codes = [], []
+        for b0 in range(0, h, 32):
+            blk = xs[b0:b0 + 32]
+            amax = max(abs(v) for v in blk)
+            shared = -127 if amax == 0 else max(-127, min(127, floor_log2(amax) - 8))
+            bytes_.append(shared + 127)
+            for j, v in enumerate(blk):
+                q = min(abs(v) * Fr(2) ** -shared, Fr(448))
+                c = e4m3_bits(round_binary(q, 3, -6))
+                codes.append(c | (0x80 if np.signbit(xf[t, b0 + j]) else 0))
+        assert bytes_ == g[dtype]["scales"][t], t
+        assert codes == want_codes[t].tolist(), t
+
+
+def test_mx_fixture_covers_its_cases():
+    """The fixture holds what it claims: a clamp at 448, the shared-exponent clamp at -127 (a bf16
+    subnormal block max among them), a byte near the top of the range, an all-zero block and -0 codes."""
+    g, xf = mx_fixture_tokens("bf16")
+    sc = np.asarray(g["bf16"]["scales"])
+    assert (np.abs(xf[0, :32]) * 64 > 448).any()
+    assert sc[2].tolist() == [0, 0] and np.abs(xf[2]).max() > 0
+    assert 0 < np.abs(xf[2, 32:]).max() < 2.0 ** -126
+    assert sc[3, 0] == 246 and (xf[1] == 0).all()
+    assert (mx_fixture_codes(g, "bf16") == 0x80).sum() >= 3
+
+
 @pytest.mark.parametrize("dtype", ["fp16", "bf16"])
 def test_combine_fixture_follows_from_exact_arithmetic(dtype):
     g, d, ids, W, epr, rows, w, assist, erc = combine_fixture_inputs(dtype)
@@ -275,6 +366,22 @@ MUTATIONS = {
     "int8_ties_away": ("rintf(v / scale)", "roundf(v / scale)"),
     # quantMode 3: multiply by the reciprocal of the group scale
     "fp8_reciprocal": ("float n = v / gs;", "float n = v * (1.0f / gs);"),
+    # quantMode 4: the frexp exponent taken as floor(log2) (one too high: a ceiling for non-powers of two)
+    "mx_ceil_exponent": ("shared = (e2 - 1) - 8;", "shared = e2 - 8;"),
+    # quantMode 4: no clamp of the scaled value to 448
+    "mx_no_448_clamp": ("        if (n > 448.0) n = 448.0;\n                        if (n < -448.0) n = -448.0;\n",
+                        ""),
+    # quantMode 4: no lower clamp of the shared exponent
+    "mx_no_low_clamp": ("if (shared < -127) shared = -127;", ""),
+    # quantMode 4: E8M0 bias off by one
+    "mx_bias_128": ("sb[b] = (uint8_t)(shared + 127);", "sb[b] = (uint8_t)(shared + 128);"),
+    # quantMode 4: blocks of 64 instead of 32
+    "mx_block_64": ("enum { MX_BLOCK = 32 };", "enum { MX_BLOCK = 64 };"),
+    # quantMode 4: E4M3's largest exponent taken as 7 (the exponent of 240, not of 448)
+    "mx_emax_7": ("shared = (e2 - 1) - 8;", "shared = (e2 - 1) - 7;"),
+    # quantMode 4: the block scale applied the wrong way round
+    "mx_scale_inverted": ("ldexp((double)load_f32(x, (size_t)(t * h + j), dtype), -shared)",
+                          "ldexp((double)load_f32(x, (size_t)(t * h + j), dtype), shared)"),
     # combine: round each product before adding it
     "combine_mul_then_add": ("acc = fmaf(load_f32(expand_x, (size_t)slot[t * K + k] * h + j, dtype), sc, acc);",
                              "acc = load_f32(expand_x, (size_t)slot[t * K + k] * h + j, dtype) * sc + acc;"),
