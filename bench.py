@@ -77,7 +77,10 @@ def algorithmic_bytes(w: wl.Workload, inp=None):
     n_scales = {2: rows, 3: rows * ((h + 127) // 128)}.get(w.quant_mode, 0)   # fp32 dynamic scales
     if w.quant_mode == 1:                         # fp32 static coefficients, read
         n_scales = {"scalar": 1, "column": h, "expert": w.num_experts * h}[w.static_scales]
-    disp = toks * h * sx + N * K * 4 + mask_b + rows * h * s_exp + rows * 12 + erc + n_scales * 4
+    scale_b = n_scales * 4
+    if w.quant_mode == 4:                         # one E8M0 byte per 32-element block
+        scale_b = rows * ((h + 31) // 32)
+    disp = toks * h * sx + N * K * 4 + mask_b + rows * h * s_exp + rows * 12 + erc + scale_b
     consts = w.const_experts * h * s_y           # the const experts' outputs, read once
     comb = (rows * h * s_y + copies * h * s_y + consts + N * K * 4 + mask_b + rows * 12 + erc + N * K * 4
             + N * h * s_y)
@@ -129,7 +132,7 @@ class StepEvents:
 
 
 QUANT_LABELS = {1: "static int8, one coefficient per %s", 2: "per-token dynamic int8",
-                3: "per-group (128) dynamic fp8 e4m3"}
+                3: "per-group (128) dynamic fp8 e4m3", 4: "mx: e4m3 codes, one e8m0 scale byte per 32"}
 
 
 def quant_label(w):
@@ -164,6 +167,11 @@ def measure(w, steps, warmup, flush, torch, moe, schedule=None):
         sc_full = buf.dynamic_scales.repeat_interleave(128, dim=1)[:, :w.h]
         y = (buf.expand_x.float() * sc_full).to(torch.bfloat16)
         del sc_full
+    elif w.quant_mode == 4:                    # 2^(byte - 127) per 32-element block, from its bits
+        b = buf.dynamic_scales.to(torch.int32)
+        s32 = torch.where(b > 0, (b << 23).view(torch.float32), torch.full(b.shape, 2.0 ** -127, device="cuda"))
+        y = (buf.expand_x.float() * s32.repeat_interleave(32, dim=1)[:, :w.h]).to(torch.bfloat16)
+        del b, s32
     else:
         y = buf.expand_x                       # identity expert: combine reads dispatch's rows
     x_out = torch.empty((w.num_tokens, w.h), dtype=y.dtype, device="cuda")
@@ -393,7 +401,7 @@ def main():
     ap.add_argument("--h", type=int, default=None,
                     help="hidden size for the main workload (same seed and recipe; default: the workload's)")
     ap.add_argument("--also", default="w8_h7168_fp16_uniform,w8_h7168_fp16_zipf,w16_h7168_bf16_fp8g128,"
-                                      "w16_h7168_bf16_static_q8,w16_h7168_bf16_q8_pair_mask,"
+                                      "w16_h7168_bf16_mxfp8,w16_h7168_bf16_static_q8,w16_h7168_bf16_q8_pair_mask,"
                                       "w16_h7168_bf16_q8_special",
                     help="comma-separated extra workloads reported under 'also' ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -431,7 +439,7 @@ def main():
     if args.h is not None and args.h != w.h:
         w = dataclasses.replace(w, h=args.h, name="%s_h%d" % (w.name, args.h))
     sched = None
-    if args.schedule == "segment" and w.quant_mode in (1, 3):
+    if args.schedule == "segment" and w.quant_mode in (1, 3, 4):
         print("the segment schedule takes copies and per-token int8 only", file=sys.stderr)
         sys.exit(2)
     if args.schedule != "adaptive" or args.large_bytes >= 0:

@@ -26,7 +26,7 @@ MOE_OK = 0
 (MOE_ERR_NULLPTR, MOE_ERR_SHAPE, MOE_ERR_DTYPE, MOE_ERR_QUANT, MOE_ERR_WORKSPACE, MOE_ERR_LAUNCH, MOE_ERR_SCHEDULE,
  MOE_ERR_ALIGN, MOE_ERR_MASK) = range(1, 10)
 MOE_INT32, MOE_FP16, MOE_BF16 = 0, 1, 2
-MOE_QUANT_NONE, MOE_QUANT_STATIC, MOE_QUANT_DYN_TOKEN, MOE_QUANT_DYN_GROUP = 0, 1, 2, 3
+MOE_QUANT_NONE, MOE_QUANT_STATIC, MOE_QUANT_DYN_TOKEN, MOE_QUANT_DYN_GROUP, MOE_QUANT_MX = 0, 1, 2, 3, 4
 MOE_SCHED_TOKEN, MOE_SCHED_SEGMENT, MOE_SCHED_ADAPTIVE = 0, 1, 2
 MOE_MASK_NONE, MOE_MASK_TOKEN, MOE_MASK_PAIR = 0, 1, 2
 
@@ -183,6 +183,12 @@ def combine_workspace_size(ep_world, bs, experts_per_rank, h, topk, dtype) -> in
     return n.value
 
 
+def _out_dtype(quant_mode, dtype):
+    """expand_x's element type: int8 codes (quantMode 1, 2), E4M3 codes (3, 4), else the token dtype."""
+    return {MOE_QUANT_STATIC: torch.int8, MOE_QUANT_DYN_TOKEN: torch.int8, MOE_QUANT_DYN_GROUP: torch.float8_e4m3fn,
+            MOE_QUANT_MX: torch.float8_e4m3fn}.get(quant_mode, dtype)
+
+
 class DispatchBuffers:
     """Preallocated outputs + workspace for repeated dispatch calls of one shape."""
 
@@ -191,13 +197,13 @@ class DispatchBuffers:
         rows = ep_world * bs * topk
         self.shape = (ep_world, bs, experts_per_rank, h, topk)
         self.dtype, self.quant_mode = dtype, quant_mode
-        out_dt = {MOE_QUANT_STATIC: torch.int8, MOE_QUANT_DYN_TOKEN: torch.int8,
-                  MOE_QUANT_DYN_GROUP: torch.float8_e4m3fn}.get(quant_mode, dtype)
-        self.expand_x = torch.empty((rows, h), dtype=out_dt, device=device)
+        self.expand_x = torch.empty((rows, h), dtype=_out_dtype(quant_mode, dtype), device=device)
         if quant_mode == MOE_QUANT_DYN_TOKEN:
             self.dynamic_scales = torch.empty((rows,), dtype=torch.float32, device=device)
         elif quant_mode == MOE_QUANT_DYN_GROUP:          # one scale per 128-element group
             self.dynamic_scales = torch.empty((rows, (h + 127) // 128), dtype=torch.float32, device=device)
+        elif quant_mode == MOE_QUANT_MX:                 # one E8M0 byte per 32-element block
+            self.dynamic_scales = torch.empty((rows, (h + 31) // 32), dtype=torch.uint8, device=device)
         else:
             self.dynamic_scales = None
         self.assist_info = torch.empty((rows, 3), dtype=torch.int32, device=device)
@@ -219,13 +225,13 @@ class DispatchBuffers:
         W, bs, epr, h, K = self.shape
         rows = W * bs * K
         dev = _gpu_device("expand_x", self.expand_x)
-        out_dt = {MOE_QUANT_STATIC: torch.int8, MOE_QUANT_DYN_TOKEN: torch.int8,
-                  MOE_QUANT_DYN_GROUP: torch.float8_e4m3fn}.get(self.quant_mode, self.dtype)
-        _check_tensor("expand_x", self.expand_x, out_dt, (rows, h), dev)
+        _check_tensor("expand_x", self.expand_x, _out_dtype(self.quant_mode, self.dtype), (rows, h), dev)
         if self.quant_mode == MOE_QUANT_DYN_TOKEN:
             _check_tensor("dynamic_scales", self.dynamic_scales, torch.float32, (rows,), dev)
         elif self.quant_mode == MOE_QUANT_DYN_GROUP:
             _check_tensor("dynamic_scales", self.dynamic_scales, torch.float32, (rows, (h + 127) // 128), dev)
+        elif self.quant_mode == MOE_QUANT_MX:
+            _check_tensor("dynamic_scales", self.dynamic_scales, torch.uint8, (rows, (h + 31) // 32), dev)
         _check_tensor("assist_info", self.assist_info, torch.int32, (rows, 3), dev)
         _check_tensor("ep_recv_count", self.ep_recv_count, torch.int32, (W, epr * W), dev)
         if self.expand_scales is not None:
@@ -318,7 +324,10 @@ def dispatch(x: torch.Tensor, expert_ids: torch.Tensor, ep_world: int, experts_p
     experts (ids E.. for zero_experts, then copy_experts, then const_experts), whose
     pairs get no row.
     quant_mode 1 (static int8) takes its coefficients in quant_scales (fp32, 1, h or
-    E*h values) and returns no dynamic scales.
+    E*h values) and returns no dynamic scales. quant_mode 3 returns float8_e4m3fn
+    codes and fp32 scales per 128-element group; quant_mode 4 (MXFP8) returns
+    float8_e4m3fn codes and uint8 E8M0 bytes per 32-element block (the scale
+    2^(byte - 127)).
     """
     dev = _gpu_device("x", x)
     _gpu_device("expert_ids", expert_ids)

@@ -1153,12 +1153,99 @@ __device__ __forceinline__ void quant_store_wave_fp8(const DispatchArgs &a, int 
     }
 }
 
-// The quantising scatter (aclnnMoeDistributeDispatchV4 quantMode 1, 2 and 3),
+// ---- quantMode 4: MX (OCP Microscaling v1.0), E4M3 elements, blocks of 32 ----
+// 8 elements -> 8 E4M3 bytes. mult = 2^-shared is a power of two, so |x| * mult
+// is exact (or, below 2^-126, rounds to a value whose E4M3 code is 0 anyway);
+// it is clamped to 448 and converted with x's sign by v_cvt_pk_fp8_f32, the
+// conversion checked for every binary32 |v| <= 448 (see fp8_u4).
+template <class T>
+__device__ __forceinline__ uint2 mx_u4(uint4 v, float mult)
+{
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float c[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint16_t bits = (uint16_t)(w[i >> 1] >> ((i & 1) * 16));
+        const float q = fabsf(T::load(bits)) * mult;
+        c[i] = __uint_as_float(__float_as_uint(fminf(q, 448.0f)) | ((uint32_t)(bits & 0x8000u) << 16));
+    }
+    uint32_t o[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        int p = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * h], c[4 * h + 1], 0, false);
+        p = __builtin_amdgcn_cvt_pk_fp8_f32(c[4 * h + 2], c[4 * h + 3], p, true);
+        o[h] = (uint32_t)p;
+    }
+    return make_uint2(o[0], o[1]);
+}
+
+// A block of 32 elements is two neighbouring lanes of one chunk (16 elements
+// each), so its max is one xor shuffle. The shared exponent floor(log2 max) - 8,
+// clamped below at -127, is the max's binary32 exponent field minus 8 (at least
+// 0), which is also the E8M0 byte: a subnormal or zero max has field 0, and a
+// 16-bit token's max keeps the byte at or below 246, so 2^(127 - byte) is a
+// normal binary32 number. The row's bytes leave as 4-byte words: lane r*8 of
+// chunk j packs blocks 32j + 4r .. + 3 with three shuffles, and lane g of the
+// store loop takes word g (one 224-byte store per row at h = 7168); rows whose
+// byte count is not a multiple of 4 take byte stores instead.
+template <class T, int J>
+__device__ __forceinline__ void quant_store_wave_mx(const DispatchArgs &a, int lane, const uint4 (&v)[J][2],
+                                                    int my_row)
+{
+    const int K = a.K, noc = a.h / 16, B = (a.h + 31) / 32, G4 = (B + 3) / 4;
+    uint8_t *sbytes = reinterpret_cast<uint8_t *>(a.dyn);
+    uint32_t dw[J];
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int c = lane + 64 * j;
+        const bool live = c < noc;
+        float amax = live ? fmaxf(amax_u4<T>(v[j][0]), amax_u4<T>(v[j][1])) : 0.0f;
+        amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+        const uint32_t byte = (uint32_t)max((int)(__float_as_uint(amax) >> 23) - 8, 0);
+        const float mult = __uint_as_float((254u - byte) << 23);
+        dw[j] = byte | ((uint32_t)__shfl_down((int)byte, 2, 64) << 8) |
+                ((uint32_t)__shfl_down((int)byte, 4, 64) << 16) | ((uint32_t)__shfl_down((int)byte, 6, 64) << 24);
+        if (!live) continue;
+        const uint2 lo = mx_u4<T>(v[j][0], mult), hi = mx_u4<T>(v[j][1], mult);
+        const uint4 q = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        for (int k = 0; k < K; ++k) {
+            const int row = __builtin_amdgcn_readlane(my_row, k);
+            if (row < 0) continue;
+            uint4 *dst = reinterpret_cast<uint4 *>(a.expand_x + (size_t)row * a.h) + c;
+            if (stream_piece(a, j, k)) store_stream(dst, q);   // see store_stream
+            else *dst = q;
+        }
+    }
+    const bool words = (B & 3) == 0 && (reinterpret_cast<uintptr_t>(sbytes) & 3) == 0;
+    for (int g0 = 0; g0 < G4; g0 += 64) {
+        const int g = g0 + lane;
+        uint32_t word = 0;
+#pragma unroll
+        for (int j = 0; j < J; ++j) {
+            const uint32_t wj = (uint32_t)__shfl((int)dw[j], (g & 7) << 3, 64);
+            if ((g >> 3) == j) word = wj;
+        }
+        if (g >= G4) continue;
+        for (int k = 0; k < K; ++k) {
+            const int row = __builtin_amdgcn_readlane(my_row, k);
+            if (row < 0) continue;
+            uint8_t *dst = sbytes + (size_t)row * B + 4 * g;
+            if (words) {
+                *reinterpret_cast<uint32_t *>(dst) = word;
+            } else {
+                for (int i = 0; i < 4; ++i)
+                    if (4 * g + i < B) dst[i] = (uint8_t)(word >> (8 * i));
+            }
+        }
+    }
+}
+
+// The quantising scatter (aclnnMoeDistributeDispatchV4 quantMode 1, 2, 3 and 4),
 // one wavefront per token. QM 1: the static codes above (one coefficient or one
 // per column; per-expert coefficients take the source-group kernel below); QM 2:
 // scale = max|x| / 127 over the token (fp32, correctly rounded),
 // q = rint(x / scale) (0 for an all-zero token); QM 3: the per-group FP8 codes
-// above. Codes go to every destination row. Lane k loads pair k's id and
+// above; QM 4: the MX codes and scale bytes above. Codes go to every destination row. Lane k loads pair k's id and
 // in-chunk rank before the row's 16-byte loads, so both are in flight together;
 // rows reach the store loop through readlane. No LDS, no barrier. Needs
 // h % 16 == 0, h <= 1024 * J, topk <= kQuantMaxK.
@@ -1187,6 +1274,7 @@ __global__ __launch_bounds__(kQuantThreads) void scatter_quant_wave_kernel(Dispa
         __builtin_amdgcn_sched_barrier(0);
         const int my_row = lane_pair_row<SKIP>(a, t, lane, e, l, true);
         if constexpr (QM == MOE_QUANT_DYN_GROUP) quant_store_wave_fp8<T, J>(a, lane, v, my_row);
+        else if constexpr (QM == MOE_QUANT_MX) quant_store_wave_mx<T, J>(a, lane, v, my_row);
         else if constexpr (QM == MOE_QUANT_STATIC) quant_store_wave_static<T, J>(a, lane, v, my_row);
         else quant_store_wave<T, J>(a, lane, v, my_row);
     }
@@ -2362,10 +2450,10 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
     if (!bytes) return MOE_ERR_NULLPTR;
     int rc = check_scalars(ep_world, bs, experts_per_rank, h, topk, dtype);
     if (rc) return rc;
-    if (quant_mode < MOE_QUANT_NONE || quant_mode > MOE_QUANT_DYN_GROUP) return MOE_ERR_QUANT;
+    if (quant_mode < MOE_QUANT_NONE || quant_mode > MOE_QUANT_MX) return MOE_ERR_QUANT;
     if (quant_mode != MOE_QUANT_NONE && dtype == MOE_INT32) return MOE_ERR_QUANT;
-    // the static and per-group quantisers are the wavefront-per-token kernel only
-    if ((quant_mode == MOE_QUANT_STATIC || quant_mode == MOE_QUANT_DYN_GROUP) &&
+    // the static, per-group and MX quantisers are the wavefront-per-token kernel only
+    if ((quant_mode == MOE_QUANT_STATIC || quant_mode == MOE_QUANT_DYN_GROUP || quant_mode == MOE_QUANT_MX) &&
         (h % 16 != 0 || h > kQuantMaxH || topk > kQuantMaxK))
         return MOE_ERR_QUANT;
     *bytes = dispatch_layout(ep_world, bs, experts_per_rank, topk).total;
@@ -2375,7 +2463,7 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
 int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_scales,
                  const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
                  int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype, int quant_mode,
-                 const float *quant_scales, int64_t quant_scales_numel, void *expand_x, float *dynamic_scales,
+                 const float *quant_scales, int64_t quant_scales_numel, void *expand_x, void *dynamic_scales,
                  int32_t *assist_info, int32_t *ep_recv_count, void *expand_scales,
                  const moe_schedule *schedule, void *workspace, size_t workspace_bytes, void *stream)
 {
@@ -2387,6 +2475,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     const bool quant = quant_mode != MOE_QUANT_NONE;
     const bool group_quant = quant_mode == MOE_QUANT_DYN_GROUP;
     const bool static_quant = quant_mode == MOE_QUANT_STATIC;
+    const bool mx_quant = quant_mode == MOE_QUANT_MX;
     const bool dyn_quant = quant && !static_quant;       // writes dynamic_scales
     if (!ep_recv_count || !workspace) return MOE_ERR_NULLPTR;
     if (N > 0 && (!x || !expert_ids || !expand_x || !assist_info)) return MOE_ERR_NULLPTR;
@@ -2427,19 +2516,19 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                           (long long)bs * h * elem_out >= large;
     const bool want_seg = mode == MOE_SCHED_SEGMENT || seg_flags;
     if (want_seg && (long long)W * S > kSegLdsMax) return MOE_ERR_SCHEDULE;
-    if ((group_quant || static_quant) && mode == MOE_SCHED_SEGMENT) return MOE_ERR_SCHEDULE;
+    if ((group_quant || static_quant || mx_quant) && mode == MOE_SCHED_SEGMENT) return MOE_ERR_SCHEDULE;
 
     const size_t rowbytes = (size_t)h * xs;
     if (!aligned(x, xs) || !aligned(expert_ids, 4) || !aligned(expert_scales, 4) ||
-        !aligned(expand_x, quant ? 1 : xs) || !aligned(dynamic_scales, 4) || !aligned(assist_info, 4) ||
+        !aligned(expand_x, quant ? 1 : xs) || !aligned(dynamic_scales, mx_quant ? 1 : 4) || !aligned(assist_info, 4) ||
         !aligned(ep_recv_count, 4) || !aligned(expand_scales, 4) || !aligned(workspace, 16) ||
         !aligned(seg_flags, 4) || !aligned(quant_scales, qkind == kStaticOne ? 4 : 16))
         return MOE_ERR_ALIGN;
     // per-token int8 takes the wavefront kernel when it can, a block kernel
-    // otherwise; per-group FP8 needs the wavefront kernel's 16-byte rows
+    // otherwise; per-group FP8 and MX need the wavefront kernel's 16-byte rows
     const bool wave = quant && h % 16 == 0 && h <= kQuantMaxH && K <= kQuantMaxK && aligned(x, 16) &&
                       aligned(expand_x, 16);
-    if ((group_quant || static_quant) && !wave && N > 0) return MOE_ERR_ALIGN;
+    if ((group_quant || static_quant || mx_quant) && !wave && N > 0) return MOE_ERR_ALIGN;
 
     const DispatchLayout L = dispatch_layout(W, bs, epr, K);
     char *ws = static_cast<char *>(workspace);
@@ -2460,7 +2549,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
     a.ids = expert_ids;
     a.esc_in = static_cast<const int32_t *>(expert_scales);
     a.expand_x = static_cast<char *>(expand_x);
-    a.dyn = dynamic_scales;
+    a.dyn = static_cast<float *>(dynamic_scales);     // uint8 scale bytes for MX
     a.assist = assist_info;
     a.esc_out = static_cast<int32_t *>(expand_scales);
     a.erc = ep_recv_count;
@@ -2636,11 +2725,13 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                         }
                     } else if (dtype == MOE_FP16) {
                         if (group_quant) launch_quant_wave<F16, MOE_QUANT_DYN_GROUP>(J, g, b, st, a);
+                        else if (mx_quant) launch_quant_wave<F16, MOE_QUANT_MX>(J, g, b, st, a);
                         else if (static_quant) launch_quant_wave<F16, MOE_QUANT_STATIC>(J, g, b, st, a);
                         else if (adaptive) launch_quant_wave<F16, MOE_QUANT_DYN_TOKEN, true>(J, g, b, st, a);
                         else launch_quant_wave<F16, MOE_QUANT_DYN_TOKEN>(J, g, b, st, a);
                     } else {
                         if (group_quant) launch_quant_wave<BF16, MOE_QUANT_DYN_GROUP>(J, g, b, st, a);
+                        else if (mx_quant) launch_quant_wave<BF16, MOE_QUANT_MX>(J, g, b, st, a);
                         else if (static_quant) launch_quant_wave<BF16, MOE_QUANT_STATIC>(J, g, b, st, a);
                         else if (adaptive) launch_quant_wave<BF16, MOE_QUANT_DYN_TOKEN, true>(J, g, b, st, a);
                         else launch_quant_wave<BF16, MOE_QUANT_DYN_TOKEN>(J, g, b, st, a);
@@ -2679,7 +2770,7 @@ int moe_dispatch_noalloc(const void *x, const int32_t *expert_ids, const void *e
                          const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
                          int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype, int quant_mode,
                          const float *quant_scales, int64_t quant_scales_numel, void *expand_x,
-                         float *dynamic_scales, int32_t *assist_info, int32_t *ep_recv_count, void *expand_scales,
+                         void *dynamic_scales, int32_t *assist_info, int32_t *ep_recv_count, void *expand_scales,
                          const moe_schedule *schedule, void *stream)
 {
     size_t need = 0;

@@ -70,7 +70,7 @@ enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
 
 /* Quantisation modes; the numbering follows quantMode of
  * aclnnMoeDistributeDispatchV4 (0 = none, 1 = static, 2 = per-token dynamic,
- * 3 = per-group dynamic).
+ * 3 = per-group dynamic, 4 = mx).
  *  MOE_QUANT_STATIC: int8 codes rint(x * c) of the exact product, ties to
  *      even, saturated to [-128, 127] (a NaN product gives -128). c
  *      comes from quant_scales (fp32, caller-owned device memory): one value,
@@ -93,8 +93,21 @@ enum moe_dtype { MOE_INT32 = 0, MOE_FP16 = 1, MOE_BF16 = 2 };
  *      size are garbled, and these are the readings taken.) Needs h % 16 == 0,
  *      h <= 16384, topk <= 64, 16-byte aligned x and expand_x, and a
  *      token-major schedule (not MOE_SCHED_SEGMENT; the adaptive one runs
- *      this mode token-major). */
-enum moe_quant { MOE_QUANT_NONE = 0, MOE_QUANT_STATIC = 1, MOE_QUANT_DYN_TOKEN = 2, MOE_QUANT_DYN_GROUP = 3 };
+ *      this mode token-major).
+ *  MOE_QUANT_MX: the OCP Microscaling (MX v1.0) format with E4M3 elements
+ *      (MXFP8), per block of 32 elements of h (the last block may be shorter):
+ *      shared = floor(log2 max|x|) - 8 over the block, clamped to [-127, 127]
+ *      (-127 for an all-zero block); code = E4M3 nearest to x * 2^-shared
+ *      clamped to +-448, ties to even, sign of x kept (-0 gives 0x80).
+ *      dynamic_scales is uint8 [ROWS, ceil(h/32)], one E8M0 byte shared + 127
+ *      per block (the scale 2^(byte - 127)); any alignment. (The page lists mx
+ *      quantisation with four output types, no scale input and a garbled
+ *      scale shape; E4M3 elements are the reading taken, and the other three
+ *      types are not provided.) Inputs must be finite. Same limits as
+ *      MOE_QUANT_DYN_GROUP. */
+enum moe_quant {
+    MOE_QUANT_NONE = 0, MOE_QUANT_STATIC = 1, MOE_QUANT_DYN_TOKEN = 2, MOE_QUANT_DYN_GROUP = 3, MOE_QUANT_MX = 4
+};
 
 /* Token masks: xActiveMaskOptional of aclnnMoeDistributeDispatchV4 (参数说明):
  * a 1D mask (BS,) per rank or a 2D mask (BS, K); a token whose K entries are
@@ -202,12 +215,13 @@ int moe_dispatch_workspace_size(int ep_world, int bs, int experts_per_rank, int 
  *                                        ranges are legal and produce no row
  *  quant_scales   fp32 [quant_scales_numel]  quant_mode 1 only (NULL and 0 otherwise):
  *                                        1, h or E*h coefficients, see MOE_QUANT_STATIC
- *  expand_x       [ROWS, h]              dtype; int8 when quant_mode is 1 or 2, E4M3 bytes when 3. Row order:
+ *  expand_x       [ROWS, h]              dtype; int8 when quant_mode is 1 or 2, E4M3 bytes when 3 or 4. Row order:
  *                                        rank r, then local expert, then source rank,
  *                                        then ascending source token
- *  dynamic_scales [ROWS] fp32            per-row token scale max|x|/127 (quant_mode 2), or
- *                 [ROWS, ceil(h/128)]    per-group scales max|x|/448 (quant_mode 3);
- *                                        required for quant_mode 2 and 3, NULL otherwise
+ *  dynamic_scales [ROWS] fp32            per-row token scale max|x|/127 (quant_mode 2),
+ *                 [ROWS, ceil(h/128)]    per-group fp32 scales max|x|/448 (quant_mode 3), or
+ *                 [ROWS, ceil(h/32)]     uint8 E8M0 block scale bytes (quant_mode 4);
+ *                                        required for quant_mode 2, 3 and 4, NULL otherwise
  *  assist_info    [ROWS, 3] int32        (src_rank, src_token, topk_id) of each row
  *  ep_recv_count  [W, S] int32           per rank, inclusive prefix of the row counts of
  *                                        its segments ordered el*W + s
@@ -231,7 +245,7 @@ int moe_dispatch(const void *x, const int32_t *expert_ids, const void *expert_sc
                  const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
                  int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype,
                  int quant_mode, const float *quant_scales, int64_t quant_scales_numel,
-                 void *expand_x, float *dynamic_scales, int32_t *assist_info,
+                 void *expand_x, void *dynamic_scales, int32_t *assist_info,
                  int32_t *ep_recv_count, void *expand_scales, const moe_schedule *schedule,
                  void *workspace, size_t workspace_bytes, void *stream);
 
@@ -258,7 +272,7 @@ int moe_dispatch_noalloc(const void *x, const int32_t *expert_ids, const void *e
                          const uint8_t *x_active_mask, int mask_kind, const moe_special_experts *special,
                          int ep_world, int bs, int experts_per_rank, int h, int topk, int dtype,
                          int quant_mode, const float *quant_scales, int64_t quant_scales_numel,
-                         void *expand_x, float *dynamic_scales, int32_t *assist_info,
+                         void *expand_x, void *dynamic_scales, int32_t *assist_info,
                          int32_t *ep_recv_count, void *expand_scales, const moe_schedule *schedule,
                          void *stream);
 

@@ -79,7 +79,13 @@ def _ws(*args):
     ((2, 4, 2, 16400, 1, 2, 3), QUANT),       # ... and h <= 16384
     ((2, 4, 2, 16384, 1, 2, 3), OK),
     ((8, 4, 16, 64, 65, 2, 3), QUANT),        # ... and topk <= 64
-    ((2, 4, 2, 16, 1, 1, 4), QUANT),
+    ((2, 4, 2, 16, 1, 1, 4), OK),             # MX (MXFP8)
+    ((16, 256, 16, 7168, 8, 2, 4), OK),
+    ((2, 4, 2, 16, 1, 0, 4), QUANT),          # int32 cannot be quantised
+    ((2, 4, 2, 7176, 1, 2, 4), QUANT),        # MX needs h % 16 == 0
+    ((2, 4, 2, 16400, 1, 2, 4), QUANT),       # ... and h <= 16384
+    ((8, 4, 16, 64, 65, 2, 4), QUANT),        # ... and topk <= 64
+    ((2, 4, 2, 16, 1, 1, 5), QUANT),
 ])
 def test_dispatch_workspace_query(args, want):
     rc, n = _ws(*args)
@@ -126,7 +132,11 @@ def _dispatch(**kw):
     (dict(W=1), SHAPE),
     (dict(K=5), SHAPE),
     (dict(dtype=7), DTYPE),
-    (dict(quant=4), QUANT),
+    (dict(quant=5), QUANT),
+    (dict(quant=4), NULLPTR),                        # MX needs its scale bytes
+    (dict(dtype=0, quant=4, dyn=7 * A), QUANT),
+    (dict(quant=4, dyn=7 * A + 1, sched=moe.MoeSchedule(mode=1)), SCHEDULE),   # MX: token schedule only
+    (dict(quant=4, dyn=7 * A + 1, x=A + 2), ALIGN),                         # MX: 16-byte rows
     (dict(quant=3), NULLPTR),                        # per-group quantising needs dynamic_scales
     (dict(dtype=0, quant=2, dyn=7 * A), QUANT),
     (dict(x=None), NULLPTR),

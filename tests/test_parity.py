@@ -42,10 +42,21 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.numpy()
 
 
+def mx_scale_f32(sb):
+    """2^(byte - 127) as float32, built from its bits (byte 0 is the subnormal 2^-127)."""
+    b = sb.to(torch.int32)
+    normal = (b << 23).view(torch.float32)
+    return torch.where(b > 0, normal, torch.full_like(normal, 2.0 ** -127))
+
+
 def gpu_identity_expert(expand_x, dyn):
-    """bf16(f32(q) * scale): one scale per row (int8), or per 128-element group (E4M3)."""
+    """bf16(f32(q) * scale): one scale per row (int8), per 128-element group (E4M3), or 2^(byte - 127) per
+    32-element block (MX: uint8 scale bytes)."""
     if dyn is None:
         return expand_x
+    if dyn.dtype == torch.uint8:
+        sc = mx_scale_f32(dyn).repeat_interleave(32, dim=1)[:, :expand_x.shape[1]]
+        return (expand_x.float() * sc).to(torch.bfloat16)
     if dyn.dim() == 2:
         sc = dyn.repeat_interleave(128, dim=1)[:, :expand_x.shape[1]]
         return (expand_x.float() * sc).to(torch.bfloat16)
@@ -132,6 +143,9 @@ def assert_parity(w, g, o):
     if w.quant_mode in (2, 3):
         assert (g["dynamic_scales"][:A].view(np.uint32).tobytes()
                 == o["dynamic_scales"][:A].view(np.uint32).tobytes()), "dynamic_scales"
+    if w.quant_mode == 4:
+        assert g["dynamic_scales"].dtype == np.uint8
+        assert g["dynamic_scales"][:A].tobytes() == o["dynamic_scales"][:A].tobytes(), "scale bytes"
     if w.dtype == "int32":
         assert (g["x_out"] == o["x_out"]).all(), "x_out"
     else:
@@ -305,6 +319,113 @@ def test_group_quant_tiny_and_zero_groups(exp):
 
 def test_group_quant_with_a_mask():
     check_masked(wl.custom(4, 96, 2048, 6, 4, "bf16", "zipf_topk", quant_mode=3, name="fp8_masked"), "pair")
+
+
+# --------------------------------------------------------------------------
+# quantMode 4: MX (OCP MXFP8: E4M3 codes, one E8M0 byte per 32-element block)
+# --------------------------------------------------------------------------
+
+MX_QUANT = [
+    wl.BY_NAME["w16_h7168_bf16_mxfp8"],                                                   # 224 bytes a row
+    wl.custom(3, 300, 1040, 4, 3, "fp16", "zipf_topk", quant_mode=4, name="fp16_h1040_ragged_block"),   # 33
+    wl.custom(2, 5, 16, 3, 2, "bf16", "gauss_topk", quant_mode=4, name="h16_one_partial_block"),
+    wl.custom(2, 7, 48, 2, 2, "fp16", "gauss_topk", quant_mode=4, name="h48_two_bytes"),
+    wl.custom(4, 257, 8192, 2, 4, "bf16", "gauss_topk", quant_mode=4, name="h8192_j8_64_words"),
+    wl.custom(65, 2, 256, 2, 4, "fp16", "gauss_topk", quant_mode=4, name="65_chunks_scanned_offsets"),
+    wl.custom(2, 2, 128, 64, 40, "bf16", "gauss_topk", quant_mode=4, name="topk64"),
+    wl.custom(2, 40, 12288, 4, 4, "bf16", "gauss_topk", quant_mode=4, name="h12288_j12_two_word_passes"),
+    wl.custom(2, 40, 16384, 4, 4, "fp16", "zipf_topk", quant_mode=4, name="h16384_j16"),
+    wl.custom(2, 33, 16336, 3, 4, "bf16", "zipf_topk", quant_mode=4, name="h16336_j16_511_bytes"),
+    wl.custom(16, 448, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=4, index=4, name="mx_411MB"),
+]
+
+
+@pytest.mark.parametrize("w", MX_QUANT, ids=lambda w: w.name)
+def test_mx_quant_shapes(w):
+    check(w)
+
+
+def test_mx_quant_tiny_huge_subnormal_and_zero_blocks():
+    """Block maxima that clamp the shared exponent at -127 (2^-125, and bf16 subnormals around 2^-130), a
+    block near the top of bf16's range (byte 246), all-zero blocks (byte 0) and -0 codes; the dispatch outputs
+    bit for bit (the identity expert's products would be subnormal here, so the combine is left out)."""
+    w = wl.custom(2, 8, 512, 2, 2, "bf16", "gauss_topk", quant_mode=4, name="mx_edges")
+    inp = wl.make_inputs(w)
+    rng = np.random.default_rng(29)
+    g = rng.standard_normal((w.num_tokens, w.h)).astype(np.float32)
+    g[:, 32:64] *= np.float32(2.0 ** -125)
+    g[:, 64:96] *= np.float32(2.0 ** -131)               # bf16 subnormals
+    g[:, 96:128] = 0.0
+    g[:, 128:160] = (g[:, 128:160] * np.float32(2.0 ** 124)).astype(np.float32)
+    g[3, 300] = -0.0
+    g[4] = -0.0
+    g[5, 200:232] = -0.0
+    inp["x"] = wl.f32_to_bf16_bits(g)
+    x, ids = to_dev(inp["x"], True), to_dev(inp["ids"])
+    ex, dyn, assist, erc = moe.dispatch(x, ids, w.ep_world, w.experts_per_rank, 4)
+    torch.cuda.synchronize()
+    d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, 4, bf16=True)
+    assert (to_np(erc) == d["ep_recv_count"]).all()
+    assert (to_np(assist) == d["assist_info"]).all()
+    assert to_np(ex).tobytes() == d["expand_x"].tobytes()
+    sb = to_np(dyn)
+    assert sb.tobytes() == d["dynamic_scales"].tobytes()
+    assert (sb[:, 1] == 0).all() and (sb[:, 2] == 0).all() and (sb[:, 3] == 0).all()
+    assert sb[:, 4].max() >= 240 and (to_np(ex) == 0x80).any()
+
+
+def test_mx_quant_with_a_mask_and_special_experts():
+    check_masked(wl.custom(4, 96, 2048, 6, 4, "bf16", "zipf_topk", quant_mode=4, name="mx_masked"), "pair")
+    check(wl.custom(4, 33, 2048, 8, 4, "bf16", "zipf_topk", quant_mode=4, zero_experts=4, copy_experts=8,
+                    const_experts=2, name="mx_special"))
+
+
+def test_mx_scale_bytes_at_any_alignment():
+    """Scale rows of 224 bytes (words) and 33 bytes (bytes), written at an odd address: the bytes are the
+    ones written at an aligned address."""
+    for w in (wl.custom(2, 64, 7168, 4, 4, "bf16", "gauss_topk", quant_mode=4, name="mx_words"),
+              wl.custom(2, 64, 1040, 4, 4, "fp16", "gauss_topk", quant_mode=4, name="mx_bytes")):
+        inp = wl.make_inputs(w)
+        bf = w.dtype == "bf16"
+        x, ids = to_dev(inp["x"], bf), to_dev(inp["ids"])
+        B = (w.h + 31) // 32
+        buf = moe.DispatchBuffers(w.ep_world, w.bs, w.experts_per_rank, w.h, w.topk, x.dtype, 4, DEV)
+        store = torch.zeros(w.rows * B + 1, dtype=torch.uint8, device=DEV)
+        buf.dynamic_scales = store[1:].view(w.rows, B)
+        moe.dispatch_into(buf, x, ids)
+        torch.cuda.synchronize()
+        d = oracle.dispatch(inp["x"], inp["ids"], w.ep_world, w.experts_per_rank, 4, bf16=bf)
+        assert to_np(buf.dynamic_scales).tobytes() == d["dynamic_scales"].tobytes(), w.name
+        assert to_np(buf.expand_x).tobytes() == d["expand_x"].tobytes(), w.name
+        assert int(store[0]) == 0
+
+
+def random_mx_case(i):
+    rng = np.random.default_rng(2900 + i)
+    W = int(rng.choice([2, 3, 4, 8, 16, 65]))
+    bs = int(rng.integers(1, max(2, 2048 // W)))
+    epr = int(rng.integers(1, max(2, min(9, 1024 // W))))
+    K = int(rng.integers(1, min(W * epr, 12) + 1))
+    dtype = str(rng.choice(["fp16", "bf16"]))
+    h = 16 * int(rng.integers(1, 400))
+    routing = str(rng.choice(["gauss_topk", "zipf_topk"]))
+    zero = int(rng.integers(0, 3))
+    copy = 0 if dtype != "bf16" else int(rng.integers(0, 3))
+    kind = str(rng.choice(["none", "token_any", "pair"]))
+    w = wl.custom(W, bs, h, K, epr, dtype, routing, quant_mode=4, zero_experts=zero, copy_experts=copy,
+                  index=2300 + i, name="random_mx%d" % i)
+    return w, kind
+
+
+RANDOM_MX_CASES = [random_mx_case(i) for i in range(12)]
+
+
+@pytest.mark.parametrize("w,kind", RANDOM_MX_CASES, ids=lambda v: v if isinstance(v, str) else v.name)
+def test_random_configurations_mx(w, kind):
+    if kind == "none":
+        check(w)
+    else:
+        check_masked(w, kind)
 
 
 # --------------------------------------------------------------------------
@@ -678,6 +799,8 @@ def check_masked(w, kind, seed=1, schedule=None):
     assert to_np(esc)[:A].view(np.uint32).tobytes() == d["expand_scales"][:A].view(np.uint32).tobytes()
     if w.quant_mode in (2, 3):
         assert to_np(dyn)[:A].view(np.uint32).tobytes() == d["dynamic_scales"][:A].view(np.uint32).tobytes()
+    if w.quant_mode == 4:
+        assert to_np(dyn)[:A].tobytes() == d["dynamic_scales"][:A].tobytes(), "scale bytes"
     g = to_np(xo)
     if w.dtype == "int32":
         assert (g == xo_o).all(), "x_out"

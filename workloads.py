@@ -92,6 +92,8 @@ WORKLOADS = [
 # with per-group FP8 E4M3 quantisation (quantMode 3) instead of per-token int8.
 EXTRA_WORKLOADS = [
     Workload("w16_h7168_bf16_fp8g128", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=3),
+    # and with MX quantisation (quantMode 4: MXFP8, E4M3 codes and one E8M0 byte per 32 elements)
+    Workload("w16_h7168_bf16_mxfp8", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=4),
     # and with static int8 quantisation (quantMode 1), one coefficient per expert and column
     Workload("w16_h7168_bf16_static_q8", 4, 16, 256, 7168, 8, 16, "bf16", "gauss_topk", quant_mode=1),
     # per-token int8 with a per-pair token mask (3/4 of the pairs active)
