@@ -1065,6 +1065,8 @@ GRAPH_CASES = [
     (wl.custom(4, 64, 1024, 8, 4, "bf16", "zipf_topk", quant_mode=2, name="bf16_q8_graph_adaptive_T0"),
      (moe.MOE_SCHED_ADAPTIVE, 0)),
     (wl.custom(4, 64, 1024, 8, 4, "fp16", "zipf_topk", name="fp16_copy_graph_segment_T0"), (moe.MOE_SCHED_SEGMENT, 0)),
+    # MXFP8 codes and scale bytes (h = 1040: 33 bytes a row, byte stores)
+    (wl.custom(4, 64, 1040, 8, 4, "bf16", "gauss_topk", quant_mode=4, name="bf16_mx_graph"), None),
 ]
 
 

@@ -37,6 +37,8 @@ CASES = [
      dict(mode=moe.MOE_SCHED_SEGMENT, large_segment_bytes=0)),
     # smaller still, with a token mask and more than 64 route chunks (the single-block scan)
     (wl.custom(80, 260, 64, 4, 2, "bf16", "gauss_topk", quant_mode=2, name="bf16_scan_path"), "mask"),
+    # MXFP8 (uint8 scale bytes), smaller again
+    (wl.custom(8, 40, 2048, 8, 4, "fp16", "zipf_topk", quant_mode=4, name="fp16_mx"), None),
 ]
 
 
