@@ -1186,8 +1186,9 @@ __device__ __forceinline__ uint2 mx_u4(uint4 v, float mult)
 // 16-bit token's max keeps the byte at or below 246, so 2^(127 - byte) is a
 // normal binary32 number. The row's bytes leave as 4-byte words: lane r*8 of
 // chunk j packs blocks 32j + 4r .. + 3 with three shuffles, and lane g of the
-// store loop takes word g (one 224-byte store per row at h = 7168); rows whose
-// byte count is not a multiple of 4 take byte stores instead.
+// store loop takes word g (one 224-byte store per row at h = 7168); where the
+// row's byte count or the buffer's address is not a multiple of 4, each word
+// leaves as byte stores instead.
 template <class T, int J>
 __device__ __forceinline__ void quant_store_wave_mx(const DispatchArgs &a, int lane, const uint4 (&v)[J][2],
                                                     int my_row)
