@@ -24,9 +24,10 @@
  *    all-to-all expandXOut = AllToAllV(X)); the two-phase call (a workspace
  *    query that validates, then the execution); the aclnnStatus return code;
  *    parameter ranges (epWorldSize in [2, 768], moeExpertNum in (0, 1024],
- *    quantMode 0 or 2 on the A2/A3 parts); 约束说明: deterministic by default,
- *    dispatch outputs are handed to combine unchanged and are opaque to the
- *    caller, and scalar parameters must match between dispatch and combine.
+ *    quantMode 0 or 2 on the A2/A3 parts, 0 to 4 on another part); 约束说明:
+ *    deterministic by default, dispatch outputs are handed to combine
+ *    unchanged and are opaque to the caller, and scalar parameters must match
+ *    between dispatch and combine.
  *  - "双平面 MoE Combine 示例" (CANN SHMEM combine_doubleplane README):
  *    功能说明 (expand_x grouped by expert; assist_info_for_combine rows
  *    [src_rank_id, src_token_id, src_topk_id]; ep_recv_count, the cumulative
