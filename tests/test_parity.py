@@ -599,6 +599,12 @@ def test_empty_batch_writes_zero_counts():
     assert (to_np(buf.ep_recv_count) == 0).all()
     xo = moe.combine(ex, assist, erc, ids, torch.empty((0, K), dtype=torch.float32, device=DEV), W, epr)
     assert xo.shape == (0, h)
+    # and with each quantiser: zero counts, empty codes and scales
+    xb = torch.empty((0, h), dtype=torch.bfloat16, device=DEV)
+    for q in (moe.MOE_QUANT_DYN_TOKEN, moe.MOE_QUANT_DYN_GROUP, moe.MOE_QUANT_MX):
+        ex, dyn, assist, erc = moe.dispatch(xb, ids, W, epr, q)
+        torch.cuda.synchronize()
+        assert ex.shape == (0, h) and dyn.shape[0] == 0 and (to_np(erc) == 0).all(), q
 
 
 # --------------------------------------------------------------------------
