@@ -646,6 +646,20 @@ def test_schedules_are_result_neutral_and_flag_the_right_segments(w, mode, T):
         assert want.sum() == 0     # the README's 2 MiB never fires on the page workloads
 
 
+@pytest.mark.parametrize("q", [1, 3, 4], ids=["static", "fp8_group", "mx"])
+@pytest.mark.parametrize("mode", [moe.MOE_SCHED_TOKEN, moe.MOE_SCHED_ADAPTIVE], ids=["token", "adaptive"])
+def test_token_major_quantisers_report_segment_flags(q, mode):
+    """The quantisers that run token-major only, with segment flags requested: the scan block then forms the
+    offsets (and the flags) in place of the per-pair chunk sums; outputs and flags match the oracle."""
+    w = wl.custom(4, 192, 2048, 4, 2, "bf16", "zipf_topk", quant_mode=q, name="flags_q%d" % q)
+    inp = wl.make_inputs(w)
+    flags = torch.full((w.ep_world, w.experts_per_rank * w.ep_world), -1, dtype=torch.int32, device=DEV)
+    sched = moe.MoeSchedule(mode=mode, large_segment_bytes=4096, segment_is_large=flags.data_ptr())
+    g, o = check(w, inp, sched)
+    want = oracle.large_segments(o["ep_recv_count"], w.ep_world, w.experts_per_rank, w.h, 1, 4096)
+    assert want.sum() > 0 and (to_np(flags) == want.astype(np.int32)).all()
+
+
 ADAPTIVE_FLAG_CASES = [SCHED_CASES[i] for i in (2, 3, 4, 5, 6, 9, 12, 13)]
 
 
