@@ -39,6 +39,9 @@ CASES = [
     (wl.custom(80, 260, 64, 4, 2, "bf16", "gauss_topk", quant_mode=2, name="bf16_scan_path"), "mask"),
     # MXFP8 (uint8 scale bytes), smaller again
     (wl.custom(8, 40, 2048, 8, 4, "fp16", "zipf_topk", quant_mode=4, name="fp16_mx"), None),
+    # the adaptive schedule with its large-segment pass engaged (row flags in the scratch)
+    (wl.custom(4, 64, 1024, 8, 4, "bf16", "zipf_topk", quant_mode=2, name="bf16_adaptive_T0"),
+     dict(mode=moe.MOE_SCHED_ADAPTIVE, large_segment_bytes=0)),
 ]
 
 
